@@ -1,0 +1,246 @@
+"""Pins that tie the fp64 oracle to something other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+closed form, an invariant, a library routine or a brute-force evaluation on a
+tiny input.  ``tests/test_oracle_pins.py`` runs them; ``tests/test_oracle_mutants.py``
+plants plausible mistakes in the oracle (on the CPU) and checks that at least
+one pin fails for every mistake.
+
+The pages print no worked numerical example for these subgraphs, so no pin
+compares against a printed value; the closed-form values used here are
+derived in ``tests/golden/closed_forms.json``.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, rtol, atol=0.0, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = np.abs(a - b)
+    bound = atol + rtol * np.abs(b)
+    assert np.all(err <= bound), f"{what}: max err {err.max():.3e}"
+
+
+# ----------------------------------------------------------------- brute force
+
+def _bf_softmax(rows):
+    """Direct definition exp(x_j) / sum_k exp(x_k), pure Python, no max shift."""
+    out = []
+    for row in rows:
+        e = [math.exp(v) for v in row]
+        s = math.fsum(e)
+        out.append([v / s for v in e])
+    return out
+
+
+def _bf_layernorm(rows, eps):
+    out = []
+    for row in rows:
+        n = len(row)
+        mean = math.fsum(row) / n
+        var = math.fsum((v - mean) ** 2 for v in row) / n
+        out.append([(v - mean) / math.sqrt(var + eps) for v in row])
+    return out
+
+
+def _bf_matmul(a, b):
+    m, k = len(a), len(a[0])
+    n = len(b[0])
+    return [[math.fsum(a[i][t] * b[t][j] for t in range(k)) for j in range(n)] for i in range(m)]
+
+
+# --------------------------------------------------------------------- softmax
+
+def pin_softmax_rows_sum_to_one():
+    for shape in [(7, 13), (5, 1000), (3, 1)]:
+        x = _rng(11).normal(size=shape) * 3.0
+        y = oracle.softmax_rows(x)
+        assert np.all(y > 0.0) and np.all(y <= 1.0), "softmax outside (0, 1]"
+        assert np.max(np.abs(1.0 - y.sum(axis=1))) <= 1e-12, "softmax rows do not sum to 1"
+
+
+def pin_softmax_constant_row():
+    for n in [1, 7, 1024, 30000]:
+        x = np.full((3, n), -2.75)
+        y = oracle.softmax_rows(x)
+        assert np.array_equal(y, np.full((3, n), 1.0 / n)), f"constant row n={n} is not 1/n"
+
+
+def pin_softmax_one_hot():
+    g = _golden()["softmax_one_hot"]
+    n, t = g["n"], g["t"]
+    x = np.zeros((n, n))
+    for i in range(n):          # the hot entry moves along the diagonal: pins indexing
+        x[i, i] = t
+    y = oracle.softmax_rows(x)
+    hot = 1.0 / (1.0 + (n - 1) * math.exp(-t))
+    cold = math.exp(-t) * hot
+    _close(np.diag(y), np.full(n, hot), 1e-14, what="one-hot hot entry")
+    _close(y[~np.eye(n, dtype=bool)], np.full(n * (n - 1), cold), 1e-14, what="one-hot cold entries")
+    _close([hot, cold], [g["hot"], g["cold"]], 1e-12, what="one-hot golden")
+
+
+def pin_softmax_shift_invariance():
+    x = _rng(12).normal(size=(9, 77))
+    c = _rng(13).uniform(-50, 50, size=(9, 1))
+    _close(oracle.softmax_rows(x + c), oracle.softmax_rows(x), 0.0, 1e-13, what="shift invariance")
+
+
+def pin_softmax_brute_force():
+    for n in range(1, 9):
+        x = _rng(100 + n).normal(size=(3, n)) * 2.0
+        _close(oracle.softmax_rows(x), _bf_softmax(x.tolist()), 1e-14, what=f"softmax brute n={n}")
+
+
+def pin_softmax_large_inputs():
+    """Entries near 1000 overflow exp unless the row maximum is subtracted first."""
+    x = np.array([[1000.0, 999.0, 998.0], [1000.0, 0.0, -1000.0], [-1000.0, -1001.0, -999.0]])
+    y = oracle.softmax_rows(x)
+    d = np.array([[0.0, -1.0, -2.0], [0.0, -1000.0, -2000.0], [-1.0, -2.0, 0.0]])
+    expect = [[math.exp(v) / math.fsum(math.exp(w) for w in row) for v in row] for row in d.tolist()]
+    _close(y, expect, 1e-14, what="large-magnitude softmax")
+
+
+# ------------------------------------------------------------------- LayerNorm
+
+def pin_layernorm_invariants():
+    eps = 1e-5
+    for shape in [(5, 37), (4, 32), (3, 4096)]:
+        x = _rng(21).uniform(-1, 1, size=shape)
+        y = oracle.layernorm_rows(x, eps)
+        var = np.var(x, axis=1)                     # library routine, ddof=0
+        assert np.max(np.abs(y.mean(axis=1))) <= 1e-12, "LN mean is not 0"
+        _close((y * y).mean(axis=1), var / (var + eps), 1e-12, what="LN mean of squares")
+
+
+def pin_layernorm_constant_row():
+    for val in [0.5, 3.0, -7.25]:
+        x = np.full((2, 32), val)
+        assert np.array_equal(oracle.layernorm_rows(x, 1e-5), np.zeros((2, 32))), "constant row is not 0"
+
+
+def pin_layernorm_alternating():
+    eps = 1e-5
+    for a in [1e-3, 1.0, 7.0]:
+        row = np.array([a if j % 2 == 0 else -a for j in range(32)])
+        y = oracle.layernorm_rows(row[None, :], eps)
+        _close(y[0], row / math.sqrt(a * a + eps), 1e-14, what=f"alternating a={a}")
+    g = _golden()["layernorm_alternating"]
+    y = oracle.layernorm_rows(np.array([[g["a"], -g["a"]] * 4]), g["eps"])
+    _close(y[0], [g["value"], -g["value"]] * 4, 1e-14, what="alternating golden")
+
+
+def pin_layernorm_numpy():
+    eps = 1e-5
+    x = _rng(22).normal(size=(6, 129))
+    ref = (x - x.mean(axis=1, keepdims=True)) / np.sqrt(x.var(axis=1, keepdims=True) + eps)
+    _close(oracle.layernorm_rows(x, eps), ref, 1e-12, 1e-14, what="LN vs numpy mean/var")
+
+
+def pin_layernorm_brute_force():
+    eps = 1e-5
+    for shape in [(3, 5), (2, 2), (4, 9)]:
+        x = _rng(23).normal(size=shape)
+        _close(oracle.layernorm_rows(x, eps), _bf_layernorm(x.tolist(), eps), 1e-13, 1e-15,
+               what=f"LN brute {shape}")
+
+
+# ---------------------------------------------------------- pow-broadcast-add
+
+def pin_pow_closed_forms():
+    g = _golden()["pow_1_5"]
+    v = np.array(g["v"])
+    x = np.zeros((len(v), 3))
+    _, y = oracle.pow_bcast_add_softmax(x, v, 1.5)
+    _close(y, np.repeat(np.array(g["v_pow_1_5"])[:, None], 3, axis=1), 1e-15, what="v^1.5 closed forms")
+
+
+def pin_pow_brute_force():
+    for shape in [(3, 5), (7, 9)]:
+        x = _rng(31).normal(size=shape)
+        v = _rng(32).uniform(0.1, 2.0, size=shape[0])
+        out, y = oracle.pow_bcast_add_softmax(x, v, 1.5)
+        yb = [[x[i, j] + math.pow(v[i], 1.5) for j in range(shape[1])] for i in range(shape[0])]
+        _close(y, yb, 1e-15, 1e-15, what=f"pow-bcast-add brute {shape}")
+        _close(out, _bf_softmax(yb), 1e-14, what=f"softmax of Y brute {shape}")
+
+
+def pin_pow_softmax_identity():
+    """softmax(X + c_i) = softmax(X): the power stage cannot change the final output."""
+    x = _rng(33).normal(size=(8, 300))
+    v = _rng(34).uniform(0.1, 2.0, size=8)
+    out, _ = oracle.pow_bcast_add_softmax(x, v, 1.5)
+    _close(out, oracle.softmax_rows(x), 0.0, 1e-13, what="pow identity")
+
+
+# ------------------------------------------------------------------- GEMMs
+
+def pin_gemm_ones():
+    for (m, n, k) in [(4, 6, 5), (3, 3, 1024)]:
+        a, w = np.ones((m, k)), np.ones((k, n))
+        bias, r = np.zeros(n), np.zeros((m, n))
+        gamma = _rng(41).uniform(0.5, 1.5, size=n)
+        beta = _rng(42).normal(size=n)
+        y = oracle.gemm_ln(a, w, bias, r, gamma, beta, 1e-5)
+        assert np.array_equal(y, np.repeat(beta[None, :], m, axis=0)), "ones GEMM+LN is not beta"
+        s = oracle.gemm_softmax(np.ones((m, k)), np.ones((n, k)), 0.125)
+        assert np.array_equal(s, np.full((m, n), 1.0 / n)), "ones GEMM+softmax is not 1/N"
+
+
+def pin_gemm_softmax_zero_q():
+    q, k = np.zeros((5, 16)), _rng(43).normal(size=(64, 16))
+    assert np.array_equal(oracle.gemm_softmax(q, k, 0.25), np.full((5, 64), 1.0 / 64)), "Q=0 is not 1/N"
+
+
+def pin_gemm_ln_brute_force():
+    eps = 1e-5
+    for (m, n, k) in [(3, 6, 4), (5, 5, 5), (2, 7, 3)]:
+        rng = _rng(44 + m)
+        a, w = rng.normal(size=(m, k)), rng.normal(size=(k, n))
+        bias, gamma, beta = rng.normal(size=n), 1 + 0.1 * rng.normal(size=n), rng.normal(size=n)
+        r = rng.normal(size=(m, n))
+        z = _bf_matmul(a.tolist(), w.tolist())
+        u = [[z[i][j] + bias[j] + r[i, j] for j in range(n)] for i in range(m)]
+        nrm = _bf_layernorm(u, eps)
+        yb = [[nrm[i][j] * gamma[j] + beta[j] for j in range(n)] for i in range(m)]
+        _close(oracle.gemm_ln(a, w, bias, r, gamma, beta, eps), yb, 1e-12, 1e-13, what=f"GEMM+LN brute {m,n,k}")
+        # without residual
+        u0 = [[z[i][j] + bias[j] for j in range(n)] for i in range(m)]
+        n0 = _bf_layernorm(u0, eps)
+        y0 = [[n0[i][j] * gamma[j] + beta[j] for j in range(n)] for i in range(m)]
+        _close(oracle.gemm_ln(a, w, bias, None, gamma, beta, eps), y0, 1e-12, 1e-13, what="GEMM+LN brute no R")
+
+
+def pin_gemm_softmax_brute_force():
+    for (m, n, d) in [(3, 5, 4), (4, 4, 4), (6, 2, 7)]:
+        rng = _rng(50 + m)
+        q, k = rng.normal(size=(m, d)), rng.normal(size=(n, d))
+        sc = 1.0 / math.sqrt(d)
+        kt = [[k[j, t] for j in range(n)] for t in range(d)]
+        p = _bf_matmul(q.tolist(), kt)
+        yb = _bf_softmax([[sc * v for v in row] for row in p])
+        _close(oracle.gemm_softmax(q, k, sc), yb, 1e-13, what=f"GEMM+softmax brute {m,n,d}")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
