@@ -1,0 +1,328 @@
+"""Benchmark of the stitched / GEMM-fused hot path on one MI355X.
+
+One step = one call of each of the five fused entry points (the whole hot
+path) on its workload, inputs resident in HBM.  Each call is bracketed by HIP
+events on the stream it runs on, with a 512 MiB cache-evicting fill before it
+(outside the events) so every call reads its inputs from HBM.  The headline
+line reports the tall-skinny LayerNorm workload (750000 x 32 fp32); the other
+four workloads are reported under "per_config" in the same line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
+                       [--no-unfused] [--no-cpu] [--calibrate-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "effective HBM GB/s per stitched subgraph; TFLOP/s for fused GEMM+LN/softmax"
+HEADLINE = "layernorm_750000x32"
+FLUSH_BYTES = 512 << 20
+KERNEL_SOURCES = ["broadcast_subgraphs_amd/csrc/" + f for f in
+                  ("stitch.hip", "gemm.hip", "dev.hpp", "kernels.hpp", "api.hip")]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default=None, help="run one workload only (for profiling)")
+    ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the 256 MiB copy kernel (hardware byte-counter calibration)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ workloads
+
+class Workload:
+    """Inputs, outputs and the fused / unfused calls of one workload."""
+
+    def __init__(self, name, torch, cf, gen):
+        self.name = name
+        self.torch = torch
+        dev = "cuda"
+        d32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+        dbf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(torch.bfloat16)
+        if name == "softmax_256x1024":
+            x = gen.softmax_inputs(seed=1)["x"]
+            self.inp = {"x": x}
+            X, Y = d32(x), torch.empty(256, 1024, device=dev)
+            self.out = Y
+            self.bytes, self.flops = 2 * x.nbytes, 0
+            self.fused = lambda ws=None: cf.cf_stitch_softmax(X, Y, ws=ws)
+            self.unfused = lambda ws=None: cf.cf_stitch_softmax(X, Y, ws=ws, unfused=True)
+            self.op, self.dims = cf.CF_OP_STITCH_SOFTMAX, (256, 1024, 0)
+        elif name == "layernorm_750000x32":
+            x = gen.layernorm_inputs(seed=2)["x"]
+            self.inp = {"x": x}
+            X, Y = d32(x), torch.empty(750000, 32, device=dev)
+            self.out = Y
+            self.bytes, self.flops = 2 * x.nbytes, 0
+            self.fused = lambda ws=None: cf.cf_stitch_layernorm(X, Y, 1e-5, ws=ws)
+            self.unfused = lambda ws=None: cf.cf_stitch_layernorm(X, Y, 1e-5, ws=ws, unfused=True)
+            self.op, self.dims = cf.CF_OP_STITCH_LAYERNORM, (750000, 32, 0)
+        elif name == "pow_bcast_add_softmax_64x30000":
+            d = gen.pow_bcast_add_inputs(seed=3)
+            self.inp = d
+            X, V, Y = d32(d["x"]), d32(d["v"]), torch.empty(64, 30000, device=dev)
+            self.out = Y
+            self.bytes, self.flops = 2 * d["x"].nbytes + d["v"].nbytes, 0
+            self.fused = lambda ws=None: cf.cf_stitch_pow_bcast_add(X, V, 1.5, Y, None, ws=ws)
+            self.unfused = lambda ws=None: cf.cf_stitch_pow_bcast_add(X, V, 1.5, Y, None, ws=ws, unfused=True)
+            self.op, self.dims = cf.CF_OP_STITCH_POW_BCAST_ADD, (64, 30000, 0)
+        elif name == "gemm_ln_4096x4096x1024":
+            M, N, K = 4096, 4096, 1024
+            d = gen.gemm_ln_inputs(seed=4)
+            self.inp = d
+            A, W, R = dbf(d["a_bits"]), dbf(d["w_bits"]), dbf(d["r_bits"])
+            bias, gamma, beta = d32(d["bias"]), d32(d["gamma"]), d32(d["beta"])
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            self.out = Y
+            self.bytes = 2 * (M * K + K * N + 2 * M * N) + 4 * 3 * N
+            self.flops = 2 * M * N * K
+            self.fused = lambda ws=None: cf.cf_gemm_ln(A, W, bias, R, gamma, beta, Y, 1e-5, ws=ws)
+            self.unfused = lambda ws=None: cf.cf_gemm_ln(A, W, bias, R, gamma, beta, Y, 1e-5, ws=ws, unfused=True)
+            self.op, self.dims = cf.CF_OP_GEMM_LN, (M, N, K)
+        elif name == "gemm_softmax_8192x8192x128":
+            M, N, D = 8192, 8192, 128
+            d = gen.gemm_softmax_inputs(seed=5)
+            self.inp = d
+            Q, Kt = dbf(d["q_bits"]), dbf(d["k_bits"])
+            S = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            self.out = S
+            self.bytes = 2 * (M * D + N * D + M * N)
+            self.flops = 2 * M * N * D
+            self.fused = lambda ws=None: cf.cf_gemm_softmax(Q, Kt, d["scale"], S, ws=ws)
+            self.unfused = lambda ws=None: cf.cf_gemm_softmax(Q, Kt, d["scale"], S, ws=ws, unfused=True)
+            self.op, self.dims = cf.CF_OP_GEMM_SOFTMAX, (M, N, D)
+        else:
+            raise ValueError(name)
+        self.bound = "mfma" if name == "gemm_ln_4096x4096x1024" else "hbm"
+        nb = cf.cf_workspace_bytes(self.op, *self.dims)
+        self.ws = cf.Workspace(nb) if nb else None
+        self.uws = None
+
+    def oracle_once(self, oracle):
+        d = self.inp
+        if self.name == "softmax_256x1024":
+            return oracle.softmax_rows(d["x"])
+        if self.name == "layernorm_750000x32":
+            return oracle.layernorm_rows(d["x"], 1e-5)
+        if self.name == "pow_bcast_add_softmax_64x30000":
+            return oracle.pow_bcast_add_softmax(d["x"], d["v"], 1.5)
+        if self.name == "gemm_ln_4096x4096x1024":
+            return oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"], d["beta"], 1e-5)
+        return oracle.gemm_softmax(d["q"], d["k"], d["scale"])
+
+
+WORKLOAD_NAMES = ["softmax_256x1024", "layernorm_750000x32", "pow_bcast_add_softmax_64x30000",
+                  "gemm_ln_4096x4096x1024", "gemm_softmax_8192x8192x128"]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(the path shards by rows with no exchange, but no multi-GPU run is built)"}))
+        sys.exit(2)
+
+    import torch
+
+    import broadcast_subgraphs_amd as cf
+    import gen
+
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def do_flush():
+        if not args.no_flush:
+            cf.cf_util_fill_f32(flush, 0.0)
+
+    if args.calibrate_copy:
+        n = (256 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty(n, device="cuda")
+        for _ in range(args.warmup + args.steps):
+            do_flush()
+            cf.cf_util_copy_f32(src, dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
+                          "launches": args.warmup + args.steps}))
+        return
+
+    names = [args.only] if args.only else WORKLOAD_NAMES
+    wl = [Workload(n, torch, cf, gen) for n in names]
+    torch.cuda.synchronize()
+
+    def run_step(w, fn, ws, ev=None):
+        do_flush()
+        if ev is not None:
+            ev[0].record(stream)
+        fn(ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    # ---- warmup
+    for _ in range(args.warmup):
+        for w in wl:
+            run_step(w, w.fused, w.ws)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps of the whole hot path
+    events = {w.name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(args.steps)] for w in wl}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for w in wl:
+            run_step(w, w.fused, w.ws, events[w.name][k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {}
+    for w in wl:
+        ts = np.array([a.elapsed_time(b) for a, b in events[w.name]]) * 1e3  # us
+        t = float(ts.mean())
+        ent = {"us_mean": round(t, 3), "us_median": round(float(np.median(ts)), 3),
+               "us_p10": round(float(np.percentile(ts, 10)), 3), "us_p90": round(float(np.percentile(ts, 90)), 3),
+               "alg_bytes": w.bytes, "GBps": round(w.bytes / t / 1e3, 1),
+               "frac_hbm_peak": round(w.bytes / t / 1e3 / HBM_PEAK_GBS, 4)}
+        if w.flops:
+            ent["alg_flops"] = w.flops
+            ent["TFLOPs"] = round(w.flops / t / 1e6, 1)
+            ent["frac_mfma_peak"] = round(w.flops / t / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)
+        ent["bound"] = w.bound
+        ent["plan"] = None
+        per[w.name] = ent
+    # plans (one extra untimed call each)
+    for w in wl:
+        w.fused(w.ws)
+        per[w.name]["plan"] = json.loads(cf.last_plan())
+    torch.cuda.synchronize()
+    for w in wl:
+        if w.ws is not None:
+            assert w.ws.error_word() == 0, f"{w.name}: a cross-workgroup wait gave up"
+
+    # ---- unfused baselines, stream-launched and graph-replayed
+    if not args.no_unfused:
+        for w in wl:
+            w.uws = cf.Workspace(cf.cf_unfused_workspace_bytes(w.op, *w.dims))
+            ks = max(3, min(args.steps, 10))
+            for _ in range(2):
+                run_step(w, w.unfused, w.uws)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ks)]
+            for k in range(ks):
+                run_step(w, w.unfused, w.uws, ev[k])
+            torch.cuda.synchronize()
+            t_stream = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+            cs = torch.cuda.Stream()
+            with torch.cuda.stream(cs):
+                cs.synchronize()
+                cf.cf_graph_begin()
+                w.unfused(w.uws)
+                h = cf.cf_graph_end()
+                evg = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ks)]
+                for k in range(ks + 2):
+                    if not args.no_flush:
+                        cf.cf_util_fill_f32(flush, 0.0)
+                    if k >= 2:
+                        evg[k - 2][0].record(cs)
+                    cf.cf_graph_launch(h)
+                    if k >= 2:
+                        evg[k - 2][1].record(cs)
+                cs.synchronize()
+                cf.cf_graph_destroy(h)
+            t_graph = float(np.mean([a.elapsed_time(b) for a, b in evg])) * 1e3
+            per[w.name]["unfused_stream_us"] = round(t_stream, 3)
+            per[w.name]["unfused_graph_us"] = round(t_graph, 3)
+            per[w.name]["speedup_vs_unfused_graph"] = round(t_graph / per[w.name]["us_mean"], 2)
+            per[w.name]["launch_savings_us"] = round(t_stream - t_graph, 3)
+            per[w.name]["roundtrip_savings_us"] = round(t_graph - per[w.name]["us_mean"], 3)
+            del w.uws
+            torch.cuda.empty_cache()
+
+    # ---- CPU baseline: the oracle, on rank 0, on a bounded sample
+    cpu = None
+    head = next((w for w in wl if w.name == HEADLINE), wl[0])
+    if not args.no_cpu:
+        import oracle
+        reps, t_cpu = 0, 0.0
+        t_start = time.perf_counter()
+        while True:
+            head.oracle_once(oracle)
+            reps += 1
+            t_cpu = time.perf_counter() - t_start
+            if t_cpu >= 10.0 or reps >= 50:
+                break
+        cpu = {"value": round(head.bytes * reps / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{reps} full passes of the fp64 op-by-op oracle over the {head.name} input "
+                         f"({t_cpu:.1f} s; numpy elementwise ops, single-threaded)"}
+
+    # ---- roofline of the headline kernel
+    h = per[head.name]
+    achieved = h["GBps"] if head.bound == "hbm" else h["TFLOPs"]
+    roof = {"bound": head.bound, "achieved": achieved,
+            "peak": HBM_PEAK_GBS if head.bound == "hbm" else MFMA_BF16_PEAK_TFLOPS,
+            "unit": "GB/s" if head.bound == "hbm" else "TFLOP/s",
+            "frac": round(achieved / (HBM_PEAK_GBS if head.bound == "hbm" else MFMA_BF16_PEAK_TFLOPS), 4),
+            "traffic": None}
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{head.name}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == source_hash():
+            roof["traffic"] = tr.get("bytes_per_launch")
+            roof["traffic_detail"] = {k: tr[k] for k in ("fetch_bytes", "write_bytes", "scale") if k in tr}
+
+    ms_per_step = sum(p["us_mean"] for p in per.values()) / 1e3
+    line = {
+        "metric": METRIC,
+        "value": h["GBps"] if head.bound == "hbm" else h["TFLOPs"],
+        "unit": "GB/s" if head.bound == "hbm" else "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": head.name, "rows": 750000, "cols": 32, "eps": 1e-5,
+                   "step": "one fused call per workload: " + ", ".join(w.name for w in wl)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_config": per,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

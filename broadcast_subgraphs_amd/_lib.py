@@ -1,0 +1,284 @@
+"""ctypes binding of libcf.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls and forwards
+device pointers, sizes and the HIP stream.  All arithmetic runs in the HIP
+kernels; there is no CPU fallback: if the library is missing or fails to
+load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcf.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "cf.h")
+
+CF_OK, CF_EINVAL, CF_EUNSUPPORTED, CF_EALIGN, CF_EWORKSPACE, CF_EOCCUPANCY, CF_EHIP = range(7)
+CF_OP_STITCH_SOFTMAX, CF_OP_STITCH_LAYERNORM, CF_OP_STITCH_POW_BCAST_ADD, CF_OP_GEMM_LN, CF_OP_GEMM_SOFTMAX = 1, 2, 3, 4, 5
+
+_lib = None
+_lock = threading.Lock()
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+_ST = ctypes.c_int
+
+_SIGS = {
+    "cf_workspace_bytes": (_SZ, [ctypes.c_int, _I64, _I64, _I64]),
+    "cf_unfused_workspace_bytes": (_SZ, [ctypes.c_int, _I64, _I64, _I64]),
+    "cf_status_str": (ctypes.c_char_p, [_ST]),
+    "cf_last_plan": (ctypes.c_int, [ctypes.c_char_p, _SZ]),
+    "cf_stitch_softmax": (_ST, [_P, _P, _I64, _I64, _P, _SZ, _P]),
+    "cf_stitch_layernorm": (_ST, [_P, _P, _I64, _I64, _F, _P, _SZ, _P]),
+    "cf_stitch_pow_bcast_add": (_ST, [_P, _P, _F, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "cf_gemm_ln": (_ST, [_P, _P, _P, _P, _P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "cf_gemm_softmax": (_ST, [_P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "cf_unfused_stitch_softmax": (_ST, [_P, _P, _I64, _I64, _P, _SZ, _P]),
+    "cf_unfused_stitch_layernorm": (_ST, [_P, _P, _I64, _I64, _F, _P, _SZ, _P]),
+    "cf_unfused_stitch_pow_bcast_add": (_ST, [_P, _P, _F, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "cf_unfused_gemm_ln": (_ST, [_P, _P, _P, _P, _P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "cf_unfused_gemm_softmax": (_ST, [_P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "cf_graph_begin": (_ST, [_P]),
+    "cf_graph_end": (_ST, [_P, ctypes.POINTER(_P)]),
+    "cf_graph_launch": (_ST, [_P, _P]),
+    "cf_graph_destroy": (_ST, [_P]),
+    "cf_util_fill_f32": (_ST, [_P, _I64, _F, _P]),
+    "cf_util_copy_f32": (_ST, [_P, _P, _I64, _P]),
+}
+
+
+class CFError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        super().__init__(f"{call} failed: {status_str(status)}")
+
+
+def header_functions() -> list[str]:
+    """Names of every function the C header declares."""
+    with open(HEADER_PATH) as f:
+        txt = f.read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(cf_[a-z0-9_]+)\s*\(", txt)))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcf.so once; raise if it is missing (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m broadcast_subgraphs_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().cf_status_str(int(status)).decode()
+
+
+def last_plan() -> str:
+    buf = ctypes.create_string_buffer(1024)
+    lib().cf_last_plan(buf, 1024)
+    return buf.value.decode()
+
+
+def _check(name: str, status: int) -> None:
+    if status != CF_OK:
+        raise CFError(name, status)
+
+
+# ----------------------------------------------------------------- torch glue
+# PyTorch only supplies device memory and the stream.
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+class Workspace:
+    """A caller-owned device workspace, zero-filled once at allocation."""
+
+    def __init__(self, nbytes: int, device=None):
+        torch = _torch()
+        self.nbytes = max(int(nbytes), 256)
+        self.buf = torch.zeros(self.nbytes, dtype=torch.uint8, device=device or "cuda")
+        torch.cuda.synchronize(self.buf.device)
+
+    def ptr(self):
+        return ctypes.c_void_p(self.buf.data_ptr())
+
+    def error_word(self) -> int:
+        """Non-zero if a cross-workgroup wait gave up (read after the stream finished)."""
+        return int(self.buf[:4].view(_torch().int32).item())
+
+    def clear_error(self) -> None:
+        self.buf[:4].zero_()
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(nbytes: int, device, stream) -> Workspace:
+    if nbytes == 0:
+        return None
+    key = (device.index, int(stream.value or 0))
+    ws = _ws_cache.get(key)
+    if ws is None or ws.nbytes < nbytes:
+        ws = Workspace(nbytes, device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _ws_args(op, d0, d1, d2, ws, device, stream, unfused=False):
+    L = lib()
+    nbytes = (L.cf_unfused_workspace_bytes if unfused else L.cf_workspace_bytes)(op, d0, d1, d2)
+    if nbytes == ctypes.c_size_t(-1).value:
+        raise CFError("cf_workspace_bytes" if not unfused else "cf_unfused_workspace_bytes", CF_EUNSUPPORTED)
+    if ws is None:
+        ws = _workspace(nbytes, device, stream)
+    if ws is None:
+        return None, 0, None
+    return ws.ptr(), ws.nbytes, ws
+
+
+# ----------------------------------------------------------------- entry points
+
+def cf_stitch_softmax(x, y, ws=None, stream=None, unfused=False):
+    torch = _torch()
+    _need(x, torch.float32, "x", 2)
+    _need(y, torch.float32, "y", 2)
+    rows, cols = x.shape
+    st = _stream(stream)
+    p, n, w = _ws_args(CF_OP_STITCH_SOFTMAX, rows, cols, 0, ws, x.device, st, unfused)
+    name = "cf_unfused_stitch_softmax" if unfused else "cf_stitch_softmax"
+    _check(name, getattr(lib(), name)(_ptr(x), _ptr(y), rows, cols, p, n, st))
+    return w
+
+
+def cf_stitch_layernorm(x, y, eps=1e-5, ws=None, stream=None, unfused=False):
+    torch = _torch()
+    _need(x, torch.float32, "x", 2)
+    _need(y, torch.float32, "y", 2)
+    rows, cols = x.shape
+    st = _stream(stream)
+    p, n, w = _ws_args(CF_OP_STITCH_LAYERNORM, rows, cols, 0, ws, x.device, st, unfused)
+    name = "cf_unfused_stitch_layernorm" if unfused else "cf_stitch_layernorm"
+    _check(name, getattr(lib(), name)(_ptr(x), _ptr(y), rows, cols, float(eps), p, n, st))
+    return w
+
+
+def cf_stitch_pow_bcast_add(x, v, p, y, y_pre=None, ws=None, stream=None, unfused=False):
+    torch = _torch()
+    _need(x, torch.float32, "x", 2)
+    _need(v, torch.float32, "v", 1)
+    _need(y, torch.float32, "y", 2)
+    if y_pre is not None:
+        _need(y_pre, torch.float32, "y_pre", 2)
+    rows, cols = x.shape
+    st = _stream(stream)
+    wp, n, w = _ws_args(CF_OP_STITCH_POW_BCAST_ADD, rows, cols, 0, ws, x.device, st, unfused)
+    name = "cf_unfused_stitch_pow_bcast_add" if unfused else "cf_stitch_pow_bcast_add"
+    _check(name, getattr(lib(), name)(_ptr(x), _ptr(v), float(p), _ptr(y), _ptr(y_pre), rows, cols, wp, n, st))
+    return w
+
+
+def cf_gemm_ln(A, W, bias, R, gamma, beta, Y, eps=1e-5, ws=None, stream=None, unfused=False):
+    """A [M,K], W [K,N], R [M,N] or None, Y [M,N]: bf16 tensors; bias/gamma/beta fp32 [N]."""
+    torch = _torch()
+    for t, nm in ((A, "A"), (W, "W"), (Y, "Y")):
+        _need(t, torch.bfloat16, nm, 2)
+    if R is not None:
+        _need(R, torch.bfloat16, "R", 2)
+    for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta")):
+        _need(t, torch.float32, nm, 1)
+    M, K = A.shape
+    N = W.shape[1]
+    st = _stream(stream)
+    p, n, w = _ws_args(CF_OP_GEMM_LN, M, N, K, ws, A.device, st, unfused)
+    name = "cf_unfused_gemm_ln" if unfused else "cf_gemm_ln"
+    _check(name, getattr(lib(), name)(_ptr(A), _ptr(W), _ptr(bias), _ptr(R), _ptr(gamma), _ptr(beta),
+                                      float(eps), _ptr(Y), M, N, K, p, n, st))
+    return w
+
+
+def cf_gemm_softmax(Q, K, scale, S, ws=None, stream=None, unfused=False):
+    """Q [M,D], K [N,D], S [M,N]: bf16 tensors."""
+    torch = _torch()
+    for t, nm in ((Q, "Q"), (K, "K"), (S, "S")):
+        _need(t, torch.bfloat16, nm, 2)
+    M, D = Q.shape
+    N = K.shape[0]
+    st = _stream(stream)
+    p, n, w = _ws_args(CF_OP_GEMM_SOFTMAX, M, N, D, ws, Q.device, st, unfused)
+    name = "cf_unfused_gemm_softmax" if unfused else "cf_gemm_softmax"
+    _check(name, getattr(lib(), name)(_ptr(Q), _ptr(K), float(scale), _ptr(S), M, N, D, p, n, st))
+    return w
+
+
+def cf_workspace_bytes(op, d0, d1, d2=0):
+    return lib().cf_workspace_bytes(op, d0, d1, d2)
+
+
+def cf_unfused_workspace_bytes(op, d0, d1, d2=0):
+    return lib().cf_unfused_workspace_bytes(op, d0, d1, d2)
+
+
+def cf_graph_begin(stream=None):
+    _check("cf_graph_begin", lib().cf_graph_begin(_stream(stream)))
+
+
+def cf_graph_end(stream=None):
+    h = ctypes.c_void_p()
+    _check("cf_graph_end", lib().cf_graph_end(_stream(stream), ctypes.byref(h)))
+    return h
+
+
+def cf_graph_launch(exec_handle, stream=None):
+    _check("cf_graph_launch", lib().cf_graph_launch(exec_handle, _stream(stream)))
+
+
+def cf_graph_destroy(exec_handle):
+    _check("cf_graph_destroy", lib().cf_graph_destroy(exec_handle))
+
+
+def cf_util_fill_f32(p, value=0.0, stream=None):
+    _check("cf_util_fill_f32", lib().cf_util_fill_f32(_ptr(p), p.numel(), float(value), _stream(stream)))
+
+
+def cf_util_copy_f32(src, dst, stream=None):
+    _check("cf_util_copy_f32", lib().cf_util_copy_f32(_ptr(src), _ptr(dst), src.numel(), _stream(stream)))

@@ -1,0 +1,588 @@
+// C-ABI entry points: argument validation, planning and launch.
+//
+// The planner is a pure function of the shape and the device's properties,
+// with no autotuning ([AStitch] "Adaptive thread mapping": the mapping is
+// chosen just in time from the real shapes).  Rows that fit a workgroup are
+// packed (many short rows per workgroup, several rows in flight per lane) or
+// mapped one per workgroup; rows that do not fit are split across workgroups
+// that aggregate through global memory.  Any plan whose workgroups wait on
+// each other is sized to the grid the device keeps resident at once
+// ([AStitch] "What it costs"), or refused with CF_EOCCUPANCY.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "../../include/cf.h"
+#include "kernels.hpp"
+
+using namespace cf;
+
+namespace {
+
+thread_local std::string g_last_plan;
+
+struct DevInfo {
+  int cus = 0;
+  bool ok = false;
+};
+constexpr int kMaxDev = 64;
+DevInfo g_dev[kMaxDev];
+std::once_flag g_dev_once[kMaxDev];
+
+cf_status dev_info(DevInfo** out) {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDev) return CF_EHIP;
+  std::call_once(g_dev_once[d], [d] {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, d) == hipSuccess) {
+      g_dev[d].cus = p.multiProcessorCount;
+      g_dev[d].ok = true;
+    }
+  });
+  if (!g_dev[d].ok) return CF_EHIP;
+  *out = &g_dev[d];
+  return CF_OK;
+}
+
+long env_int(const char* name, long dflt) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  return strtol(s, nullptr, 10);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int pow2ceil(int64_t v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+// Workspace layout, the same for every plan of every op:
+//   [0, 256)                      header (u32 error word at offset 0)
+//   [256, 256 + 8 * kMaxJoins)    join words, one per group of cooperating
+//                                 workgroups (group membership is fixed for a
+//                                 launch, so a join word serves every round)
+//   [kPartialsOff, ...)           per-row partials
+// Because the join region is fixed, one op's partials never overwrite another
+// op's join words, and every completed join leaves its count at 0: a workspace
+// can be reused by any later call of any op.
+constexpr size_t kHeader = 256;
+constexpr int64_t kMaxJoins = 16384;
+constexpr size_t kPartialsOff = kHeader + kMaxJoins * sizeof(JoinWord);
+
+struct WsLayout {
+  size_t joins_off = 0, partials_off = 0, total = 0;
+};
+
+WsLayout ws_layout(int64_t npartial_floats) {
+  WsLayout L;
+  L.joins_off = kHeader;
+  L.partials_off = kPartialsOff;
+  L.total = align_up(kPartialsOff + (size_t)npartial_floats * sizeof(float), 256);
+  return L;
+}
+
+// ------------------------------------------------------------ row planning
+
+cf_status plan_rows(int op, int64_t rows, int64_t cols, bool vec_ok, RowPlan* pl) {
+  DevInfo* di = nullptr;
+  cf_status s = dev_info(&di);
+  if (s != CF_OK) return s;
+  RowPlan p;
+  p.w = (vec_ok && cols % 4 == 0) ? 4 : 1;
+  const int64_t nvec = (cols + p.w - 1) / p.w;
+  const long force_split = env_int("CF_FORCE_SPLIT", 0);
+  if (nvec <= 64 && force_split <= 1) {
+    p.lpr = (int)std::max<int64_t>(4, pow2ceil(nvec));
+    p.nv = 1;
+    p.rpi = (int)env_int("CF_FORCE_RPI", p.lpr <= 16 ? 4 : 1);
+  } else if (nvec <= 256 * 16 && force_split <= 1) {
+    p.lpr = 256;
+    p.nv = pow2ceil((nvec + 255) / 256);
+    p.rpi = 1;
+  } else {
+    // task splitting: S members per row, each holding <= 16 fragments per lane
+    const int64_t s_min = (nvec + 256 * 16 - 1) / (256 * 16);
+    int64_t S = std::max<int64_t>(s_min, rows >= di->cus ? 1 : pow2ceil((di->cus + rows - 1) / rows));
+    if (force_split > 1) S = force_split;
+    const int64_t slice_vec = (nvec + S - 1) / S;
+    p.split = (int)S;
+    p.nv = pow2ceil((slice_vec + 255) / 256);
+    if (p.nv > 16) return CF_EUNSUPPORTED;
+    p.slice = slice_vec * p.w;
+    p.lpr = 256;
+    p.rpi = 1;
+  }
+  const int rows_per_blk = (256 / p.lpr) * p.rpi;
+  if (p.split == 1) {
+    const int64_t nblk = (rows + rows_per_blk - 1) / rows_per_blk;
+    const int64_t cap = (int64_t)di->cus * env_int("CF_ROWS_WG_PER_CU", 8);
+    p.grid = (int)std::min<int64_t>(nblk, env_int("CF_FORCE_GRID", cap));
+  } else {
+    int occ = 0;
+    if (rows_split_occupancy(op, p, &occ) != hipSuccess || occ <= 0) return CF_EHIP;
+    p.occupancy = occ;
+    const int64_t cap = (int64_t)occ * di->cus;
+    const int64_t items = rows * p.split;
+    int64_t G = std::min<int64_t>(items, cap / p.split * p.split);
+    if (G < p.split) return CF_EOCCUPANCY;
+    if (G / p.split > kMaxJoins) G = kMaxJoins * p.split;
+    p.grid = (int)G;
+  }
+  *pl = p;
+  return CF_OK;
+}
+
+size_t rows_ws_bytes(const RowPlan& p, int64_t rows) {
+  if (p.split <= 1) return 0;
+  return ws_layout(rows * p.split * 4).total;
+}
+
+void record_rows_plan(const char* name, const RowPlan& p, int64_t rows, int64_t cols) {
+  char buf[512];
+  snprintf(buf, sizeof buf,
+           "{\"call\":\"%s\",\"rows\":%lld,\"cols\":%lld,\"kernel\":\"%s\",\"frag_floats\":%d,"
+           "\"lanes_per_row\":%d,\"frags_per_lane\":%d,\"rows_in_flight\":%d,\"split\":%d,"
+           "\"slice\":%lld,\"grid\":%d,\"block\":256,\"aggregation\":\"%s\",\"occupancy\":%d}",
+           name, (long long)rows, (long long)cols, p.split > 1 ? "k_rows_split" : "k_rows", p.w, p.lpr,
+           p.nv, p.rpi, p.split, (long long)p.slice, p.grid, p.split > 1 ? "all-read" : "none", p.occupancy);
+  g_last_plan = buf;
+}
+
+cf_status run_rows(const char* name, int op, const float* x, float* y, float* y_pre, const float* v, float pw,
+                   float eps, int64_t rows, int64_t cols, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (!x || !y || rows <= 0 || cols <= 0) return CF_EINVAL;
+  if (op == kPowSoftmax && !v) return CF_EINVAL;
+  if (op == kLayerNorm && !(eps >= 0.0f)) return CF_EINVAL;
+  const size_t bytes = (size_t)rows * cols * sizeof(float);
+  if (overlap(x, bytes, y, bytes)) return CF_EINVAL;
+  if (y_pre && (overlap(y_pre, bytes, y, bytes) || overlap(y_pre, bytes, x, bytes))) return CF_EINVAL;
+  const bool vec_ok = aligned16(x) && aligned16(y) && (!y_pre || aligned16(y_pre));
+  RowPlan p;
+  cf_status s = plan_rows(op, rows, cols, vec_ok, &p);
+  if (s != CF_OK) return s;
+  const size_t need = rows_ws_bytes(p, rows);
+  if (need > 0 && (!ws || ws_bytes < need)) return CF_EWORKSPACE;
+  RowArgs a{};
+  a.x = x; a.y = y; a.y_pre = y_pre; a.v = v; a.p = pw; a.eps = eps;
+  a.rows = rows; a.cols = cols;
+  if (need > 0) {
+    const WsLayout L = ws_layout(rows * p.split * 4);
+    char* base = static_cast<char*>(ws);
+    a.err = reinterpret_cast<uint32_t*>(base);
+    a.joins = reinterpret_cast<JoinWord*>(base + L.joins_off);
+    a.partials = reinterpret_cast<float*>(base + L.partials_off);
+  }
+  a.S = p.split;
+  a.slice = p.slice;
+  record_rows_plan(name, p, rows, cols);
+  return launch_rows(op, p, a, st) == hipSuccess ? CF_OK : CF_EHIP;
+}
+
+// ------------------------------------------------------------ GEMM planning
+
+cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan* pl) {
+  DevInfo* di = nullptr;
+  cf_status s = dev_info(&di);
+  if (s != CF_OK) return s;
+  GemmPlan p;
+  p.nn = nn ? 1 : 0;
+  // default tile configs: the largest spill-free tile per epilogue
+  const int dflt = epi == kEpiStoreF32 ? 0 : 3;
+  p.cfg = (int)env_int(epi == kEpiSoftmax ? "CF_GEMM_SOFTMAX_CFG" : (epi == kEpiLN ? "CF_GEMM_LN_CFG" : "CF_GEMM_CFG"), dflt);
+  if (!gemm_tile_config(p.cfg, &p.bm, &p.bn, &p.bk)) return CF_EUNSUPPORTED;
+  const int64_t tn = (N + p.bn - 1) / p.bn, tm = (M + p.bm - 1) / p.bm;
+  p.tiles = (int)(tn * tm);
+  int occ = 0;
+  if (gemm_occupancy(epi, p, &occ) != hipSuccess || occ <= 0) return CF_EHIP;
+  p.occupancy = occ;
+  const int64_t cap = (int64_t)occ * di->cus;
+  if (epi == kEpiStoreF32) {
+    p.grid = (int)std::min<int64_t>(p.tiles, std::max<int64_t>(cap, 1) * 4);
+  } else {
+    const int64_t G = std::min<int64_t>(p.tiles, cap / tn * tn);
+    if (G < tn) return CF_EOCCUPANCY;
+    if (G / tn > kMaxJoins) return CF_EUNSUPPORTED;
+    p.grid = (int)G;
+  }
+  p.rounds = (int)((p.tiles + p.grid - 1) / p.grid);
+  *pl = p;
+  return CF_OK;
+}
+
+size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N) {
+  const int64_t tn = (N + p.bn - 1) / p.bn, tm = (M + p.bm - 1) / p.bm;
+  (void)tm;
+  return ws_layout(M * tn * 4).total;
+}
+
+void record_gemm_plan(const char* name, const GemmPlan& p, int64_t M, int64_t N, int64_t K, int leader) {
+  char buf[512];
+  snprintf(buf, sizeof buf,
+           "{\"call\":\"%s\",\"M\":%lld,\"N\":%lld,\"K\":%lld,\"kernel\":\"k_gemm\",\"tile\":[%d,%d,%d],"
+           "\"layout\":\"%s\",\"tiles\":%d,\"row_group\":%lld,\"grid\":%d,\"block\":256,\"occupancy\":%d,"
+           "\"rounds\":%d,\"aggregation\":\"%s\"}",
+           name, (long long)M, (long long)N, (long long)K, p.bm, p.bn, p.bk, p.nn ? "NN" : "NT", p.tiles,
+           (long long)((N + p.bn - 1) / p.bn), p.grid, p.occupancy, p.rounds, leader ? "leader" : "all-read");
+  g_last_plan = buf;
+}
+
+cf_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return CF_EINVAL;
+  if (N % 8 != 0 || K % 8 != 0) return CF_EUNSUPPORTED;
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31) return CF_EUNSUPPORTED;
+  return CF_OK;
+}
+
+}  // namespace
+
+// =================================================================== C-ABI
+
+extern "C" {
+
+const char* cf_status_str(cf_status s) {
+  switch (s) {
+    case CF_OK: return "CF_OK";
+    case CF_EINVAL: return "CF_EINVAL: invalid argument";
+    case CF_EUNSUPPORTED: return "CF_EUNSUPPORTED: shape not supported";
+    case CF_EALIGN: return "CF_EALIGN: pointer not 16-byte aligned";
+    case CF_EWORKSPACE: return "CF_EWORKSPACE: workspace missing or too small";
+    case CF_EOCCUPANCY: return "CF_EOCCUPANCY: cooperating workgroups cannot all be resident";
+    case CF_EHIP: return "CF_EHIP: HIP runtime error";
+  }
+  return "unknown cf_status";
+}
+
+int cf_last_plan(char* buf, size_t n) {
+  if (buf && n > 0) {
+    const size_t k = std::min(n - 1, g_last_plan.size());
+    memcpy(buf, g_last_plan.data(), k);
+    buf[k] = 0;
+  }
+  return (int)g_last_plan.size();
+}
+
+size_t cf_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2) {
+  if (d0 <= 0 || d1 <= 0) return (size_t)-1;
+  switch (op) {
+    case CF_OP_STITCH_SOFTMAX:
+    case CF_OP_STITCH_LAYERNORM:
+    case CF_OP_STITCH_POW_BCAST_ADD: {
+      const int rop = op == CF_OP_STITCH_SOFTMAX ? kSoftmax : (op == CF_OP_STITCH_LAYERNORM ? kLayerNorm : kPowSoftmax);
+      RowPlan p;
+      if (plan_rows(rop, d0, d1, true, &p) != CF_OK) return (size_t)-1;
+      const size_t a = rows_ws_bytes(p, d0);
+      RowPlan q;  // the 4-byte-fragment plan may split differently
+      if (plan_rows(rop, d0, d1, false, &q) != CF_OK) return (size_t)-1;
+      return std::max(a, rows_ws_bytes(q, d0));
+    }
+    case CF_OP_GEMM_LN:
+    case CF_OP_GEMM_SOFTMAX: {
+      if (d2 <= 0) return (size_t)-1;
+      GemmPlan p;
+      if (plan_gemm(op == CF_OP_GEMM_LN ? kEpiLN : kEpiSoftmax, op == CF_OP_GEMM_LN, d0, d1, d2, &p) != CF_OK)
+        return (size_t)-1;
+      return gemm_ws_bytes(p, d0, d1);
+    }
+  }
+  return (size_t)-1;
+}
+
+cf_status cf_stitch_softmax(const float* x, float* y, int64_t rows, int64_t cols, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  return run_rows("cf_stitch_softmax", kSoftmax, x, y, nullptr, nullptr, 0.f, 0.f, rows, cols, ws, ws_bytes, stream);
+}
+
+cf_status cf_stitch_layernorm(const float* x, float* y, int64_t rows, int64_t cols, float eps, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  return run_rows("cf_stitch_layernorm", kLayerNorm, x, y, nullptr, nullptr, 0.f, eps, rows, cols, ws, ws_bytes,
+                  stream);
+}
+
+cf_status cf_stitch_pow_bcast_add(const float* x, const float* v, float p, float* y, float* y_pre, int64_t rows,
+                                  int64_t cols, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_rows("cf_stitch_pow_bcast_add", kPowSoftmax, x, y, y_pre, v, p, 0.f, rows, cols, ws, ws_bytes, stream);
+}
+
+static cf_status run_gemm(const char* name, int epi, bool nn, GemmArgs a, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  GemmPlan p;
+  cf_status s = plan_gemm(epi, nn, a.M, a.N, a.K, &p);
+  if (s != CF_OK) return s;
+  const size_t need = gemm_ws_bytes(p, a.M, a.N);
+  if (!ws || ws_bytes < need) return CF_EWORKSPACE;
+  const int64_t tn = (a.N + p.bn - 1) / p.bn, tm = (a.M + p.bm - 1) / p.bm;
+  const WsLayout L = ws_layout(a.M * tn * 4);
+  char* base = static_cast<char*>(ws);
+  a.err = reinterpret_cast<uint32_t*>(base);
+  a.joins = reinterpret_cast<JoinWord*>(base + L.joins_off);
+  a.partials = reinterpret_cast<float*>(base + L.partials_off);
+  a.tiles_n = (int)tn;
+  a.tiles_m = (int)tm;
+  a.agg_leader = 0;
+  record_gemm_plan(name, p, a.M, a.N, a.K, a.agg_leader);
+  return launch_gemm(epi, p, a, stream) == hipSuccess ? CF_OK : CF_EHIP;
+}
+
+cf_status cf_gemm_ln(const cf_bf16* A, const cf_bf16* W, const float* bias, const cf_bf16* R, const float* gamma,
+                     const float* beta, float eps, cf_bf16* Y, int64_t M, int64_t N, int64_t K, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  if (!A || !W || !bias || !gamma || !beta || !Y || !(eps >= 0.0f)) return CF_EINVAL;
+  cf_status s = check_gemm_shape(M, N, K);
+  if (s != CF_OK) return s;
+  if (!aligned16(A) || !aligned16(W) || !aligned16(Y) || !aligned16(bias) || !aligned16(gamma) ||
+      !aligned16(beta) || (R && !aligned16(R)))
+    return CF_EALIGN;
+  const size_t ybytes = (size_t)M * N * 2;
+  if (overlap(Y, ybytes, A, (size_t)M * K * 2) || overlap(Y, ybytes, W, (size_t)K * N * 2) ||
+      (R && overlap(Y, ybytes, R, ybytes)))
+    return CF_EINVAL;
+  GemmArgs a{};
+  a.A = A; a.B = W; a.bias = bias; a.R = R; a.gamma = gamma; a.beta = beta; a.eps = eps; a.Y = Y;
+  a.M = M; a.N = N; a.K = K;
+  return run_gemm("cf_gemm_ln", kEpiLN, true, a, ws, ws_bytes, stream);
+}
+
+cf_status cf_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scale, cf_bf16* S, int64_t M, int64_t N,
+                          int64_t D, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!Q || !K || !S || !(scale == scale) || scale - scale != 0.0f) return CF_EINVAL;
+  cf_status s = check_gemm_shape(M, N, D);
+  if (s != CF_OK) return s;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(S)) return CF_EALIGN;
+  const size_t sbytes = (size_t)M * N * 2;
+  if (overlap(S, sbytes, Q, (size_t)M * D * 2) || overlap(S, sbytes, K, (size_t)N * D * 2)) return CF_EINVAL;
+  GemmArgs a{};
+  a.A = Q; a.B = K; a.scale = scale; a.Y = S;
+  a.M = M; a.N = N; a.K = D;
+  return run_gemm("cf_gemm_softmax", kEpiSoftmax, false, a, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------ unfused chains
+// Workspace: fp32 intermediates.  Vectors first (aligned), then full-size
+// buffers.  Each operator materializes its output.
+
+size_t cf_unfused_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2) {
+  if (d0 <= 0 || d1 <= 0) return (size_t)-1;
+  const size_t vec = align_up((size_t)d0 * 4, 256);
+  const size_t full = align_up((size_t)d0 * d1 * 4, 256);
+  switch (op) {
+    case CF_OP_STITCH_SOFTMAX: return 2 * vec + 2 * full;
+    case CF_OP_STITCH_LAYERNORM: return 4 * vec + 2 * full;
+    case CF_OP_STITCH_POW_BCAST_ADD: return 3 * vec + 3 * full;
+    case CF_OP_GEMM_LN: return d2 > 0 ? 4 * vec + 3 * full : (size_t)-1;
+    case CF_OP_GEMM_SOFTMAX: return d2 > 0 ? 2 * vec + 3 * full : (size_t)-1;
+  }
+  return (size_t)-1;
+}
+
+#define CF_TRY(call)                        \
+  do {                                      \
+    if ((call) != hipSuccess) return CF_EHIP; \
+  } while (0)
+
+static cf_status unfused_softmax_chain(const float* x, float* y, int64_t rows, int64_t cols, char* ws,
+                                       hipStream_t st) {
+  const size_t vec = align_up((size_t)rows * 4, 256), full = align_up((size_t)rows * cols * 4, 256);
+  float* m = reinterpret_cast<float*>(ws);
+  float* s = reinterpret_cast<float*>(ws + vec);
+  float* d = reinterpret_cast<float*>(ws + 2 * vec);
+  float* e = reinterpret_cast<float*>(ws + 2 * vec + full);
+  CF_TRY(u_rowreduce(x, m, rows, cols, 1, st));
+  CF_TRY(u_bcast_col(x, m, d, rows, cols, 0, st));
+  CF_TRY(u_map(d, e, rows * cols, 0, 0.f, 0.f, st));
+  CF_TRY(u_rowreduce(e, s, rows, cols, 0, st));
+  CF_TRY(u_bcast_col(e, s, y, rows, cols, 1, st));
+  return CF_OK;
+}
+
+static cf_status unfused_ln_chain(const float* x, float* y, int64_t rows, int64_t cols, float eps, char* ws,
+                                  hipStream_t st) {
+  const size_t vec = align_up((size_t)rows * 4, 256), full = align_up((size_t)rows * cols * 4, 256);
+  float* s = reinterpret_cast<float*>(ws);
+  float* mu = reinterpret_cast<float*>(ws + vec);
+  float* ss = reinterpret_cast<float*>(ws + 2 * vec);
+  float* r = reinterpret_cast<float*>(ws + 3 * vec);
+  float* c = reinterpret_cast<float*>(ws + 4 * vec);
+  float* q = reinterpret_cast<float*>(ws + 4 * vec + full);
+  CF_TRY(u_rowreduce(x, s, rows, cols, 0, st));
+  CF_TRY(u_map(s, mu, rows, 4, 1.0f / (float)cols, 0.f, st));
+  CF_TRY(u_bcast_col(x, mu, c, rows, cols, 0, st));
+  CF_TRY(u_map(c, q, rows * cols, 1, 0.f, 0.f, st));
+  CF_TRY(u_rowreduce(q, ss, rows, cols, 0, st));
+  CF_TRY(u_map(ss, r, rows, 3, eps, 1.0f / (float)cols, st));
+  CF_TRY(u_bcast_col(c, r, y, rows, cols, 2, st));
+  return CF_OK;
+}
+
+cf_status cf_unfused_stitch_softmax(const float* x, float* y, int64_t rows, int64_t cols, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  if (!x || !y || rows <= 0 || cols <= 0) return CF_EINVAL;
+  if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_STITCH_SOFTMAX, rows, cols, 0)) return CF_EWORKSPACE;
+  g_last_plan = "{\"call\":\"cf_unfused_stitch_softmax\",\"kernels\":5}";
+  return unfused_softmax_chain(x, y, rows, cols, static_cast<char*>(ws), stream);
+}
+
+cf_status cf_unfused_stitch_layernorm(const float* x, float* y, int64_t rows, int64_t cols, float eps, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  if (!x || !y || rows <= 0 || cols <= 0 || !(eps >= 0.f)) return CF_EINVAL;
+  if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_STITCH_LAYERNORM, rows, cols, 0)) return CF_EWORKSPACE;
+  g_last_plan = "{\"call\":\"cf_unfused_stitch_layernorm\",\"kernels\":7}";
+  return unfused_ln_chain(x, y, rows, cols, eps, static_cast<char*>(ws), stream);
+}
+
+cf_status cf_unfused_stitch_pow_bcast_add(const float* x, const float* v, float p, float* y, float* y_pre,
+                                          int64_t rows, int64_t cols, void* ws, size_t ws_bytes,
+                                          hipStream_t stream) {
+  if (!x || !v || !y || rows <= 0 || cols <= 0) return CF_EINVAL;
+  if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_STITCH_POW_BCAST_ADD, rows, cols, 0)) return CF_EWORKSPACE;
+  // layout: pv [rows] | softmax chain scratch (2 vectors + 2 full) | Y (full, when y_pre is NULL)
+  char* w = static_cast<char*>(ws);
+  const size_t vec = align_up((size_t)rows * 4, 256), full = align_up((size_t)rows * cols * 4, 256);
+  float* pv = reinterpret_cast<float*>(w);
+  char* chain = w + vec;
+  float* Y = y_pre ? y_pre : reinterpret_cast<float*>(w + 3 * vec + 2 * full);
+  g_last_plan = "{\"call\":\"cf_unfused_stitch_pow_bcast_add\",\"kernels\":7}";
+  CF_TRY(u_map(v, pv, rows, 2, p, 0.f, stream));
+  CF_TRY(u_bcast_col(x, pv, Y, rows, cols, 3, stream));
+  return unfused_softmax_chain(Y, y, rows, cols, chain, stream);
+}
+
+cf_status cf_unfused_gemm_ln(const cf_bf16* A, const cf_bf16* W, const float* bias, const cf_bf16* R,
+                             const float* gamma, const float* beta, float eps, cf_bf16* Y, int64_t M, int64_t N,
+                             int64_t K, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!A || !W || !bias || !gamma || !beta || !Y || !(eps >= 0.f)) return CF_EINVAL;
+  cf_status s = check_gemm_shape(M, N, K);
+  if (s != CF_OK) return s;
+  if (!aligned16(A) || !aligned16(W)) return CF_EALIGN;
+  if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_GEMM_LN, M, N, K)) return CF_EWORKSPACE;
+  char* w = static_cast<char*>(ws);
+  const size_t vec = align_up((size_t)M * 4, 256), full = align_up((size_t)M * N * 4, 256);
+  float* z = reinterpret_cast<float*>(w + 4 * vec);
+  float* u = reinterpret_cast<float*>(w + 4 * vec + full);
+  float* n = reinterpret_cast<float*>(w + 4 * vec + 2 * full);
+  GemmPlan p;
+  s = plan_gemm(kEpiStoreF32, true, M, N, K, &p);
+  if (s != CF_OK) return s;
+  GemmArgs a{};
+  a.A = A; a.B = W; a.Z = z; a.M = M; a.N = N; a.K = K;
+  a.tiles_n = (int)((N + p.bn - 1) / p.bn);
+  a.tiles_m = (int)((M + p.bm - 1) / p.bm);
+  CF_TRY(launch_gemm(kEpiStoreF32, p, a, stream));
+  CF_TRY(u_bcast_row(z, bias, u, M, N, 3, stream));
+  if (R) {
+    CF_TRY(u_add_bf16(u, R, z, M * N, stream));
+  } else {
+    CF_TRY(u_copy(u, z, M * N, stream));
+  }
+  // LN chain on z (uses the 4 vectors and two full buffers u, n)
+  float* sv = reinterpret_cast<float*>(w);
+  float* mu = reinterpret_cast<float*>(w + vec);
+  float* ss = reinterpret_cast<float*>(w + 2 * vec);
+  float* r = reinterpret_cast<float*>(w + 3 * vec);
+  CF_TRY(u_rowreduce(z, sv, M, N, 0, stream));
+  CF_TRY(u_map(sv, mu, M, 4, 1.0f / (float)N, 0.f, stream));
+  CF_TRY(u_bcast_col(z, mu, u, M, N, 0, stream));
+  CF_TRY(u_map(u, n, M * N, 1, 0.f, 0.f, stream));
+  CF_TRY(u_rowreduce(n, ss, M, N, 0, stream));
+  CF_TRY(u_map(ss, r, M, 3, eps, 1.0f / (float)N, stream));
+  CF_TRY(u_bcast_col(u, r, n, M, N, 2, stream));
+  CF_TRY(u_bcast_row(n, gamma, u, M, N, 2, stream));
+  CF_TRY(u_bcast_row(u, beta, n, M, N, 3, stream));
+  CF_TRY(u_cast_bf16(n, Y, M * N, stream));
+  g_last_plan = "{\"call\":\"cf_unfused_gemm_ln\",\"kernels\":13}";
+  return CF_OK;
+}
+
+cf_status cf_unfused_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scale, cf_bf16* S, int64_t M, int64_t N,
+                                  int64_t D, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!Q || !K || !S) return CF_EINVAL;
+  cf_status s = check_gemm_shape(M, N, D);
+  if (s != CF_OK) return s;
+  if (!aligned16(Q) || !aligned16(K)) return CF_EALIGN;
+  if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_GEMM_SOFTMAX, M, N, D)) return CF_EWORKSPACE;
+  char* w = static_cast<char*>(ws);
+  const size_t vec = align_up((size_t)M * 4, 256), full = align_up((size_t)M * N * 4, 256);
+  // layout: m [M] | s [M] | B0 | B1 | B2 (full fp32 buffers); each operator
+  // reads and writes distinct buffers.
+  float* m = reinterpret_cast<float*>(w);
+  float* sv = reinterpret_cast<float*>(w + vec);
+  float* B0 = reinterpret_cast<float*>(w + 2 * vec);
+  float* B1 = reinterpret_cast<float*>(w + 2 * vec + full);
+  float* B2 = reinterpret_cast<float*>(w + 2 * vec + 2 * full);
+  GemmPlan p;
+  s = plan_gemm(kEpiStoreF32, false, M, N, D, &p);
+  if (s != CF_OK) return s;
+  GemmArgs a{};
+  a.A = Q; a.B = K; a.Z = B0; a.M = M; a.N = N; a.K = D;
+  a.tiles_n = (int)((N + p.bn - 1) / p.bn);
+  a.tiles_m = (int)((M + p.bm - 1) / p.bm);
+  CF_TRY(launch_gemm(kEpiStoreF32, p, a, stream));   // P = Q.K^T
+  CF_TRY(u_map(B0, B1, M * N, 4, scale, 0.f, stream)); // S1 = scale * P
+  CF_TRY(u_rowreduce(B1, m, M, N, 1, stream));        // m = rowmax
+  CF_TRY(u_bcast_col(B1, m, B2, M, N, 0, stream));    // d = S1 - m
+  CF_TRY(u_map(B2, B0, M * N, 0, 0.f, 0.f, stream));  // e = exp(d)
+  CF_TRY(u_rowreduce(B0, sv, M, N, 0, stream));       // s = rowsum
+  CF_TRY(u_bcast_col(B0, sv, B1, M, N, 1, stream));   // y = e / s
+  CF_TRY(u_cast_bf16(B1, S, M * N, stream));
+  g_last_plan = "{\"call\":\"cf_unfused_gemm_softmax\",\"kernels\":8}";
+  return CF_OK;
+}
+
+// ---------------------------------------------------------------- graphs
+
+cf_status cf_graph_begin(hipStream_t stream) {
+  return hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal) == hipSuccess ? CF_OK : CF_EHIP;
+}
+
+cf_status cf_graph_end(hipStream_t stream, void** exec) {
+  if (!exec) return CF_EINVAL;
+  hipGraph_t g = nullptr;
+  if (hipStreamEndCapture(stream, &g) != hipSuccess || !g) return CF_EHIP;
+  hipGraphExec_t e = nullptr;
+  const hipError_t r = hipGraphInstantiate(&e, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (r != hipSuccess) return CF_EHIP;
+  if (hipGraphUpload(e, stream) != hipSuccess) {
+    (void)hipGraphExecDestroy(e);
+    return CF_EHIP;
+  }
+  *exec = e;
+  return CF_OK;
+}
+
+cf_status cf_graph_launch(void* exec, hipStream_t stream) {
+  if (!exec) return CF_EINVAL;
+  return hipGraphLaunch(static_cast<hipGraphExec_t>(exec), stream) == hipSuccess ? CF_OK : CF_EHIP;
+}
+
+cf_status cf_graph_destroy(void* exec) {
+  if (!exec) return CF_EINVAL;
+  return hipGraphExecDestroy(static_cast<hipGraphExec_t>(exec)) == hipSuccess ? CF_OK : CF_EHIP;
+}
+
+// ---------------------------------------------------------------- utilities
+
+cf_status cf_util_fill_f32(float* p, int64_t n, float value, hipStream_t stream) {
+  if (!p || n <= 0 || !aligned16(p)) return CF_EINVAL;
+  return u_fill(p, n, value, stream) == hipSuccess ? CF_OK : CF_EHIP;
+}
+
+cf_status cf_util_copy_f32(const float* src, float* dst, int64_t n, hipStream_t stream) {
+  if (!src || !dst || n <= 0) return CF_EINVAL;
+  if (!aligned16(src) || !aligned16(dst)) return CF_EALIGN;
+  if (overlap(src, (size_t)n * 4, dst, (size_t)n * 4)) return CF_EINVAL;
+  return u_copy(src, dst, n, stream) == hipSuccess ? CF_OK : CF_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Host-visible launch interfaces of the kernels (internal to libcf.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dev.hpp"
+
+namespace cf {
+
+enum RowOp { kSoftmax = 0, kLayerNorm = 1, kPowSoftmax = 2 };
+
+struct RowArgs {
+  const float* x;
+  float* y;
+  float* y_pre;     // pow-softmax only, nullable
+  const float* v;   // pow-softmax only
+  float p;
+  float eps;
+  int64_t rows;
+  int64_t cols;
+  uint32_t* err;    // workspace error word
+  JoinWord* joins;  // split plans: one join per group of S workgroups
+  float* partials;  // split plans: rows * S * 4 floats
+  int S;            // workgroups per row (split plans)
+  int64_t slice;    // columns per member (split plans)
+};
+
+struct RowPlan {
+  int w = 4;      // floats per fragment (4 or 1)
+  int lpr = 256;  // lanes per row (in-workgroup plans)
+  int nv = 1;     // fragments per lane per row
+  int rpi = 1;    // rows in flight per lane
+  int split = 1;  // workgroups per row (>1: split plan)
+  int64_t slice = 0;
+  int grid = 1;
+  int occupancy = 0;  // resident workgroups per CU (split plans)
+};
+
+hipError_t launch_rows(int op, const RowPlan& pl, const RowArgs& a, hipStream_t st);
+hipError_t rows_split_occupancy(int op, const RowPlan& pl, int* per_cu);
+
+// ----------------------------------------------------------------- GEMM
+enum GemmEpi { kEpiStoreF32 = 0, kEpiLN = 1, kEpiSoftmax = 2 };
+
+struct GemmArgs {
+  const uint16_t* A;   // [M x K] bf16 (GEMM left operand; Q for softmax)
+  const uint16_t* B;   // NN: W [K x N]; NT: K [N x K] (bf16)
+  const float* bias;   // LN: [N]
+  const uint16_t* R;   // LN: [M x N] bf16, nullable
+  const float* gamma;  // LN: [N]
+  const float* beta;   // LN: [N]
+  float eps;
+  float scale;         // softmax: multiplies the accumulator
+  uint16_t* Y;         // bf16 [M x N] output (LN, softmax)
+  float* Z;            // fp32 [M x N] output (plain GEMM)
+  int64_t M, N, K;
+  int tiles_n;         // column tiles per row group = ceil(N / BN)
+  int tiles_m;
+  uint32_t* err;
+  JoinWord* joins;     // one per group of tiles_n workgroups
+  float* partials;     // M * tiles_n * 4 floats
+  int agg_leader;      // 0: every member reads all partials; 1: last arriver combines
+};
+
+struct GemmPlan {
+  int cfg = 0;        // tile configuration id
+  int bm = 256, bn = 256, bk = 64;
+  int nn = 1;         // 1: B is [K x N]; 0: B is [N x K]
+  int grid = 0;
+  int occupancy = 0;  // resident workgroups per CU
+  int tiles = 0;
+  int rounds = 0;
+};
+
+hipError_t launch_gemm(int epi, const GemmPlan& pl, const GemmArgs& a, hipStream_t st);
+hipError_t gemm_occupancy(int epi, const GemmPlan& pl, int* per_cu);
+bool gemm_tile_config(int cfg, int* bm, int* bn, int* bk);
+
+// ----------------------------------------------------------- unfused ops
+hipError_t u_rowreduce(const float* x, float* out, int64_t rows, int64_t cols, int is_max, hipStream_t st);
+// y = x (op) c[row]  for op: 0 sub, 1 div, 2 mul, 3 add
+hipError_t u_bcast_col(const float* x, const float* c, float* y, int64_t rows, int64_t cols, int op, hipStream_t st);
+// y = x (op) r[col]  for op: 2 mul, 3 add
+hipError_t u_bcast_row(const float* x, const float* r, float* y, int64_t rows, int64_t cols, int op, hipStream_t st);
+// y = f(x) elementwise: 0 exp, 1 square, 2 pow(x, p), 3 rsqrt(x/n + eps) , 4 scale(x, p)
+hipError_t u_map(const float* x, float* y, int64_t n, int op, float p, float q, hipStream_t st);
+hipError_t u_add_bf16(const float* x, const uint16_t* r, float* y, int64_t n, hipStream_t st);
+hipError_t u_cast_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t st);
+hipError_t u_fill(float* p, int64_t n, float v, hipStream_t st);
+hipError_t u_copy(const float* s, float* d, int64_t n, hipStream_t st);
+
+}  // namespace cf

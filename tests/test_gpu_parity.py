@@ -1,0 +1,348 @@
+"""HIP path vs the fp64 oracle, through the C-ABI (needs an MI355X).
+
+Error metric for every subgraph: per-row normalised max error
+    err = max_i  max_j |g_ij - o_ij| / max_j |o_ij|
+bounded by 1e-4 for the fp32 paths and 2e-2 for the bf16-output GEMM paths.
+"""
+import numpy as np
+import pytest
+import torch
+
+import broadcast_subgraphs_amd as cf
+import gen
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+
+
+def rownorm_err(g, o):
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    assert g.shape == o.shape
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    den = np.max(np.abs(o), axis=1)
+    den[den == 0] = 1.0
+    return float(np.max(np.max(np.abs(g - o), axis=1) / den))
+
+
+def d32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def dbf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+def check_ws(ws):
+    torch.cuda.synchronize()
+    if ws is not None:
+        assert ws.error_word() == 0, "a cross-workgroup wait gave up"
+
+
+def empty_f32(rows, cols, misalign=False):
+    if not misalign:
+        return torch.full((rows, cols), float("nan"), dtype=torch.float32, device="cuda")
+    buf = torch.full((rows * cols + 1,), float("nan"), dtype=torch.float32, device="cuda")
+    return buf[1:].view(rows, cols)
+
+
+# ------------------------------------------------------------------ softmax
+
+SOFTMAX_SHAPES = [(256, 1024), (1, 1), (3, 5), (7, 13), (5, 64), (33, 100), (4099, 32), (17, 1000),
+                  (9, 4096), (3, 16384), (4, 20000), (2, 65537), (1, 30000)]
+
+
+@pytest.mark.parametrize("rows,cols", SOFTMAX_SHAPES)
+def test_softmax(rows, cols):
+    x = gen.softmax_inputs(seed=1, rows=rows, cols=cols)["x"]
+    y = empty_f32(rows, cols)
+    ws = cf.cf_stitch_softmax(d32(x), y)
+    check_ws(ws)
+    err = rownorm_err(host(y), oracle.softmax_rows(x))
+    assert err <= TOL_F32, (err, cf.last_plan())
+
+
+def test_softmax_misaligned_pointers():
+    rows, cols = 6, 1024
+    x = gen.softmax_inputs(seed=11, rows=rows, cols=cols)["x"]
+    xb = torch.empty(rows * cols + 1, dtype=torch.float32, device="cuda")
+    xb[1:] = d32(x).view(-1)
+    xd = xb[1:].view(rows, cols)
+    y = empty_f32(rows, cols, misalign=True)
+    cf.cf_stitch_softmax(xd, y)
+    assert '"frag_floats":1' in cf.last_plan()
+    assert rownorm_err(host(y), oracle.softmax_rows(x)) <= TOL_F32
+
+
+# ---------------------------------------------------------------- LayerNorm
+
+LN_SHAPES = [(750000, 32), (1, 1), (5, 3), (1000, 32), (999, 36), (7, 100), (3, 1024), (4, 5000),
+             (2, 30000), (3, 70001)]
+
+
+@pytest.mark.parametrize("rows,cols", LN_SHAPES)
+def test_layernorm(rows, cols):
+    x = gen.layernorm_inputs(seed=2, rows=rows, cols=cols)["x"]
+    y = empty_f32(rows, cols)
+    ws = cf.cf_stitch_layernorm(d32(x), y, eps=1e-5)
+    check_ws(ws)
+    err = rownorm_err(host(y), oracle.layernorm_rows(x, 1e-5))
+    assert err <= TOL_F32, (err, cf.last_plan())
+
+
+def test_layernorm_constant_rows_are_zero():
+    x = np.full((64, 32), 0.75, dtype=np.float32)
+    y = empty_f32(64, 32)
+    cf.cf_stitch_layernorm(d32(x), y, eps=1e-5)
+    assert np.array_equal(host(y), np.zeros((64, 32), np.float32))
+
+
+# -------------------------------------------------------- pow-broadcast-add
+
+POW_SHAPES = [(64, 30000), (3, 5), (7, 9), (64, 1024), (5, 20001), (1000, 32), (130, 8)]
+
+
+@pytest.mark.parametrize("rows,cols", POW_SHAPES)
+def test_pow_bcast_add(rows, cols):
+    d = gen.pow_bcast_add_inputs(seed=3, rows=rows, cols=cols)
+    y = empty_f32(rows, cols)
+    ypre = empty_f32(rows, cols)
+    ws = cf.cf_stitch_pow_bcast_add(d32(d["x"]), d32(d["v"]), d["p"], y, ypre)
+    check_ws(ws)
+    o, oy = oracle.pow_bcast_add_softmax(d["x"], d["v"], d["p"])
+    assert rownorm_err(host(y), o) <= TOL_F32, cf.last_plan()
+    assert rownorm_err(host(ypre), oy) <= TOL_F32, cf.last_plan()
+
+
+def test_pow_bcast_add_without_y_pre():
+    d = gen.pow_bcast_add_inputs(seed=33, rows=64, cols=30000)
+    y = empty_f32(64, 30000)
+    cf.cf_stitch_pow_bcast_add(d32(d["x"]), d32(d["v"]), d["p"], y, None)
+    o, _ = oracle.pow_bcast_add_softmax(d["x"], d["v"], d["p"])
+    assert rownorm_err(host(y), o) <= TOL_F32
+
+
+# ---------------------------------------------------------------- GEMM + LN
+
+GEMM_LN_SHAPES = [(300, 264, 72), (512, 1024, 256), (256, 128, 64), (17, 8, 8), (4096, 4096, 1024)]
+
+
+def _gemm_ln_run(d, M, N, K, residual=True, unfused=False):
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = cf.cf_gemm_ln(dbf16(d["a_bits"]), dbf16(d["w_bits"]), d32(d["bias"]),
+                       dbf16(d["r_bits"]) if residual else None, d32(d["gamma"]), d32(d["beta"]), Y,
+                       eps=d["eps"], unfused=unfused)
+    if not unfused:
+        check_ws(ws)
+    return host(Y)
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_LN_SHAPES)
+def test_gemm_ln(M, N, K):
+    d = gen.gemm_ln_inputs(seed=4, M=M, N=N, K=K)
+    g = _gemm_ln_run(d, M, N, K)
+    o = oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"], d["beta"], d["eps"])
+    err = rownorm_err(g, o)
+    assert err <= TOL_BF16, (err, cf.last_plan())
+
+
+def test_gemm_ln_no_residual():
+    M, N, K = 300, 264, 72
+    d = gen.gemm_ln_inputs(seed=44, M=M, N=N, K=K, residual=False)
+    g = _gemm_ln_run(d, M, N, K, residual=False)
+    o = oracle.gemm_ln(d["a"], d["w"], d["bias"], None, d["gamma"], d["beta"], d["eps"])
+    assert rownorm_err(g, o) <= TOL_BF16
+
+
+def test_gemm_ln_ones_gives_beta_exactly():
+    """A = W = 1, bias = 0, R = 0: every row of A.W is K, so y = beta_j (bf16-rounded) exactly."""
+    M, N, K = 512, 4096, 1024
+    d = gen.gemm_ln_inputs(seed=4, M=M, N=N, K=K)
+    one = gen.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    zero = gen.f32_to_bf16_bits(np.zeros(1, np.float32))[0]
+    d["a_bits"] = np.full((M, K), one, np.uint16)
+    d["w_bits"] = np.full((K, N), one, np.uint16)
+    d["r_bits"] = np.full((M, N), zero, np.uint16)
+    d["bias"] = np.zeros(N, np.float32)
+    g = _gemm_ln_run(d, M, N, K)
+    beta_bf16 = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(d["beta"]))
+    assert np.array_equal(g, np.repeat(beta_bf16[None, :], M, axis=0))
+
+
+# ----------------------------------------------------------- GEMM + softmax
+
+GEMM_SM_SHAPES = [(300, 264, 72), (512, 1024, 128), (256, 128, 64), (17, 8, 8), (8192, 8192, 128)]
+
+
+def _gemm_sm_run(d, M, N, D, unfused=False):
+    S = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = cf.cf_gemm_softmax(dbf16(d["q_bits"]), dbf16(d["k_bits"]), d["scale"], S, unfused=unfused)
+    if not unfused:
+        check_ws(ws)
+    return host(S)
+
+
+@pytest.mark.parametrize("M,N,D", GEMM_SM_SHAPES)
+def test_gemm_softmax(M, N, D):
+    d = gen.gemm_softmax_inputs(seed=5, M=M, N=N, D=D)
+    g = _gemm_sm_run(d, M, N, D)
+    o = oracle.gemm_softmax(d["q"], d["k"], d["scale"])
+    err = rownorm_err(g, o)
+    assert err <= TOL_BF16, (err, cf.last_plan())
+    rs = g.astype(np.float64).sum(axis=1)
+    assert np.max(np.abs(rs - 1.0)) <= 8e-3  # bf16 rounding of each term is within 2^-9 relative
+
+
+def test_gemm_softmax_zero_q_is_exact():
+    """Q = 0: every score is equal, so every output is 1/8192 = 2^-13, exact in bf16."""
+    M, N, D = 512, 8192, 128
+    d = gen.gemm_softmax_inputs(seed=5, M=M, N=N, D=D)
+    d["q_bits"] = np.zeros((M, D), np.uint16)
+    g = _gemm_sm_run(d, M, N, D)
+    assert np.array_equal(g, np.full((M, N), 2.0 ** -13, np.float32))
+
+
+# ------------------------------------------------------------- determinism
+
+def test_deterministic_runs():
+    x = gen.pow_bcast_add_inputs(seed=3)
+    y1, y2 = empty_f32(64, 30000), empty_f32(64, 30000)
+    cf.cf_stitch_pow_bcast_add(d32(x["x"]), d32(x["v"]), 1.5, y1)
+    cf.cf_stitch_pow_bcast_add(d32(x["x"]), d32(x["v"]), 1.5, y2)
+    assert torch.equal(y1, y2)
+    d = gen.gemm_ln_inputs(seed=4, M=1024, N=4096, K=256)
+    assert np.array_equal(_gemm_ln_run(d, 1024, 4096, 256), _gemm_ln_run(d, 1024, 4096, 256))
+    q = gen.gemm_softmax_inputs(seed=5, M=1024, N=8192, D=128)
+    assert np.array_equal(_gemm_sm_run(q, 1024, 8192, 128), _gemm_sm_run(q, 1024, 8192, 128))
+
+
+# ------------------------------------------------------------ metamorphic
+
+def test_row_permutation():
+    rng = np.random.default_rng(0)
+    d = gen.pow_bcast_add_inputs(seed=3)
+    perm = rng.permutation(64)
+    y, yp = empty_f32(64, 30000), empty_f32(64, 30000)
+    cf.cf_stitch_pow_bcast_add(d32(d["x"]), d32(d["v"]), 1.5, y)
+    cf.cf_stitch_pow_bcast_add(d32(d["x"][perm]), d32(d["v"][perm]), 1.5, yp)
+    assert np.array_equal(host(y)[perm], host(yp))
+    M, N, K = 512, 1024, 128
+    g = gen.gemm_ln_inputs(seed=4, M=M, N=N, K=K)
+    p = rng.permutation(M)
+    base = _gemm_ln_run(g, M, N, K)
+    g2 = dict(g)
+    g2["a_bits"], g2["r_bits"] = g["a_bits"][p], g["r_bits"][p]
+    assert np.array_equal(base[p], _gemm_ln_run(g2, M, N, K))
+
+
+def test_column_permutation_gemm():
+    rng = np.random.default_rng(1)
+    M, N, K = 256, 1024, 128
+    g = gen.gemm_ln_inputs(seed=4, M=M, N=N, K=K)
+    p = rng.permutation(N)
+    base = _gemm_ln_run(g, M, N, K)
+    g2 = dict(g)
+    g2["w_bits"], g2["r_bits"] = g["w_bits"][:, p], g["r_bits"][:, p]
+    g2["bias"], g2["gamma"], g2["beta"] = g["bias"][p], g["gamma"][p], g["beta"][p]
+    assert rownorm_err(_gemm_ln_run(g2, M, N, K), base[:, p]) <= TOL_BF16
+    q = gen.gemm_softmax_inputs(seed=5, M=M, N=N, D=128)
+    sb = _gemm_sm_run(q, M, N, 128)
+    q2 = dict(q)
+    q2["k_bits"] = q["k_bits"][p]
+    assert rownorm_err(_gemm_sm_run(q2, M, N, 128), sb[:, p]) <= TOL_BF16
+
+
+# ------------------------------------------------- unfused chains and graphs
+
+def test_unfused_chains_match_oracle():
+    x = gen.softmax_inputs(seed=1)["x"]
+    y = empty_f32(256, 1024)
+    cf.cf_stitch_softmax(d32(x), y, unfused=True)
+    assert rownorm_err(host(y), oracle.softmax_rows(x)) <= TOL_F32
+    x = gen.layernorm_inputs(seed=2, rows=10000)["x"]
+    y = empty_f32(10000, 32)
+    cf.cf_stitch_layernorm(d32(x), y, unfused=True)
+    assert rownorm_err(host(y), oracle.layernorm_rows(x)) <= TOL_F32
+    d = gen.pow_bcast_add_inputs(seed=3)
+    y, yp = empty_f32(64, 30000), empty_f32(64, 30000)
+    cf.cf_stitch_pow_bcast_add(d32(d["x"]), d32(d["v"]), 1.5, y, yp, unfused=True)
+    o, oy = oracle.pow_bcast_add_softmax(d["x"], d["v"], 1.5)
+    assert rownorm_err(host(y), o) <= TOL_F32 and rownorm_err(host(yp), oy) <= TOL_F32
+    g = gen.gemm_ln_inputs(seed=4, M=512, N=1024, K=256)
+    o = oracle.gemm_ln(g["a"], g["w"], g["bias"], g["r"], g["gamma"], g["beta"])
+    assert rownorm_err(_gemm_ln_run(g, 512, 1024, 256, unfused=True), o) <= TOL_BF16
+    q = gen.gemm_softmax_inputs(seed=5, M=512, N=1024, D=128)
+    o = oracle.gemm_softmax(q["q"], q["k"], q["scale"])
+    assert rownorm_err(_gemm_sm_run(q, 512, 1024, 128, unfused=True), o) <= TOL_BF16
+
+
+def test_graph_replay_is_bitwise_equal_to_stream_launch():
+    d = gen.gemm_softmax_inputs(seed=5, M=512, N=1024, D=128)
+    Q, K = dbf16(d["q_bits"]), dbf16(d["k_bits"])
+    S1 = torch.empty((512, 1024), dtype=torch.bfloat16, device="cuda")
+    S2 = torch.zeros_like(S1)
+    ws = cf.Workspace(cf.cf_unfused_workspace_bytes(cf.CF_OP_GEMM_SOFTMAX, 512, 1024, 128))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        cf.cf_gemm_softmax(Q, K, d["scale"], S1, ws=ws, unfused=True)
+        s.synchronize()
+        cf.cf_graph_begin()
+        cf.cf_gemm_softmax(Q, K, d["scale"], S2, ws=ws, unfused=True)
+        h = cf.cf_graph_end()
+        for _ in range(3):
+            S2.zero_()
+            cf.cf_graph_launch(h)
+            s.synchronize()
+            assert torch.equal(S1, S2)
+        cf.cf_graph_destroy(h)
+
+
+def test_one_workspace_shared_by_every_op():
+    """Any later call of any op accepts a workspace earlier calls left behind."""
+    big = max(cf.cf_workspace_bytes(op, *dims) for op, dims in [
+        (cf.CF_OP_STITCH_SOFTMAX, (4, 20000, 0)), (cf.CF_OP_STITCH_LAYERNORM, (3, 70001, 0)),
+        (cf.CF_OP_STITCH_POW_BCAST_ADD, (64, 30000, 0)), (cf.CF_OP_GEMM_LN, (512, 1024, 128)),
+        (cf.CF_OP_GEMM_SOFTMAX, (512, 1024, 128))])
+    ws = cf.Workspace(big)
+    s = gen.softmax_inputs(seed=1, rows=4, cols=20000)["x"]
+    l = gen.layernorm_inputs(seed=2, rows=3, cols=70001)["x"]
+    p = gen.pow_bcast_add_inputs(seed=3)
+    g = gen.gemm_ln_inputs(seed=4, M=512, N=1024, K=128)
+    q = gen.gemm_softmax_inputs(seed=5, M=512, N=1024, D=128)
+    og = oracle.gemm_ln(g["a"], g["w"], g["bias"], g["r"], g["gamma"], g["beta"])
+    oq = oracle.gemm_softmax(q["q"], q["k"], q["scale"])
+    for _ in range(2):
+        for step in range(5):
+            if step == 0:
+                y = empty_f32(4, 20000)
+                cf.cf_stitch_softmax(d32(s), y, ws=ws)
+                err = rownorm_err(host(y), oracle.softmax_rows(s))
+            elif step == 1:
+                Y = torch.empty((512, 1024), dtype=torch.bfloat16, device="cuda")
+                cf.cf_gemm_ln(dbf16(g["a_bits"]), dbf16(g["w_bits"]), d32(g["bias"]), dbf16(g["r_bits"]),
+                              d32(g["gamma"]), d32(g["beta"]), Y, ws=ws)
+                err = rownorm_err(host(Y), og) / TOL_BF16 * TOL_F32
+            elif step == 2:
+                y = empty_f32(3, 70001)
+                cf.cf_stitch_layernorm(d32(l), y, ws=ws)
+                err = rownorm_err(host(y), oracle.layernorm_rows(l))
+            elif step == 3:
+                S = torch.empty((512, 1024), dtype=torch.bfloat16, device="cuda")
+                cf.cf_gemm_softmax(dbf16(q["q_bits"]), dbf16(q["k_bits"]), q["scale"], S, ws=ws)
+                err = rownorm_err(host(S), oq) / TOL_BF16 * TOL_F32
+            else:
+                y = empty_f32(64, 30000)
+                cf.cf_stitch_pow_bcast_add(d32(p["x"]), d32(p["v"]), 1.5, y, ws=ws)
+                err = rownorm_err(host(y), oracle.pow_bcast_add_softmax(p["x"], p["v"], 1.5)[0])
+            assert ws.error_word() == 0, f"step {step}: a join gave up"
+            assert err <= TOL_F32, (step, err)
