@@ -79,7 +79,7 @@ int pow2ceil(int64_t v) {
 // can be reused by any later call of any op.
 constexpr size_t kHeader = 256;
 constexpr int64_t kMaxJoins = 16384;
-constexpr size_t kPartialsOff = kHeader + kMaxJoins * sizeof(JoinWord);
+constexpr size_t kPartialsOff = kHeader + kMaxJoins * sizeof(uint64_t);
 
 struct WsLayout {
   size_t joins_off = 0, partials_off = 0, total = 0;
@@ -115,7 +115,7 @@ cf_status plan_rows(int op, int64_t rows, int64_t cols, bool vec_ok, RowPlan* pl
     // task splitting: S members per row, each holding <= 16 fragments per lane
     const int64_t s_min = (nvec + 256 * 16 - 1) / (256 * 16);
     int64_t S = std::max<int64_t>(s_min, rows >= di->cus ? 1 : pow2ceil((di->cus + rows - 1) / rows));
-    if (force_split > 1) S = force_split;
+    if (force_split > 1) S = std::max<int64_t>(force_split, s_min);
     const int64_t slice_vec = (nvec + S - 1) / S;
     p.split = (int)S;
     p.nv = pow2ceil((slice_vec + 255) / 256);
@@ -181,7 +181,7 @@ cf_status run_rows(const char* name, int op, const float* x, float* y, float* y_
     const WsLayout L = ws_layout(rows * p.split * 4);
     char* base = static_cast<char*>(ws);
     a.err = reinterpret_cast<uint32_t*>(base);
-    a.joins = reinterpret_cast<JoinWord*>(base + L.joins_off);
+    a.joins = reinterpret_cast<uint64_t*>(base + L.joins_off);
     a.partials = reinterpret_cast<float*>(base + L.partials_off);
   }
   a.S = p.split;
@@ -198,8 +198,10 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   if (s != CF_OK) return s;
   GemmPlan p;
   p.nn = nn ? 1 : 0;
-  // default tile configs: the largest spill-free tile per epilogue
-  const int dflt = epi == kEpiStoreF32 ? 0 : 3;
+  // Default tiles (measured on MI355X): GEMM+LN 128x256 (a 4096-wide row spans
+  // 16 tiles), GEMM+softmax 64x512 (an 8192-wide row spans 16 tiles), plain
+  // GEMM 256x256.
+  const int dflt = epi == kEpiSoftmax ? 4 : (epi == kEpiLN ? 2 : 0);
   p.cfg = (int)env_int(epi == kEpiSoftmax ? "CF_GEMM_SOFTMAX_CFG" : (epi == kEpiLN ? "CF_GEMM_LN_CFG" : "CF_GEMM_CFG"), dflt);
   if (!gemm_tile_config(p.cfg, &p.bm, &p.bn, &p.bk)) return CF_EUNSUPPORTED;
   const int64_t tn = (N + p.bn - 1) / p.bn, tm = (M + p.bm - 1) / p.bm;
@@ -217,31 +219,37 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
     p.grid = (int)G;
   }
   p.rounds = (int)((p.tiles + p.grid - 1) / p.grid);
+  // [ComFuse] dual-mode inter-CTA aggregation: peer-to-peer for small groups,
+  // leader-follower for large ones (threshold from measurement on MI355X).
+  const long agg = env_int("CF_AGG_LEADER", -1);
+  p.leader = agg >= 0 ? (agg != 0) : (tn > 8);
   *pl = p;
   return CF_OK;
 }
 
 size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N) {
-  const int64_t tn = (N + p.bn - 1) / p.bn, tm = (M + p.bm - 1) / p.bm;
-  (void)tm;
-  return ws_layout(M * tn * 4).total;
+  const int64_t tn = (N + p.bn - 1) / p.bn;
+  return ws_layout(M * tn * 4 + M * 2).total;
 }
 
-void record_gemm_plan(const char* name, const GemmPlan& p, int64_t M, int64_t N, int64_t K, int leader) {
+void record_gemm_plan(const char* name, const GemmPlan& p, int64_t M, int64_t N, int64_t K) {
   char buf[512];
   snprintf(buf, sizeof buf,
            "{\"call\":\"%s\",\"M\":%lld,\"N\":%lld,\"K\":%lld,\"kernel\":\"k_gemm\",\"tile\":[%d,%d,%d],"
            "\"layout\":\"%s\",\"tiles\":%d,\"row_group\":%lld,\"grid\":%d,\"block\":256,\"occupancy\":%d,"
            "\"rounds\":%d,\"aggregation\":\"%s\"}",
            name, (long long)M, (long long)N, (long long)K, p.bm, p.bn, p.bk, p.nn ? "NN" : "NT", p.tiles,
-           (long long)((N + p.bn - 1) / p.bn), p.grid, p.occupancy, p.rounds, leader ? "leader" : "all-read");
+           (long long)((N + p.bn - 1) / p.bn), p.grid, p.occupancy, p.rounds, p.leader ? "leader" : "peer-to-peer");
   g_last_plan = buf;
 }
 
 cf_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return CF_EINVAL;
   if (N % 8 != 0 || K % 8 != 0) return CF_EUNSUPPORTED;
-  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31) return CF_EUNSUPPORTED;
+  // every operand is addressed through a buffer descriptor with 32-bit offsets
+  // below 2^31 (the out-of-range offset)
+  const int64_t lim = (int64_t)1 << 31;
+  if (M * K * 2 >= lim || N * K * 2 >= lim || M * N * 2 >= lim) return CF_EUNSUPPORTED;
   return CF_OK;
 }
 
@@ -323,15 +331,16 @@ static cf_status run_gemm(const char* name, int epi, bool nn, GemmArgs a, void* 
   const size_t need = gemm_ws_bytes(p, a.M, a.N);
   if (!ws || ws_bytes < need) return CF_EWORKSPACE;
   const int64_t tn = (a.N + p.bn - 1) / p.bn, tm = (a.M + p.bm - 1) / p.bm;
-  const WsLayout L = ws_layout(a.M * tn * 4);
+  const WsLayout L = ws_layout(a.M * tn * 4 + a.M * 2);
   char* base = static_cast<char*>(ws);
   a.err = reinterpret_cast<uint32_t*>(base);
-  a.joins = reinterpret_cast<JoinWord*>(base + L.joins_off);
+  a.joins = reinterpret_cast<uint64_t*>(base + L.joins_off);
   a.partials = reinterpret_cast<float*>(base + L.partials_off);
+  a.finals = a.partials + a.M * tn * 4;
   a.tiles_n = (int)tn;
   a.tiles_m = (int)tm;
-  a.agg_leader = 0;
-  record_gemm_plan(name, p, a.M, a.N, a.K, a.agg_leader);
+  a.agg_leader = p.leader ? 1 : 0;
+  record_gemm_plan(name, p, a.M, a.N, a.K);
   return launch_gemm(epi, p, a, stream) == hipSuccess ? CF_OK : CF_EHIP;
 }
 

@@ -1,29 +1,32 @@
 // bf16 MFMA GEMM whose epilogue runs a stitched stage DAG across output tiles.
 //
-// MainLoop ([ComFuse] Stage-Stream Execution Model, tile-level streaming):
-// each workgroup of 4 waves (2 x 2) computes a BM x BN accumulator tile with
-// v_mfma_f32_32x32x16_bf16, staging BK-deep operand tiles in a two-stage LDS
-// ring fed through registers (the next stage's global loads are in flight
-// while the current stage feeds the MFMAs; [ComFuse] B2BGEMM producer and
-// multi-stage circular buffer).  LDS rows are XOR-swizzled so fragment reads
-// are bank-conflict free.  A [M x K] is K-contiguous.  The right operand is
-// either W [K x N] (N-contiguous; fragments come from the LDS transpose read
-// ds_read_b64_tr_b16) or K [N x K] (K-contiguous; plain 16-byte reads).
+// MainLoop ([ComFuse] Stage-Stream Execution Model, tile-level streaming;
+// B2BGEMM producer with a multi-stage circular buffer): each workgroup of 4
+// waves computes a BM x BN fp32 accumulator tile with v_mfma_f32_32x32x16_bf16.
+// Operand tiles BK deep stream into a STAGES-deep LDS ring with direct
+// global->LDS buffer loads (no VGPR staging; out-of-range chunks read as zero
+// through the buffer descriptor's range check).  LDS rows are XOR-swizzled so
+// the fragment reads are bank-conflict free.  A [M x K] is K-contiguous.  The
+// right operand is W [K x N] (N-contiguous; fragments come from the LDS
+// transpose read ds_read_b64_tr_b16) or K [N x K] (K-contiguous).
 //
-// The MFMA is issued with the operands swapped (MFMA A = right operand,
-// MFMA B = left operand) and with a fixed permutation of the right operand's
-// columns, so that each lane's 16 accumulator values are 16 CONSECUTIVE
-// columns of ONE output row.  Row reductions are therefore mostly
-// thread-local, and epilogue loads/stores are 32-byte row segments.
+// The MFMA is issued with its operands swapped (MFMA A = right operand,
+// MFMA B = left operand) and a fixed permutation of the right operand's
+// columns, so each lane's 16 accumulator values are 16 CONSECUTIVE columns of
+// ONE output row: row statistics are mostly thread-local.
 //
-// Epilogue ([ComFuse] Fig. 3 stage chain with bypass; inter-CTA level): the
-// accumulator stays in registers through every stage.  Per-row statistics are
-// reduced thread -> lane pair -> LDS (across the 2 column waves) -> across the
-// tiles of the row group through global memory with an in-kernel join.  A
-// persistent grid walks tiles in rounds that contain whole row groups, and the
-// host sizes the grid to what is resident at once, so every join completes
-// ([AStitch] "What it costs": barrier validity requires residency).  Each
-// output element has exactly one owning tile ([sass2mlir] "Epilogue fusion").
+// Epilogue ([ComFuse] Fig. 3 stage chain with bypass; inter-CTA level with
+// dual-mode aggregation): the accumulator stays in registers through every
+// stage.  The residual tile arrives through LDS with coalesced loads; per-row
+// statistics reduce thread -> lane pair -> LDS (across column waves) -> across
+// the tiles of the row group through global memory with an in-kernel join.
+// Small row groups aggregate peer to peer (every member reads every partial);
+// large ones elect the last arriver as leader, which combines and publishes
+// one result per row that followers read, keeping the exchange traffic linear
+// in the group size.  The output tile is staged in LDS and written as whole
+// rows.  A persistent grid walks tiles in rounds of whole row groups sized to
+// what is resident at once ([AStitch] "What it costs"); each output element
+// has one owner ([sass2mlir] "Epilogue fusion").
 #include "dev.hpp"
 #include "kernels.hpp"
 
@@ -36,8 +39,10 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kThreads = 256;
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset beyond every range: reads zero
 
 // 16-byte-chunk XOR swizzle for K-contiguous tiles [rows][BK]: 8 consecutive
 // rows reading the same logical chunk hit 8 distinct 16-byte bank groups.
@@ -49,144 +54,160 @@ __device__ __forceinline__ int swz(int row, int c) {
   return c ^ ((row / RD) % MOD);
 }
 
-// Byte-offset XOR for N-contiguous tiles [BK][BN]: the 4 k-rows a transpose
+// Byte-offset XOR for N-contiguous tiles [BK][BN]: the 4 k-rows one transpose
 // read touches land 0, 16, 64 and 80 bytes apart modulo the bank width.
 __device__ __forceinline__ int nn_mask(int k) { return ((k & 1) << 4) | (((k >> 1) & 1) << 6); }
 
 // Output column (within a 32-column block) of MFMA row i under the permutation
-// that makes lane (l >> 5) hold columns 16*(l>>5) .. 16*(l>>5)+15.
+// that gives lane l the columns 16*(l>>5) .. 16*(l>>5)+15.
 __device__ __forceinline__ int sigma(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
+// 16-byte chunk swizzle of the epilogue's row-major LDS tiles (residual in,
+// output out): lanes 0..31 touch 32 rows at one column.
+__device__ __forceinline__ int eswz(int row, int c) { return c ^ (row & 7); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// One 16-byte direct global->LDS load per lane: lane p of the wave writes
+// lds_base + 16 * p (lds_base is wave-uniform).  voff = kOOB loads zeros.
+__device__ __forceinline__ void g2l16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, (int)voff, 0, 0, 0);
+}
+
 template <int BM, int BN, int BK, bool NN>
-struct Tile {
-  static constexpr int CPR = BK / 8;             // 16-byte chunks per K-row
-  static constexpr int CA = BM * BK / 8 / kThreads;
-  static constexpr int CB = BN * BK / 8 / kThreads;
-  static constexpr int A_ELEMS = BM * BK;
-  static constexpr int B_ELEMS = BN * BK;
-  static constexpr int STAGE = A_ELEMS + B_ELEMS;  // bf16 elements per LDS stage
-  static_assert(CA * kThreads * 8 == BM * BK && CB * kThreads * 8 == BN * BK, "tile/threads");
+struct Ring {
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = BN * BK * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LA = A_BYTES / 4096;  // 1 KB wave loads per thread for A
+  static constexpr int LB = B_BYTES / 4096;
+  static_assert(LA * 4096 == A_BYTES && LB * 4096 == B_BYTES, "tile bytes must be a multiple of 4 KB");
 
-  uint4 ra[CA];
-  uint4 rb[CB];
-
-  __device__ __forceinline__ void load(const GemmArgs& a, int64_t m0, int64_t n0, int64_t k0) {
-    const int t = threadIdx.x;
+  // Issue the direct loads of one K-stage into `st`.  Lane p of wave w in
+  // instruction j writes LDS byte (j*4 + w)*1024 + 16p of the operand region;
+  // the lane picks the global chunk that belongs at that (swizzled) position.
+  __device__ __forceinline__ static void load(const GemmArgs& a, __amdgpu_buffer_rsrc_t ra,
+                                              __amdgpu_buffer_rsrc_t rb, char* st, int64_t m0, int64_t n0,
+                                              int64_t k0) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < CA; ++j) {
-      const int id = j * kThreads + t;
-      const int row = id / CPR, c = id % CPR;
+    for (int j = 0; j < LA; ++j) {
+      const int o = (j * 4 + w) * 1024 + lane * 16;
+      const int row = o / (BK * 2), pc = (o % (BK * 2)) / 16;
+      const int c = swz<BK>(row, pc);  // logical chunk stored at physical chunk pc
       const int64_t gm = m0 + row, gk = k0 + 8 * c;
-      ra[j] = (gm < a.M && gk < a.K) ? *reinterpret_cast<const uint4*>(a.A + gm * a.K + gk)
-                                     : make_uint4(0, 0, 0, 0);
+      const uint32_t off = (gm < a.M && gk < a.K) ? (uint32_t)((gm * a.K + gk) * 2) : kOOB;
+      g2l16(ra, st + (j * 4 + w) * 1024, off);
     }
-    if constexpr (NN) {
-      constexpr int CPRB = BN / 8;
 #pragma unroll
-      for (int j = 0; j < CB; ++j) {
-        const int id = j * kThreads + t;
-        const int k = id / CPRB, c = id % CPRB;
-        const int64_t gk = k0 + k, gn = n0 + 8 * c;
-        rb[j] = (gk < a.K && gn < a.N) ? *reinterpret_cast<const uint4*>(a.B + gk * a.N + gn)
-                                       : make_uint4(0, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < CB; ++j) {
-        const int id = j * kThreads + t;
-        const int row = id / CPR, c = id % CPR;
+    for (int j = 0; j < LB; ++j) {
+      const int o = (j * 4 + w) * 1024 + lane * 16;
+      uint32_t off;
+      if constexpr (NN) {
+        const int k = o / (BN * 2), pb = o % (BN * 2);
+        const int cb = (pb ^ nn_mask(k)) / 16;  // logical 16-byte chunk along N
+        const int64_t gk = k0 + k, gn = n0 + 8 * cb;
+        off = (gk < a.K && gn < a.N) ? (uint32_t)((gk * a.N + gn) * 2) : kOOB;
+      } else {
+        const int row = o / (BK * 2), pc = (o % (BK * 2)) / 16;
+        const int c = swz<BK>(row, pc);
         const int64_t gn = n0 + row, gk = k0 + 8 * c;
-        rb[j] = (gn < a.N && gk < a.K) ? *reinterpret_cast<const uint4*>(a.B + gn * a.K + gk)
-                                       : make_uint4(0, 0, 0, 0);
+        off = (gn < a.N && gk < a.K) ? (uint32_t)((gn * a.K + gk) * 2) : kOOB;
       }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint16_t* st) const {
-    const int t = threadIdx.x;
-    uint16_t* As = st;
-    uint16_t* Bs = st + A_ELEMS;
-#pragma unroll
-    for (int j = 0; j < CA; ++j) {
-      const int id = j * kThreads + t;
-      const int row = id / CPR, c = id % CPR;
-      *reinterpret_cast<uint4*>(As + row * BK + 8 * swz<BK>(row, c)) = ra[j];
-    }
-    if constexpr (NN) {
-      constexpr int CPRB = BN / 8;
-#pragma unroll
-      for (int j = 0; j < CB; ++j) {
-        const int id = j * kThreads + t;
-        const int k = id / CPRB, c = id % CPRB;
-        char* rowp = reinterpret_cast<char*>(Bs) + k * (BN * 2);
-        *reinterpret_cast<uint4*>(rowp + ((16 * c) ^ nn_mask(k))) = rb[j];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < CB; ++j) {
-        const int id = j * kThreads + t;
-        const int row = id / CPR, c = id % CPR;
-        *reinterpret_cast<uint4*>(Bs + row * BK + 8 * swz<BK>(row, c)) = rb[j];
-      }
+      g2l16(rb, st + A_BYTES + (j * 4 + w) * 1024, off);
     }
   }
 };
 
-// One BK-deep stage of MFMAs from LDS.
+// Fragment reads for one 16-deep k-step from an LDS stage.
 template <int BM, int BN, int BK, bool NN, int RB, int CB>
-__device__ __forceinline__ void mma_stage(const uint16_t* st, f32x16 (&acc)[RB][CB], int wm, int wn) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+__device__ __forceinline__ void load_frags(const char* st, int ks, bf16x8_t (&bop)[RB], bf16x8_t (&aop)[CB], int wm,
+                                           int wn) {
+  constexpr int WM = RB * 32, WN = CB * 32;
   const int lane = threadIdx.x & 63;
-  const uint16_t* As = st;
-  const uint16_t* Bs = st + BM * BK;
+  const uint16_t* As = reinterpret_cast<const uint16_t*>(st);
+  const char* Bs = st + BM * BK * 2;
 #pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    bf16x8_t bop[RB];  // left operand rows (MFMA B)
-    bf16x8_t aop[CB];  // right operand columns (MFMA A)
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = wm * WM + rb * 32 + (lane & 31);
+    const int c = 2 * ks + (lane >> 5);
+    bop[rb] = *reinterpret_cast<const bf16x8_t*>(As + row * BK + 8 * swz<BK>(row, c));
+  }
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int row = wm * WM + rb * 32 + (lane & 31);
-      const int c = 2 * ks + (lane >> 5);
-      bop[rb] = *reinterpret_cast<const bf16x8_t*>(As + row * BK + 8 * swz<BK>(row, c));
-    }
+  for (int cb = 0; cb < CB; ++cb) {
+    if constexpr (NN) {
+      const int G = lane >> 4, L = lane & 15;
+      const int e = L >> 2, cc = L & 3;
+      const int kbase = 8 * (G >> 1);
+      const int n = wn * WN + cb * 32 + 16 * (cc & 1) + 8 * (G & 1) + 4 * (cc >> 1);
+      bf16x4_t h[2];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      if constexpr (NN) {
-        const int G = lane >> 4, L = lane & 15;
-        const int e = L >> 2, cc = L & 3;
-        const int kbase = 8 * (G >> 1);
-        const int n = wn * WN + cb * 32 + 16 * (cc & 1) + 8 * (G & 1) + 4 * (cc >> 1);
-        bf16x4_t h[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int k = ks * 16 + kbase + 4 * hh + e;
-          const char* p = reinterpret_cast<const char*>(Bs) + k * (BN * 2) + ((2 * n) ^ nn_mask(k));
-          h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
-        }
-        aop[cb] = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
-      } else {
-        const int n = wn * WN + cb * 32 + sigma(lane & 31);
-        const int c = 2 * ks + (lane >> 5);
-        aop[cb] = *reinterpret_cast<const bf16x8_t*>(Bs + n * BK + 8 * swz<BK>(n, c));
+      for (int hh = 0; hh < 2; ++hh) {
+        const int k = ks * 16 + kbase + 4 * hh + e;
+        const char* p = Bs + k * (BN * 2) + ((2 * n) ^ nn_mask(k));
+        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
       }
+      aop[cb] = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      const int n = wn * WN + cb * 32 + sigma(lane & 31);
+      const int c = 2 * ks + (lane >> 5);
+      aop[cb] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const uint16_t*>(Bs) + n * BK +
+                                                   8 * swz<BK>(n, c));
     }
+  }
+}
+
+// One BK-deep stage of MFMAs from LDS.  The fragments of k-step ks+1 are read
+// while the MFMAs of step ks issue (two fragment register sets), and the
+// scheduler is asked to interleave LDS reads and the next stage's buffer loads
+// one by one between MFMAs, so a single wave per SIMD keeps the matrix core fed.
+template <int BM, int BN, int BK, bool NN, int RB, int CB, int NVMEM>
+__device__ __forceinline__ void mma_stage(const char* st, f32x16 (&acc)[RB][CB], int wm, int wn) {
+  constexpr int KS = BK / 16;
+  constexpr int NDS = RB + (NN ? 2 : 1) * CB;  // LDS read instructions per k-step
+  bf16x8_t bop[2][RB], aop[2][CB];
+  load_frags<BM, BN, BK, NN, RB, CB>(st, 0, bop[0], aop[0], wm, wn);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < KS) load_frags<BM, BN, BK, NN, RB, CB>(st, ks + 1, bop[cur ^ 1], aop[cur ^ 1], wm, wn);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
-        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[cb], bop[rb], acc[rb][cb], 0, 0, 0);
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[cur][cb], bop[cur][rb], acc[rb][cb], 0, 0, 0);
+    // interleave: each MFMA followed by up to one LDS read and one buffer load
+    constexpr int NM = RB * CB;
+    const int nds = (ks + 1 < KS) ? NDS : 0;
+    constexpr int nvm = (NVMEM + KS - 1) / KS;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // 1 MFMA
+      if (i < nds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // 1 DS read
+      if (i < nvm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // 1 VMEM read
+    }
   }
 }
 
-// Cross-wave (column halves) combine of per-row values through LDS.  red has
-// 2 slots x 2 waves x BM floats; the slot alternates per call.
-template <class Op, int BM, int RB>
+// Cross-wave (column waves) combine of per-row values through LDS.
+// red: 2 slots x WGN x BM floats; the slot alternates per call, so one barrier
+// per reduction suffices.
+template <class Op, int BM, int WGN, int RB>
 __device__ __forceinline__ void tile_row_reduce(float (&v)[RB], float* red, int& slot, int wm, int wn) {
-  constexpr int WM = BM / 2;
+  constexpr int WM = RB * 32;
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) v[rb] = Op::op(v[rb], __shfl_xor(v[rb], 32, kWave));
-  float* s = red + slot * (2 * BM);
+  float* s = red + slot * (WGN * BM);
   if (lane < 32) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) s[wn * BM + wm * WM + rb * 32 + lane] = v[rb];
@@ -195,28 +216,77 @@ __device__ __forceinline__ void tile_row_reduce(float (&v)[RB], float* red, int&
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int r = wm * WM + rb * 32 + (lane & 31);
-    v[rb] = Op::op(s[r], s[BM + r]);
+    float x = s[r];
+#pragma unroll
+    for (int q = 1; q < WGN; ++q) x = Op::op(x, s[q * BM + r]);
+    v[rb] = x;
   }
   slot ^= 1;
 }
 
+// Row statistics merges (member order fixed, so every member gets identical bits).
+// LN: (count, mean, M2) by Chan's pairwise update.  Softmax: (max, sum) online.
+struct MergeLN {
+  float n = 0.f, mean = 0.f, m2 = 0.f;
+  __device__ void add(float4 q) {
+    const float nb = q.x;
+    if (nb == 0.f) return;
+    const float nn = n + nb;
+    const float d = q.y - mean;
+    mean += d * (nb / nn);
+    m2 += q.z + d * d * (n * nb / nn);
+    n = nn;
+  }
+  __device__ float4 part() const { return make_float4(n, mean, m2, 0.f); }
+};
+struct MergeSM {
+  float m = -INFINITY, l = 0.f;
+  __device__ void add(float4 q) {
+    if (q.x == -INFINITY) return;
+    if (q.x > m) {
+      l = l * __builtin_amdgcn_exp2f(m - q.x) + q.y;
+      m = q.x;
+    } else {
+      l += q.y * __builtin_amdgcn_exp2f(q.x - m);
+    }
+  }
+  __device__ float4 part() const { return make_float4(m, l, 0.f, 0.f); }
+};
+
+template <int EPI, int BM, int BN, int BK, int STAGES>
+constexpr int gemm_lds_bytes() {
+  constexpr int ring = STAGES * (BM + BN) * BK * 2;
+  // bf16 tile + red (2 x 4 x BM floats) + pub (BM float4) + parts (256 float4) + stat (BM float2) + flags
+  constexpr int epi = EPI == kEpiStoreF32 ? BM * BN * 4 / 2
+                                          : BM * BN * 2 + 32 * BM + 16 * BM + 16 * 256 + 8 * BM + 64;
+  return ring > epi ? ring : epi;
+}
+
 }  // namespace
 
-template <int EPI, bool NN, int BM, int BN, int BK, int MINB>
+template <int EPI, bool NN, int BM, int BN, int BK, int WGM, int STAGES, int MINB>
 __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
-  using T = Tile<BM, BN, BK, NN>;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  using RG = Ring<BM, BN, BK, NN>;
+  constexpr int WGN = 4 / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int RB = WM / 32, CB = WN / 32;
-  __shared__ __align__(16) uint16_t lds[2 * T::STAGE];
+  constexpr int LDS = gemm_lds_bytes<EPI, BM, BN, BK, STAGES>();
+  constexpr int C16 = BN * 2 / 16;  // 16-byte chunks per bf16 output row
+  constexpr int NP = BM >= kThreads ? 1 : kThreads / BM;  // threads combining one row's partials
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && WGM * WGN == 4, "wave tile");
+  static_assert(C16 >= 8 && (BM * C16) % kThreads == 0, "epilogue tile");
+  __shared__ __align__(16) char lds[LDS];
 
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WGN, wn = w % WGN;
   const int hl = lane >> 5, l32 = lane & 31;
   const int KT = (int)((a.K + BK - 1) / BK);
   const uint32_t G = gridDim.x;
   const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
   const uint32_t g = (EPI == kEpiStoreF32) ? blockIdx.x : xcd_local_id(blockIdx.x, G);
+  const __amdgpu_buffer_rsrc_t rA = rsrc(a.A, (uint32_t)(a.M * a.K * 2));
+  const __amdgpu_buffer_rsrc_t rB = rsrc(a.B, (uint32_t)(a.N * a.K * 2));
 
   for (int64_t tile = g; tile < tiles; tile += G) {
     const int64_t rowblk = tile / a.tiles_n;
@@ -232,41 +302,65 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
         for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
 
     // ------------------------------------------------------------ MainLoop
-    T tl;
-    tl.load(a, m0, n0, 0);
-    tl.store(lds);
-    __syncthreads();
+    // Stage kt lives in ring slot kt % STAGES.  Before computing stage kt each
+    // thread waits until at most STAGES-2 later stages' loads are outstanding;
+    // the barrier then publishes stage kt to every wave and retires slot
+    // (kt-1) % STAGES, which the next stage's loads refill.
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) RG::load(a, rA, rB, lds + s * RG::STAGE_BYTES, m0, n0, (int64_t)s * BK);
+    // One stage is issued every iteration (stages past K read zeros through the
+    // range check and move no data), so exactly STAGES-2 later stages are in
+    // flight when stage kt is awaited and the loop body has no branch.
     for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) tl.load(a, m0, n0, (int64_t)(kt + 1) * BK);
-      mma_stage<BM, BN, BK, NN, RB, CB>(lds + cur * T::STAGE, acc, wm, wn);
-      if (kt + 1 < KT) tl.store(lds + (cur ^ 1) * T::STAGE);
+      wait_vm<(STAGES - 2) * (RG::LA + RG::LB)>();
       __syncthreads();
+      RG::load(a, rA, rB, lds + ((kt + STAGES - 1) % STAGES) * RG::STAGE_BYTES, m0, n0,
+               (int64_t)(kt + STAGES - 1) * BK);
+      mma_stage<BM, BN, BK, NN, RB, CB, RG::LA + RG::LB>(lds + (kt % STAGES) * RG::STAGE_BYTES, acc, wm, wn);
     }
+    wait_vm<0>();
+    __syncthreads();  // every wave is done with the ring: it is free from here on
 
     // lane's output coordinates: row(rb) = m0 + wm*WM + rb*32 + l32,
     // cols(cb) = n0 + wn*WN + cb*32 + 16*hl + [0, 16)
     if constexpr (EPI == kEpiStoreF32) {
+      // fp32 tile staged through LDS half a tile at a time, written as rows
+      float* ot = reinterpret_cast<float*>(lds);
+      constexpr int F4 = BN / 4;     // float4 chunks per row
+      constexpr int HROWS = BM / 2;  // rows per half
+      for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int64_t row = m0 + wm * WM + rb * 32 + l32;
-        if (row >= a.M) continue;
+        for (int rb = 0; rb < RB; ++rb) {
+          const int rl = wm * WM + rb * 32 + l32;
+          if (rl / HROWS != half) continue;
+          const int rr = rl - half * HROWS;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const int64_t col = n0 + wn * WN + cb * 32 + 16 * hl;
+          for (int cb = 0; cb < CB; ++cb) {
+            const int c4 = (wn * WN + cb * 32 + 16 * hl) / 4;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (col + 4 * q < a.N)
-              st4_stream(a.Z + row * a.N + col + 4 * q,
-                         make_float4(acc[rb][cb][4 * q], acc[rb][cb][4 * q + 1], acc[rb][cb][4 * q + 2],
-                                     acc[rb][cb][4 * q + 3]));
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<float4*>(ot + rr * BN + 4 * ((c4 + q) ^ (rr & 7))) =
+                  make_float4(acc[rb][cb][4 * q], acc[rb][cb][4 * q + 1], acc[rb][cb][4 * q + 2],
+                              acc[rb][cb][4 * q + 3]);
+          }
         }
+        __syncthreads();
+        for (int id = t; id < HROWS * F4; id += kThreads) {
+          const int rr = id / F4, c = id % F4;
+          const int64_t row = m0 + half * HROWS + rr, col = n0 + 4 * c;
+          if (row < a.M && col < a.N)
+            st4_stream(a.Z + row * a.N + col, *reinterpret_cast<const float4*>(ot + rr * BN + 4 * (c ^ (rr & 7))));
+        }
+        __syncthreads();
       }
     } else {
-      // The staging ring is free now; reuse it as the epilogue's LDS scratch.
-      float* red = reinterpret_cast<float*>(lds);        // 2 slots x 2 x BM
-      float4* pub = reinterpret_cast<float4*>(red + 4 * BM);  // BM published partials
-      float2* stat = reinterpret_cast<float2*>(pub + BM);     // BM combined statistics
+      // LDS carve-up (the ring is free): output / residual tile, then scratch.
+      uint16_t* tile16 = reinterpret_cast<uint16_t*>(lds);                  // BM x BN bf16
+      float* red = reinterpret_cast<float*>(lds + BM * BN * 2);              // 2 x WGN x BM
+      float4* pub = reinterpret_cast<float4*>(red + 2 * 4 * BM);             // BM
+      float4* parts = pub + BM;                                              // 256 (NP per row)
+      float2* stat = reinterpret_cast<float2*>(parts + kThreads);            // BM
+      int* flag = reinterpret_cast<int*>(stat + BM);                         // last-arriver flag, gen0
       int slot = 0;
       const float n_tile = (float)(a.N - n0 < BN ? a.N - n0 : (int64_t)BN);
 
@@ -280,37 +374,47 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
 
       float p0[RB], p1[RB], p2[RB];
       if constexpr (EPI == kEpiLN) {
+        // residual tile -> LDS with coalesced direct loads (whole rows)
+        if (a.R != nullptr) {
+          const __amdgpu_buffer_rsrc_t rR = rsrc(a.R, (uint32_t)(a.M * a.N * 2));
+#pragma unroll
+          for (int j = 0; j < BM * C16 / kThreads; ++j) {
+            const int o = (j * 4 + w) * 1024 + lane * 16;
+            const int row = o / (BN * 2), pc = (o % (BN * 2)) / 16;
+            const int c = eswz(row, pc);
+            const int64_t gm = m0 + row, gn = n0 + 8 * c;
+            const uint32_t off = (gm < a.M && gn < a.N) ? (uint32_t)((gm * a.N + gn) * 2) : kOOB;
+            g2l16(rR, lds + (j * 4 + w) * 1024, off);
+          }
+        }
+        wait_vm<0>();
+        __syncthreads();
         // stage 1: u = acc + bias_j + R_ij, kept in the accumulator registers
-        float bv[CB][16];
+        // (one column block at a time, so only its 16 bias values are live)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          const int64_t col = n0 + wn * WN + cb * 32 + 16 * hl;
+          const int cl0 = wn * WN + cb * 32 + 16 * hl;
+          const int64_t col = n0 + cl0;
+          float bv[16];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float4 b = colok[cb][q >> 1] ? *reinterpret_cast<const float4*>(a.bias + col + 4 * q)
                                                : make_float4(0.f, 0.f, 0.f, 0.f);
-            bv[cb][4 * q] = b.x; bv[cb][4 * q + 1] = b.y; bv[cb][4 * q + 2] = b.z; bv[cb][4 * q + 3] = b.w;
-          }
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int64_t row = m0 + wm * WM + rb * 32 + l32;
-          u32x4 rr[CB][2];
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            const int64_t col = n0 + wn * WN + cb * 32 + 16 * hl;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              rr[cb][h] = (a.R != nullptr && row < a.M && colok[cb][h])
-                              ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.R + row * a.N + col + 8 * h))
-                              : u32x4{0u, 0u, 0u, 0u};
+            bv[4 * q] = b.x; bv[4 * q + 1] = b.y; bv[4 * q + 2] = b.z; bv[4 * q + 3] = b.w;
           }
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
+          for (int rb = 0; rb < RB; ++rb) {
+            const int rl = wm * WM + rb * 32 + l32;
+            u32x4 rr[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+            if (a.R != nullptr) {
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                rr[h] = *reinterpret_cast<const u32x4*>(tile16 + rl * BN + 8 * eswz(rl, cl0 / 8 + h));
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const uint32_t wv = rr[cb][r >> 3][(r & 7) >> 1];
-              const float u = acc[rb][cb][r] + bv[cb][r] + ((r & 1) ? bf16_hi(wv) : bf16_lo(wv));
+              const uint32_t wv = rr[r >> 3][(r & 7) >> 1];
+              const float u = acc[rb][cb][r] + bv[r] + ((r & 1) ? bf16_hi(wv) : bf16_lo(wv));
               acc[rb][cb][r] = colok[cb][r >> 3] ? u : 0.0f;
             }
           }
@@ -326,7 +430,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
             for (int r = 0; r < 16; ++r) v += acc[rb][cb][r];
           s[rb] = v;
         }
-        tile_row_reduce<OpSum, BM, RB>(s, red, slot, wm, wn);
+        tile_row_reduce<OpSum, BM, WGN, RB>(s, red, slot, wm, wn);
         float mt[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) mt[rb] = s[rb] / n_tile;
@@ -343,7 +447,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
             }
           s[rb] = v;
         }
-        tile_row_reduce<OpSum, BM, RB>(s, red, slot, wm, wn);
+        tile_row_reduce<OpSum, BM, WGN, RB>(s, red, slot, wm, wn);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           p0[rb] = n_tile;
@@ -366,7 +470,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
             }
           mx[rb] = v;
         }
-        tile_row_reduce<OpMax, BM, RB>(mx, red, slot, wm, wn);
+        tile_row_reduce<OpMax, BM, WGN, RB>(mx, red, slot, wm, wn);
         float l[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -381,7 +485,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
             }
           l[rb] = v;
         }
-        tile_row_reduce<OpSum, BM, RB>(l, red, slot, wm, wn);
+        tile_row_reduce<OpSum, BM, WGN, RB>(l, red, slot, wm, wn);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           p0[rb] = mx[rb];
@@ -396,93 +500,180 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
         for (int rb = 0; rb < RB; ++rb) pub[wm * WM + rb * 32 + l32] = make_float4(p0[rb], p1[rb], p2[rb], 0.f);
       }
       __syncthreads();
+      uint64_t* jw = a.joins + g / a.tiles_n;  // the members of a row group share g / tiles_n every round
+      const int T = a.tiles_n;
       if (w == 0) {
-        float* P = a.partials;
+        float4* P = reinterpret_cast<float4*>(a.partials);
         for (int r = lane; r < BM; r += kWave) {
           const int64_t row = m0 + r;
-          if (row < a.M) {
-            const float4 v = pub[r];
-            float* d = P + ((size_t)row * a.tiles_n + tn) * 4;
-            st_agent(d + 0, v.x);
-            st_agent(d + 1, v.y);
-            st_agent(d + 2, v.z);
-          }
+          if (row < a.M) st_dev4(P + (size_t)row * T + tn, pub[r]);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        // the members of a row group share g / tiles_n in every round
-        if (lane == 0) join_arrive_and_wait(a.joins + g / a.tiles_n, (uint32_t)a.tiles_n, a.err);
+        wait_stores();
+        if (lane == 0) {
+          const uint64_t old = __hip_atomic_fetch_add(jw, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          flag[0] = ((uint32_t)old == (uint32_t)(T - 1)) ? 1 : 0;
+          flag[1] = (int)(uint32_t)(old >> 32);
+        }
       }
       __syncthreads();
+      const bool last = flag[0] != 0;
+      const uint32_t gen0 = (uint32_t)flag[1];
+      const bool leader_mode = a.agg_leader != 0;
 
-      // every member combines all members' partials, in member order
-      if (t < BM) {
-        const int64_t row = m0 + t;
-        float2 st2 = make_float2(0.f, 0.f);
-        if (row < a.M) {
-          const float* P = a.partials + (size_t)row * a.tiles_n * 4;
-          if constexpr (EPI == kEpiLN) {
-            float n = 0.f, mean = 0.f, M2 = 0.f;
-            for (int k = 0; k < a.tiles_n; ++k) {
-              const float nb = ld_agent(P + 4 * k), mb = ld_agent(P + 4 * k + 1), m2b = ld_agent(P + 4 * k + 2);
-              const float nn = n + nb;
-              const float d = mb - mean;
-              mean += d * (nb / nn);
-              M2 += m2b + d * d * (n * nb / nn);
-              n = nn;
+      // Combine every row's T partials with all 256 threads: thread t merges
+      // part t / BM (a contiguous run of members) of row t % BM, then one
+      // thread per row merges the NP parts in order.  Device-scope loads.
+      auto combine_rows = [&]() {
+        const int r = t % BM, q = t / BM;
+        const int per = (T + NP - 1) / NP;
+        const int kb = q * per, ke = min(T, kb + per);
+        const float4* P = reinterpret_cast<const float4*>(a.partials) + (size_t)(m0 + r) * T;
+        const bool valid = (m0 + r < a.M) && q < NP;
+        float4 part;
+        if constexpr (EPI == kEpiLN) {
+          MergeLN mg;
+          if (valid)
+            for (int k0 = kb; k0 < ke; k0 += 8) {
+              float4 v[8];
+#pragma unroll
+              for (int k = 0; k < 8; ++k) v[k] = k0 + k < ke ? ld_dev4(P + k0 + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+              for (int k = 0; k < 8; ++k) mg.add(v[k]);
             }
-            st2 = make_float2(mean, rsqrtf(M2 / (float)a.N + a.eps));
-          } else {
-            float M = -INFINITY;
-            for (int k = 0; k < a.tiles_n; ++k) M = fmaxf(M, ld_agent(P + 4 * k));
-            float L = 0.f;
-            for (int k = 0; k < a.tiles_n; ++k) L += ld_agent(P + 4 * k + 1) * __builtin_amdgcn_exp2f(ld_agent(P + 4 * k) - M);
-            st2 = make_float2(M, 1.0f / L);
+          part = mg.part();
+        } else {
+          MergeSM mg;
+          if (valid)
+            for (int k0 = kb; k0 < ke; k0 += 8) {
+              float4 v[8];
+#pragma unroll
+              for (int k = 0; k < 8; ++k)
+                v[k] = k0 + k < ke ? ld_dev4(P + k0 + k) : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+#pragma unroll
+              for (int k = 0; k < 8; ++k) mg.add(v[k]);
+            }
+          part = mg.part();
+        }
+        if (q < NP) parts[q * BM + r] = part;
+        __syncthreads();
+        if (t < BM) {
+          float2 st2 = make_float2(0.f, 0.f);
+          if (m0 + t < a.M) {
+            if constexpr (EPI == kEpiLN) {
+              MergeLN mg;
+              for (int k = 0; k < NP; ++k) mg.add(parts[k * BM + t]);
+              st2 = make_float2(mg.mean, rsqrtf(mg.m2 / (float)a.N + a.eps));
+            } else {
+              MergeSM mg;
+              for (int k = 0; k < NP; ++k) mg.add(parts[k * BM + t]);
+              st2 = make_float2(mg.m, 1.0f / mg.l);
+            }
+          }
+          stat[t] = st2;
+        }
+      };
+      auto wait_gen = [&]() {
+        uint32_t it = 0;
+        for (; it < kSpinCap; ++it) {
+          const uint64_t wv = __hip_atomic_load(jw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((uint32_t)(wv >> 32) != gen0) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (it == kSpinCap) __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      };
+
+      float2* fin = reinterpret_cast<float2*>(a.finals);
+      if (leader_mode) {
+        if (last) {
+          // leader: combine every row of the group once, publish, release
+          combine_rows();
+          if (t < BM && m0 + t < a.M) {
+            st_dev(reinterpret_cast<float*>(fin + m0 + t), stat[t].x);
+            st_dev(reinterpret_cast<float*>(fin + m0 + t) + 1, stat[t].y);
+          }
+          wait_stores();
+          __syncthreads();
+          if (t == 0) __hip_atomic_fetch_add(jw, (1ull << 32) - (uint64_t)T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          if (t == 0) wait_gen();
+          __syncthreads();
+          if (t < BM) {
+            const int64_t row = m0 + t;
+            stat[t] = row < a.M ? make_float2(ld_dev(reinterpret_cast<const float*>(fin + row)),
+                                              ld_dev(reinterpret_cast<const float*>(fin + row) + 1))
+                                : make_float2(0.f, 0.f);
           }
         }
-        stat[t] = st2;
+      } else {
+        // peer to peer: the last arriver releases at once; every member combines
+        if (t == 0) {
+          if (last) __hip_atomic_fetch_add(jw, (1ull << 32) - (uint64_t)T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else wait_gen();
+        }
+        __syncthreads();
+        combine_rows();
       }
       __syncthreads();
 
       // ------------------------------------------------ final stage + commit
+      // results go to the LDS output tile (bf16, swizzled chunks), then rows out
+      float fa[RB], fb[RB];  // LN: y = (acc - fb) * fa * gamma + beta; softmax: y = acc * fa
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int rl = wm * WM + rb * 32 + l32;
-        const int64_t row = m0 + rl;
-        const float2 st2 = stat[rl];
-        float fa, fb;  // LN: y = (acc - fb) * fa * gamma + beta; softmax: y = acc * fa
+        const float2 st2 = stat[wm * WM + rb * 32 + l32];
         if constexpr (EPI == kEpiLN) {
-          fa = st2.y;
-          fb = st2.x;
+          fa[rb] = st2.y;
+          fb[rb] = st2.x;
         } else {
-          fa = __builtin_amdgcn_exp2f(p0[rb] - st2.x) * st2.y;
-          fb = 0.f;
+          fa[rb] = __builtin_amdgcn_exp2f(p0[rb] - st2.x) * st2.y;
+          fb[rb] = 0.f;
         }
-        if (row >= a.M) continue;
+      }
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const int64_t col = n0 + wn * WN + cb * 32 + 16 * hl;
+      for (int cb = 0; cb < CB; ++cb) {
+        const int cl0 = wn * WN + cb * 32 + 16 * hl;
+        const int64_t col = n0 + cl0;
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            if (!colok[cb][h]) continue;
+        for (int h = 0; h < 2; ++h) {
+          float gg[8], bb[8];
+          if constexpr (EPI == kEpiLN) {
+            float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0, b0 = g0, b1 = g0;
+            if (colok[cb][h]) {
+              g0 = *reinterpret_cast<const float4*>(a.gamma + col + 8 * h);
+              g1 = *reinterpret_cast<const float4*>(a.gamma + col + 8 * h + 4);
+              b0 = *reinterpret_cast<const float4*>(a.beta + col + 8 * h);
+              b1 = *reinterpret_cast<const float4*>(a.beta + col + 8 * h + 4);
+            }
+            gg[0] = g0.x; gg[1] = g0.y; gg[2] = g0.z; gg[3] = g0.w; gg[4] = g1.x; gg[5] = g1.y; gg[6] = g1.z; gg[7] = g1.w;
+            bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w; bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
+          }
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const int rl = wm * WM + rb * 32 + l32;
             float o[8];
             if constexpr (EPI == kEpiLN) {
-              const float4 g0 = *reinterpret_cast<const float4*>(a.gamma + col + 8 * h);
-              const float4 g1 = *reinterpret_cast<const float4*>(a.gamma + col + 8 * h + 4);
-              const float4 b0 = *reinterpret_cast<const float4*>(a.beta + col + 8 * h);
-              const float4 b1 = *reinterpret_cast<const float4*>(a.beta + col + 8 * h + 4);
-              const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-              const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-              for (int e = 0; e < 8; ++e) o[e] = fmaf((acc[rb][cb][8 * h + e] - fb) * fa, gg[e], bb[e]);
+              for (int e = 0; e < 8; ++e) o[e] = fmaf((acc[rb][cb][8 * h + e] - fb[rb]) * fa[rb], gg[e], bb[e]);
             } else {
 #pragma unroll
-              for (int e = 0; e < 8; ++e) o[e] = acc[rb][cb][8 * h + e] * fa;
+              for (int e = 0; e < 8; ++e) o[e] = acc[rb][cb][8 * h + e] * fa[rb];
             }
             const u32x4 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
                               pack_bf16x2(o[6], o[7])};
-            __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(a.Y + row * a.N + col + 8 * h));
+            *reinterpret_cast<u32x4*>(tile16 + rl * BN + 8 * eswz(rl, cl0 / 8 + h)) = pk;
           }
         }
+      }
+      __syncthreads();
+      // each wave instruction stores 1 KB of whole output row segments
+#pragma unroll
+      for (int j = 0; j < BM * C16 / kThreads; ++j) {
+        const int id = j * kThreads + t;
+        const int rr = id / C16, c = id % C16;
+        const int64_t row = m0 + rr, col = n0 + 8 * c;
+        if (row < a.M && col < a.N)
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tile16 + rr * BN + 8 * eswz(rr, c)),
+                                      reinterpret_cast<u32x4*>(a.Y + row * a.N + col));
       }
     }
     __syncthreads();  // LDS is reused by the next tile's prologue
@@ -491,28 +682,43 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
 
 // ---------------------------------------------------------------- dispatch
 
+struct TileCfg {
+  int bm, bn, bk;
+};
+
+// Tile configurations (id -> shape); the launch list below must match.
+static const TileCfg kCfgs[] = {
+    {256, 256, 64},  // 0: 2x2 waves of 128x128, 2-stage ring 128 KB, 1 WG/CU
+    {256, 128, 64},  // 1: 2x2 waves of 128x64, 2-stage ring 96 KB, 1 WG/CU
+    {128, 256, 64},  // 2: 2x2 waves of 64x128, 2-stage ring 96 KB, 1 WG/CU
+    {128, 128, 64},  // 3: 2x2 waves of 64x64, 2-stage ring 64 KB, 2 WG/CU
+    {64, 512, 64},   // 4: 1x4 waves of 64x128, 2-stage ring 144 KB, 1 WG/CU
+    {128, 256, 32},  // 5: 2x2 waves of 64x128, 3-stage ring 72 KB, 2 WG/CU
+};
+
 bool gemm_tile_config(int cfg, int* bm, int* bn, int* bk) {
-  switch (cfg) {
-    case 0: *bm = 256; *bn = 256; *bk = 64; return true;
-    case 1: *bm = 128; *bn = 256; *bk = 32; return true;
-    case 2: *bm = 128; *bn = 128; *bk = 64; return true;
-    case 3: *bm = 256; *bn = 128; *bk = 64; return true;
-    default: return false;
-  }
+  if (cfg < 0 || cfg >= (int)(sizeof(kCfgs) / sizeof(kCfgs[0]))) return false;
+  *bm = kCfgs[cfg].bm;
+  *bn = kCfgs[cfg].bn;
+  *bk = kCfgs[cfg].bk;
+  return true;
 }
 
 template <int EPI, bool NN>
 static hipError_t launch_gemm_t(const GemmPlan& pl, const GemmArgs& a, hipStream_t st, int* occ) {
-#define CF_GEMM(CFG, BM, BN, BK, MINB)                                                             \
-  if (pl.cfg == CFG) {                                                                             \
-    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, k_gemm<EPI, NN, BM, BN, BK, MINB>, kThreads, 0); \
-    hipLaunchKernelGGL((k_gemm<EPI, NN, BM, BN, BK, MINB>), dim3(pl.grid), dim3(kThreads), 0, st, a); \
-    return hipGetLastError();                                                                      \
+#define CF_GEMM(CFG, BM, BN, BK, WGM, STG, MINB)                                                        \
+  if (pl.cfg == CFG) {                                                                                  \
+    auto kfn = k_gemm<EPI, NN, BM, BN, BK, WGM, STG, MINB>;                                              \
+    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kfn, kThreads, 0);                \
+    hipLaunchKernelGGL(kfn, dim3(pl.grid), dim3(kThreads), 0, st, a);                                   \
+    return hipGetLastError();                                                                           \
   }
-  CF_GEMM(0, 256, 256, 64, 1)
-  CF_GEMM(1, 128, 256, 32, 2)
-  CF_GEMM(2, 128, 128, 64, 2)
-  CF_GEMM(3, 256, 128, 64, 1)
+  CF_GEMM(0, 256, 256, 64, 2, 2, 1)
+  CF_GEMM(1, 256, 128, 64, 2, 2, 1)
+  CF_GEMM(2, 128, 256, 64, 2, 2, 1)
+  CF_GEMM(3, 128, 128, 64, 2, 2, 2)
+  CF_GEMM(4, 64, 512, 64, 1, 2, 1)
+  CF_GEMM(5, 128, 256, 32, 2, 3, 2)
 #undef CF_GEMM
   return hipErrorInvalidConfiguration;
 }

@@ -20,7 +20,7 @@ struct RowArgs {
   int64_t rows;
   int64_t cols;
   uint32_t* err;    // workspace error word
-  JoinWord* joins;  // split plans: one join per group of S workgroups
+  uint64_t* joins;  // split plans: one join word per group of S workgroups
   float* partials;  // split plans: rows * S * 4 floats
   int S;            // workgroups per row (split plans)
   int64_t slice;    // columns per member (split plans)
@@ -58,8 +58,9 @@ struct GemmArgs {
   int tiles_n;         // column tiles per row group = ceil(N / BN)
   int tiles_m;
   uint32_t* err;
-  JoinWord* joins;     // one per group of tiles_n workgroups
+  uint64_t* joins;     // one join word per group of tiles_n workgroups
   float* partials;     // M * tiles_n * 4 floats
+  float* finals;       // M * 2 floats (leader aggregation)
   int agg_leader;      // 0: every member reads all partials; 1: last arriver combines
 };
 
@@ -71,6 +72,7 @@ struct GemmPlan {
   int occupancy = 0;  // resident workgroups per CU
   int tiles = 0;
   int rounds = 0;
+  bool leader = false;  // last-arriver aggregation (else every member reads all partials)
 };
 
 hipError_t launch_gemm(int epi, const GemmPlan& pl, const GemmArgs& a, hipStream_t st);

@@ -337,23 +337,29 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
     }
 
     // ---- global level: publish, join, read all members' partials
-    float* P = a.partials + (size_t)row * S * 4;
+    float4* P = reinterpret_cast<float4*>(a.partials) + (size_t)row * S;
     if (t == 0) {
-      st_agent(P + s * 4 + 0, part0);
-      st_agent(P + s * 4 + 1, part1);
-      st_agent(P + s * 4 + 2, part2);
+      st_dev4(P + s, make_float4(part0, part1, part2, 0.0f));
+      wait_stores();
       join_arrive_and_wait(a.joins + g / S, (uint32_t)S, a.err);  // members share g / S every round
     }
     __syncthreads();
-
+    // Partials are read with device-scope loads, 8 in flight per batch.
     if constexpr (OP == kSoftmax || OP == kPowSoftmax) {
-      float M = -INFINITY;
-      for (int k = 0; k < S; ++k) M = fmaxf(M, ld_agent(P + k * 4 + 0));
-      float L = 0.0f;
-      for (int k = 0; k < S; ++k) {
-        const float mk = ld_agent(P + k * 4 + 0);
-        const float lk = ld_agent(P + k * 4 + 1);
-        L += mk == -INFINITY ? 0.0f : lk * __builtin_amdgcn_exp2f(mk - M);
+      float M = -INFINITY, L = 0.0f;
+      for (int k0 = 0; k0 < S; k0 += 8) {  // 8 partials in flight per batch
+        float4 q[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) q[k] = k0 + k < S ? ld_dev4(P + k0 + k) : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) M = fmaxf(M, q[k].x);
+      }
+      for (int k0 = 0; k0 < S; k0 += 8) {
+        float4 q[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) q[k] = k0 + k < S ? ld_dev4(P + k0 + k) : make_float4(-INFINITY, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) L += q[k].x == -INFINITY ? 0.0f : q[k].y * __builtin_amdgcn_exp2f(q[k].x - M);
       }
       const float f = (part0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(part0 - M)) / L;
 #pragma unroll
@@ -368,16 +374,20 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
     } else {
       // Chan's pairwise merge of (count, mean, M2), members in order.
       float n = 0.0f, mean = 0.0f, M2 = 0.0f;
-      for (int k = 0; k < S; ++k) {
-        const float nb = ld_agent(P + k * 4 + 0);
-        if (nb == 0.0f) continue;
-        const float mb = ld_agent(P + k * 4 + 1);
-        const float m2b = ld_agent(P + k * 4 + 2);
-        const float nn = n + nb;
-        const float d = mb - mean;
-        mean += d * (nb / nn);
-        M2 += m2b + d * d * (n * nb / nn);
-        n = nn;
+      for (int k0 = 0; k0 < S; k0 += 8) {
+        float4 q[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) q[k] = k0 + k < S ? ld_dev4(P + k0 + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float nb = q[k].x;
+          if (nb == 0.0f) continue;
+          const float nn = n + nb;
+          const float d = q[k].y - mean;
+          mean += d * (nb / nn);
+          M2 += q[k].z + d * d * (n * nb / nn);
+          n = nn;
+        }
       }
       const float rs = rsqrtf(M2 / (float)cols + a.eps);
       const float shift = part1 - mean;  // this member's values are x - mean_loc
