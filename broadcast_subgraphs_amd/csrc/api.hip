@@ -198,10 +198,10 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   if (s != CF_OK) return s;
   GemmPlan p;
   p.nn = nn ? 1 : 0;
-  // Default tiles (measured on MI355X): GEMM+LN 128x256 (a 4096-wide row spans
-  // 16 tiles), GEMM+softmax 64x512 (an 8192-wide row spans 16 tiles), plain
-  // GEMM 256x256.
-  const int dflt = epi == kEpiSoftmax ? 4 : (epi == kEpiLN ? 2 : 0);
+  // Default tiles (measured on MI355X): 64x512 for both fused epilogues (a
+  // 4096-wide LN row spans 8 tiles, an 8192-wide softmax row 16), 128x128 at
+  // two workgroups per CU for the plain fp32-output GEMM.
+  const int dflt = epi == kEpiStoreF32 ? 3 : 4;
   p.cfg = (int)env_int(epi == kEpiSoftmax ? "CF_GEMM_SOFTMAX_CFG" : (epi == kEpiLN ? "CF_GEMM_LN_CFG" : "CF_GEMM_CFG"), dflt);
   if (!gemm_tile_config(p.cfg, &p.bm, &p.bn, &p.bk)) return CF_EUNSUPPORTED;
   const int64_t tn = (N + p.bn - 1) / p.bn, tm = (M + p.bm - 1) / p.bm;

@@ -255,10 +255,10 @@ struct MergeSM {
 
 template <int EPI, int BM, int BN, int BK, int STAGES>
 constexpr int gemm_lds_bytes() {
-  constexpr int ring = STAGES * (BM + BN) * BK * 2;
+  constexpr int ring = (BM + BN) * BK * 2;  // slot 0 (slot 1 is its own object)
   // bf16 tile + red (2 x 4 x BM floats) + pub (BM float4) + parts (256 float4) + stat (BM float2) + flags
-  constexpr int epi = EPI == kEpiStoreF32 ? BM * BN * 4 / 2
-                                          : BM * BN * 2 + 32 * BM + 16 * BM + 16 * 256 + 8 * BM + 64;
+  constexpr int epi = EPI == kEpiStoreF32 ? BM * BN * 4 / 4
+                                          : BM * BN * 2 + 32 * BM + 16 * BM + 16 * 256 + 8 * BM + 64 + 3 * BN * 4;
   return ring > epi ? ring : epi;
 }
 
@@ -272,10 +272,15 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
   constexpr int RB = WM / 32, CB = WN / 32;
   constexpr int LDS = gemm_lds_bytes<EPI, BM, BN, BK, STAGES>();
   constexpr int C16 = BN * 2 / 16;  // 16-byte chunks per bf16 output row
+  static_assert(STAGES == 2, "ring slots are separate LDS objects; two are instantiated");
   constexpr int NP = BM >= kThreads ? 1 : kThreads / BM;  // threads combining one row's partials
   static_assert(WM % 32 == 0 && WN % 32 == 0 && WGM * WGN == 4, "wave tile");
   static_assert(C16 >= 8 && (BM * C16) % kThreads == 0, "epilogue tile");
+  // Ring slot 0 doubles as the epilogue's LDS; slot 1 is a separate object so
+  // the compiler can see that fragment reads of one slot never alias the
+  // direct loads filling the other (no conservative wait on the prefetch).
   __shared__ __align__(16) char lds[LDS];
+  __shared__ __align__(16) char lds1[RG::STAGE_BYTES];
 
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
@@ -302,21 +307,23 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
         for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
 
     // ------------------------------------------------------------ MainLoop
-    // Stage kt lives in ring slot kt % STAGES.  Before computing stage kt each
-    // thread waits until at most STAGES-2 later stages' loads are outstanding;
-    // the barrier then publishes stage kt to every wave and retires slot
-    // (kt-1) % STAGES, which the next stage's loads refill.
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) RG::load(a, rA, rB, lds + s * RG::STAGE_BYTES, m0, n0, (int64_t)s * BK);
-    // One stage is issued every iteration (stages past K read zeros through the
-    // range check and move no data), so exactly STAGES-2 later stages are in
-    // flight when stage kt is awaited and the loop body has no branch.
-    for (int kt = 0; kt < KT; ++kt) {
-      wait_vm<(STAGES - 2) * (RG::LA + RG::LB)>();
+    // Two-slot ring: stage kt lives in slot kt & 1.  Each step waits for its
+    // own stage, publishes it with a barrier (which also retires the other
+    // slot), issues the next stage into the other slot, and computes.  Stages
+    // past K read zeros through the range check and move no data, so the loop
+    // body has no branch.
+    RG::load(a, rA, rB, lds, m0, n0, 0);
+    for (int kt = 0; kt < KT; kt += 2) {
+      wait_vm<0>();
       __syncthreads();
-      RG::load(a, rA, rB, lds + ((kt + STAGES - 1) % STAGES) * RG::STAGE_BYTES, m0, n0,
-               (int64_t)(kt + STAGES - 1) * BK);
-      mma_stage<BM, BN, BK, NN, RB, CB, RG::LA + RG::LB>(lds + (kt % STAGES) * RG::STAGE_BYTES, acc, wm, wn);
+      RG::load(a, rA, rB, lds1, m0, n0, (int64_t)(kt + 1) * BK);
+      mma_stage<BM, BN, BK, NN, RB, CB, RG::LA + RG::LB>(lds, acc, wm, wn);
+      if (kt + 1 < KT) {
+        wait_vm<0>();
+        __syncthreads();
+        RG::load(a, rA, rB, lds, m0, n0, (int64_t)(kt + 2) * BK);
+        mma_stage<BM, BN, BK, NN, RB, CB, RG::LA + RG::LB>(lds1, acc, wm, wn);
+      }
     }
     wait_vm<0>();
     __syncthreads();  // every wave is done with the ring: it is free from here on
@@ -324,16 +331,16 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
     // lane's output coordinates: row(rb) = m0 + wm*WM + rb*32 + l32,
     // cols(cb) = n0 + wn*WN + cb*32 + 16*hl + [0, 16)
     if constexpr (EPI == kEpiStoreF32) {
-      // fp32 tile staged through LDS half a tile at a time, written as rows
+      // fp32 tile staged through LDS a quarter tile at a time, written as rows
       float* ot = reinterpret_cast<float*>(lds);
       constexpr int F4 = BN / 4;     // float4 chunks per row
-      constexpr int HROWS = BM / 2;  // rows per half
-      for (int half = 0; half < 2; ++half) {
+      constexpr int QROWS = BM / 4;  // rows per quarter
+      for (int qt = 0; qt < 4; ++qt) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const int rl = wm * WM + rb * 32 + l32;
-          if (rl / HROWS != half) continue;
-          const int rr = rl - half * HROWS;
+          if (rl / QROWS != qt) continue;
+          const int rr = rl - qt * QROWS;
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) {
             const int c4 = (wn * WN + cb * 32 + 16 * hl) / 4;
@@ -345,9 +352,9 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
           }
         }
         __syncthreads();
-        for (int id = t; id < HROWS * F4; id += kThreads) {
+        for (int id = t; id < QROWS * F4; id += kThreads) {
           const int rr = id / F4, c = id % F4;
-          const int64_t row = m0 + half * HROWS + rr, col = n0 + 4 * c;
+          const int64_t row = m0 + qt * QROWS + rr, col = n0 + 4 * c;
           if (row < a.M && col < a.N)
             st4_stream(a.Z + row * a.N + col, *reinterpret_cast<const float4*>(ot + rr * BN + 4 * (c ^ (rr & 7))));
         }
@@ -361,6 +368,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
       float4* parts = pub + BM;                                              // 256 (NP per row)
       float2* stat = reinterpret_cast<float2*>(parts + kThreads);            // BM
       int* flag = reinterpret_cast<int*>(stat + BM);                         // last-arriver flag, gen0
+      float* vec = reinterpret_cast<float*>(flag + 16);                      // bias | gamma | beta slices (BN each)
       int slot = 0;
       const float n_tile = (float)(a.N - n0 < BN ? a.N - n0 : (int64_t)BN);
 
@@ -387,6 +395,18 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
             g2l16(rR, lds + (j * 4 + w) * 1024, off);
           }
         }
+        // bias / gamma / beta slices of this tile -> LDS (zero past N), so the
+        // epilogue reads them from LDS instead of holding them in registers
+        {
+          constexpr int V4 = BN / 4;  // float4 chunks per slice
+          for (int id = t; id < 3 * V4; id += kThreads) {
+            const int which = id / V4, c = id % V4;
+            const int64_t gn = n0 + 4 * c;
+            const float* src = which == 0 ? a.bias : (which == 1 ? a.gamma : a.beta);
+            reinterpret_cast<float4*>(vec + which * BN)[c] =
+                gn < a.N ? *reinterpret_cast<const float4*>(src + gn) : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
         wait_vm<0>();
         __syncthreads();
         // stage 1: u = acc + bias_j + R_ij, kept in the accumulator registers
@@ -394,12 +414,10 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
           const int cl0 = wn * WN + cb * 32 + 16 * hl;
-          const int64_t col = n0 + cl0;
           float bv[16];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 b = colok[cb][q >> 1] ? *reinterpret_cast<const float4*>(a.bias + col + 4 * q)
-                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 b = *reinterpret_cast<const float4*>(vec + cl0 + 4 * q);
             bv[4 * q] = b.x; bv[4 * q + 1] = b.y; bv[4 * q + 2] = b.z; bv[4 * q + 3] = b.w;
           }
 #pragma unroll
@@ -632,18 +650,14 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int cl0 = wn * WN + cb * 32 + 16 * hl;
-        const int64_t col = n0 + cl0;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           float gg[8], bb[8];
           if constexpr (EPI == kEpiLN) {
-            float4 g0 = make_float4(0.f, 0.f, 0.f, 0.f), g1 = g0, b0 = g0, b1 = g0;
-            if (colok[cb][h]) {
-              g0 = *reinterpret_cast<const float4*>(a.gamma + col + 8 * h);
-              g1 = *reinterpret_cast<const float4*>(a.gamma + col + 8 * h + 4);
-              b0 = *reinterpret_cast<const float4*>(a.beta + col + 8 * h);
-              b1 = *reinterpret_cast<const float4*>(a.beta + col + 8 * h + 4);
-            }
+            const float4 g0 = *reinterpret_cast<const float4*>(vec + BN + cl0 + 8 * h);
+            const float4 g1 = *reinterpret_cast<const float4*>(vec + BN + cl0 + 8 * h + 4);
+            const float4 b0 = *reinterpret_cast<const float4*>(vec + 2 * BN + cl0 + 8 * h);
+            const float4 b1 = *reinterpret_cast<const float4*>(vec + 2 * BN + cl0 + 8 * h + 4);
             gg[0] = g0.x; gg[1] = g0.y; gg[2] = g0.z; gg[3] = g0.w; gg[4] = g1.x; gg[5] = g1.y; gg[6] = g1.z; gg[7] = g1.w;
             bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w; bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
           }
@@ -688,12 +702,12 @@ struct TileCfg {
 
 // Tile configurations (id -> shape); the launch list below must match.
 static const TileCfg kCfgs[] = {
-    {256, 256, 64},  // 0: 2x2 waves of 128x128, 2-stage ring 128 KB, 1 WG/CU
+    {256, 256, 64},  // 0: 2x2 waves of 128x128, 2-slot ring 128 KB, 1 WG/CU
     {256, 128, 64},  // 1: 2x2 waves of 128x64, 2-stage ring 96 KB, 1 WG/CU
     {128, 256, 64},  // 2: 2x2 waves of 64x128, 2-stage ring 96 KB, 1 WG/CU
     {128, 128, 64},  // 3: 2x2 waves of 64x64, 2-stage ring 64 KB, 2 WG/CU
     {64, 512, 64},   // 4: 1x4 waves of 64x128, 2-stage ring 144 KB, 1 WG/CU
-    {128, 256, 32},  // 5: 2x2 waves of 64x128, 3-stage ring 72 KB, 2 WG/CU
+    {128, 128, 32},  // 5: 2x2 waves of 64x64, 2-stage ring 32 KB, 2 WG/CU
 };
 
 bool gemm_tile_config(int cfg, int* bm, int* bn, int* bk) {
@@ -707,6 +721,7 @@ bool gemm_tile_config(int cfg, int* bm, int* bn, int* bk) {
 template <int EPI, bool NN>
 static hipError_t launch_gemm_t(const GemmPlan& pl, const GemmArgs& a, hipStream_t st, int* occ) {
 #define CF_GEMM(CFG, BM, BN, BK, WGM, STG, MINB)                                                        \
+  if constexpr (EPI == kEpiStoreF32 || BM * BN <= 128 * 256)                                            \
   if (pl.cfg == CFG) {                                                                                  \
     auto kfn = k_gemm<EPI, NN, BM, BN, BK, WGM, STG, MINB>;                                              \
     if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kfn, kThreads, 0);                \
@@ -718,7 +733,7 @@ static hipError_t launch_gemm_t(const GemmPlan& pl, const GemmArgs& a, hipStream
   CF_GEMM(2, 128, 256, 64, 2, 2, 1)
   CF_GEMM(3, 128, 128, 64, 2, 2, 2)
   CF_GEMM(4, 64, 512, 64, 1, 2, 1)
-  CF_GEMM(5, 128, 256, 32, 2, 3, 2)
+  CF_GEMM(5, 128, 128, 32, 2, 2, 2)
 #undef CF_GEMM
   return hipErrorInvalidConfiguration;
 }
