@@ -192,16 +192,49 @@ cf_status run_rows(const char* name, int op, const float* x, float* y, float* y_
 
 // ------------------------------------------------------------ GEMM planning
 
+// Strip softmax: 128 x 128 tiles; each row block's column tiles are cut into
+// S strips of C consecutive tiles (no strip empty), one per resident
+// workgroup where the rows allow.
+static cf_status plan_gemm_strips(int64_t M, int64_t N, DevInfo* di, GemmPlan* p0, GemmPlan* pl) {
+  GemmPlan p = *p0;
+  p.bm = 128;
+  p.bn = 128;
+  p.bk = 128;
+  int occ = 0;
+  if (gemm_occupancy(kEpiSoftmax, p, &occ) != hipSuccess || occ <= 0) return CF_EHIP;
+  p.occupancy = occ;
+  const int64_t cap = (int64_t)occ * di->cus;
+  const int64_t tn = (N + 127) / 128, tm = (M + 127) / 128;
+  if (tm > kMaxJoins) return CF_EUNSUPPORTED;
+  int64_t S = std::max<int64_t>(1, std::min<int64_t>(tn, cap / tm));
+  const int64_t C = (tn + S - 1) / S;
+  S = (tn + C - 1) / C;
+  const int64_t units = tm * S;
+  p.strips = (int)S;
+  p.tiles = (int)(tm * tn);
+  p.grid = (int)std::min<int64_t>(units, cap);
+  p.rounds = (int)((units + p.grid - 1) / p.grid);
+  if (p.rounds > kMaxRounds) return CF_EUNSUPPORTED;
+  p.leader = true;
+  *pl = p;
+  return CF_OK;
+}
+
 cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan* pl) {
   DevInfo* di = nullptr;
   cf_status s = dev_info(&di);
   if (s != CF_OK) return s;
   GemmPlan p;
   p.nn = nn ? 1 : 0;
-  // Default tiles (measured on MI355X): 64x512 for both fused epilogues (a
-  // 4096-wide LN row spans 8 tiles, an 8192-wide softmax row 16), 128x128 at
-  // two workgroups per CU for the plain fp32-output GEMM.
-  const int dflt = epi == kEpiStoreF32 ? 3 : 4;
+  // softmax with a reduction dimension of at most 128 runs by strips
+  const int dalgo = (epi == kEpiSoftmax && K <= 128) ? 2 : 1;
+  p.algo = epi == kEpiStoreF32 ? 0 : (int)env_int("CF_GEMM_ALGO", dalgo);
+  if (p.algo == 2 && (epi != kEpiSoftmax || K > 128)) return CF_EUNSUPPORTED;
+  if (p.algo == 2) return plan_gemm_strips(M, N, di, &p, pl);
+  // Default tiles (measured on MI355X): 128x128 at two workgroups per CU for
+  // the plain GEMM and the overlapped epilogues, 64x512 for the round-based
+  // epilogues.
+  const int dflt = (epi == kEpiStoreF32 || p.algo == 1) ? 3 : 4;
   p.cfg = (int)env_int(epi == kEpiSoftmax ? "CF_GEMM_SOFTMAX_CFG" : (epi == kEpiLN ? "CF_GEMM_LN_CFG" : "CF_GEMM_CFG"), dflt);
   if (!gemm_tile_config(p.cfg, &p.bm, &p.bn, &p.bk)) return CF_EUNSUPPORTED;
   const int64_t tn = (N + p.bn - 1) / p.bn, tm = (M + p.bm - 1) / p.bm;
@@ -212,6 +245,14 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   const int64_t cap = (int64_t)occ * di->cus;
   if (epi == kEpiStoreF32) {
     p.grid = (int)std::min<int64_t>(p.tiles, std::max<int64_t>(cap, 1) * 4);
+  } else if (p.algo == 1) {
+    // one join word per row block; every workgroup resident; a row block's
+    // tiles within two consecutive rounds (the LN pipeline's progress bound)
+    const int64_t G = std::min<int64_t>(p.tiles, cap);
+    if (tm > kMaxJoins) return CF_EUNSUPPORTED;
+    if (G < 1 || tn > 2 * G) return CF_EOCCUPANCY;
+    if ((p.tiles + G - 1) / G > kMaxRounds) return CF_EUNSUPPORTED;
+    p.grid = (int)G;
   } else {
     const int64_t G = std::min<int64_t>(p.tiles, cap / tn * tn);
     if (G < tn) return CF_EOCCUPANCY;
@@ -232,14 +273,18 @@ size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N) {
   return ws_layout(M * tn * 4 + M * 2).total;
 }
 
-void record_gemm_plan(const char* name, const GemmPlan& p, int64_t M, int64_t N, int64_t K) {
+void record_gemm_plan(const char* name, int epi, const GemmPlan& p, int64_t M, int64_t N, int64_t K) {
+  const bool ov = p.algo >= 1 && epi != kEpiStoreF32;
+  const char* kernel = p.algo == 2 ? "k_gemm_sm3" : (ov ? (epi == kEpiLN ? "k_gemm_ln2" : "k_gemm_sm2") : "k_gemm");
+  const char* sched = p.algo == 2 ? "strips" : (ov ? (epi == kEpiLN ? "pipelined" : "two-sweep") : "rounds");
   char buf[512];
   snprintf(buf, sizeof buf,
-           "{\"call\":\"%s\",\"M\":%lld,\"N\":%lld,\"K\":%lld,\"kernel\":\"k_gemm\",\"tile\":[%d,%d,%d],"
+           "{\"call\":\"%s\",\"M\":%lld,\"N\":%lld,\"K\":%lld,\"kernel\":\"%s\",\"tile\":[%d,%d,%d],"
            "\"layout\":\"%s\",\"tiles\":%d,\"row_group\":%lld,\"grid\":%d,\"block\":256,\"occupancy\":%d,"
-           "\"rounds\":%d,\"aggregation\":\"%s\"}",
-           name, (long long)M, (long long)N, (long long)K, p.bm, p.bn, p.bk, p.nn ? "NN" : "NT", p.tiles,
-           (long long)((N + p.bn - 1) / p.bn), p.grid, p.occupancy, p.rounds, p.leader ? "leader" : "peer-to-peer");
+           "\"rounds\":%d,\"aggregation\":\"%s\",\"schedule\":\"%s\"}",
+           name, (long long)M, (long long)N, (long long)K, kernel, p.bm, p.bn, p.bk, p.nn ? "NN" : "NT", p.tiles,
+           p.algo == 2 ? (long long)p.strips : (long long)((N + p.bn - 1) / p.bn), p.grid, p.occupancy, p.rounds,
+           (ov || p.leader) ? "leader" : "peer-to-peer", sched);
   g_last_plan = buf;
 }
 
@@ -340,7 +385,8 @@ static cf_status run_gemm(const char* name, int epi, bool nn, GemmArgs a, void* 
   a.tiles_n = (int)tn;
   a.tiles_m = (int)tm;
   a.agg_leader = p.leader ? 1 : 0;
-  record_gemm_plan(name, p, a.M, a.N, a.K);
+  a.strips = p.strips;
+  record_gemm_plan(name, epi, p, a.M, a.N, a.K);
   return launch_gemm(epi, p, a, stream) == hipSuccess ? CF_OK : CF_EHIP;
 }
 

@@ -120,6 +120,17 @@ __device__ __forceinline__ float4 ld_dev4(const float4* p) {
   return make_float4(ld_dev(f + 0), ld_dev(f + 1), ld_dev(f + 2), ld_dev(f + 3));
 }
 
+// 8-byte pairs as one device-scope access.
+__device__ __forceinline__ void st_dev2(float2* p, float2 v) {
+  const uint64_t b = (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float2* p) {
+  const uint64_t b = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float2*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+}
+
 // Called by ONE lane after the caller's wave published its partials with
 // st_dev*/wait_stores().  Returns false if the spin cap was hit (the error
 // word is then set); true once every member has arrived.

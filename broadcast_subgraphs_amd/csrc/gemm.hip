@@ -96,16 +96,16 @@ struct Ring {
   // instruction j writes LDS byte (j*4 + w)*1024 + 16p of the operand region;
   // the lane picks the global chunk that belongs at that (swizzled) position.
   __device__ __forceinline__ static void load(const GemmArgs& a, __amdgpu_buffer_rsrc_t ra,
-                                              __amdgpu_buffer_rsrc_t rb, char* st, int64_t m0, int64_t n0,
-                                              int64_t k0) {
+                                              __amdgpu_buffer_rsrc_t rb, char* st, int m0, int n0, int k0) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int M = (int)a.M, N = (int)a.N, K = (int)a.K;  // every operand is below 2^31 bytes
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
       const int o = (j * 4 + w) * 1024 + lane * 16;
       const int row = o / (BK * 2), pc = (o % (BK * 2)) / 16;
       const int c = swz<BK>(row, pc);  // logical chunk stored at physical chunk pc
-      const int64_t gm = m0 + row, gk = k0 + 8 * c;
-      const uint32_t off = (gm < a.M && gk < a.K) ? (uint32_t)((gm * a.K + gk) * 2) : kOOB;
+      const int gm = m0 + row, gk = k0 + 8 * c;
+      const uint32_t off = (gm < M && gk < K) ? (uint32_t)(gm * K + gk) * 2u : kOOB;
       g2l16(ra, st + (j * 4 + w) * 1024, off);
     }
 #pragma unroll
@@ -115,13 +115,13 @@ struct Ring {
       if constexpr (NN) {
         const int k = o / (BN * 2), pb = o % (BN * 2);
         const int cb = (pb ^ nn_mask(k)) / 16;  // logical 16-byte chunk along N
-        const int64_t gk = k0 + k, gn = n0 + 8 * cb;
-        off = (gk < a.K && gn < a.N) ? (uint32_t)((gk * a.N + gn) * 2) : kOOB;
+        const int gk = k0 + k, gn = n0 + 8 * cb;
+        off = (gk < K && gn < N) ? (uint32_t)(gk * N + gn) * 2u : kOOB;
       } else {
         const int row = o / (BK * 2), pc = (o % (BK * 2)) / 16;
         const int c = swz<BK>(row, pc);
-        const int64_t gn = n0 + row, gk = k0 + 8 * c;
-        off = (gn < a.N && gk < a.K) ? (uint32_t)((gn * a.K + gk) * 2) : kOOB;
+        const int gn = n0 + row, gk = k0 + 8 * c;
+        off = (gn < N && gk < K) ? (uint32_t)(gn * K + gk) * 2u : kOOB;
       }
       g2l16(rb, st + A_BYTES + (j * 4 + w) * 1024, off);
     }
@@ -253,6 +253,139 @@ struct MergeSM {
   __device__ float4 part() const { return make_float4(m, l, 0.f, 0.f); }
 };
 
+// MainLoop of one tile over a two-slot ring (slot objects s0, s1).  On entry
+// stage 0 of the tile has been issued into s0.  Stage kt lives in slot kt & 1:
+// each step waits for its own stage, publishes it with a barrier (which also
+// retires the other slot), issues the next stage into the other slot and
+// computes.  With `nxt`, stage 0 of the tile at (nm0, nn0) goes into s0 as
+// soon as s0 is free, so its latency overlaps the caller's epilogue.  Waves
+// may still read s1 on return; the next call's first barrier covers that.
+template <int BM, int BN, int BK, bool NN, int RB, int CB>
+__device__ __forceinline__ void main_loop(const GemmArgs& a, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB,
+                                          char* s0, char* s1, int m0, int n0, bool nxt, int nm0, int nn0,
+                                          f32x16 (&acc)[RB][CB], int KT, int wm, int wn) {
+  using RG = Ring<BM, BN, BK, NN>;
+  constexpr int NV = RG::LA + RG::LB;
+  for (int kt = 0; kt < KT; kt += 2) {
+    wait_vm<0>();
+    __syncthreads();
+    const bool two = kt + 1 < KT;
+    if (two) RG::load(a, rA, rB, s1, m0, n0, (kt + 1) * BK);
+    mma_stage<BM, BN, BK, NN, RB, CB, NV>(s0, acc, wm, wn);
+    if (!two) {
+      if (nxt) {
+        __syncthreads();  // every wave is done with s0
+        RG::load(a, rA, rB, s0, nm0, nn0, 0);
+      }
+      break;
+    }
+    wait_vm<0>();
+    __syncthreads();
+    if (kt + 2 < KT) RG::load(a, rA, rB, s0, m0, n0, (kt + 2) * BK);
+    else if (nxt) RG::load(a, rA, rB, s0, nm0, nn0, 0);
+    mma_stage<BM, BN, BK, NN, RB, CB, NV>(s1, acc, wm, wn);
+  }
+}
+
+// Pairwise merges of row statistics.  Both are symmetric in their arguments
+// up to the order fixed by the caller, so lanes that merge the same values in
+// the same order hold identical bits.
+// Softmax (max, sum of 2^(s - max)) in the base-2 domain.
+__device__ __forceinline__ void merge_sm(float& m, float& l, float mo, float lo) {
+  const float mx = fmaxf(m, mo);
+  if (mx == -INFINITY) {
+    m = mx;
+    l = 0.0f;
+    return;
+  }
+  l = l * __builtin_amdgcn_exp2f(m - mx) + lo * __builtin_amdgcn_exp2f(mo - mx);
+  m = mx;
+}
+// LayerNorm (count, mean, M2): Chan's pairwise update, (a) then (b).
+__device__ __forceinline__ void merge_ln(float& n, float& mu, float& m2, float nb, float mub, float m2b) {
+  if (nb == 0.0f) return;
+  if (n == 0.0f) {
+    n = nb;
+    mu = mub;
+    m2 = m2b;
+    return;
+  }
+  const float nn = n + nb, d = mub - mu;
+  mu += d * (nb / nn);
+  m2 += m2b + d * d * (n * nb / nn);
+  n = nn;
+}
+
+// Tile-level row statistics from per-lane ones: the lane pair that shares a
+// row (lanes l and l ^ 32) merges lower half first, then the WGN column waves
+// merge through LDS in wave order.  Every lane of the row ends with the same
+// bits.  One barrier; `red` must not be rewritten before the next barrier.
+template <int BM, int WGN, int RB>
+__device__ __forceinline__ void tile_merge_sm(float (&m)[RB], float (&l)[RB], float2* red, int wm, int wn) {
+  constexpr int WM = RB * 32;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float mo = __shfl_xor(m[rb], 32, kWave), lo = __shfl_xor(l[rb], 32, kWave);
+    merge_sm(m[rb], l[rb], mo, lo);
+    if (lane < 32) red[wn * BM + wm * WM + rb * 32 + lane] = make_float2(m[rb], l[rb]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = wm * WM + rb * 32 + (lane & 31);
+    float2 x = red[r];
+#pragma unroll
+    for (int q = 1; q < WGN; ++q) merge_sm(x.x, x.y, red[q * BM + r].x, red[q * BM + r].y);
+    m[rb] = x.x;
+    l[rb] = x.y;
+  }
+}
+template <int BM, int WGN, int RB>
+__device__ __forceinline__ void tile_merge_ln(float (&n)[RB], float (&mu)[RB], float (&m2)[RB], float4* red, int wm,
+                                              int wn) {
+  constexpr int WM = RB * 32;
+  const int lane = threadIdx.x & 63;
+  const bool lo_half = lane < 32;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float no = __shfl_xor(n[rb], 32, kWave), muo = __shfl_xor(mu[rb], 32, kWave),
+                m2o = __shfl_xor(m2[rb], 32, kWave);
+    if (lo_half) {
+      merge_ln(n[rb], mu[rb], m2[rb], no, muo, m2o);
+    } else {
+      float a0 = no, a1 = muo, a2 = m2o;
+      merge_ln(a0, a1, a2, n[rb], mu[rb], m2[rb]);
+      n[rb] = a0;
+      mu[rb] = a1;
+      m2[rb] = a2;
+    }
+    if (lo_half) red[wn * BM + wm * WM + rb * 32 + lane] = make_float4(n[rb], mu[rb], m2[rb], 0.0f);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = wm * WM + rb * 32 + (lane & 31);
+    float4 x = red[r];
+#pragma unroll
+    for (int q = 1; q < WGN; ++q) merge_ln(x.x, x.y, x.z, red[q * BM + r].x, red[q * BM + r].y, red[q * BM + r].z);
+    n[rb] = x.x;
+    mu[rb] = x.y;
+    m2[rb] = x.z;
+  }
+}
+
+// Spin until the join word's generation differs from gen0 (one lane).
+__device__ __forceinline__ void wait_generation(uint64_t* jw, uint32_t gen0, uint32_t* err) {
+  uint32_t it = 0;
+  for (; it < kSpinCap; ++it) {
+    const uint64_t wv = __hip_atomic_load(jw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(wv >> 32) != gen0) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (it == kSpinCap) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int EPI, int BM, int BN, int BK, int STAGES>
 constexpr int gemm_lds_bytes() {
   constexpr int ring = (BM + BN) * BK * 2;  // slot 0 (slot 1 is its own object)
@@ -307,24 +440,8 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
         for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
 
     // ------------------------------------------------------------ MainLoop
-    // Two-slot ring: stage kt lives in slot kt & 1.  Each step waits for its
-    // own stage, publishes it with a barrier (which also retires the other
-    // slot), issues the next stage into the other slot, and computes.  Stages
-    // past K read zeros through the range check and move no data, so the loop
-    // body has no branch.
-    RG::load(a, rA, rB, lds, m0, n0, 0);
-    for (int kt = 0; kt < KT; kt += 2) {
-      wait_vm<0>();
-      __syncthreads();
-      RG::load(a, rA, rB, lds1, m0, n0, (int64_t)(kt + 1) * BK);
-      mma_stage<BM, BN, BK, NN, RB, CB, RG::LA + RG::LB>(lds, acc, wm, wn);
-      if (kt + 1 < KT) {
-        wait_vm<0>();
-        __syncthreads();
-        RG::load(a, rA, rB, lds, m0, n0, (int64_t)(kt + 2) * BK);
-        mma_stage<BM, BN, BK, NN, RB, CB, RG::LA + RG::LB>(lds1, acc, wm, wn);
-      }
-    }
+    RG::load(a, rA, rB, lds, (int)m0, (int)n0, 0);
+    main_loop<BM, BN, BK, NN, RB, CB>(a, rA, rB, lds, lds1, (int)m0, (int)n0, false, 0, 0, acc, KT, wm, wn);
     wait_vm<0>();
     __syncthreads();  // every wave is done with the ring: it is free from here on
 
@@ -694,6 +811,643 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
   }
 }
 
+// ------------------------------------------- epilogues overlapped with MainLoops
+//
+// The round-based kernel above idles every member of a row group from its
+// publish until the slowest member arrives.  The two kernels below keep the
+// matrix cores busy across that wait instead.
+//
+// Lane (rb, cb) output coordinates, as above: row m0 + wm*WM + rb*32 + l32,
+// 16 consecutive columns n0 + wn*WN + cb*32 + 16*hl + [0, 16).  With that
+// layout each lane's 32 output bytes per (rb, cb) are contiguous, and the
+// epilogues load and store them straight from registers (plain accesses, so
+// the two 16-byte halves of a row segment written by different instructions
+// merge in L2 before they reach HBM).
+
+
+// 16-byte buffer accesses with 32-bit offsets (kOOB: loads read zero, stores
+// are dropped).
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ float4 bld16f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
+template <int RB, int CB>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[RB][CB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
+}
+
+// GEMM + row softmax in two sweeps over the same tile sequence.
+//   Sweep 1: each tile's per-row (max, sum) in the base-2 domain is published
+//   without waiting; the last member of a row block to arrive merges the
+//   block's partials in member order and publishes (max, 1/sum) per row.
+//   Sweep 2: each tile's product is computed again, scaled and normalised
+//   with the merged statistics (waiting, rarely, for a block still in flight)
+//   and stored as bf16.
+// The product is recomputed rather than held across the wait: with a short
+// reduction dimension the second MainLoop costs less than the exchange it
+// hides, and the output tile never leaves registers.
+template <int BM, int BN, int BK, int WGM, int MINB>
+__global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm2(GemmArgs a) {
+  using RG = Ring<BM, BN, BK, false>;
+  constexpr int WGN = 4 / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int RB = WM / 32, CB = WN / 32;
+  constexpr int NP = kThreads / BM;  // threads merging one row's partials
+  static_assert(BM <= kThreads && kThreads % BM == 0 && WM % 32 == 0 && WN % 32 == 0, "tile");
+  __shared__ __align__(16) char s0[RG::STAGE_BYTES];
+  __shared__ __align__(16) char s1[RG::STAGE_BYTES];
+  __shared__ float2 red[WGN * BM];
+  __shared__ float2 parts[kThreads];
+  __shared__ uint32_t gens[kMaxRounds];
+  __shared__ int last;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int lrow = wm * WM + l32, lcol = wn * WN + 16 * hl;  // lane's first row / column in a tile
+  const int M = (int)a.M, N = (int)a.N;
+  const int KT = (int)((a.K + BK - 1) / BK);
+  const int G = (int)gridDim.x;
+  const int g = (int)xcd_local_id(blockIdx.x, (uint32_t)G);
+  const int T = a.tiles_n;
+  const int tiles = a.tiles_m * T;
+  if (g >= tiles) return;
+  const __amdgpu_buffer_rsrc_t rA = rsrc(a.A, (uint32_t)(a.M * a.K * 2));
+  const __amdgpu_buffer_rsrc_t rB = rsrc(a.B, (uint32_t)(a.N * a.K * 2));
+  const __amdgpu_buffer_rsrc_t rY = rsrc(a.Y, (uint32_t)(a.M * a.N * 2));
+  const float sc = a.scale * kLog2e;
+  float2* P = reinterpret_cast<float2*>(a.partials);
+  float2* F = reinterpret_cast<float2*>(a.finals);
+
+  RG::load(a, rA, rB, s0, (g / T) * BM, (g % T) * BN, 0);
+
+  // ------------------------------------------------ sweep 1: statistics
+  int i = 0;
+  for (int tile = g; tile < tiles; tile += G, ++i) {
+    const int rowblk = tile / T, tn = tile - rowblk * T;
+    const int m0 = rowblk * BM, n0 = tn * BN;
+    const int nt = tile + G < tiles ? tile + G : g;  // sweep 2 starts again at g
+    f32x16 acc[RB][CB];
+    zero_acc(acc);
+    main_loop<BM, BN, BK, false, RB, CB>(a, rA, rB, s0, s1, m0, n0, true, (nt / T) * BM, (nt % T) * BN, acc, KT,
+                                         wm, wn);
+    float mr[RB], lr[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (n0 + lcol + cb * 32 + (r & 8) < N) m = fmaxf(m, acc[rb][cb][r] * sc);
+      float l = 0.0f;
+      if (m != -INFINITY) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (n0 + lcol + cb * 32 + (r & 8) < N) l += __builtin_amdgcn_exp2f(acc[rb][cb][r] * sc - m);
+      }
+      mr[rb] = m;
+      lr[rb] = l;
+    }
+    tile_merge_sm<BM, WGN, RB>(mr, lr, red, wm, wn);
+    if (wn == 0 && hl == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = m0 + lrow + rb * 32;
+        if (row < M) st_dev2(P + (size_t)row * T + tn, make_float2(mr[rb], lr[rb]));
+      }
+    }
+    wait_stores();
+    __syncthreads();
+    uint64_t* jw = a.joins + rowblk;
+    if (t == 0) {
+      const uint64_t old = __hip_atomic_fetch_add(jw, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = ((uint32_t)old == (uint32_t)(T - 1)) ? 1 : 0;
+      gens[i] = (uint32_t)(old >> 32);
+    }
+    __syncthreads();
+    if (last) {
+      // merge the block's rows: NP threads per row over contiguous runs of
+      // members, then one thread per row over the NP runs, in order
+      const int r = t % BM, q = t / BM;
+      const int per = (T + NP - 1) / NP;
+      const int kb = q * per, ke = min(T, kb + per);
+      float m = -INFINITY, l = 0.0f;
+      if (m0 + r < M) {
+        const float2* Pr = P + (size_t)(m0 + r) * T;
+        for (int k0 = kb; k0 < ke; k0 += 8) {
+          float2 v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[k] = k0 + k < ke ? ld_dev2(Pr + k0 + k) : make_float2(-INFINITY, 0.0f);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) merge_sm(m, l, v[k].x, v[k].y);
+        }
+      }
+      parts[q * BM + r] = make_float2(m, l);
+      __syncthreads();
+      if (t < BM && m0 + t < M) {
+        float2 x = parts[t];
+        for (int k = 1; k < NP; ++k) merge_sm(x.x, x.y, parts[k * BM + t].x, parts[k * BM + t].y);
+        st_dev2(F + m0 + t, make_float2(x.x, 1.0f / x.y));
+      }
+      wait_stores();
+      __syncthreads();
+      if (t == 0) __hip_atomic_fetch_add(jw, (1ull << 32) - (uint64_t)T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // ------------------------------------------------ sweep 2: normalise, store
+  i = 0;
+  for (int tile = g; tile < tiles; tile += G, ++i) {
+    const int rowblk = tile / T, tn = tile - rowblk * T;
+    const int m0 = rowblk * BM, n0 = tn * BN;
+    const bool more = tile + G < tiles;
+    const int nt = more ? tile + G : 0;
+    f32x16 acc[RB][CB];
+    zero_acc(acc);
+    main_loop<BM, BN, BK, false, RB, CB>(a, rA, rB, s0, s1, m0, n0, more, (nt / T) * BM, (nt % T) * BN, acc, KT,
+                                         wm, wn);
+    if (t == 0) wait_generation(a.joins + rowblk, gens[i], a.err);
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = m0 + lrow + rb * 32;
+      const float2 st = row < M ? ld_dev2(F + row) : make_float2(0.0f, 0.0f);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = n0 + lcol + cb * 32 + 8 * h;
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = __builtin_amdgcn_exp2f(acc[rb][cb][8 * h + e] * sc - st.x) * st.y;
+          const u32x4 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                            pack_bf16x2(o[6], o[7])};
+          bst16(rY, (row < M && col < N) ? (uint32_t)(row * N + col) * 2u : kOOB, pk);
+        }
+      }
+    }
+  }
+}
+
+// Two bf16 lanes from two fp32 values, round to nearest even (one gfx950
+// conversion instruction).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// GEMM + row softmax by strips, for a reduction dimension of at most 128.
+// A workgroup owns a strip: BM = 128 rows (32 per wave) by a contiguous run
+// of BN = 128-column tiles.  Its Q rows stay in registers as MFMA operands;
+// only the K tiles stream through a two-slot LDS ring.  Every wave owns whole
+// rows of each tile, so per-tile row statistics are lane-local plus one lane
+// exchange, and they accumulate online across the strip.
+//   Sweep 1: strip statistics (max, sum of 2^(s - max)) per row, published
+//   once; the last strip of a row block to arrive merges the block's strips
+//   in order and publishes (max, 1/sum) per row.
+//   Sweep 2: after the row block's statistics are in (usually long before),
+//   the strip is computed again, normalised and stored as bf16.
+// The strip is recomputed rather than held across the wait: with a short
+// reduction dimension the second pass costs less than the exchange it hides.
+constexpr int kSmBM = 128, kSmBN = 128, kSmBK = 128;
+
+template <int MINB>
+__global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
+  constexpr int BM = kSmBM, BN = kSmBN, BK = kSmBK;
+  constexpr int CB = BN / 32, KS = BK / 16;
+  constexpr int SLOT = BN * BK * 2;  // one K tile: BN keys x BK dims
+  constexpr int LB = SLOT / 4096;    // 16-byte direct loads per lane per tile
+  __shared__ __align__(16) char s0[SLOT];
+  __shared__ __align__(16) char s1[SLOT];
+  __shared__ uint32_t gens[kMaxRounds];
+  __shared__ int last;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int M = (int)a.M, N = (int)a.N, D = (int)a.K;
+  const int G = (int)gridDim.x;
+  const int g = (int)xcd_local_id(blockIdx.x, (uint32_t)G);
+  const int T = a.tiles_n;        // column tiles per row
+  const int S = a.strips;         // strips per row block
+  const int C = (T + S - 1) / S;  // tiles per strip
+  const int units = a.tiles_m * S;
+  if (g >= units) return;
+  const int ksteps = (D + 15) / 16;
+  const __amdgpu_buffer_rsrc_t rA = rsrc(a.A, (uint32_t)(a.M * a.K * 2));
+  const __amdgpu_buffer_rsrc_t rB = rsrc(a.B, (uint32_t)(a.N * a.K * 2));
+  const __amdgpu_buffer_rsrc_t rY = rsrc(a.Y, (uint32_t)(a.M * a.N * 2));
+  const float sc = a.scale * kLog2e;
+  float2* P = reinterpret_cast<float2*>(a.partials);
+  float2* F = reinterpret_cast<float2*>(a.finals);
+
+  // direct loads of K tile j (keys j*BN .., all dims) into a slot
+  auto load_tile = [&](char* slot, int j) {
+#pragma unroll
+    for (int q = 0; q < LB; ++q) {
+      const int o = (q * 4 + w) * 1024 + lane * 16;
+      const int key = o / (BK * 2), pc = (o % (BK * 2)) / 16;
+      const int c = swz<BK>(key, pc);
+      const int gn = j * BN + key, gk = 8 * c;
+      g2l16(rB, slot + (q * 4 + w) * 1024, (gn < N && gk < D) ? (uint32_t)(gn * D + gk) * 2u : kOOB);
+    }
+  };
+  // strip u's first tile, and the tile that follows tile j of strip u
+  auto strip_first = [&](int u) { return (u % S) * C; };
+  auto strip_end = [&](int u) { return min(T, (u % S) * C + C); };
+
+  // one tile's MFMAs from a slot: acc[cb] += K-tile rows (permuted) x Q rows
+  auto mma_tile = [&](const char* slot, const bf16x8_t (&qf)[KS], f32x16 (&acc)[CB]) {
+    bf16x8_t kf[2][CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int key = cb * 32 + sigma(l32);
+      kf[0][cb] = *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz<BK>(key, hl));
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks >= ksteps) break;
+      const int cur = ks & 1;
+      if (ks + 1 < KS && ks + 1 < ksteps) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int key = cb * 32 + sigma(l32);
+          kf[cur ^ 1][cb] =
+              *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz<BK>(key, 2 * (ks + 1) + hl));
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][cb], qf[ks], acc[cb], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+      }
+    }
+  };
+  auto load_q = [&](int m0, bf16x8_t (&qf)[KS]) {
+    const int row = m0 + w * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int k = 16 * ks + 8 * hl;
+      qf[ks] = __builtin_bit_cast(bf16x8_t, bld16(rA, (row < M && k < D) ? (uint32_t)(row * D + k) * 2u : kOOB));
+    }
+  };
+
+  // the tile stream: sweep 1 over this workgroup's strips, then sweep 2 over
+  // the same strips; stage st of the stream lives in slot st & 1
+  int st = 0;
+  load_tile(s0, strip_first(g));
+  auto next_tile = [&](int sweep, int u, int j, int* nj) -> bool {
+    if (j + 1 < strip_end(u)) { *nj = j + 1; return true; }
+    if (u + G < units) { *nj = strip_first(u + G); return true; }
+    if (sweep == 1) { *nj = strip_first(g); return true; }
+    return false;
+  };
+  // wait for stage st, free the other slot, prefetch the next stage into it,
+  // then run the tile from stage st's slot
+  auto step = [&](int sweep, int u, int j, const bf16x8_t (&qf)[KS], f32x16 (&acc)[CB]) {
+    wait_vm<0>();
+    __syncthreads();
+    int nj = 0;
+    const bool more = next_tile(sweep, u, j, &nj);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
+    if (st & 1) {
+      if (more) load_tile(s0, nj);
+      mma_tile(s1, qf, acc);
+    } else {
+      if (more) load_tile(s1, nj);
+      mma_tile(s0, qf, acc);
+    }
+    ++st;
+  };
+
+  // ------------------------------------------------ sweep 1: statistics
+  int i = 0;
+  for (int u = g; u < units; u += G, ++i) {
+    const int rowblk = u / S, m0 = rowblk * BM;
+    bf16x8_t qf[KS];
+    load_q(m0, qf);
+    float m = -INFINITY, l = 0.0f;  // running, base-2 domain, this lane's row
+    for (int j = strip_first(u); j < strip_end(u); ++j) {
+      f32x16 acc[CB];
+      step(1, u, j, qf, acc);
+      const int c0 = j * BN + 16 * hl;
+      // the row max of the scaled values from the raw ones (scaling is monotone)
+      float ex = sc >= 0.0f ? -INFINITY : INFINITY;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (c0 + cb * 32 + (r & 8) < N) ex = sc >= 0.0f ? fmaxf(ex, acc[cb][r]) : fminf(ex, acc[cb][r]);
+      if (ex != INFINITY && ex != -INFINITY) {
+        const float mn = fmaxf(m, ex * sc);
+        float add = 0.0f;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (c0 + cb * 32 + (r & 8) < N) add += __builtin_amdgcn_exp2f(fmaf(acc[cb][r], sc, -mn));
+        l = l * __builtin_amdgcn_exp2f(m - mn) + add;
+        m = mn;
+      }
+    }
+    merge_sm(m, l, __shfl_xor(m, 32, kWave), __shfl_xor(l, 32, kWave));
+    const int row = m0 + w * 32 + l32;
+    if (hl == 0 && row < M) st_dev2(P + (size_t)row * S + (u % S), make_float2(m, l));
+    wait_stores();
+    __syncthreads();
+    uint64_t* jw = a.joins + rowblk;
+    if (t == 0) {
+      const uint64_t old = __hip_atomic_fetch_add(jw, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = ((uint32_t)old == (uint32_t)(S - 1)) ? 1 : 0;
+      gens[i] = (uint32_t)(old >> 32);
+    }
+    __syncthreads();
+    if (last) {
+      // merge the block's strips per row, in strip order, all loads in flight
+      if (t < BM && m0 + t < M) {
+        const float2* Pr = P + (size_t)(m0 + t) * S;
+        float mm = -INFINITY, ll = 0.0f;
+        for (int k0 = 0; k0 < S; k0 += 8) {
+          float2 v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[k] = k0 + k < S ? ld_dev2(Pr + k0 + k) : make_float2(-INFINITY, 0.0f);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) merge_sm(mm, ll, v[k].x, v[k].y);
+        }
+        st_dev2(F + m0 + t, make_float2(mm, 1.0f / ll));
+      }
+      wait_stores();
+      __syncthreads();
+      if (t == 0) __hip_atomic_fetch_add(jw, (1ull << 32) - (uint64_t)S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // ------------------------------------------------ sweep 2: normalise, store
+  i = 0;
+  for (int u = g; u < units; u += G, ++i) {
+    const int rowblk = u / S, m0 = rowblk * BM;
+    bf16x8_t qf[KS];
+    load_q(m0, qf);
+    if (t == 0) wait_generation(a.joins + rowblk, gens[i], a.err);
+    __syncthreads();
+    const int row = m0 + w * 32 + l32;
+    const float2 fs = row < M ? ld_dev2(F + row) : make_float2(0.0f, 0.0f);
+    for (int j = strip_first(u); j < strip_end(u); ++j) {
+      f32x16 acc[CB];
+      step(2, u, j, qf, acc);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = j * BN + cb * 32 + 16 * hl + 8 * h;
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * h + e], sc, -fs.x)) * fs.y;
+          const u32x4 pk = {cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]), cvt_bf16x2(o[4], o[5]),
+                            cvt_bf16x2(o[6], o[7])};
+          bst16(rY, (row < M && col < N) ? (uint32_t)(row * N + col) * 2u : kOOB, pk);
+        }
+    }
+  }
+}
+
+// GEMM + bias + residual + LayerNorm with each tile's join waited on only
+// after the NEXT tile's MainLoop: a workgroup computes tile j, publishes its
+// row statistics and arrives (the last member of the row block merges them),
+// computes tile j+1, and only then waits for tile j's block, normalises and
+// stores it.  Deadlock-free while every workgroup is resident and a row
+// block's tiles span at most two rounds: a workgroup never waits before it
+// has published the tile after the one it waits for.
+template <int BM, int BN, int BK, int WGM, int MINB>
+__global__ __launch_bounds__(kThreads, MINB) void k_gemm_ln2(GemmArgs a) {
+  using RG = Ring<BM, BN, BK, true>;
+  constexpr int WGN = 4 / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int RB = WM / 32, CB = WN / 32;
+  constexpr int NP = kThreads / BM;
+  static_assert(BM <= kThreads && kThreads % BM == 0 && WM % 32 == 0 && WN % 32 == 0, "tile");
+  __shared__ __align__(16) char s0[RG::STAGE_BYTES];
+  __shared__ __align__(16) char s1[RG::STAGE_BYTES];
+  __shared__ float4 red[WGN * BM];
+  __shared__ float4 parts[kThreads];
+  __shared__ int last;
+  __shared__ uint32_t gen_sh;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int lrow = wm * WM + l32, lcol = wn * WN + 16 * hl;
+  const int M = (int)a.M, N = (int)a.N;
+  const int KT = (int)((a.K + BK - 1) / BK);
+  const int G = (int)gridDim.x;
+  const int g = (int)xcd_local_id(blockIdx.x, (uint32_t)G);
+  const int T = a.tiles_n;
+  const int tiles = a.tiles_m * T;
+  if (g >= tiles) return;
+  const __amdgpu_buffer_rsrc_t rA = rsrc(a.A, (uint32_t)(a.M * a.K * 2));
+  const __amdgpu_buffer_rsrc_t rB = rsrc(a.B, (uint32_t)(a.N * a.K * 2));
+  const __amdgpu_buffer_rsrc_t rY = rsrc(a.Y, (uint32_t)(a.M * a.N * 2));
+  const __amdgpu_buffer_rsrc_t rR = rsrc(a.R, a.R ? (uint32_t)(a.M * a.N * 2) : 0u);  // no residual: reads zero
+  const __amdgpu_buffer_rsrc_t rBias = rsrc(a.bias, (uint32_t)(a.N * 4));
+  const __amdgpu_buffer_rsrc_t rGam = rsrc(a.gamma, (uint32_t)(a.N * 4));
+  const __amdgpu_buffer_rsrc_t rBet = rsrc(a.beta, (uint32_t)(a.N * 4));
+  float4* P = reinterpret_cast<float4*>(a.partials);
+  float2* F = reinterpret_cast<float2*>(a.finals);
+
+  // MainLoop, u = acc + bias + R, tile statistics, publish and arrive (and
+  // merge when last).  Returns the generation the tile's row block arrived in.
+  auto produce = [&](f32x16(&acc)[RB][CB], int tile) -> uint32_t {
+    const int rowblk = tile / T, tn = tile - rowblk * T;
+    const int m0 = rowblk * BM, n0 = tn * BN;
+    const bool more = tile + G < tiles;
+    const int nt = more ? tile + G : 0;
+    zero_acc(acc);
+    main_loop<BM, BN, BK, true, RB, CB>(a, rA, rB, s0, s1, m0, n0, more, (nt / T) * BM, (nt % T) * BN, acc, KT, wm,
+                                        wn);
+    // stage 1: u = acc + bias_j + R_ij in the accumulator registers (zero on
+    // columns past N), then the lane's (count, mean, M2) over valid columns
+    float n_[RB], mu[RB], m2[RB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int col = n0 + lcol + cb * 32 + 8 * h;
+        const bool ok = col < N;
+        const float4 b0 = bld16f(rBias, ok ? (uint32_t)col * 4u : kOOB);
+        const float4 b1 = bld16f(rBias, ok ? (uint32_t)col * 4u + 16u : kOOB);
+        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int row = m0 + lrow + rb * 32;
+          const u32x4 rr = bld16(rR, (ok && row < M) ? (uint32_t)(row * N + col) * 2u : kOOB);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t wv = rr[e >> 1];
+            const float u = acc[rb][cb][8 * h + e] + bv[e] + ((e & 1) ? bf16_hi(wv) : bf16_lo(wv));
+            acc[rb][cb][8 * h + e] = ok ? u : 0.0f;
+          }
+        }
+      }
+    }
+    int nvalid = 0;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) nvalid += (n0 + lcol + cb * 32 + 8 * h < N) ? 8 : 0;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += acc[rb][cb][r];
+      const float mean = nvalid > 0 ? sum / (float)nvalid : 0.0f;
+      float q2 = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float d = (n0 + lcol + cb * 32 + (r & 8) < N) ? acc[rb][cb][r] - mean : 0.0f;
+          q2 = fmaf(d, d, q2);
+        }
+      n_[rb] = (float)nvalid;
+      mu[rb] = mean;
+      m2[rb] = q2;
+    }
+    tile_merge_ln<BM, WGN, RB>(n_, mu, m2, red, wm, wn);
+    if (wn == 0 && hl == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = m0 + lrow + rb * 32;
+        if (row < M) {
+          float2* d = reinterpret_cast<float2*>(P + (size_t)row * T + tn);
+          st_dev2(d, make_float2(n_[rb], mu[rb]));
+          st_dev2(d + 1, make_float2(m2[rb], 0.0f));
+        }
+      }
+    }
+    wait_stores();
+    __syncthreads();
+    uint64_t* jw = a.joins + rowblk;
+    if (t == 0) {
+      const uint64_t old = __hip_atomic_fetch_add(jw, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = ((uint32_t)old == (uint32_t)(T - 1)) ? 1 : 0;
+      gen_sh = (uint32_t)(old >> 32);
+    }
+    __syncthreads();
+    const uint32_t gen0 = gen_sh;
+    if (last) {
+      const int r = t % BM, q = t / BM;
+      const int per = (T + NP - 1) / NP;
+      const int kb = q * per, ke = min(T, kb + per);
+      float cn = 0.0f, cm = 0.0f, c2 = 0.0f;
+      if (m0 + r < M) {
+        const float2* Pr = reinterpret_cast<const float2*>(P + (size_t)(m0 + r) * T);
+        for (int k0 = kb; k0 < ke; k0 += 4) {
+          float2 v[4][2];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            v[k][0] = k0 + k < ke ? ld_dev2(Pr + 2 * (k0 + k)) : make_float2(0.0f, 0.0f);
+            v[k][1] = k0 + k < ke ? ld_dev2(Pr + 2 * (k0 + k) + 1) : make_float2(0.0f, 0.0f);
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) merge_ln(cn, cm, c2, v[k][0].x, v[k][0].y, v[k][1].x);
+        }
+      }
+      parts[q * BM + r] = make_float4(cn, cm, c2, 0.0f);
+      __syncthreads();
+      if (t < BM && m0 + t < M) {
+        float4 x = parts[t];
+        for (int k = 1; k < NP; ++k) merge_ln(x.x, x.y, x.z, parts[k * BM + t].x, parts[k * BM + t].y, parts[k * BM + t].z);
+        st_dev2(F + m0 + t, make_float2(x.y, rsqrtf(x.z / (float)N + a.eps)));
+      }
+      wait_stores();
+      __syncthreads();
+      if (t == 0) __hip_atomic_fetch_add(jw, (1ull << 32) - (uint64_t)T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return gen0;
+  };
+
+  // wait for the tile's row block, y = (u - mean) * rstd * gamma + beta, store
+  auto finish = [&](f32x16(&acc)[RB][CB], int tile, uint32_t gen0) {
+    const int rowblk = tile / T, tn = tile - rowblk * T;
+    const int m0 = rowblk * BM, n0 = tn * BN;
+    if (t == 0) wait_generation(a.joins + rowblk, gen0, a.err);
+    __syncthreads();
+    float2 st[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = m0 + lrow + rb * 32;
+      st[rb] = row < M ? ld_dev2(F + row) : make_float2(0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int col = n0 + lcol + cb * 32 + 8 * h;
+        const bool ok = col < N;
+        const uint32_t vo = ok ? (uint32_t)col * 4u : kOOB;
+        const float4 g0 = bld16f(rGam, vo), g1 = bld16f(rGam, vo + 16u);
+        const float4 b0 = bld16f(rBet, vo), b1 = bld16f(rBet, vo + 16u);
+        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int row = m0 + lrow + rb * 32;
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = fmaf((acc[rb][cb][8 * h + e] - st[rb].x) * st[rb].y, gg[e], bb[e]);
+          const u32x4 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                            pack_bf16x2(o[6], o[7])};
+          bst16(rY, (ok && row < M) ? (uint32_t)(row * N + col) * 2u : kOOB, pk);
+        }
+      }
+    }
+  };
+
+  // cur holds the tile waiting for its join while nxt's MainLoop runs
+  f32x16 cur[RB][CB], nxt[RB][CB];
+  RG::load(a, rA, rB, s0, (g / T) * BM, (g % T) * BN, 0);
+  int tc = g;
+  uint32_t gc = produce(cur, tc);
+  for (;;) {
+    const int tn1 = tc + G;
+    uint32_t gn = 0;
+    if (tn1 < tiles) gn = produce(nxt, tn1);
+    finish(cur, tc, gc);
+    if (tn1 >= tiles) break;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) cur[rb][cb] = nxt[rb][cb];
+    tc = tn1;
+    gc = gn;
+  }
+}
+
 // ---------------------------------------------------------------- dispatch
 
 struct TileCfg {
@@ -738,9 +1492,41 @@ static hipError_t launch_gemm_t(const GemmPlan& pl, const GemmArgs& a, hipStream
   return hipErrorInvalidConfiguration;
 }
 
+template <int EPI>
+static hipError_t launch_gemm_overlap(const GemmPlan& pl, const GemmArgs& a, hipStream_t st, int* occ) {
+#define CF_GEMM2(CFG, BM, BN, BK, WGM, MINB)                                                            \
+  if (pl.cfg == CFG) {                                                                                  \
+    auto kfn = k_gemm_sm2<BM, BN, BK, WGM, MINB>;                                                        \
+    if constexpr (EPI == kEpiLN) kfn = k_gemm_ln2<BM, BN, BK, WGM, MINB>;                               \
+    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kfn, kThreads, 0);                \
+    hipLaunchKernelGGL(kfn, dim3(pl.grid), dim3(kThreads), 0, st, a);                                   \
+    return hipGetLastError();                                                                           \
+  }
+  CF_GEMM2(1, 256, 128, 64, 2, 1)
+  CF_GEMM2(2, 128, 256, 64, 2, 1)
+  CF_GEMM2(3, 128, 128, 64, 2, 2)
+  CF_GEMM2(4, 64, 512, 64, 1, 1)
+  CF_GEMM2(5, 128, 128, 32, 2, 2)
+#undef CF_GEMM2
+  return hipErrorInvalidConfiguration;
+}
+
 static hipError_t gemm_dispatch(int epi, const GemmPlan& pl, const GemmArgs& a, hipStream_t st, int* occ) {
-  if (epi == kEpiLN) return pl.nn ? launch_gemm_t<kEpiLN, true>(pl, a, st, occ) : hipErrorInvalidConfiguration;
-  if (epi == kEpiSoftmax) return pl.nn ? hipErrorInvalidConfiguration : launch_gemm_t<kEpiSoftmax, false>(pl, a, st, occ);
+  if (epi == kEpiLN) {
+    if (!pl.nn) return hipErrorInvalidConfiguration;
+    return pl.algo == 1 ? launch_gemm_overlap<kEpiLN>(pl, a, st, occ) : launch_gemm_t<kEpiLN, true>(pl, a, st, occ);
+  }
+  if (epi == kEpiSoftmax) {
+    if (pl.nn) return hipErrorInvalidConfiguration;
+    if (pl.algo == 2) {
+      auto kfn = k_gemm_sm3<2>;
+      if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kfn, kThreads, 0);
+      hipLaunchKernelGGL(kfn, dim3(pl.grid), dim3(kThreads), 0, st, a);
+      return hipGetLastError();
+    }
+    return pl.algo == 1 ? launch_gemm_overlap<kEpiSoftmax>(pl, a, st, occ)
+                        : launch_gemm_t<kEpiSoftmax, false>(pl, a, st, occ);
+  }
   return pl.nn ? launch_gemm_t<kEpiStoreF32, true>(pl, a, st, occ) : launch_gemm_t<kEpiStoreF32, false>(pl, a, st, occ);
 }
 

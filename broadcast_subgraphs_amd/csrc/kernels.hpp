@@ -62,6 +62,7 @@ struct GemmArgs {
   float* partials;     // M * tiles_n * 4 floats
   float* finals;       // M * 2 floats (leader aggregation)
   int agg_leader;      // 0: every member reads all partials; 1: last arriver combines
+  int strips;          // strip softmax: strips per row block
 };
 
 struct GemmPlan {
@@ -73,7 +74,14 @@ struct GemmPlan {
   int tiles = 0;
   int rounds = 0;
   bool leader = false;  // last-arriver aggregation (else every member reads all partials)
+  int algo = 1;         // fused epilogues: 0 = one join per round, 1 = joins overlapped with MainLoops,
+                        // 2 = softmax by strips (reduction dimension <= 128)
+  int strips = 1;       // algo 2: strips per row block
 };
+
+// Tiles one workgroup may take per sweep in the two-sweep softmax epilogue
+// (the generation each tile's row block arrived in is logged in LDS).
+constexpr int kMaxRounds = 256;
 
 hipError_t launch_gemm(int epi, const GemmPlan& pl, const GemmArgs& a, hipStream_t st);
 hipError_t gemm_occupancy(int epi, const GemmPlan& pl, int* per_cu);

@@ -212,6 +212,42 @@ def test_gemm_softmax_zero_q_is_exact():
     assert np.array_equal(g, np.full((M, N), 2.0 ** -13, np.float32))
 
 
+# Every GEMM epilogue schedule the planner can pick (forced through its
+# CF_GEMM_ALGO override): 0 one join per round, 1 joins overlapped with
+# MainLoops, 2 softmax by strips.
+SCHEDULE_SHAPES = [(300, 264, 72), (512, 1024, 128), (17, 8, 8), (1000, 2056, 128)]
+
+
+@pytest.mark.parametrize("algo", [0, 1])
+@pytest.mark.parametrize("M,N,K", SCHEDULE_SHAPES)
+def test_gemm_ln_every_schedule(monkeypatch, algo, M, N, K):
+    monkeypatch.setenv("CF_GEMM_ALGO", str(algo))
+    d = gen.gemm_ln_inputs(seed=6, M=M, N=N, K=K)
+    g = _gemm_ln_run(d, M, N, K)
+    o = oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"], d["beta"], d["eps"])
+    assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
+
+
+@pytest.mark.parametrize("algo", [0, 1, 2])
+@pytest.mark.parametrize("M,N,D", SCHEDULE_SHAPES)
+def test_gemm_softmax_every_schedule(monkeypatch, algo, M, N, D):
+    monkeypatch.setenv("CF_GEMM_ALGO", str(algo))
+    d = gen.gemm_softmax_inputs(seed=7, M=M, N=N, D=D)
+    g = _gemm_sm_run(d, M, N, D)
+    o = oracle.gemm_softmax(d["q"], d["k"], d["scale"])
+    assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
+
+
+def test_gemm_softmax_negative_scale():
+    """A negative scale flips which raw score is the row maximum."""
+    M, N, D = 256, 1000, 64
+    d = gen.gemm_softmax_inputs(seed=8, M=M, N=N, D=D)
+    d["scale"] = -abs(d["scale"])
+    g = _gemm_sm_run(d, M, N, D)
+    o = oracle.gemm_softmax(d["q"], d["k"], d["scale"])
+    assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
+
+
 # ------------------------------------------------------------- determinism
 
 def test_deterministic_runs():
