@@ -195,11 +195,11 @@ cf_status run_rows(const char* name, int op, const float* x, float* y, float* y_
 // Strip softmax: 128 x 128 tiles; each row block's column tiles are cut into
 // S strips of C consecutive tiles (no strip empty), one per resident
 // workgroup where the rows allow.
-static cf_status plan_gemm_strips(int64_t M, int64_t N, DevInfo* di, GemmPlan* p0, GemmPlan* pl) {
+static cf_status plan_gemm_strips(int64_t M, int64_t N, int64_t K, DevInfo* di, GemmPlan* p0, GemmPlan* pl) {
   GemmPlan p = *p0;
   p.bm = 128;
   p.bn = 128;
-  p.bk = 128;
+  p.bk = K <= 32 ? 32 : (K <= 64 ? 64 : 128);  // reduction depth the kernel covers (zero-padded)
   int occ = 0;
   if (gemm_occupancy(kEpiSoftmax, p, &occ) != hipSuccess || occ <= 0) return CF_EHIP;
   p.occupancy = occ;
@@ -230,13 +230,13 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   const int dalgo = (epi == kEpiSoftmax && K <= 128) ? 2 : 1;
   p.algo = epi == kEpiStoreF32 ? 0 : (int)env_int("CF_GEMM_ALGO", dalgo);
   if (p.algo == 2 && (epi != kEpiSoftmax || K > 128)) return CF_EUNSUPPORTED;
-  if (p.algo == 2) return plan_gemm_strips(M, N, di, &p, pl);
+  if (p.algo == 2) return plan_gemm_strips(M, N, K, di, &p, pl);
   // Default tiles (measured on MI355X): 128x128 at two workgroups per CU for
   // the plain GEMM and the overlapped epilogues, 64x512 for the round-based
   // epilogues.
   const int dflt = (epi == kEpiStoreF32 || p.algo == 1) ? 3 : 4;
   p.cfg = (int)env_int(epi == kEpiSoftmax ? "CF_GEMM_SOFTMAX_CFG" : (epi == kEpiLN ? "CF_GEMM_LN_CFG" : "CF_GEMM_CFG"), dflt);
-  if (!gemm_tile_config(p.cfg, &p.bm, &p.bn, &p.bk)) return CF_EUNSUPPORTED;
+  if (!gemm_tile_config(epi, p.algo, p.cfg, &p.bm, &p.bn, &p.bk)) return CF_EUNSUPPORTED;
   const int64_t tn = (N + p.bn - 1) / p.bn, tm = (M + p.bm - 1) / p.bm;
   p.tiles = (int)(tn * tm);
   int occ = 0;
@@ -246,11 +246,15 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   if (epi == kEpiStoreF32) {
     p.grid = (int)std::min<int64_t>(p.tiles, std::max<int64_t>(cap, 1) * 4);
   } else if (p.algo == 1) {
-    // one join word per row block; every workgroup resident; a row block's
-    // tiles within two consecutive rounds (the LN pipeline's progress bound)
-    const int64_t G = std::min<int64_t>(p.tiles, cap);
+    // one join word per row block; every workgroup resident.  Pipelined
+    // kernels: a row block's tiles within two consecutive rounds (their
+    // progress bound).  The one-tile-at-a-time LN kernel (256 x 256): whole
+    // row blocks per round.
     if (tm > kMaxJoins) return CF_EUNSUPPORTED;
-    if (G < 1 || tn > 2 * G) return CF_EOCCUPANCY;
+    int64_t G = std::min<int64_t>(p.tiles, cap);
+    const bool one_at_a_time = epi == kEpiLN && p.cfg == 0;  // k_gemm_ln2 without pipelining
+    if (one_at_a_time) G = std::min<int64_t>(p.tiles, cap / tn * tn);
+    if (G < 1 || tn > 2 * G || (one_at_a_time && G < tn)) return CF_EOCCUPANCY;
     if ((p.tiles + G - 1) / G > kMaxRounds) return CF_EUNSUPPORTED;
     p.grid = (int)G;
   } else {
@@ -295,6 +299,10 @@ cf_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
   // below 2^31 (the out-of-range offset)
   const int64_t lim = (int64_t)1 << 31;
   if (M * K * 2 >= lim || N * K * 2 >= lim || M * N * 2 >= lim) return CF_EUNSUPPORTED;
+  // offsets of a tile that overhangs the last row (by at most 256) stay
+  // below 2^32, so they land out of range instead of wrapping
+  const int64_t lim32 = (int64_t)1 << 32;
+  if ((M + 256) * K * 2 >= lim32 || (N + 256) * K * 2 >= lim32 || (M + 256) * N * 2 >= lim32) return CF_EUNSUPPORTED;
   return CF_OK;
 }
 
@@ -424,21 +432,26 @@ cf_status cf_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scale, cf_bf
 }
 
 // ------------------------------------------------------------ unfused chains
-// Workspace: fp32 intermediates.  Vectors first (aligned), then full-size
-// buffers.  Each operator materializes its output.
+// Workspace: fp32 intermediates, placed after the header and the join words
+// (which they never touch, so one zero-filled workspace serves fused and
+// unfused calls alike).  Vectors first (aligned), then full-size buffers.
+// Each operator materializes its output.
+
+static char* unfused_base(void* ws) { return static_cast<char*>(ws) + kPartialsOff; }
 
 size_t cf_unfused_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2) {
   if (d0 <= 0 || d1 <= 0) return (size_t)-1;
   const size_t vec = align_up((size_t)d0 * 4, 256);
   const size_t full = align_up((size_t)d0 * d1 * 4, 256);
+  size_t n = (size_t)-1;
   switch (op) {
-    case CF_OP_STITCH_SOFTMAX: return 2 * vec + 2 * full;
-    case CF_OP_STITCH_LAYERNORM: return 4 * vec + 2 * full;
-    case CF_OP_STITCH_POW_BCAST_ADD: return 3 * vec + 3 * full;
-    case CF_OP_GEMM_LN: return d2 > 0 ? 4 * vec + 3 * full : (size_t)-1;
-    case CF_OP_GEMM_SOFTMAX: return d2 > 0 ? 2 * vec + 3 * full : (size_t)-1;
+    case CF_OP_STITCH_SOFTMAX: n = 2 * vec + 2 * full; break;
+    case CF_OP_STITCH_LAYERNORM: n = 4 * vec + 2 * full; break;
+    case CF_OP_STITCH_POW_BCAST_ADD: n = 3 * vec + 3 * full; break;
+    case CF_OP_GEMM_LN: n = d2 > 0 ? 4 * vec + 3 * full : (size_t)-1; break;
+    case CF_OP_GEMM_SOFTMAX: n = d2 > 0 ? 2 * vec + 3 * full : (size_t)-1; break;
   }
-  return (size_t)-1;
+  return n == (size_t)-1 ? n : kPartialsOff + n;
 }
 
 #define CF_TRY(call)                        \
@@ -485,7 +498,7 @@ cf_status cf_unfused_stitch_softmax(const float* x, float* y, int64_t rows, int6
   if (!x || !y || rows <= 0 || cols <= 0) return CF_EINVAL;
   if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_STITCH_SOFTMAX, rows, cols, 0)) return CF_EWORKSPACE;
   g_last_plan = "{\"call\":\"cf_unfused_stitch_softmax\",\"kernels\":5}";
-  return unfused_softmax_chain(x, y, rows, cols, static_cast<char*>(ws), stream);
+  return unfused_softmax_chain(x, y, rows, cols, unfused_base(ws), stream);
 }
 
 cf_status cf_unfused_stitch_layernorm(const float* x, float* y, int64_t rows, int64_t cols, float eps, void* ws,
@@ -493,7 +506,7 @@ cf_status cf_unfused_stitch_layernorm(const float* x, float* y, int64_t rows, in
   if (!x || !y || rows <= 0 || cols <= 0 || !(eps >= 0.f)) return CF_EINVAL;
   if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_STITCH_LAYERNORM, rows, cols, 0)) return CF_EWORKSPACE;
   g_last_plan = "{\"call\":\"cf_unfused_stitch_layernorm\",\"kernels\":7}";
-  return unfused_ln_chain(x, y, rows, cols, eps, static_cast<char*>(ws), stream);
+  return unfused_ln_chain(x, y, rows, cols, eps, unfused_base(ws), stream);
 }
 
 cf_status cf_unfused_stitch_pow_bcast_add(const float* x, const float* v, float p, float* y, float* y_pre,
@@ -502,7 +515,7 @@ cf_status cf_unfused_stitch_pow_bcast_add(const float* x, const float* v, float 
   if (!x || !v || !y || rows <= 0 || cols <= 0) return CF_EINVAL;
   if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_STITCH_POW_BCAST_ADD, rows, cols, 0)) return CF_EWORKSPACE;
   // layout: pv [rows] | softmax chain scratch (2 vectors + 2 full) | Y (full, when y_pre is NULL)
-  char* w = static_cast<char*>(ws);
+  char* w = unfused_base(ws);
   const size_t vec = align_up((size_t)rows * 4, 256), full = align_up((size_t)rows * cols * 4, 256);
   float* pv = reinterpret_cast<float*>(w);
   char* chain = w + vec;
@@ -521,7 +534,7 @@ cf_status cf_unfused_gemm_ln(const cf_bf16* A, const cf_bf16* W, const float* bi
   if (s != CF_OK) return s;
   if (!aligned16(A) || !aligned16(W)) return CF_EALIGN;
   if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_GEMM_LN, M, N, K)) return CF_EWORKSPACE;
-  char* w = static_cast<char*>(ws);
+  char* w = unfused_base(ws);
   const size_t vec = align_up((size_t)M * 4, 256), full = align_up((size_t)M * N * 4, 256);
   float* z = reinterpret_cast<float*>(w + 4 * vec);
   float* u = reinterpret_cast<float*>(w + 4 * vec + full);
@@ -566,7 +579,7 @@ cf_status cf_unfused_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scal
   if (s != CF_OK) return s;
   if (!aligned16(Q) || !aligned16(K)) return CF_EALIGN;
   if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_GEMM_SOFTMAX, M, N, D)) return CF_EWORKSPACE;
-  char* w = static_cast<char*>(ws);
+  char* w = unfused_base(ws);
   const size_t vec = align_up((size_t)M * 4, 256), full = align_up((size_t)M * N * 4, 256);
   // layout: m [M] | s [M] | B0 | B1 | B2 (full fp32 buffers); each operator
   // reads and writes distinct buffers.

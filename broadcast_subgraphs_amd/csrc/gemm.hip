@@ -83,47 +83,74 @@ __device__ __forceinline__ void g2l16(__amdgpu_buffer_rsrc_t r, void* lds_base, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, (int)voff, 0, 0, 0);
 }
 
-template <int BM, int BN, int BK, bool NN>
+template <int BM, int BN, int BK, bool NN, int NWAVES = 4>
 struct Ring {
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int B_BYTES = BN * BK * 2;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LA = A_BYTES / 4096;  // 1 KB wave loads per thread for A
-  static constexpr int LB = B_BYTES / 4096;
-  static_assert(LA * 4096 == A_BYTES && LB * 4096 == B_BYTES, "tile bytes must be a multiple of 4 KB");
+  static constexpr int LA = A_BYTES / (NWAVES * 1024);  // 1 KB wave loads per thread for A
+  static constexpr int LB = B_BYTES / (NWAVES * 1024);
+  static_assert(LA * NWAVES * 1024 == A_BYTES && LB * NWAVES * 1024 == B_BYTES, "tile bytes per workgroup load");
 
-  // Issue the direct loads of one K-stage into `st`.  Lane p of wave w in
-  // instruction j writes LDS byte (j*4 + w)*1024 + 16p of the operand region;
-  // the lane picks the global chunk that belongs at that (swizzled) position.
-  __device__ __forceinline__ static void load(const GemmArgs& a, __amdgpu_buffer_rsrc_t ra,
-                                              __amdgpu_buffer_rsrc_t rb, char* st, int m0, int n0, int k0) {
+  // Lane p of wave w in load j writes LDS byte (j*NWAVES + w)*1024 + 16p of
+  // the operand region and fetches the global chunk that belongs at that
+  // (swizzled) position.  Its global byte offset is a uniform part (tile
+  // origin and k0) plus a per-lane part fixed for the whole kernel, kept in
+  // ao / bo.  Rows past M (A), past N (K) and W's rows past K fall outside the
+  // buffer's range and read zero.  A chunk of W past N wraps into the next
+  // row but feeds only output columns past N, which are never stored or
+  // counted.  A chunk past K of a K-contiguous operand (A, K) would wrap into
+  // the next row, so the last k-stage masks those to zero.
+  uint32_t ao[LA], bo[LB];
+  int N, K;
+
+  __device__ __forceinline__ explicit Ring(const GemmArgs& a) : N((int)a.N), K((int)a.K) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int M = (int)a.M, N = (int)a.N, K = (int)a.K;  // every operand is below 2^31 bytes
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
-      const int o = (j * 4 + w) * 1024 + lane * 16;
-      const int row = o / (BK * 2), pc = (o % (BK * 2)) / 16;
-      const int c = swz<BK>(row, pc);  // logical chunk stored at physical chunk pc
-      const int gm = m0 + row, gk = k0 + 8 * c;
-      const uint32_t off = (gm < M && gk < K) ? (uint32_t)(gm * K + gk) * 2u : kOOB;
-      g2l16(ra, st + (j * 4 + w) * 1024, off);
+      const int o = (j * NWAVES + w) * 1024 + lane * 16;
+      const int row = o / (BK * 2), c = swz<BK>(row, (o % (BK * 2)) / 16);
+      ao[j] = (uint32_t)(row * K + 8 * c) * 2u;
     }
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
-      const int o = (j * 4 + w) * 1024 + lane * 16;
-      uint32_t off;
+      const int o = (j * NWAVES + w) * 1024 + lane * 16;
       if constexpr (NN) {
-        const int k = o / (BN * 2), pb = o % (BN * 2);
-        const int cb = (pb ^ nn_mask(k)) / 16;  // logical 16-byte chunk along N
-        const int gk = k0 + k, gn = n0 + 8 * cb;
-        off = (gk < K && gn < N) ? (uint32_t)(gk * N + gn) * 2u : kOOB;
+        const int k = o / (BN * 2), cb = ((o % (BN * 2)) ^ nn_mask(k)) / 16;
+        bo[j] = (uint32_t)(k * N + 8 * cb) * 2u;
       } else {
-        const int row = o / (BK * 2), pc = (o % (BK * 2)) / 16;
-        const int c = swz<BK>(row, pc);
-        const int gn = n0 + row, gk = k0 + 8 * c;
-        off = (gn < N && gk < K) ? (uint32_t)(gn * K + gk) * 2u : kOOB;
+        const int row = o / (BK * 2), c = swz<BK>(row, (o % (BK * 2)) / 16);
+        bo[j] = (uint32_t)(row * K + 8 * c) * 2u;
       }
-      g2l16(rb, st + A_BYTES + (j * 4 + w) * 1024, off);
+    }
+  }
+
+  // Issue the direct loads of one K-stage into `st`.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, char* st, int m0,
+                                       int n0, int k0) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const bool ktail = k0 + BK > K;
+    const uint32_t ab = (uint32_t)(m0 * K + k0) * 2u;
+    const uint32_t bb = NN ? (uint32_t)(k0 * N + n0) * 2u : (uint32_t)(n0 * K + k0) * 2u;
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+      uint32_t off = ab + ao[j];
+      if (ktail) {
+        const int o = (j * NWAVES + w) * 1024 + lane * 16;
+        const int c = swz<BK>(o / (BK * 2), (o % (BK * 2)) / 16);
+        if (k0 + 8 * c >= K) off = kOOB;
+      }
+      g2l16(ra, st + (j * NWAVES + w) * 1024, off);
+    }
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+      uint32_t off = bb + bo[j];
+      if (!NN && ktail) {
+        const int o = (j * NWAVES + w) * 1024 + lane * 16;
+        const int c = swz<BK>(o / (BK * 2), (o % (BK * 2)) / 16);
+        if (k0 + 8 * c >= K) off = kOOB;
+      }
+      g2l16(rb, st + A_BYTES + (j * NWAVES + w) * 1024, off);
     }
   }
 };
@@ -166,35 +193,27 @@ __device__ __forceinline__ void load_frags(const char* st, int ks, bf16x8_t (&bo
   }
 }
 
-// One BK-deep stage of MFMAs from LDS.  The fragments of k-step ks+1 are read
-// while the MFMAs of step ks issue (two fragment register sets), and the
-// scheduler is asked to interleave LDS reads and the next stage's buffer loads
-// one by one between MFMAs, so a single wave per SIMD keeps the matrix core fed.
+// One BK-deep stage of MFMAs from LDS.  The fragments of k-step ks+1 are all
+// read before the MFMAs of step ks issue (two fragment register sets), with
+// hard scheduling barriers around each group: otherwise the compiler pulls
+// each read down next to its MFMA and reuses one register set, and every
+// MFMA then waits out a full LDS latency.
 template <int BM, int BN, int BK, bool NN, int RB, int CB, int NVMEM>
 __device__ __forceinline__ void mma_stage(const char* st, f32x16 (&acc)[RB][CB], int wm, int wn) {
   constexpr int KS = BK / 16;
-  constexpr int NDS = RB + (NN ? 2 : 1) * CB;  // LDS read instructions per k-step
   bf16x8_t bop[2][RB], aop[2][CB];
   load_frags<BM, BN, BK, NN, RB, CB>(st, 0, bop[0], aop[0], wm, wn);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int cur = ks & 1;
     if (ks + 1 < KS) load_frags<BM, BN, BK, NN, RB, CB>(st, ks + 1, bop[cur ^ 1], aop[cur ^ 1], wm, wn);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
         acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[cur][cb], bop[cur][rb], acc[rb][cb], 0, 0, 0);
-    // interleave: each MFMA followed by up to one LDS read and one buffer load
-    constexpr int NM = RB * CB;
-    const int nds = (ks + 1 < KS) ? NDS : 0;
-    constexpr int nvm = (NVMEM + KS - 1) / KS;
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // 1 MFMA
-      if (i < nds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // 1 DS read
-      if (i < nvm) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // 1 VMEM read
-    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -260,31 +279,95 @@ struct MergeSM {
 // computes.  With `nxt`, stage 0 of the tile at (nm0, nn0) goes into s0 as
 // soon as s0 is free, so its latency overlaps the caller's epilogue.  Waves
 // may still read s1 on return; the next call's first barrier covers that.
-template <int BM, int BN, int BK, bool NN, int RB, int CB>
-__device__ __forceinline__ void main_loop(const GemmArgs& a, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rB,
+template <int BM, int BN, int BK, bool NN, int RB, int CB, int NWAVES = 4>
+__device__ __forceinline__ void main_loop(const Ring<BM, BN, BK, NN, NWAVES>& rg, __amdgpu_buffer_rsrc_t rA,
+                                          __amdgpu_buffer_rsrc_t rB,
                                           char* s0, char* s1, int m0, int n0, bool nxt, int nm0, int nn0,
                                           f32x16 (&acc)[RB][CB], int KT, int wm, int wn) {
-  using RG = Ring<BM, BN, BK, NN>;
+  using RG = Ring<BM, BN, BK, NN, NWAVES>;
   constexpr int NV = RG::LA + RG::LB;
   for (int kt = 0; kt < KT; kt += 2) {
     wait_vm<0>();
     __syncthreads();
     const bool two = kt + 1 < KT;
-    if (two) RG::load(a, rA, rB, s1, m0, n0, (kt + 1) * BK);
+    if (two) rg.load(rA, rB, s1, m0, n0, (kt + 1) * BK);
     mma_stage<BM, BN, BK, NN, RB, CB, NV>(s0, acc, wm, wn);
     if (!two) {
       if (nxt) {
         __syncthreads();  // every wave is done with s0
-        RG::load(a, rA, rB, s0, nm0, nn0, 0);
+        rg.load(rA, rB, s0, nm0, nn0, 0);
       }
       break;
     }
     wait_vm<0>();
     __syncthreads();
-    if (kt + 2 < KT) RG::load(a, rA, rB, s0, m0, n0, (kt + 2) * BK);
-    else if (nxt) RG::load(a, rA, rB, s0, nm0, nn0, 0);
+    if (kt + 2 < KT) rg.load(rA, rB, s0, m0, n0, (kt + 2) * BK);
+    else if (nxt) rg.load(rA, rB, s0, nm0, nn0, 0);
     mma_stage<BM, BN, BK, NN, RB, CB, NV>(s1, acc, wm, wn);
   }
+}
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 63] (one immediate per case).
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+#define CF_W(k) \
+  case k:       \
+    wait_vm<k>(); \
+    return;
+    CF_W(0) CF_W(1) CF_W(2) CF_W(3) CF_W(4) CF_W(5) CF_W(6) CF_W(7) CF_W(8) CF_W(9) CF_W(10) CF_W(11) CF_W(12)
+    CF_W(13) CF_W(14) CF_W(15) CF_W(16) CF_W(17) CF_W(18) CF_W(19) CF_W(20) CF_W(21) CF_W(22) CF_W(23) CF_W(24)
+    CF_W(25) CF_W(26) CF_W(27) CF_W(28) CF_W(29) CF_W(30) CF_W(31) CF_W(32)
+#undef CF_W
+    default:
+      wait_vm<32>();
+      return;
+  }
+}
+
+// MainLoop of one tile over an NS-slot ring (separate LDS objects sl[0..NS-1],
+// so the compiler can tell the slot being read from the ones being filled).
+// Stage s lives in slot s % NS and is issued NS-1 stages ahead, so NS-1 loads
+// are in flight behind the one being computed; each step waits only for its
+// own stage (vector-memory loads complete in issue order), publishes it with
+// a barrier that also retires the slot computed last, refills that slot and
+// computes.  On entry stages 0 .. min(NS-1, KT)-1 of the tile have been issued
+// into slots 0, 1, ...  With `nxt` (requires KT % NS == 0), stages 0 .. NS-2
+// of the tile at (nm0, nn0) are issued the same way as the tail frees slots,
+// so the next call's entry condition holds and their latency overlaps the
+// caller's epilogue.
+template <int BM, int BN, int BK, bool NN, int RB, int CB, int NWAVES, int NS>
+__device__ __forceinline__ void main_loop_ns(const Ring<BM, BN, BK, NN, NWAVES>& rg, __amdgpu_buffer_rsrc_t rA,
+                                             __amdgpu_buffer_rsrc_t rB, char* const (&sl)[NS], int m0, int n0,
+                                             bool nxt, int nm0, int nn0, f32x16 (&acc)[RB][CB], int KT, int wm,
+                                             int wn) {
+  using RG = Ring<BM, BN, BK, NN, NWAVES>;
+  constexpr int LPS = RG::LA + RG::LB;  // loads per lane per stage
+  static_assert(NS >= 2 && (NS - 2) * LPS <= 32, "ring depth");
+  for (int kt = 0; kt < KT; kt += NS) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int st = kt + i;
+      if (st >= KT) break;
+      // stages issued after this one, whose loads may stay in flight
+      const int after = nxt ? NS - 2 : min(NS - 2, KT - 1 - st);
+      wait_vm_n(after * LPS);
+      __syncthreads();
+      const int sn = st + NS - 1;
+      if (sn < KT) rg.load(rA, rB, sl[(i + NS - 1) % NS], m0, n0, sn * BK);
+      else if (nxt && sn - KT < NS - 1) rg.load(rA, rB, sl[(i + NS - 1) % NS], nm0, nn0, (sn - KT) * BK);
+      mma_stage<BM, BN, BK, NN, RB, CB, LPS>(sl[i], acc, wm, wn);
+    }
+  }
+}
+
+// Issue the first min(NS-1, KT) stages of a tile into slots 0, 1, ...
+template <int BM, int BN, int BK, bool NN, int NWAVES, int NS>
+__device__ __forceinline__ void prologue_ns(const Ring<BM, BN, BK, NN, NWAVES>& rg, __amdgpu_buffer_rsrc_t rA,
+                                            __amdgpu_buffer_rsrc_t rB, char* const (&sl)[NS], int m0, int n0,
+                                            int KT) {
+#pragma unroll
+  for (int q = 0; q < NS - 1; ++q)
+    if (q < KT) rg.load(rA, rB, sl[q], m0, n0, q * BK);
 }
 
 // Pairwise merges of row statistics.  Both are symmetric in their arguments
@@ -425,6 +508,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
   const uint32_t g = (EPI == kEpiStoreF32) ? blockIdx.x : xcd_local_id(blockIdx.x, G);
   const __amdgpu_buffer_rsrc_t rA = rsrc(a.A, (uint32_t)(a.M * a.K * 2));
   const __amdgpu_buffer_rsrc_t rB = rsrc(a.B, (uint32_t)(a.N * a.K * 2));
+  const RG rg(a);
 
   for (int64_t tile = g; tile < tiles; tile += G) {
     const int64_t rowblk = tile / a.tiles_n;
@@ -440,8 +524,8 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
         for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.0f;
 
     // ------------------------------------------------------------ MainLoop
-    RG::load(a, rA, rB, lds, (int)m0, (int)n0, 0);
-    main_loop<BM, BN, BK, NN, RB, CB>(a, rA, rB, lds, lds1, (int)m0, (int)n0, false, 0, 0, acc, KT, wm, wn);
+    rg.load(rA, rB, lds, (int)m0, (int)n0, 0);
+    main_loop<BM, BN, BK, NN, RB, CB>(rg, rA, rB, lds, lds1, (int)m0, (int)n0, false, 0, 0, acc, KT, wm, wn);
     wait_vm<0>();
     __syncthreads();  // every wave is done with the ring: it is free from here on
 
@@ -837,6 +921,14 @@ __device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, u3
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
 }
 
+// The same with device-scope coherence (sc1), for cross-workgroup partials.
+__device__ __forceinline__ u32x4 bld16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16);
+}
+__device__ __forceinline__ void bst16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16);
+}
+
 template <int RB, int CB>
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[RB][CB]) {
 #pragma unroll
@@ -891,7 +983,8 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm2(GemmArgs a) {
   float2* P = reinterpret_cast<float2*>(a.partials);
   float2* F = reinterpret_cast<float2*>(a.finals);
 
-  RG::load(a, rA, rB, s0, (g / T) * BM, (g % T) * BN, 0);
+  const RG rg(a);
+  rg.load(rA, rB, s0, (g / T) * BM, (g % T) * BN, 0);
 
   // ------------------------------------------------ sweep 1: statistics
   int i = 0;
@@ -901,7 +994,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm2(GemmArgs a) {
     const int nt = tile + G < tiles ? tile + G : g;  // sweep 2 starts again at g
     f32x16 acc[RB][CB];
     zero_acc(acc);
-    main_loop<BM, BN, BK, false, RB, CB>(a, rA, rB, s0, s1, m0, n0, true, (nt / T) * BM, (nt % T) * BN, acc, KT,
+    main_loop<BM, BN, BK, false, RB, CB>(rg, rA, rB, s0, s1, m0, n0, true, (nt / T) * BM, (nt % T) * BN, acc, KT,
                                          wm, wn);
     float mr[RB], lr[RB];
 #pragma unroll
@@ -979,7 +1072,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm2(GemmArgs a) {
     const int nt = more ? tile + G : 0;
     f32x16 acc[RB][CB];
     zero_acc(acc);
-    main_loop<BM, BN, BK, false, RB, CB>(a, rA, rB, s0, s1, m0, n0, more, (nt / T) * BM, (nt % T) * BN, acc, KT,
+    main_loop<BM, BN, BK, false, RB, CB>(rg, rA, rB, s0, s1, m0, n0, more, (nt / T) * BM, (nt % T) * BN, acc, KT,
                                          wm, wn);
     if (t == 0) wait_generation(a.joins + rowblk, gens[i], a.err);
     __syncthreads();
@@ -1028,10 +1121,10 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 // reduction dimension the second pass costs less than the exchange it hides.
 constexpr int kSmBM = 128, kSmBN = 128, kSmBK = 128;
 
-template <int MINB>
+template <int KS, int MINB>
 __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
   constexpr int BM = kSmBM, BN = kSmBN, BK = kSmBK;
-  constexpr int CB = BN / 32, KS = BK / 16;
+  constexpr int CB = BN / 32;  // KS: 16-deep k-steps covering the reduction dimension
   constexpr int SLOT = BN * BK * 2;  // one K tile: BN keys x BK dims
   constexpr int LB = SLOT / 4096;    // 16-byte direct loads per lane per tile
   __shared__ __align__(16) char s0[SLOT];
@@ -1050,7 +1143,6 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
   const int C = (T + S - 1) / S;  // tiles per strip
   const int units = a.tiles_m * S;
   if (g >= units) return;
-  const int ksteps = (D + 15) / 16;
   const __amdgpu_buffer_rsrc_t rA = rsrc(a.A, (uint32_t)(a.M * a.K * 2));
   const __amdgpu_buffer_rsrc_t rB = rsrc(a.B, (uint32_t)(a.N * a.K * 2));
   const __amdgpu_buffer_rsrc_t rY = rsrc(a.Y, (uint32_t)(a.M * a.N * 2));
@@ -1058,22 +1150,29 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
   float2* P = reinterpret_cast<float2*>(a.partials);
   float2* F = reinterpret_cast<float2*>(a.finals);
 
-  // direct loads of K tile j (keys j*BN .., all dims) into a slot
-  auto load_tile = [&](char* slot, int j) {
+  // direct loads of K tile j (keys j*BN .., all dims) into a slot.  The
+  // lane's byte offset within a tile is fixed (kOOB past the reduction
+  // dimension); keys past N fall outside the buffer's range and read zero.
+  uint32_t koff[LB];
 #pragma unroll
-    for (int q = 0; q < LB; ++q) {
-      const int o = (q * 4 + w) * 1024 + lane * 16;
-      const int key = o / (BK * 2), pc = (o % (BK * 2)) / 16;
-      const int c = swz<BK>(key, pc);
-      const int gn = j * BN + key, gk = 8 * c;
-      g2l16(rB, slot + (q * 4 + w) * 1024, (gn < N && gk < D) ? (uint32_t)(gn * D + gk) * 2u : kOOB);
-    }
+  for (int q = 0; q < LB; ++q) {
+    const int o = (q * 4 + w) * 1024 + lane * 16;
+    const int key = o / (BK * 2), pc = (o % (BK * 2)) / 16;
+    const int gk = 8 * swz<BK>(key, pc);
+    koff[q] = gk < D ? (uint32_t)(key * D + gk) * 2u : kOOB;
+  }
+  auto load_tile = [&](char* slot, int j) {
+    const uint32_t base = (uint32_t)(j * BN) * (uint32_t)D * 2u;
+#pragma unroll
+    for (int q = 0; q < LB; ++q) g2l16(rB, slot + (q * 4 + w) * 1024, koff[q] + base);
   };
   // strip u's first tile, and the tile that follows tile j of strip u
   auto strip_first = [&](int u) { return (u % S) * C; };
   auto strip_end = [&](int u) { return min(T, (u % S) * C + C); };
 
-  // one tile's MFMAs from a slot: acc[cb] += K-tile rows (permuted) x Q rows
+  // one tile's MFMAs from a slot: acc[cb] += K-tile rows (permuted) x Q rows;
+  // step ks+1's fragments are all read before step ks's MFMAs issue (hard
+  // scheduling barriers keep the two register sets apart)
   auto mma_tile = [&](const char* slot, const bf16x8_t (&qf)[KS], f32x16 (&acc)[CB]) {
     bf16x8_t kf[2][CB];
 #pragma unroll
@@ -1083,9 +1182,8 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks >= ksteps) break;
       const int cur = ks & 1;
-      if (ks + 1 < KS && ks + 1 < ksteps) {
+      if (ks + 1 < KS) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
           const int key = cb * 32 + sigma(l32);
@@ -1093,13 +1191,10 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
               *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz<BK>(key, 2 * (ks + 1) + hl));
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][cb], qf[ks], acc[cb], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < CB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto load_q = [&](int m0, bf16x8_t (&qf)[KS]) {
@@ -1152,23 +1247,62 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
     for (int j = strip_first(u); j < strip_end(u); ++j) {
       f32x16 acc[CB];
       step(1, u, j, qf, acc);
+      // 8-column chunks of this lane's row: chunk q = (cb, h) holds columns
+      // j*BN + cb*32 + 16*hl + 8*h + [0, 8); it is valid or not as a whole
       const int c0 = j * BN + 16 * hl;
-      // the row max of the scaled values from the raw ones (scaling is monotone)
-      float ex = sc >= 0.0f ? -INFINITY : INFINITY;
+      bool ok[2 * CB];
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+      for (int q = 0; q < 2 * CB; ++q) ok[q] = c0 + (q >> 1) * 32 + 8 * (q & 1) < N;
+      // the row max of the scaled values from the raw ones (scaling is
+      // monotone): a tree over independent chunks, no long dependency chain
+      float ex;
+      if (sc >= 0.0f) {
+        float cm[2 * CB];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (c0 + cb * 32 + (r & 8) < N) ex = sc >= 0.0f ? fmaxf(ex, acc[cb][r]) : fminf(ex, acc[cb][r]);
+        for (int q = 0; q < 2 * CB; ++q) {
+          float v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[k] = acc[q >> 1][8 * (q & 1) + k];
+          const float x = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+          cm[q] = ok[q] ? x : -INFINITY;
+        }
+#pragma unroll
+        for (int st2 = 1; st2 < 2 * CB; st2 *= 2)
+#pragma unroll
+          for (int q = 0; q + st2 < 2 * CB; q += 2 * st2) cm[q] = fmaxf(cm[q], cm[q + st2]);
+        ex = cm[0];
+      } else {
+        float cm[2 * CB];
+#pragma unroll
+        for (int q = 0; q < 2 * CB; ++q) {
+          float v[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) v[k] = acc[q >> 1][8 * (q & 1) + k];
+          const float x = fminf(fminf(fminf(v[0], v[1]), fminf(v[2], v[3])), fminf(fminf(v[4], v[5]), fminf(v[6], v[7])));
+          cm[q] = ok[q] ? x : INFINITY;
+        }
+#pragma unroll
+        for (int st2 = 1; st2 < 2 * CB; st2 *= 2)
+#pragma unroll
+          for (int q = 0; q + st2 < 2 * CB; q += 2 * st2) cm[q] = fminf(cm[q], cm[q + st2]);
+        ex = cm[0];
+      }
       if (ex != INFINITY && ex != -INFINITY) {
         const float mn = fmaxf(m, ex * sc);
-        float add = 0.0f;
+        float cs[2 * CB];
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+        for (int q = 0; q < 2 * CB; ++q) {
+          float e[8];
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (c0 + cb * 32 + (r & 8) < N) add += __builtin_amdgcn_exp2f(fmaf(acc[cb][r], sc, -mn));
-        l = l * __builtin_amdgcn_exp2f(m - mn) + add;
+          for (int k = 0; k < 8; ++k) e[k] = __builtin_amdgcn_exp2f(fmaf(acc[q >> 1][8 * (q & 1) + k], sc, -mn));
+          const float x = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+          cs[q] = ok[q] ? x : 0.0f;
+        }
+#pragma unroll
+        for (int st2 = 1; st2 < 2 * CB; st2 *= 2)
+#pragma unroll
+          for (int q = 0; q + st2 < 2 * CB; q += 2 * st2) cs[q] += cs[q + st2];
+        l = l * __builtin_amdgcn_exp2f(m - mn) + cs[0];
         m = mn;
       }
     }
@@ -1234,24 +1368,31 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
 }
 
 // GEMM + bias + residual + LayerNorm with each tile's join waited on only
-// after the NEXT tile's MainLoop: a workgroup computes tile j, publishes its
-// row statistics and arrives (the last member of the row block merges them),
-// computes tile j+1, and only then waits for tile j's block, normalises and
-// stores it.  Deadlock-free while every workgroup is resident and a row
-// block's tiles span at most two rounds: a workgroup never waits before it
-// has published the tile after the one it waits for.
-template <int BM, int BN, int BK, int WGM, int MINB>
-__global__ __launch_bounds__(kThreads, MINB) void k_gemm_ln2(GemmArgs a) {
-  using RG = Ring<BM, BN, BK, true>;
-  constexpr int WGN = 4 / WGM;
+// after the NEXT tile's MainLoop (PIPE): a workgroup computes tile j,
+// publishes its row statistics and arrives (the last member of the row block
+// merges them), computes tile j+1, and only then waits for tile j's block,
+// normalises and stores it.  Deadlock-free while every workgroup is resident
+// and a row block's tiles span at most two rounds: a workgroup never waits
+// before it has published the tile after the one it waits for.  Without PIPE
+// (tiles too large for two accumulator sets) each tile is finished before
+// the next begins, and whole row blocks fall in one round.
+template <int BM, int BN, int BK, int WGM, int MINB, int NWAVES, bool PIPE, int NS>
+__global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
+  using RG = Ring<BM, BN, BK, true, NWAVES>;
+  constexpr int THREADS = NWAVES * 64;
+  constexpr int WGN = NWAVES / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int RB = WM / 32, CB = WN / 32;
-  constexpr int NP = kThreads / BM;
-  static_assert(BM <= kThreads && kThreads % BM == 0 && WM % 32 == 0 && WN % 32 == 0, "tile");
+  constexpr int NP = THREADS / BM;
+  static_assert(BM <= THREADS && THREADS % BM == 0 && WM % 32 == 0 && WN % 32 == 0, "tile");
+  // ring slots: separate objects (unused ones shrink to a placeholder)
   __shared__ __align__(16) char s0[RG::STAGE_BYTES];
   __shared__ __align__(16) char s1[RG::STAGE_BYTES];
+  __shared__ __align__(16) char s2[NS > 2 ? RG::STAGE_BYTES : 16];
+  __shared__ __align__(16) char s3[NS > 3 ? RG::STAGE_BYTES : 16];
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
   __shared__ float4 red[WGN * BM];
-  __shared__ float4 parts[kThreads];
+  __shared__ float4 parts[THREADS];
   __shared__ int last;
   __shared__ uint32_t gen_sh;
 
@@ -1274,19 +1415,35 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_ln2(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rBias = rsrc(a.bias, (uint32_t)(a.N * 4));
   const __amdgpu_buffer_rsrc_t rGam = rsrc(a.gamma, (uint32_t)(a.N * 4));
   const __amdgpu_buffer_rsrc_t rBet = rsrc(a.beta, (uint32_t)(a.N * 4));
-  float4* P = reinterpret_cast<float4*>(a.partials);
+  // partials: one 16-byte (count, mean, M2, 0) per row and column tile
+  const __amdgpu_buffer_rsrc_t rP = rsrc(a.partials, (uint32_t)(a.M * T * 16));
   float2* F = reinterpret_cast<float2*>(a.finals);
+  const RG rg(a);
+  char* const all_slots[4] = {s0, s1, s2, s3};
+  char* sl[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) sl[q] = all_slots[q];
+  bool staged = false;  // the next tile's first stages are already in the ring
 
-  // MainLoop, u = acc + bias + R, tile statistics, publish and arrive (and
-  // merge when last).  Returns the generation the tile's row block arrived in.
-  auto produce = [&](f32x16(&acc)[RB][CB], int tile) -> uint32_t {
+  // MainLoop, u = acc + bias + R, tile statistics, publish and arrive.
+  // Returns the generation the tile's row block arrived in; is_last tells
+  // whether this workgroup completed the block (it then merges the block's
+  // statistics in finish, where the other members wait anyway, so the merge
+  // never delays its next MainLoop).
+  auto produce = [&](f32x16(&acc)[RB][CB], int tile, bool& is_last) -> uint32_t {
     const int rowblk = tile / T, tn = tile - rowblk * T;
     const int m0 = rowblk * BM, n0 = tn * BN;
     const bool more = tile + G < tiles;
     const int nt = more ? tile + G : 0;
     zero_acc(acc);
-    main_loop<BM, BN, BK, true, RB, CB>(a, rA, rB, s0, s1, m0, n0, more, (nt / T) * BM, (nt % T) * BN, acc, KT, wm,
-                                        wn);
+    if (!staged) {
+      __syncthreads();  // every wave is done with the ring
+      prologue_ns<BM, BN, BK, true, NWAVES, NS>(rg, rA, rB, sl, m0, n0, KT);
+    }
+    const bool pre = PIPE && more && KT % NS == 0;
+    main_loop_ns<BM, BN, BK, true, RB, CB, NWAVES, NS>(rg, rA, rB, sl, m0, n0, pre, (nt / T) * BM, (nt % T) * BN,
+                                                       acc, KT, wm, wn);
+    staged = pre;
     // stage 1: u = acc + bias_j + R_ij in the accumulator registers (zero on
     // columns past N), then the lane's (count, mean, M2) over valid columns
     float n_[RB], mu[RB], m2[RB];
@@ -1342,11 +1499,9 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_ln2(GemmArgs a) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int row = m0 + lrow + rb * 32;
-        if (row < M) {
-          float2* d = reinterpret_cast<float2*>(P + (size_t)row * T + tn);
-          st_dev2(d, make_float2(n_[rb], mu[rb]));
-          st_dev2(d + 1, make_float2(m2[rb], 0.0f));
-        }
+        if (row < M)
+          bst16_dev(rP, (uint32_t)(row * T + tn) * 16u,
+                    u32x4{__float_as_uint(n_[rb]), __float_as_uint(mu[rb]), __float_as_uint(m2[rb]), 0u});
       }
     }
     wait_stores();
@@ -1359,22 +1514,34 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_ln2(GemmArgs a) {
     }
     __syncthreads();
     const uint32_t gen0 = gen_sh;
-    if (last) {
+    is_last = last != 0;
+    return gen0;
+  };
+
+  // the tile's row block statistics (merged here by the block's last
+  // arriver, waited for by the others), y = (u - mean) * rstd * gamma + beta,
+  // stored
+  auto finish = [&](f32x16(&acc)[RB][CB], int tile, uint32_t gen0, bool is_last) {
+    const int rowblk = tile / T;
+    const int tn = tile - rowblk * T;
+    const int m0 = rowblk * BM, n0 = tn * BN;
+    uint64_t* jw = a.joins + rowblk;
+    if (is_last) {
+      // merge each row's T partials in member order: NP threads per row over
+      // contiguous runs (8 partials in flight per round trip; past a run
+      // reads zero, count 0), then one thread per row over the runs
       const int r = t % BM, q = t / BM;
       const int per = (T + NP - 1) / NP;
       const int kb = q * per, ke = min(T, kb + per);
       float cn = 0.0f, cm = 0.0f, c2 = 0.0f;
       if (m0 + r < M) {
-        const float2* Pr = reinterpret_cast<const float2*>(P + (size_t)(m0 + r) * T);
-        for (int k0 = kb; k0 < ke; k0 += 4) {
-          float2 v[4][2];
+        for (int k0 = kb; k0 < ke; k0 += 8) {
+          u32x4 v[8];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            v[k][0] = k0 + k < ke ? ld_dev2(Pr + 2 * (k0 + k)) : make_float2(0.0f, 0.0f);
-            v[k][1] = k0 + k < ke ? ld_dev2(Pr + 2 * (k0 + k) + 1) : make_float2(0.0f, 0.0f);
-          }
+          for (int k = 0; k < 8; ++k) v[k] = bld16_dev(rP, k0 + k < ke ? (uint32_t)((m0 + r) * T + k0 + k) * 16u : kOOB);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) merge_ln(cn, cm, c2, v[k][0].x, v[k][0].y, v[k][1].x);
+          for (int k = 0; k < 8; ++k)
+            merge_ln(cn, cm, c2, __uint_as_float(v[k][0]), __uint_as_float(v[k][1]), __uint_as_float(v[k][2]));
         }
       }
       parts[q * BM + r] = make_float4(cn, cm, c2, 0.0f);
@@ -1387,16 +1554,10 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_ln2(GemmArgs a) {
       wait_stores();
       __syncthreads();
       if (t == 0) __hip_atomic_fetch_add(jw, (1ull << 32) - (uint64_t)T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (t == 0) wait_generation(jw, gen0, a.err);
+      __syncthreads();
     }
-    return gen0;
-  };
-
-  // wait for the tile's row block, y = (u - mean) * rstd * gamma + beta, store
-  auto finish = [&](f32x16(&acc)[RB][CB], int tile, uint32_t gen0) {
-    const int rowblk = tile / T, tn = tile - rowblk * T;
-    const int m0 = rowblk * BM, n0 = tn * BN;
-    if (t == 0) wait_generation(a.joins + rowblk, gen0, a.err);
-    __syncthreads();
     float2 st[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -1428,23 +1589,33 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_ln2(GemmArgs a) {
     }
   };
 
-  // cur holds the tile waiting for its join while nxt's MainLoop runs
-  f32x16 cur[RB][CB], nxt[RB][CB];
-  RG::load(a, rA, rB, s0, (g / T) * BM, (g % T) * BN, 0);
-  int tc = g;
-  uint32_t gc = produce(cur, tc);
-  for (;;) {
-    const int tn1 = tc + G;
-    uint32_t gn = 0;
-    if (tn1 < tiles) gn = produce(nxt, tn1);
-    finish(cur, tc, gc);
-    if (tn1 >= tiles) break;
+  if constexpr (PIPE) {
+    // cur holds the tile waiting for its join while nxt's MainLoop runs
+    f32x16 cur[RB][CB], nxt[RB][CB];
+    int tc = g;
+    bool lc = false, ln = false;
+    uint32_t gc = produce(cur, tc, lc);
+    for (;;) {
+      const int tn1 = tc + G;
+      uint32_t gn = 0;
+      if (tn1 < tiles) gn = produce(nxt, tn1, ln);
+      finish(cur, tc, gc, lc);
+      if (tn1 >= tiles) break;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) cur[rb][cb] = nxt[rb][cb];
-    tc = tn1;
-    gc = gn;
+        for (int cb = 0; cb < CB; ++cb) cur[rb][cb] = nxt[rb][cb];
+      tc = tn1;
+      gc = gn;
+      lc = ln;
+    }
+  } else {
+    f32x16 acc[RB][CB];
+    for (int tile = g; tile < tiles; tile += G) {
+      bool lst = false;
+      const uint32_t gen0 = produce(acc, tile, lst);
+      finish(acc, tile, gen0, lst);
+    }
   }
 }
 
@@ -1454,7 +1625,8 @@ struct TileCfg {
   int bm, bn, bk;
 };
 
-// Tile configurations (id -> shape); the launch list below must match.
+// Tile configurations (id -> shape); the launch lists below must match.
+// Round-based kernel (plain GEMM, and the fused epilogues' schedule 0):
 static const TileCfg kCfgs[] = {
     {256, 256, 64},  // 0: 2x2 waves of 128x128, 2-slot ring 128 KB, 1 WG/CU
     {256, 128, 64},  // 1: 2x2 waves of 128x64, 2-stage ring 96 KB, 1 WG/CU
@@ -1463,12 +1635,25 @@ static const TileCfg kCfgs[] = {
     {64, 512, 64},   // 4: 1x4 waves of 64x128, 2-stage ring 144 KB, 1 WG/CU
     {128, 128, 32},  // 5: 2x2 waves of 64x64, 2-stage ring 32 KB, 2 WG/CU
 };
+// GEMM + LN with overlapped joins (k_gemm_ln2):
+static const TileCfg kLnCfgs[] = {
+    {256, 256, 32},  // 0: 8 waves of 128x64, 4-slot ring 128 KB, 1 WG/CU, one tile at a time
+    {256, 128, 32},  // 1: 2x2 waves of 128x64, 4-slot ring 96 KB, 1 WG/CU, pipelined
+    {128, 256, 32},  // 2: 2x2 waves of 64x128, 4-slot ring 96 KB, 1 WG/CU, pipelined
+    {128, 128, 64},  // 3: 2x2 waves of 64x64, 2-slot ring 64 KB, 2 WG/CU, pipelined
+    {128, 128, 64},  // 4: 2x2 waves of 64x64, 4-slot ring 128 KB, 1 WG/CU, pipelined
+    {128, 128, 32},  // 5: 2x2 waves of 64x64, 4-slot ring 64 KB, 2 WG/CU, pipelined
+    {128, 128, 32},  // 6: 2x2 waves of 64x64, 2-slot ring 32 KB, 2 WG/CU, pipelined
+};
 
-bool gemm_tile_config(int cfg, int* bm, int* bn, int* bk) {
-  if (cfg < 0 || cfg >= (int)(sizeof(kCfgs) / sizeof(kCfgs[0]))) return false;
-  *bm = kCfgs[cfg].bm;
-  *bn = kCfgs[cfg].bn;
-  *bk = kCfgs[cfg].bk;
+bool gemm_tile_config(int epi, int algo, int cfg, int* bm, int* bn, int* bk) {
+  const bool ln2 = epi == kEpiLN && algo == 1;
+  const TileCfg* t = ln2 ? kLnCfgs : kCfgs;
+  const int n = ln2 ? (int)(sizeof(kLnCfgs) / sizeof(kLnCfgs[0])) : (int)(sizeof(kCfgs) / sizeof(kCfgs[0]));
+  if (cfg < 0 || cfg >= n) return false;
+  *bm = t[cfg].bm;
+  *bn = t[cfg].bn;
+  *bk = t[cfg].bk;
   return true;
 }
 
@@ -1494,20 +1679,30 @@ static hipError_t launch_gemm_t(const GemmPlan& pl, const GemmArgs& a, hipStream
 
 template <int EPI>
 static hipError_t launch_gemm_overlap(const GemmPlan& pl, const GemmArgs& a, hipStream_t st, int* occ) {
-#define CF_GEMM2(CFG, BM, BN, BK, WGM, MINB)                                                            \
-  if (pl.cfg == CFG) {                                                                                  \
-    auto kfn = k_gemm_sm2<BM, BN, BK, WGM, MINB>;                                                        \
-    if constexpr (EPI == kEpiLN) kfn = k_gemm_ln2<BM, BN, BK, WGM, MINB>;                               \
-    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kfn, kThreads, 0);                \
-    hipLaunchKernelGGL(kfn, dim3(pl.grid), dim3(kThreads), 0, st, a);                                   \
-    return hipGetLastError();                                                                           \
+  auto go = [&](auto kfn, int threads) -> hipError_t {
+    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kfn, threads, 0);
+    hipLaunchKernelGGL(kfn, dim3(pl.grid), dim3(threads), 0, st, a);
+    return hipGetLastError();
+  };
+  if constexpr (EPI == kEpiLN) {
+    switch (pl.cfg) {
+      case 0: return go(k_gemm_ln2<256, 256, 32, 2, 1, 8, false, 4>, 512);  // 8 waves of 128x64, one tile per round
+      case 1: return go(k_gemm_ln2<256, 128, 32, 2, 1, 4, true, 4>, 256);
+      case 2: return go(k_gemm_ln2<128, 256, 32, 2, 1, 4, true, 4>, 256);
+      case 3: return go(k_gemm_ln2<128, 128, 64, 2, 2, 4, true, 2>, 256);
+      case 4: return go(k_gemm_ln2<128, 128, 64, 2, 1, 4, true, 4>, 256);
+      case 5: return go(k_gemm_ln2<128, 128, 32, 2, 2, 4, true, 4>, 256);
+      case 6: return go(k_gemm_ln2<128, 128, 32, 2, 2, 4, true, 2>, 256);
+    }
+  } else {
+    switch (pl.cfg) {
+      case 1: return go(k_gemm_sm2<256, 128, 64, 2, 1>, 256);
+      case 2: return go(k_gemm_sm2<128, 256, 64, 2, 1>, 256);
+      case 3: return go(k_gemm_sm2<128, 128, 64, 2, 2>, 256);
+      case 4: return go(k_gemm_sm2<64, 512, 64, 1, 1>, 256);
+      case 5: return go(k_gemm_sm2<128, 128, 32, 2, 2>, 256);
+    }
   }
-  CF_GEMM2(1, 256, 128, 64, 2, 1)
-  CF_GEMM2(2, 128, 256, 64, 2, 1)
-  CF_GEMM2(3, 128, 128, 64, 2, 2)
-  CF_GEMM2(4, 64, 512, 64, 1, 1)
-  CF_GEMM2(5, 128, 128, 32, 2, 2)
-#undef CF_GEMM2
   return hipErrorInvalidConfiguration;
 }
 
@@ -1519,7 +1714,7 @@ static hipError_t gemm_dispatch(int epi, const GemmPlan& pl, const GemmArgs& a, 
   if (epi == kEpiSoftmax) {
     if (pl.nn) return hipErrorInvalidConfiguration;
     if (pl.algo == 2) {
-      auto kfn = k_gemm_sm3<2>;
+      auto kfn = pl.bk <= 32 ? k_gemm_sm3<2, 2> : (pl.bk <= 64 ? k_gemm_sm3<4, 2> : k_gemm_sm3<8, 2>);
       if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kfn, kThreads, 0);
       hipLaunchKernelGGL(kfn, dim3(pl.grid), dim3(kThreads), 0, st, a);
       return hipGetLastError();

@@ -85,7 +85,7 @@ constexpr int kMaxRounds = 256;
 
 hipError_t launch_gemm(int epi, const GemmPlan& pl, const GemmArgs& a, hipStream_t st);
 hipError_t gemm_occupancy(int epi, const GemmPlan& pl, int* per_cu);
-bool gemm_tile_config(int cfg, int* bm, int* bn, int* bk);
+bool gemm_tile_config(int epi, int algo, int cfg, int* bm, int* bn, int* bk);
 
 // ----------------------------------------------------------- unfused ops
 hipError_t u_rowreduce(const float* x, float* out, int64_t rows, int64_t cols, int is_max, hipStream_t st);

@@ -146,7 +146,10 @@ cf_status cf_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scale, cf_bf
 /* Unfused baselines: the same subgraphs as one kernel per operator, with     */
 /* fp32 intermediates in the workspace (in HBM) and broadcasts folded into    */
 /* the consumer's indexing.  Same arguments and results (up to rounding) as   */
-/* the fused calls.  [AStitch] "What people did before" (kernel storm);       */
+/* the fused calls.  The intermediates sit past the workspace's header and    */
+/* join words, so one zero-filled workspace of the larger of the two sizes    */
+/* serves both kinds of call.  [AStitch] "What people did before" (kernel     */
+/* storm);                                                                    */
 /* [sass2mlir] "What graphs deliberately don't do" (round trips remain).      */
 /* ------------------------------------------------------------------------ */
 

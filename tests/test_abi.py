@@ -86,7 +86,8 @@ def test_workspace_query_rejects_bad_dims(L):
     assert L.cf_workspace_bytes(99, 4, 4, 0) == bad
     assert L.cf_workspace_bytes(cf.CF_OP_STITCH_SOFTMAX, 0, 4, 0) == bad
     assert L.cf_unfused_workspace_bytes(cf.CF_OP_GEMM_LN, 16, 16, 0) == bad
-    assert L.cf_unfused_workspace_bytes(cf.CF_OP_STITCH_SOFTMAX, 2, 3, 0) == 2 * 256 + 2 * 256
+    # intermediates follow the 256-byte header and the 16384 eight-byte join words
+    assert L.cf_unfused_workspace_bytes(cf.CF_OP_STITCH_SOFTMAX, 2, 3, 0) == 256 + 16384 * 8 + 2 * 256 + 2 * 256
 
 
 def test_last_plan_is_a_string(L):

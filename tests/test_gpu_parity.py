@@ -248,6 +248,22 @@ def test_gemm_softmax_negative_scale():
     assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
 
 
+def test_fused_after_unfused_on_one_workspace():
+    """The unfused chains' intermediates never touch the join words: a fused
+    call on a workspace an unfused call just used still joins correctly."""
+    M, N, D = 512, 1024, 128
+    q = gen.gemm_softmax_inputs(seed=5, M=M, N=N, D=D)
+    need = max(cf.cf_unfused_workspace_bytes(cf.CF_OP_GEMM_SOFTMAX, M, N, D),
+               cf.cf_workspace_bytes(cf.CF_OP_GEMM_SOFTMAX, M, N, D))
+    ws = cf.Workspace(need)
+    S = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    cf.cf_gemm_softmax(dbf16(q["q_bits"]), dbf16(q["k_bits"]), q["scale"], S, ws=ws, unfused=True)
+    cf.cf_gemm_softmax(dbf16(q["q_bits"]), dbf16(q["k_bits"]), q["scale"], S, ws=ws)
+    check_ws(ws)
+    o = oracle.gemm_softmax(q["q"], q["k"], q["scale"])
+    assert rownorm_err(host(S), o) <= TOL_BF16
+
+
 # ------------------------------------------------------------- determinism
 
 def test_deterministic_runs():
