@@ -458,13 +458,16 @@ __device__ __forceinline__ void tile_merge_ln(float (&n)[RB], float (&mu)[RB], f
   }
 }
 
-// Spin until the join word's generation differs from gen0 (one lane).
+// Spin until the join word's generation differs from gen0 (one lane).  The
+// poll interval is ~0.2 us: hundreds of waiting workgroups polling a few join
+// words back to back slow down the device-scope loads of the workgroups they
+// wait for.
 __device__ __forceinline__ void wait_generation(uint64_t* jw, uint32_t gen0, uint32_t* err) {
   uint32_t it = 0;
   for (; it < kSpinCap; ++it) {
     const uint64_t wv = __hip_atomic_load(jw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((uint32_t)(wv >> 32) != gen0) break;
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(8);
   }
   if (it == kSpinCap) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -919,6 +922,10 @@ __device__ __forceinline__ float4 bld16f(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 __device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ float bld4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
 
 // The same with device-scope coherence (sc1), for cross-workgroup partials.
@@ -1393,7 +1400,8 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
   static_assert(NS >= 2 && NS <= 4, "ring depth");
   __shared__ float4 red[WGN * BM];
   __shared__ float4 parts[THREADS];
-  __shared__ int last;
+  __shared__ float2 stat[BM];
+  __shared__ __align__(16) float vec[3 * BN];  // this tile's bias | gamma | beta slices (zero past N)
   __shared__ uint32_t gen_sh;
 
   const int t = threadIdx.x;
@@ -1415,9 +1423,10 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rBias = rsrc(a.bias, (uint32_t)(a.N * 4));
   const __amdgpu_buffer_rsrc_t rGam = rsrc(a.gamma, (uint32_t)(a.N * 4));
   const __amdgpu_buffer_rsrc_t rBet = rsrc(a.beta, (uint32_t)(a.N * 4));
-  // partials: one 16-byte (count, mean, M2, 0) per row and column tile
-  const __amdgpu_buffer_rsrc_t rP = rsrc(a.partials, (uint32_t)(a.M * T * 16));
-  float2* F = reinterpret_cast<float2*>(a.finals);
+  // partials: (mean, M2) per row and column tile, 8 bytes; a tile's count
+  // is its number of valid columns
+  const int T2 = (T + 1) & ~1;  // row stride in partials, even: 16-byte aligned pairs
+  const __amdgpu_buffer_rsrc_t rP = rsrc(a.partials, (uint32_t)(a.M * T2 * 8));
   const RG rg(a);
   char* const all_slots[4] = {s0, s1, s2, s3};
   char* sl[NS];
@@ -1426,11 +1435,8 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
   bool staged = false;  // the next tile's first stages are already in the ring
 
   // MainLoop, u = acc + bias + R, tile statistics, publish and arrive.
-  // Returns the generation the tile's row block arrived in; is_last tells
-  // whether this workgroup completed the block (it then merges the block's
-  // statistics in finish, where the other members wait anyway, so the merge
-  // never delays its next MainLoop).
-  auto produce = [&](f32x16(&acc)[RB][CB], int tile, bool& is_last) -> uint32_t {
+  // Returns the generation the tile's row block arrived in.
+  auto produce = [&](f32x16(&acc)[RB][CB], int tile) -> uint32_t {
     const int rowblk = tile / T, tn = tile - rowblk * T;
     const int m0 = rowblk * BM, n0 = tn * BN;
     const bool more = tile + G < tiles;
@@ -1447,24 +1453,40 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
     // stage 1: u = acc + bias_j + R_ij in the accumulator registers (zero on
     // columns past N), then the lane's (count, mean, M2) over valid columns
     float n_[RB], mu[RB], m2[RB];
+    {
+      // one round trip: every residual load of the tile, and the tile's bias
+      // slice into LDS
+      u32x4 rr[RB][CB][2];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int col = n0 + lcol + cb * 32 + 8 * h;
-        const bool ok = col < N;
-        const float4 b0 = bld16f(rBias, ok ? (uint32_t)col * 4u : kOOB);
-        const float4 b1 = bld16f(rBias, ok ? (uint32_t)col * 4u + 16u : kOOB);
-        const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        for (int h = 0; h < 2; ++h) {
+          const int col = n0 + lcol + cb * 32 + 8 * h;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int row = m0 + lrow + rb * 32;
-          const u32x4 rr = bld16(rR, (ok && row < M) ? (uint32_t)(row * N + col) * 2u : kOOB);
+          for (int rb = 0; rb < RB; ++rb) {
+            const int row = m0 + lrow + rb * 32;
+            rr[rb][cb][h] = bld16(rR, (col < N && row < M) ? (uint32_t)(row * N + col) * 2u : kOOB);
+          }
+        }
+      for (int c = t; c < BN; c += THREADS) vec[c] = bld4f(rBias, n0 + c < N ? (uint32_t)(n0 + c) * 4u : kOOB);
+      __syncthreads();
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t wv = rr[e >> 1];
-            const float u = acc[rb][cb][8 * h + e] + bv[e] + ((e & 1) ? bf16_hi(wv) : bf16_lo(wv));
-            acc[rb][cb][8 * h + e] = ok ? u : 0.0f;
+      for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int cl = lcol + cb * 32 + 8 * h;
+          const bool ok = n0 + cl < N;
+          const float4 b0 = *reinterpret_cast<const float4*>(vec + cl);
+          const float4 b1 = *reinterpret_cast<const float4*>(vec + cl + 4);
+          const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t wv = rr[rb][cb][h][e >> 1];
+              const float u = acc[rb][cb][8 * h + e] + bv[e] + ((e & 1) ? bf16_hi(wv) : bf16_lo(wv));
+              acc[rb][cb][8 * h + e] = ok ? u : 0.0f;
+            }
           }
         }
       }
@@ -1499,80 +1521,86 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int row = m0 + lrow + rb * 32;
-        if (row < M)
-          bst16_dev(rP, (uint32_t)(row * T + tn) * 16u,
-                    u32x4{__float_as_uint(n_[rb]), __float_as_uint(mu[rb]), __float_as_uint(m2[rb]), 0u});
+        if (row < M) st_dev2(reinterpret_cast<float2*>(a.partials) + (size_t)row * T2 + tn, make_float2(mu[rb], m2[rb]));
       }
     }
     wait_stores();
     __syncthreads();
     uint64_t* jw = a.joins + rowblk;
     if (t == 0) {
+      // arrive; the last member advances the generation at once (every
+      // member merges the partials itself, in member order)
       const uint64_t old = __hip_atomic_fetch_add(jw, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = ((uint32_t)old == (uint32_t)(T - 1)) ? 1 : 0;
+      if ((uint32_t)old == (uint32_t)(T - 1))
+        __hip_atomic_fetch_add(jw, (1ull << 32) - (uint64_t)T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       gen_sh = (uint32_t)(old >> 32);
     }
     __syncthreads();
     const uint32_t gen0 = gen_sh;
-    is_last = last != 0;
     return gen0;
   };
 
-  // the tile's row block statistics (merged here by the block's last
-  // arriver, waited for by the others), y = (u - mean) * rstd * gamma + beta,
+  // wait for the tile's row block, merge its statistics (every member, the
+  // same way: member order, NP threads per row over contiguous runs, then
+  // one thread per row over the runs), y = (u - mean) * rstd * gamma + beta,
   // stored
-  auto finish = [&](f32x16(&acc)[RB][CB], int tile, uint32_t gen0, bool is_last) {
+  auto finish = [&](f32x16(&acc)[RB][CB], int tile, uint32_t gen0) {
     const int rowblk = tile / T;
     const int tn = tile - rowblk * T;
     const int m0 = rowblk * BM, n0 = tn * BN;
-    uint64_t* jw = a.joins + rowblk;
-    if (is_last) {
-      // merge each row's T partials in member order: NP threads per row over
-      // contiguous runs (8 partials in flight per round trip; past a run
-      // reads zero, count 0), then one thread per row over the runs
+    if (t == 0) wait_generation(a.joins + rowblk, gen0, a.err);
+    __syncthreads();
+    {
+      constexpr int PER = 16;  // partials per thread per round trip (8 paired loads)
       const int r = t % BM, q = t / BM;
-      const int per = (T + NP - 1) / NP;
+      const int per = ((T + NP - 1) / NP + 1) & ~1;  // even: runs start on a 16-byte pair
       const int kb = q * per, ke = min(T, kb + per);
       float cn = 0.0f, cm = 0.0f, c2 = 0.0f;
+      // this tile's gamma and beta slices into LDS, in the same round trip
+      for (int c = t; c < 2 * BN; c += THREADS) {
+        const int cc = c < BN ? c : c - BN;
+        const float v = bld4f(c < BN ? rGam : rBet, n0 + cc < N ? (uint32_t)(n0 + cc) * 4u : kOOB);
+        vec[BN + c] = v;
+      }
       if (m0 + r < M) {
-        for (int k0 = kb; k0 < ke; k0 += 8) {
-          u32x4 v[8];
+        for (int k0 = kb; k0 < ke; k0 += PER) {
+          u32x4 v[PER / 2];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) v[k] = bld16_dev(rP, k0 + k < ke ? (uint32_t)((m0 + r) * T + k0 + k) * 16u : kOOB);
+          for (int k = 0; k < PER / 2; ++k)
+            v[k] = bld16_dev(rP, k0 + 2 * k < ke ? (uint32_t)((m0 + r) * T2 + k0 + 2 * k) * 8u : kOOB);
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            merge_ln(cn, cm, c2, __uint_as_float(v[k][0]), __uint_as_float(v[k][1]), __uint_as_float(v[k][2]));
+          for (int k = 0; k < PER; ++k) {
+            const int j = k0 + k;
+            if (j < ke) {
+              const float nj = (float)min(BN, N - j * BN);
+              merge_ln(cn, cm, c2, nj, __uint_as_float(v[k >> 1][2 * (k & 1)]), __uint_as_float(v[k >> 1][2 * (k & 1) + 1]));
+            }
+          }
         }
       }
       parts[q * BM + r] = make_float4(cn, cm, c2, 0.0f);
       __syncthreads();
-      if (t < BM && m0 + t < M) {
+      if (t < BM) {
         float4 x = parts[t];
         for (int k = 1; k < NP; ++k) merge_ln(x.x, x.y, x.z, parts[k * BM + t].x, parts[k * BM + t].y, parts[k * BM + t].z);
-        st_dev2(F + m0 + t, make_float2(x.y, rsqrtf(x.z / (float)N + a.eps)));
+        stat[t] = make_float2(x.y, rsqrtf(x.z / (float)N + a.eps));
       }
-      wait_stores();
-      __syncthreads();
-      if (t == 0) __hip_atomic_fetch_add(jw, (1ull << 32) - (uint64_t)T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      if (t == 0) wait_generation(jw, gen0, a.err);
       __syncthreads();
     }
     float2 st[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int row = m0 + lrow + rb * 32;
-      st[rb] = row < M ? ld_dev2(F + row) : make_float2(0.0f, 0.0f);
-    }
+    for (int rb = 0; rb < RB; ++rb) st[rb] = stat[lrow + rb * 32];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int col = n0 + lcol + cb * 32 + 8 * h;
+        const int cl = lcol + cb * 32 + 8 * h;
+        const int col = n0 + cl;
         const bool ok = col < N;
-        const uint32_t vo = ok ? (uint32_t)col * 4u : kOOB;
-        const float4 g0 = bld16f(rGam, vo), g1 = bld16f(rGam, vo + 16u);
-        const float4 b0 = bld16f(rBet, vo), b1 = bld16f(rBet, vo + 16u);
+        const float4 g0 = *reinterpret_cast<const float4*>(vec + BN + cl);
+        const float4 g1 = *reinterpret_cast<const float4*>(vec + BN + cl + 4);
+        const float4 b0 = *reinterpret_cast<const float4*>(vec + 2 * BN + cl);
+        const float4 b1 = *reinterpret_cast<const float4*>(vec + 2 * BN + cl + 4);
         const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
         const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
@@ -1593,13 +1621,12 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
     // cur holds the tile waiting for its join while nxt's MainLoop runs
     f32x16 cur[RB][CB], nxt[RB][CB];
     int tc = g;
-    bool lc = false, ln = false;
-    uint32_t gc = produce(cur, tc, lc);
+    uint32_t gc = produce(cur, tc);
     for (;;) {
       const int tn1 = tc + G;
       uint32_t gn = 0;
-      if (tn1 < tiles) gn = produce(nxt, tn1, ln);
-      finish(cur, tc, gc, lc);
+      if (tn1 < tiles) gn = produce(nxt, tn1);
+      finish(cur, tc, gc);
       if (tn1 >= tiles) break;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
@@ -1607,14 +1634,12 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
         for (int cb = 0; cb < CB; ++cb) cur[rb][cb] = nxt[rb][cb];
       tc = tn1;
       gc = gn;
-      lc = ln;
     }
   } else {
     f32x16 acc[RB][CB];
     for (int tile = g; tile < tiles; tile += G) {
-      bool lst = false;
-      const uint32_t gen0 = produce(acc, tile, lst);
-      finish(acc, tile, gen0, lst);
+      const uint32_t gen0 = produce(acc, tile);
+      finish(acc, tile, gen0);
     }
   }
 }
