@@ -257,6 +257,23 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
     if (G < 1 || tn > 2 * G || (one_at_a_time && G < tn)) return CF_EOCCUPANCY;
     if ((p.tiles + G - 1) / G > kMaxRounds) return CF_EUNSUPPORTED;
     p.grid = (int)G;
+    // LN: each XCD takes a compact block of every full round's tile grid
+    // (sw_a row x sw_b column splits), the one with the fewest A + W bytes
+    p.sw_a = p.sw_b = 0;
+    if (epi == kEpiLN && env_int("CF_GEMM_SWIZZLE", 0) != 0 && G % 8 == 0 && G % tn == 0) {
+      const int64_t rows = G / tn;
+      int64_t best = -1;
+      for (int sa = 1; sa <= 8; sa *= 2) {
+        const int sb = 8 / sa;
+        if (rows % sa != 0 || tn % sb != 0) continue;
+        const int64_t cost = (rows / sa) * p.bm + (tn / sb) * p.bn;
+        if (best < 0 || cost < best) {
+          best = cost;
+          p.sw_a = sa;
+          p.sw_b = sb;
+        }
+      }
+    }
   } else {
     const int64_t G = std::min<int64_t>(p.tiles, cap / tn * tn);
     if (G < tn) return CF_EOCCUPANCY;
@@ -285,10 +302,11 @@ void record_gemm_plan(const char* name, int epi, const GemmPlan& p, int64_t M, i
   snprintf(buf, sizeof buf,
            "{\"call\":\"%s\",\"M\":%lld,\"N\":%lld,\"K\":%lld,\"kernel\":\"%s\",\"tile\":[%d,%d,%d],"
            "\"layout\":\"%s\",\"tiles\":%d,\"row_group\":%lld,\"grid\":%d,\"block\":256,\"occupancy\":%d,"
-           "\"rounds\":%d,\"aggregation\":\"%s\",\"schedule\":\"%s\"}",
+           "\"rounds\":%d,\"aggregation\":\"%s\",\"schedule\":\"%s\",\"xcd_block\":[%d,%d]}",
            name, (long long)M, (long long)N, (long long)K, kernel, p.bm, p.bn, p.bk, p.nn ? "NN" : "NT", p.tiles,
            p.algo == 2 ? (long long)p.strips : (long long)((N + p.bn - 1) / p.bn), p.grid, p.occupancy, p.rounds,
-           (ov || p.leader) ? "leader" : "peer-to-peer", sched);
+           (ov || p.leader) ? (epi == kEpiLN && p.algo == 1 ? "peer-to-peer" : "leader") : "peer-to-peer", sched,
+           p.sw_a, p.sw_b);
   g_last_plan = buf;
 }
 
@@ -394,6 +412,8 @@ static cf_status run_gemm(const char* name, int epi, bool nn, GemmArgs a, void* 
   a.tiles_m = (int)tm;
   a.agg_leader = p.leader ? 1 : 0;
   a.strips = p.strips;
+  a.sw_a = p.sw_a;
+  a.sw_b = p.sw_b;
   record_gemm_plan(name, epi, p, a.M, a.N, a.K);
   return launch_gemm(epi, p, a, stream) == hipSuccess ? CF_OK : CF_EHIP;
 }

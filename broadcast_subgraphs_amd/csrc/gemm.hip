@@ -1374,6 +1374,24 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
   }
 }
 
+// Tile of logical workgroup g in round r.  Round r holds the tiles
+// [r*G, (r+1)*G) of the row-major tile order, whatever the mapping, so each
+// round's tile set (and with it every argument about which rounds a row
+// block spans) is that of the linear order.  Within a full round of whole row
+// blocks, XCD x (logical ids [x*G/8, (x+1)*G/8), see xcd_local_id) takes a
+// compact block of (rows/sa) row blocks by (T/sb) column tiles, so its L2
+// holds that block's A rows and W columns instead of every W column; an XCD
+// keeps the same column slice from round to round.  Other rounds: linear.
+__device__ __forceinline__ int round_tile(int g, int r, int G, int T, int tiles, int sa, int sb) {
+  const int base = r * G;
+  if (base + g >= tiles) return -1;
+  if (sa == 0 || base + G > tiles) return base + g;
+  const int per = G >> 3;
+  const int x = g / per, k = g - x * per;
+  const int brow = G / T / sa, bcol = T / sb;  // brow * bcol == per
+  return base + ((x / sb) * brow + k / bcol) * T + (x % sb) * bcol + k % bcol;
+}
+
 // GEMM + bias + residual + LayerNorm with each tile's join waited on only
 // after the NEXT tile's MainLoop (PIPE): a workgroup computes tile j,
 // publishes its row statistics and arrives (the last member of the row block
@@ -1436,11 +1454,11 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
 
   // MainLoop, u = acc + bias + R, tile statistics, publish and arrive.
   // Returns the generation the tile's row block arrived in.
-  auto produce = [&](f32x16(&acc)[RB][CB], int tile) -> uint32_t {
+  auto produce = [&](f32x16(&acc)[RB][CB], int tile, int next_tile) -> uint32_t {
     const int rowblk = tile / T, tn = tile - rowblk * T;
     const int m0 = rowblk * BM, n0 = tn * BN;
-    const bool more = tile + G < tiles;
-    const int nt = more ? tile + G : 0;
+    const bool more = next_tile >= 0;
+    const int nt = more ? next_tile : 0;
     zero_acc(acc);
     if (!staged) {
       __syncthreads();  // every wave is done with the ring
@@ -1617,28 +1635,32 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
     }
   };
 
+  auto tile_at = [&](int r) { return round_tile(g, r, G, T, tiles, a.sw_a, a.sw_b); };
   if constexpr (PIPE) {
     // cur holds the tile waiting for its join while nxt's MainLoop runs
     f32x16 cur[RB][CB], nxt[RB][CB];
-    int tc = g;
-    uint32_t gc = produce(cur, tc);
+    int r = 0, tc = tile_at(0);
+    uint32_t gc = produce(cur, tc, tile_at(1));
     for (;;) {
-      const int tn1 = tc + G;
+      const int tn1 = tile_at(r + 1);
       uint32_t gn = 0;
-      if (tn1 < tiles) gn = produce(nxt, tn1);
+      if (tn1 >= 0) gn = produce(nxt, tn1, tile_at(r + 2));
       finish(cur, tc, gc);
-      if (tn1 >= tiles) break;
+      if (tn1 < 0) break;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) cur[rb][cb] = nxt[rb][cb];
       tc = tn1;
       gc = gn;
+      ++r;
     }
   } else {
     f32x16 acc[RB][CB];
-    for (int tile = g; tile < tiles; tile += G) {
-      const uint32_t gen0 = produce(acc, tile);
+    for (int r = 0;; ++r) {
+      const int tile = tile_at(r);
+      if (tile < 0) break;
+      const uint32_t gen0 = produce(acc, tile, -1);
       finish(acc, tile, gen0);
     }
   }

@@ -63,6 +63,7 @@ struct GemmArgs {
   float* finals;       // M * 2 floats (leader aggregation)
   int agg_leader;      // 0: every member reads all partials; 1: last arriver combines
   int strips;          // strip softmax: strips per row block
+  int sw_a, sw_b;      // LN: per-round tile blocks per XCD (sw_a row x sw_b column splits; 0 = linear)
 };
 
 struct GemmPlan {
@@ -77,6 +78,7 @@ struct GemmPlan {
   int algo = 1;         // fused epilogues: 0 = one join per round, 1 = joins overlapped with MainLoops,
                         // 2 = softmax by strips (reduction dimension <= 128)
   int strips = 1;       // algo 2: strips per row block
+  int sw_a = 0, sw_b = 0;  // algo 1 LN: XCD tile-block split of each round (0 = linear order)
 };
 
 // Tiles one workgroup may take per sweep in the two-sweep softmax epilogue
