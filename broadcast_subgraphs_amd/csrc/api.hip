@@ -103,13 +103,21 @@ cf_status plan_rows(int op, int64_t rows, int64_t cols, bool vec_ok, RowPlan* pl
   p.w = (vec_ok && cols % 4 == 0) ? 4 : 1;
   const int64_t nvec = (cols + p.w - 1) / p.w;
   const long force_split = env_int("CF_FORCE_SPLIT", 0);
+  const long force_wide = env_int("CF_FORCE_WIDE", -1);  // 1: one wide row per workgroup, 0: never
   if (nvec <= 64 && force_split <= 1) {
     p.lpr = (int)std::max<int64_t>(4, pow2ceil(nvec));
     p.nv = 1;
-    p.rpi = (int)env_int("CF_FORCE_RPI", p.lpr <= 16 ? 4 : 1);
+    p.rpi = (int)env_int("CF_FORCE_RPI", p.lpr <= 16 ? 2 : 1);
   } else if (nvec <= 256 * 16 && force_split <= 1) {
     p.lpr = 256;
     p.nv = pow2ceil((nvec + 255) / 256);
+    p.rpi = 1;
+  } else if (force_split <= 1 && force_wide != 0 && nvec <= 1024 * 8 && (rows < di->cus || force_wide == 1)) {
+    // few wide rows: one row per workgroup of 1024 lanes holds the whole row
+    // (<= 8 fragments per lane), so no cross-workgroup exchange is needed
+    p.block = 1024;
+    p.lpr = 1024;
+    p.nv = (int)std::max<int64_t>(4, pow2ceil((nvec + 1023) / 1024));
     p.rpi = 1;
   } else {
     // task splitting: S members per row, each holding <= 16 fragments per lane
@@ -124,10 +132,10 @@ cf_status plan_rows(int op, int64_t rows, int64_t cols, bool vec_ok, RowPlan* pl
     p.lpr = 256;
     p.rpi = 1;
   }
-  const int rows_per_blk = (256 / p.lpr) * p.rpi;
+  const int rows_per_blk = (p.block / p.lpr) * p.rpi;
   if (p.split == 1) {
     const int64_t nblk = (rows + rows_per_blk - 1) / rows_per_blk;
-    const int64_t cap = (int64_t)di->cus * env_int("CF_ROWS_WG_PER_CU", 8);
+    const int64_t cap = (int64_t)di->cus * env_int("CF_ROWS_WG_PER_CU", 32);
     p.grid = (int)std::min<int64_t>(nblk, env_int("CF_FORCE_GRID", cap));
   } else {
     int occ = 0;
@@ -154,9 +162,10 @@ void record_rows_plan(const char* name, const RowPlan& p, int64_t rows, int64_t 
   snprintf(buf, sizeof buf,
            "{\"call\":\"%s\",\"rows\":%lld,\"cols\":%lld,\"kernel\":\"%s\",\"frag_floats\":%d,"
            "\"lanes_per_row\":%d,\"frags_per_lane\":%d,\"rows_in_flight\":%d,\"split\":%d,"
-           "\"slice\":%lld,\"grid\":%d,\"block\":256,\"aggregation\":\"%s\",\"occupancy\":%d}",
+           "\"slice\":%lld,\"grid\":%d,\"block\":%d,\"aggregation\":\"%s\",\"occupancy\":%d}",
            name, (long long)rows, (long long)cols, p.split > 1 ? "k_rows_split" : "k_rows", p.w, p.lpr,
-           p.nv, p.rpi, p.split, (long long)p.slice, p.grid, p.split > 1 ? "all-read" : "none", p.occupancy);
+           p.nv, p.rpi, p.split, (long long)p.slice, p.grid, p.block, p.split > 1 ? "all-read" : "none",
+           p.occupancy);
   g_last_plan = buf;
 }
 

@@ -27,6 +27,7 @@ struct RowArgs {
 };
 
 struct RowPlan {
+  int block = 256;  // lanes per workgroup (256; 512 or 1024 for one wide row per workgroup)
   int w = 4;      // floats per fragment (4 or 1)
   int lpr = 256;  // lanes per row (in-workgroup plans)
   int nv = 1;     // fragments per lane per row

@@ -30,15 +30,15 @@ constexpr int kWaves = kBlock / kWave;
 // Two LDS slots, used alternately by consecutive reductions, so one barrier
 // per reduction suffices (the slot a reduction writes was last read before the
 // previous reduction's barrier).  O(1) space however many reductions chain.
-template <class Op, int LPR>
+template <class Op, int LPR, int BLOCK = kBlock>
 __device__ __forceinline__ float row_reduce(float v, float* red, int& slot, int group, int wave_in_row) {
   if constexpr (LPR <= kWave) {
     return group_reduce<Op, LPR>(v);
   } else {
     constexpr int WPR = LPR / kWave;  // waves per row
-    constexpr int RPW = kBlock / LPR; // rows per workgroup
+    constexpr int RPW = BLOCK / LPR;  // rows per workgroup
     v = group_reduce<Op, kWave>(v);
-    float* s = red + slot * (kWaves);
+    float* s = red + slot * (BLOCK / kWave);
     if ((threadIdx.x & (kWave - 1)) == 0) s[group * WPR + wave_in_row] = v;
     __syncthreads();
     float r = s[group * WPR];
@@ -72,17 +72,19 @@ __device__ __forceinline__ void store_frag(float* p, const float (&d)[W]) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Rows held inside one workgroup.  A row is owned by a group of LPR lanes
-// (packed 256/LPR rows per workgroup when LPR < 256); lane q of the group holds
+// Rows held inside one workgroup of BLOCK lanes.  A row is owned by a group
+// of LPR lanes (packed BLOCK/LPR rows per workgroup when LPR < BLOCK; a
+// workgroup of up to 1024 lanes owns a wide row whole, with no
+// cross-workgroup exchange); lane q of the group holds
 // fragments v*LPR + q (v < NV) of W floats each, so a wave's loads are
 // contiguous.  Each lane keeps RPI rows in flight (vertical packing: a
 // workgroup walks row blocks with a grid stride).
 // ---------------------------------------------------------------------------
-template <int OP, int LPR, int NV, int W, int RPI>
-__global__ __launch_bounds__(kBlock) void k_rows(RowArgs a) {
-  constexpr int RPW = kBlock / LPR;
+template <int OP, int LPR, int NV, int W, int RPI, int BLOCK = kBlock>
+__global__ __launch_bounds__(BLOCK) void k_rows(RowArgs a) {
+  constexpr int RPW = BLOCK / LPR;
   constexpr int WPR = LPR > kWave ? LPR / kWave : 1;
-  __shared__ float red[2 * kWaves];
+  __shared__ float red[2 * (BLOCK / kWave)];
   __shared__ float pv_lds[2][RPI * RPW];
 
   const int t = threadIdx.x;
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(kBlock) void k_rows(RowArgs a) {
             x[r][v][e] *= kLog2e;
             mm = fmaxf(mm, x[r][v][e]);
           }
-        m[r] = row_reduce<OpMax, LPR>(mm, red, slot, group, wave_in_row);
+        m[r] = row_reduce<OpMax, LPR, BLOCK>(mm, red, slot, group, wave_in_row);
       }
       // stage 2: exp and row sum; exp values bypass into stage 3 in registers
       float inv[RPI];
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kBlock) void k_rows(RowArgs a) {
             x[r][v][e] = ev;
             s += ev;
           }
-        inv[r] = 1.0f / row_reduce<OpSum, LPR>(s, red, slot, group, wave_in_row);
+        inv[r] = 1.0f / row_reduce<OpSum, LPR, BLOCK>(s, red, slot, group, wave_in_row);
       }
       // stage 3: broadcast divide and store
 #pragma unroll
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(kBlock) void k_rows(RowArgs a) {
         for (int v = 0; v < NV; ++v)
 #pragma unroll
           for (int e = 0; e < W; ++e) s += x[r][v][e];
-        mu[r] = row_reduce<OpSum, LPR>(s, red, slot, group, wave_in_row) * inv_n;
+        mu[r] = row_reduce<OpSum, LPR, BLOCK>(s, red, slot, group, wave_in_row) * inv_n;
       }
       float rs[RPI];
 #pragma unroll
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(kBlock) void k_rows(RowArgs a) {
             s = fmaf(c, c, s);
           }
         }
-        const float var = row_reduce<OpSum, LPR>(s, red, slot, group, wave_in_row) * inv_n;
+        const float var = row_reduce<OpSum, LPR, BLOCK>(s, red, slot, group, wave_in_row) * inv_n;
         rs[r] = rsqrtf(var + a.eps);
       }
 #pragma unroll
@@ -422,17 +424,26 @@ static hipError_t launch_rows_w(const RowPlan& pl, const RowArgs& a, hipStream_t
     return hipErrorInvalidConfiguration;
   }
 #define CF_ROWS(LPR, NV, RPI)                                                               \
-  if (pl.lpr == LPR && pl.nv == NV && pl.rpi == RPI) {                                      \
+  if (pl.block == kBlock && pl.lpr == LPR && pl.nv == NV && pl.rpi == RPI) {                \
     hipLaunchKernelGGL((k_rows<OP, LPR, NV, W, RPI>), grid, block, 0, st, a);               \
     return hipGetLastError();                                                               \
   }
   CF_ROWS(4, 1, 4) CF_ROWS(8, 1, 4) CF_ROWS(16, 1, 4) CF_ROWS(32, 1, 4) CF_ROWS(64, 1, 4)
+  CF_ROWS(4, 1, 2) CF_ROWS(8, 1, 2) CF_ROWS(16, 1, 2) CF_ROWS(32, 1, 2) CF_ROWS(64, 1, 2)
   CF_ROWS(4, 1, 1) CF_ROWS(8, 1, 1) CF_ROWS(16, 1, 1) CF_ROWS(32, 1, 1) CF_ROWS(64, 1, 1)
-  CF_ROWS(8, 1, 2) CF_ROWS(8, 1, 8)
+  CF_ROWS(8, 1, 8)
   CF_ROWS(64, 2, 1) CF_ROWS(64, 4, 1)
   CF_ROWS(128, 1, 1) CF_ROWS(128, 2, 1) CF_ROWS(128, 4, 1)
   CF_ROWS(256, 1, 1) CF_ROWS(256, 2, 1) CF_ROWS(256, 4, 1) CF_ROWS(256, 8, 1) CF_ROWS(256, 16, 1)
 #undef CF_ROWS
+  // one wide row per workgroup of 512 or 1024 lanes
+#define CF_WIDE(BLOCK, NV)                                                                  \
+  if (pl.block == BLOCK && pl.lpr == BLOCK && pl.nv == NV && pl.rpi == 1) {                 \
+    hipLaunchKernelGGL((k_rows<OP, BLOCK, NV, W, 1, BLOCK>), grid, dim3(BLOCK), 0, st, a);  \
+    return hipGetLastError();                                                               \
+  }
+  CF_WIDE(512, 8) CF_WIDE(512, 16) CF_WIDE(1024, 4) CF_WIDE(1024, 8)
+#undef CF_WIDE
   return hipErrorInvalidConfiguration;
 }
 
