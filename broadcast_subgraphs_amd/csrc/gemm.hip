@@ -1416,10 +1416,18 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
   __shared__ __align__(16) char s2[NS > 2 ? RG::STAGE_BYTES : 16];
   __shared__ __align__(16) char s3[NS > 3 ? RG::STAGE_BYTES : 16];
   static_assert(NS >= 2 && NS <= 4, "ring depth");
-  __shared__ float4 red[WGN * BM];
-  __shared__ float4 parts[THREADS];
-  __shared__ float2 stat[BM];
-  __shared__ __align__(16) float vec[3 * BN];  // this tile's bias | gamma | beta slices (zero past N)
+  // epilogue scratch: red (WGN x BM), parts (THREADS), stat (BM), vec (this
+  // tile's bias | gamma | beta slices, zero past N).  One tile at a time, the
+  // ring is idle during the epilogue, so the scratch lives in slot 0 when it
+  // fits (more workgroups per CU); pipelined, it has its own LDS.
+  constexpr int SCR = (WGN * BM + THREADS) * 16 + BM * 8 + 3 * BN * 4;
+  constexpr bool ALIAS = !PIPE && SCR <= RG::STAGE_BYTES;
+  __shared__ __align__(16) char scr_own[ALIAS ? 16 : SCR];
+  char* const scr = ALIAS ? s0 : scr_own;
+  float4* const red = reinterpret_cast<float4*>(scr);
+  float4* const parts = red + WGN * BM;
+  float2* const stat = reinterpret_cast<float2*>(parts + THREADS);
+  float* const vec = reinterpret_cast<float*>(stat + BM);
   __shared__ uint32_t gen_sh;
 
   const int t = threadIdx.x;
@@ -1468,42 +1476,48 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
     main_loop_ns<BM, BN, BK, true, RB, CB, NWAVES, NS>(rg, rA, rB, sl, m0, n0, pre, (nt / T) * BM, (nt % T) * BN,
                                                        acc, KT, wm, wn);
     staged = pre;
+    if constexpr (ALIAS) __syncthreads();  // every wave is done with slot 0 before the scratch in it is written
     // stage 1: u = acc + bias_j + R_ij in the accumulator registers (zero on
     // columns past N), then the lane's (count, mean, M2) over valid columns
     float n_[RB], mu[RB], m2[RB];
     {
-      // one round trip: every residual load of the tile, and the tile's bias
+      // every residual load of the tile in one round trip, and the tile's bias
       // slice into LDS
-      u32x4 rr[RB][CB][2];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int col = n0 + lcol + cb * 32 + 8 * h;
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const int row = m0 + lrow + rb * 32;
-            rr[rb][cb][h] = bld16(rR, (col < N && row < M) ? (uint32_t)(row * N + col) * 2u : kOOB);
-          }
-        }
+      constexpr int CBB = CB;
       for (int c = t; c < BN; c += THREADS) vec[c] = bld4f(rBias, n0 + c < N ? (uint32_t)(n0 + c) * 4u : kOOB);
       __syncthreads();
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
+      for (int cb0 = 0; cb0 < CB; cb0 += CBB) {
+        u32x4 rr[RB][CBB][2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int cl = lcol + cb * 32 + 8 * h;
-          const bool ok = n0 + cl < N;
-          const float4 b0 = *reinterpret_cast<const float4*>(vec + cl);
-          const float4 b1 = *reinterpret_cast<const float4*>(vec + cl + 4);
-          const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        for (int cq = 0; cq < CBB; ++cq)
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
+          for (int h = 0; h < 2; ++h) {
+            const int col = n0 + lcol + (cb0 + cq) * 32 + 8 * h;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t wv = rr[rb][cb][h][e >> 1];
-              const float u = acc[rb][cb][8 * h + e] + bv[e] + ((e & 1) ? bf16_hi(wv) : bf16_lo(wv));
-              acc[rb][cb][8 * h + e] = ok ? u : 0.0f;
+            for (int rb = 0; rb < RB; ++rb) {
+              const int row = m0 + lrow + rb * 32;
+              rr[rb][cq][h] = bld16(rR, (col < N && row < M) ? (uint32_t)(row * N + col) * 2u : kOOB);
+            }
+          }
+#pragma unroll
+        for (int cq = 0; cq < CBB; ++cq) {
+          const int cb = cb0 + cq;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int cl = lcol + cb * 32 + 8 * h;
+            const bool ok = n0 + cl < N;
+            const float4 b0 = *reinterpret_cast<const float4*>(vec + cl);
+            const float4 b1 = *reinterpret_cast<const float4*>(vec + cl + 4);
+            const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t wv = rr[rb][cq][h][e >> 1];
+                const float u = acc[rb][cb][8 * h + e] + bv[e] + ((e & 1) ? bf16_hi(wv) : bf16_lo(wv));
+                acc[rb][cb][8 * h + e] = ok ? u : 0.0f;
+              }
             }
           }
         }

@@ -238,6 +238,19 @@ def test_gemm_softmax_every_schedule(monkeypatch, algo, M, N, D):
     assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
 
 
+@pytest.mark.parametrize("cfg", range(7))
+@pytest.mark.parametrize("M,N,K", [(512, 1024, 256), (300, 264, 72)])
+def test_gemm_ln_every_tile_config(monkeypatch, cfg, M, N, K):
+    """Every tile configuration of the overlapped GEMM+LN kernel (forced through
+    the planner's CF_GEMM_LN_CFG override), including the one-tile-at-a-time
+    8-wave configuration whose epilogue scratch lives in the idle ring."""
+    monkeypatch.setenv("CF_GEMM_LN_CFG", str(cfg))
+    d = gen.gemm_ln_inputs(seed=9, M=M, N=N, K=K)
+    g = _gemm_ln_run(d, M, N, K)
+    o = oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"], d["beta"], d["eps"])
+    assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
+
+
 def test_gemm_softmax_negative_scale():
     """A negative scale flips which raw score is the row maximum."""
     M, N, D = 256, 1000, 64
