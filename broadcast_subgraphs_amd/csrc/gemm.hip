@@ -44,27 +44,41 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kThreads = 256;
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset beyond every range: reads zero
 
-// 16-byte-chunk XOR swizzle for K-contiguous tiles [rows][BK]: 8 consecutive
-// rows reading the same logical chunk hit 8 distinct 16-byte bank groups.
+// 16-byte-chunk XOR swizzles for K-contiguous tiles [rows][BK].  LDS has 64
+// banks of 4 bytes (256 bytes); a 16-byte fragment read is served 16 lanes at
+// a time, so the 16 rows one lane group reads at one logical chunk must land
+// in 16 distinct 16-byte bank slots.  A row of 2*BK bytes shares its slots
+// with the rows RPB = 256/(2*BK) apart, so the XOR takes the row bits above
+// log2(RPB) (measured on MI355X with SQ_LDS_BANK_CONFLICT: the earlier
+// row % 8 swizzle cost 3.9 stall cycles per 16-byte read, these none).
+// Rows read in order (lanes 0..15 = 16 consecutive rows):
 template <int BK>
 __device__ __forceinline__ int swz(int row, int c) {
-  constexpr int CPR = BK / 8;
-  constexpr int RD = CPR >= 8 ? 1 : 8 / CPR;
-  constexpr int MOD = CPR >= 8 ? 8 : CPR;
-  return c ^ ((row / RD) % MOD);
+  static_assert(BK == 32 || BK == 64 || BK == 128, "swizzled depth");
+  constexpr int CPR = BK / 8, RPB = 128 / BK;
+  return c ^ ((row / RPB) % CPR);
+}
+// Rows read through the sigma permutation (lanes 0..15 = rows 0-3, 16-19,
+// 4-7, 20-23 of a 32-row block): the varying row bits are 0, 1, 2 and 4.
+template <int BK>
+__device__ __forceinline__ int swz_sigma(int row, int c) {
+  static_assert(BK == 32 || BK == 64 || BK == 128, "swizzled depth");
+  constexpr int CPR = BK / 8, RPB = 128 / BK;
+  return c ^ (((row / RPB) & (CPR / 2 - 1)) | (((row >> 4) & 1) * (CPR / 2)));
 }
 
-// Byte-offset XOR for N-contiguous tiles [BK][BN]: the 4 k-rows one transpose
-// read touches land 0, 16, 64 and 80 bytes apart modulo the bank width.
-__device__ __forceinline__ int nn_mask(int k) { return ((k & 1) << 4) | (((k >> 1) & 1) << 6); }
+// Byte-offset XOR for N-contiguous tiles [BK][BN] read with the transpose
+// read: the 4 k-rows one read touches land 64 bytes apart modulo the bank
+// width, so their 64-byte segments cover all banks once (rows >= 256 bytes).
+__device__ __forceinline__ int nn_mask(int k) { return (k & 3) << 6; }
 
 // Output column (within a 32-column block) of MFMA row i under the permutation
 // that gives lane l the columns 16*(l>>5) .. 16*(l>>5)+15.
 __device__ __forceinline__ int sigma(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
 // 16-byte chunk swizzle of the epilogue's row-major LDS tiles (residual in,
-// output out): lanes 0..31 touch 32 rows at one column.
-__device__ __forceinline__ int eswz(int row, int c) { return c ^ (row & 7); }
+// output out; rows of >= 256 bytes): lanes 0..31 touch 32 rows at one column.
+__device__ __forceinline__ int eswz(int row, int c) { return c ^ (row & 15); }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
@@ -91,6 +105,7 @@ struct Ring {
   static constexpr int LA = A_BYTES / (NWAVES * 1024);  // 1 KB wave loads per thread for A
   static constexpr int LB = B_BYTES / (NWAVES * 1024);
   static_assert(LA * NWAVES * 1024 == A_BYTES && LB * NWAVES * 1024 == B_BYTES, "tile bytes per workgroup load");
+  static_assert(!NN || BN * 2 >= 256, "transpose-read swizzle needs rows of at least 256 bytes");
 
   // Lane p of wave w in load j writes LDS byte (j*NWAVES + w)*1024 + 16p of
   // the operand region and fetches the global chunk that belongs at that
@@ -119,7 +134,7 @@ struct Ring {
         const int k = o / (BN * 2), cb = ((o % (BN * 2)) ^ nn_mask(k)) / 16;
         bo[j] = (uint32_t)(k * N + 8 * cb) * 2u;
       } else {
-        const int row = o / (BK * 2), c = swz<BK>(row, (o % (BK * 2)) / 16);
+        const int row = o / (BK * 2), c = swz_sigma<BK>(row, (o % (BK * 2)) / 16);
         bo[j] = (uint32_t)(row * K + 8 * c) * 2u;
       }
     }
@@ -147,7 +162,7 @@ struct Ring {
       uint32_t off = bb + bo[j];
       if (!NN && ktail) {
         const int o = (j * NWAVES + w) * 1024 + lane * 16;
-        const int c = swz<BK>(o / (BK * 2), (o % (BK * 2)) / 16);
+        const int c = swz_sigma<BK>(o / (BK * 2), (o % (BK * 2)) / 16);
         if (k0 + 8 * c >= K) off = kOOB;
       }
       g2l16(rb, st + A_BYTES + (j * NWAVES + w) * 1024, off);
@@ -188,7 +203,7 @@ __device__ __forceinline__ void load_frags(const char* st, int ks, bf16x8_t (&bo
       const int n = wn * WN + cb * 32 + sigma(lane & 31);
       const int c = 2 * ks + (lane >> 5);
       aop[cb] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const uint16_t*>(Bs) + n * BK +
-                                                   8 * swz<BK>(n, c));
+                                                   8 * swz_sigma<BK>(n, c));
     }
   }
 }
@@ -494,7 +509,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
   static_assert(STAGES == 2, "ring slots are separate LDS objects; two are instantiated");
   constexpr int NP = BM >= kThreads ? 1 : kThreads / BM;  // threads combining one row's partials
   static_assert(WM % 32 == 0 && WN % 32 == 0 && WGM * WGN == 4, "wave tile");
-  static_assert(C16 >= 8 && (BM * C16) % kThreads == 0, "epilogue tile");
+  static_assert(C16 >= 16 && (BM * C16) % kThreads == 0, "epilogue tile");
   // Ring slot 0 doubles as the epilogue's LDS; slot 1 is a separate object so
   // the compiler can see that fragment reads of one slot never alias the
   // direct loads filling the other (no conservative wait on the prefetch).
@@ -550,7 +565,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
             const int c4 = (wn * WN + cb * 32 + 16 * hl) / 4;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              *reinterpret_cast<float4*>(ot + rr * BN + 4 * ((c4 + q) ^ (rr & 7))) =
+              *reinterpret_cast<float4*>(ot + rr * BN + 4 * ((c4 + q) ^ (rr & 15))) =
                   make_float4(acc[rb][cb][4 * q], acc[rb][cb][4 * q + 1], acc[rb][cb][4 * q + 2],
                               acc[rb][cb][4 * q + 3]);
           }
@@ -560,7 +575,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
           const int rr = id / F4, c = id % F4;
           const int64_t row = m0 + qt * QROWS + rr, col = n0 + 4 * c;
           if (row < a.M && col < a.N)
-            st4_stream(a.Z + row * a.N + col, *reinterpret_cast<const float4*>(ot + rr * BN + 4 * (c ^ (rr & 7))));
+            st4_stream(a.Z + row * a.N + col, *reinterpret_cast<const float4*>(ot + rr * BN + 4 * (c ^ (rr & 15))));
         }
         __syncthreads();
       }
@@ -1165,7 +1180,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
   for (int q = 0; q < LB; ++q) {
     const int o = (q * 4 + w) * 1024 + lane * 16;
     const int key = o / (BK * 2), pc = (o % (BK * 2)) / 16;
-    const int gk = 8 * swz<BK>(key, pc);
+    const int gk = 8 * swz_sigma<BK>(key, pc);
     koff[q] = gk < D ? (uint32_t)(key * D + gk) * 2u : kOOB;
   }
   auto load_tile = [&](char* slot, int j) {
@@ -1185,7 +1200,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int key = cb * 32 + sigma(l32);
-      kf[0][cb] = *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz<BK>(key, hl));
+      kf[0][cb] = *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz_sigma<BK>(key, hl));
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -1195,7 +1210,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
         for (int cb = 0; cb < CB; ++cb) {
           const int key = cb * 32 + sigma(l32);
           kf[cur ^ 1][cb] =
-              *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz<BK>(key, 2 * (ks + 1) + hl));
+              *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz_sigma<BK>(key, 2 * (ks + 1) + hl));
         }
       }
       __builtin_amdgcn_sched_barrier(0);
