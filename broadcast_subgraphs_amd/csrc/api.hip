@@ -229,6 +229,9 @@ static cf_status plan_gemm_strips(int64_t M, int64_t N, int64_t K, DevInfo* di, 
   return CF_OK;
 }
 
+// the k_gemm_ln2 configuration without pipelining (8 waves, 256 x 256 tiles)
+static bool ln_one_at_a_time(int epi, const GemmPlan& p) { return epi == kEpiLN && p.algo == 1 && p.cfg == 0; }
+
 cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan* pl) {
   DevInfo* di = nullptr;
   cf_status s = dev_info(&di);
@@ -261,7 +264,7 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
     // row blocks per round.
     if (tm > kMaxJoins) return CF_EUNSUPPORTED;
     int64_t G = std::min<int64_t>(p.tiles, cap);
-    const bool one_at_a_time = epi == kEpiLN && p.cfg == 0;  // k_gemm_ln2 without pipelining
+    const bool one_at_a_time = ln_one_at_a_time(epi, p);
     if (one_at_a_time) G = std::min<int64_t>(p.tiles, cap / tn * tn);
     if (G < 1 || tn > 2 * G || (one_at_a_time && G < tn)) return CF_EOCCUPANCY;
     if ((p.tiles + G - 1) / G > kMaxRounds) return CF_EUNSUPPORTED;
@@ -306,14 +309,17 @@ size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N) {
 void record_gemm_plan(const char* name, int epi, const GemmPlan& p, int64_t M, int64_t N, int64_t K) {
   const bool ov = p.algo >= 1 && epi != kEpiStoreF32;
   const char* kernel = p.algo == 2 ? "k_gemm_sm3" : (ov ? (epi == kEpiLN ? "k_gemm_ln2" : "k_gemm_sm2") : "k_gemm");
-  const char* sched = p.algo == 2 ? "strips" : (ov ? (epi == kEpiLN ? "pipelined" : "two-sweep") : "rounds");
+  const bool single = ln_one_at_a_time(epi, p);
+  const char* sched =
+      p.algo == 2 ? "strips" : (ov ? (epi == kEpiLN ? (single ? "one-tile-at-a-time" : "pipelined") : "two-sweep") : "rounds");
   char buf[512];
   snprintf(buf, sizeof buf,
            "{\"call\":\"%s\",\"M\":%lld,\"N\":%lld,\"K\":%lld,\"kernel\":\"%s\",\"tile\":[%d,%d,%d],"
-           "\"layout\":\"%s\",\"tiles\":%d,\"row_group\":%lld,\"grid\":%d,\"block\":256,\"occupancy\":%d,"
+           "\"layout\":\"%s\",\"tiles\":%d,\"row_group\":%lld,\"grid\":%d,\"block\":%d,\"occupancy\":%d,"
            "\"rounds\":%d,\"aggregation\":\"%s\",\"schedule\":\"%s\",\"xcd_block\":[%d,%d]}",
            name, (long long)M, (long long)N, (long long)K, kernel, p.bm, p.bn, p.bk, p.nn ? "NN" : "NT", p.tiles,
-           p.algo == 2 ? (long long)p.strips : (long long)((N + p.bn - 1) / p.bn), p.grid, p.occupancy, p.rounds,
+           p.algo == 2 ? (long long)p.strips : (long long)((N + p.bn - 1) / p.bn), p.grid, single ? 512 : 256,
+           p.occupancy, p.rounds,
            (ov || p.leader) ? (epi == kEpiLN && p.algo == 1 ? "peer-to-peer" : "leader") : "peer-to-peer", sched,
            p.sw_a, p.sw_b);
   g_last_plan = buf;

@@ -4,6 +4,8 @@ Error metric for every subgraph: per-row normalised max error
     err = max_i  max_j |g_ij - o_ij| / max_j |o_ij|
 bounded by 1e-4 for the fp32 paths and 2e-2 for the bf16-output GEMM paths.
 """
+import json
+
 import numpy as np
 import pytest
 import torch
@@ -247,6 +249,19 @@ def test_gemm_ln_every_tile_config(monkeypatch, cfg, M, N, K):
     monkeypatch.setenv("CF_GEMM_LN_CFG", str(cfg))
     d = gen.gemm_ln_inputs(seed=9, M=M, N=N, K=K)
     g = _gemm_ln_run(d, M, N, K)
+    o = oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"], d["beta"], d["eps"])
+    assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
+
+
+def test_gemm_ln_one_tile_at_a_time_rounds(monkeypatch):
+    """More 256 x 256 tiles than resident workgroups: whole row blocks per
+    round, the epilogue scratch in the ring reused by the next tile's
+    MainLoop; ragged last row block and column tile."""
+    monkeypatch.setenv("CF_GEMM_LN_CFG", "0")
+    M, N, K = 256 * 40 - 37, 2048 - 120, 64
+    d = gen.gemm_ln_inputs(seed=10, M=M, N=N, K=K)
+    g = _gemm_ln_run(d, M, N, K)
+    assert json.loads(cf.last_plan())["rounds"] >= 2, cf.last_plan()
     o = oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"], d["beta"], d["eps"])
     assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
 
