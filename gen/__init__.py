@@ -8,6 +8,7 @@ from .inputs import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     gemm_ln_inputs,
+    gemm_softmax_gemm_inputs,
     gemm_softmax_inputs,
     layernorm_inputs,
     normal,

@@ -1,4 +1,4 @@
-"""Seeded input generators for the five stitched / GEMM-fused subgraphs.
+"""Seeded input generators for the stitched / GEMM-fused subgraphs.
 
 Recipe (the same for every caller):
   * Each tensor draws from its own stream: numpy PCG64 seeded with
@@ -25,6 +25,7 @@ WORKLOADS = {
     "pow_bcast_add_softmax_64x30000": dict(rows=64, cols=30000),
     "gemm_ln_4096x4096x1024": dict(M=4096, N=4096, K=1024),
     "gemm_softmax_8192x8192x128": dict(M=8192, N=8192, D=128),
+    "gemm_softmax_gemm_8192x8192x128x128": dict(M=8192, N=8192, D=128, Dv=128),
 }
 
 
@@ -121,5 +122,22 @@ def gemm_softmax_inputs(seed: int = 5, M: int = 8192, N: int = 8192, D: int = 12
     return {
         "q_bits": q_bits, "q": q,
         "k_bits": k_bits, "k": k,
+        "scale": float(np.float32(1.0 / np.sqrt(np.float64(D)))),
+    }
+
+
+def gemm_softmax_gemm_inputs(seed: int = 6, M: int = 8192, N: int = 8192, D: int = 128, Dv: int = 128) -> dict:
+    """Back-to-back GEMM workload, O = softmax(scale * Q.K^T).V: Q bf16 [M x D], K bf16 [N x D],
+    V bf16 [N x Dv], all ~ N(0, 1).
+
+    The scale is the float32 value nearest 1/sqrt(D); both sides receive that stored value.
+    """
+    q_bits, q = _bf16(normal(seed, 0, (M, D)))
+    k_bits, k = _bf16(normal(seed, 1, (N, D)))
+    v_bits, v = _bf16(normal(seed, 2, (N, Dv)))
+    return {
+        "q_bits": q_bits, "q": q,
+        "k_bits": k_bits, "k": k,
+        "v_bits": v_bits, "v": v,
         "scale": float(np.float32(1.0 / np.sqrt(np.float64(D)))),
     }

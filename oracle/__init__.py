@@ -19,6 +19,7 @@ from . import ops  # noqa: F401
 from .subgraphs import (  # noqa: F401
     gemm_ln,
     gemm_softmax,
+    gemm_softmax_gemm,
     layernorm_rows,
     pow_bcast_add_softmax,
     softmax_rows,

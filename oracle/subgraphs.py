@@ -12,6 +12,8 @@ its reason in the design notes):
     broadcasts, indexed by the output column).
   * Q.K^T takes K row-major [N x D]; the scale multiplies the accumulator
     before the softmax.
+  * The back-to-back product takes its second operand V row-major [N x Dv]
+    (keys by output columns): O = S.V with S the scaled row softmax above.
 """
 from __future__ import annotations
 
@@ -96,3 +98,16 @@ def gemm_softmax(q, k, scale: float) -> np.ndarray:
     p = ops.matmul(ops.f64(q), ops.transpose(ops.f64(k)))
     s = ops.scale(p, scale)
     return softmax_rows(s)
+
+
+def gemm_softmax_gemm(q, k, v, scale: float) -> np.ndarray:
+    """O = softmax(scale * Q.K^T) . V: two MatMuls back to back with the softmax between them.
+
+    ComFuse, B2BGEMM: the first MatMul's tile P becomes S = F(P) (eq. 3) with
+    F the scaled row softmax, and the second MatMul multiplies S by W2 = V
+    (eq. 4-5: partial products over the contraction dimension N1 summed into
+    the output tile; here the whole sum is one matmul, eq. 6 shapes
+    X = Q [M x K], W1 = K^T [K x N1], W2 = V [N1 x N2]).
+    """
+    s = gemm_softmax(q, k, scale)
+    return ops.matmul(s, ops.f64(v))

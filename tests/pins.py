@@ -243,4 +243,54 @@ def pin_gemm_softmax_brute_force():
         _close(oracle.gemm_softmax(q, k, sc), yb, 1e-13, what=f"GEMM+softmax brute {m,n,d}")
 
 
+# -------------------------------------------------- back-to-back GEMM (softmax between)
+
+def pin_b2b_brute_force():
+    """O_ij = sum_n softmax_n(scale * q_i . k_n) v_nj, every sum written out in pure Python."""
+    for (m, n, d, dv) in [(3, 5, 4, 2), (4, 4, 4, 4), (2, 7, 3, 5)]:
+        rng = _rng(60 + m + n)
+        q, k, v = rng.normal(size=(m, d)), rng.normal(size=(n, d)), rng.normal(size=(n, dv))
+        sc = 1.0 / math.sqrt(d)
+        kt = [[k[j, t] for j in range(n)] for t in range(d)]
+        p = _bf_matmul(q.tolist(), kt)
+        sm = _bf_softmax([[sc * x for x in row] for row in p])
+        ob = _bf_matmul(sm, v.tolist())
+        _close(oracle.gemm_softmax_gemm(q, k, v, sc), ob, 1e-12, 1e-14, what=f"B2B brute {m,n,d,dv}")
+
+
+def pin_b2b_ones_v():
+    """Every softmax row sums to one, so a V of ones gives an output of ones."""
+    rng = _rng(64)
+    q, k = rng.normal(size=(6, 16)), rng.normal(size=(40, 16))
+    o = oracle.gemm_softmax_gemm(q, k, np.ones((40, 3)), 0.25)
+    _close(o, np.ones((6, 3)), 0.0, 1e-14, what="B2B ones V")
+
+
+def pin_b2b_zero_q():
+    """Q = 0 makes every score equal: each output row is the column mean of V."""
+    rng = _rng(65)
+    k, v = rng.normal(size=(30, 8)), rng.normal(size=(30, 5))
+    o = oracle.gemm_softmax_gemm(np.zeros((4, 8)), k, v, 0.5)
+    _close(o, np.repeat(v.mean(axis=0)[None, :], 4, axis=0), 1e-13, 1e-15, what="B2B zero Q")
+
+
+def pin_b2b_key_permutation():
+    """Reordering the keys (rows of K and V together) leaves the output unchanged."""
+    rng = _rng(66)
+    q, k, v = rng.normal(size=(5, 12)), rng.normal(size=(33, 12)), rng.normal(size=(33, 7))
+    perm = rng.permutation(33)
+    _close(oracle.gemm_softmax_gemm(q, k[perm], v[perm], 0.3), oracle.gemm_softmax_gemm(q, k, v, 0.3),
+           1e-12, 1e-14, what="B2B key permutation")
+
+
+def pin_b2b_one_hot():
+    """Orthogonal keys and a large scale: each row's softmax is one-hot, so the row copies one row of V."""
+    n = 8
+    k = np.eye(n)
+    q = np.eye(n)[[3, 0, 7, 5]]
+    v = _rng(67).normal(size=(n, 4))
+    o = oracle.gemm_softmax_gemm(q, k, v, 100.0)
+    _close(o, v[[3, 0, 7, 5]], 1e-12, 1e-12, what="B2B one-hot")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

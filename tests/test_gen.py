@@ -49,3 +49,7 @@ def test_workload_shapes():
     d = gen.gemm_softmax_inputs(M=8, N=16, D=4)
     assert d["k_bits"].shape == (16, 4)
     assert d["scale"] == float(np.float32(0.5))
+    d = gen.gemm_softmax_gemm_inputs(M=8, N=16, D=4, Dv=12)
+    assert d["q_bits"].shape == (8, 4) and d["k_bits"].shape == (16, 4) and d["v_bits"].shape == (16, 12)
+    assert np.array_equal(gen.bf16_bits_to_f32(d["v_bits"]), d["v"])
+    assert d["scale"] == float(np.float32(0.5))

@@ -43,6 +43,17 @@ def _gemm_softmax_scale_after(q, k, scale):
     return ops.scale(subgraphs.softmax_rows(p), scale)
 
 
+def _b2b_softmax_over_keys_axis0(q, k, v, scale):
+    s = ops.scale(ops.matmul(ops.f64(q), ops.transpose(ops.f64(k))), scale)
+    e = np.exp(s - s.max(axis=0)[None, :])
+    return ops.matmul(e / e.sum(axis=0)[None, :], ops.f64(v))
+
+
+def _b2b_unnormalized(q, k, v, scale):
+    s = ops.scale(ops.matmul(ops.f64(q), ops.transpose(ops.f64(k))), scale)
+    return ops.matmul(np.exp(s - s.max(axis=1)[:, None]), ops.f64(v))
+
+
 def _pow_row_broadcast(x, v, p=1.5):
     x = ops.f64(x)
     pv = ops.map_pow(ops.f64(v), p)
@@ -86,6 +97,8 @@ MUTANTS = {
     "gemm_ln_residual_after_norm": (subgraphs, "gemm_ln", _gemm_ln_residual_after_norm),
     "gemm_softmax_scale_after": (subgraphs, "gemm_softmax", _gemm_softmax_scale_after),
     "pow_row_broadcast": (subgraphs, "pow_bcast_add_softmax", _pow_row_broadcast),
+    "b2b_softmax_over_wrong_axis": (subgraphs, "gemm_softmax_gemm", _b2b_softmax_over_keys_axis0),
+    "b2b_unnormalized": (subgraphs, "gemm_softmax_gemm", _b2b_unnormalized),
 }
 
 
