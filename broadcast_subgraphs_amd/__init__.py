@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     CF_OK,
     CF_OP_GEMM_LN,
     CF_OP_GEMM_SOFTMAX,
+    CF_OP_GEMM_SOFTMAX_GEMM,
     CF_OP_STITCH_LAYERNORM,
     CF_OP_STITCH_POW_BCAST_ADD,
     CF_OP_STITCH_SOFTMAX,
@@ -22,6 +23,7 @@ from ._lib import (  # noqa: F401
     Workspace,
     cf_gemm_ln,
     cf_gemm_softmax,
+    cf_gemm_softmax_gemm,
     cf_graph_begin,
     cf_graph_destroy,
     cf_graph_end,

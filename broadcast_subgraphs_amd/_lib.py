@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libcf.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "cf.h")
 
 CF_OK, CF_EINVAL, CF_EUNSUPPORTED, CF_EALIGN, CF_EWORKSPACE, CF_EOCCUPANCY, CF_EHIP = range(7)
-CF_OP_STITCH_SOFTMAX, CF_OP_STITCH_LAYERNORM, CF_OP_STITCH_POW_BCAST_ADD, CF_OP_GEMM_LN, CF_OP_GEMM_SOFTMAX = 1, 2, 3, 4, 5
+(CF_OP_STITCH_SOFTMAX, CF_OP_STITCH_LAYERNORM, CF_OP_STITCH_POW_BCAST_ADD, CF_OP_GEMM_LN, CF_OP_GEMM_SOFTMAX,
+ CF_OP_GEMM_SOFTMAX_GEMM) = 1, 2, 3, 4, 5, 6
 
 _lib = None
 _lock = threading.Lock()
@@ -38,11 +39,13 @@ _SIGS = {
     "cf_stitch_pow_bcast_add": (_ST, [_P, _P, _F, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "cf_gemm_ln": (_ST, [_P, _P, _P, _P, _P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_gemm_softmax": (_ST, [_P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "cf_gemm_softmax_gemm": (_ST, [_P, _P, _P, _F, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_unfused_stitch_softmax": (_ST, [_P, _P, _I64, _I64, _P, _SZ, _P]),
     "cf_unfused_stitch_layernorm": (_ST, [_P, _P, _I64, _I64, _F, _P, _SZ, _P]),
     "cf_unfused_stitch_pow_bcast_add": (_ST, [_P, _P, _F, _P, _P, _I64, _I64, _P, _SZ, _P]),
     "cf_unfused_gemm_ln": (_ST, [_P, _P, _P, _P, _P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_unfused_gemm_softmax": (_ST, [_P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "cf_unfused_gemm_softmax_gemm": (_ST, [_P, _P, _P, _F, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_graph_begin": (_ST, [_P]),
     "cf_graph_end": (_ST, [_P, ctypes.POINTER(_P)]),
     "cf_graph_launch": (_ST, [_P, _P]),
@@ -247,6 +250,20 @@ def cf_gemm_softmax(Q, K, scale, S, ws=None, stream=None, unfused=False):
     p, n, w = _ws_args(CF_OP_GEMM_SOFTMAX, M, N, D, ws, Q.device, st, unfused)
     name = "cf_unfused_gemm_softmax" if unfused else "cf_gemm_softmax"
     _check(name, getattr(lib(), name)(_ptr(Q), _ptr(K), float(scale), _ptr(S), M, N, D, p, n, st))
+    return w
+
+
+def cf_gemm_softmax_gemm(Q, K, V, scale, O, ws=None, stream=None, unfused=False):
+    """Q [M,D], K [N,D], V [N,Dv], O [M,Dv]: bf16 tensors; O = softmax(scale * Q.K^T).V."""
+    torch = _torch()
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (O, "O")):
+        _need(t, torch.bfloat16, nm, 2)
+    M, D = Q.shape
+    N, Dv = V.shape
+    st = _stream(stream)
+    p, n, w = _ws_args(CF_OP_GEMM_SOFTMAX_GEMM, M, N, D, ws, Q.device, st, unfused)
+    name = "cf_unfused_gemm_softmax_gemm" if unfused else "cf_gemm_softmax_gemm"
+    _check(name, getattr(lib(), name)(_ptr(Q), _ptr(K), _ptr(V), float(scale), _ptr(O), M, N, D, Dv, p, n, st))
     return w
 
 

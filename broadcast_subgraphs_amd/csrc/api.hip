@@ -204,17 +204,24 @@ cf_status run_rows(const char* name, int op, const float* x, float* y, float* y_
 // Strip softmax: 128 x 128 tiles; each row block's column tiles are cut into
 // S strips of C consecutive tiles (no strip empty), one per resident
 // workgroup where the rows allow.
-static cf_status plan_gemm_strips(int64_t M, int64_t N, int64_t K, DevInfo* di, GemmPlan* p0, GemmPlan* pl) {
+// Strips (softmax, and the softmax between two GEMMs): 128-row units of
+// contiguous column tiles (128 columns; 64 for the back-to-back GEMM, whose
+// output accumulator needs the registers).
+static cf_status plan_gemm_strips(int epi, int64_t M, int64_t N, int64_t K, DevInfo* di, GemmPlan* p0,
+                                  GemmPlan* pl) {
   GemmPlan p = *p0;
+  p.algo = 2;
+  p.nn = 0;
   p.bm = 128;
-  p.bn = 128;
+  p.bn = epi == kEpiSoftmaxGemm ? 64 : 128;
   p.bk = K <= 32 ? 32 : (K <= 64 ? 64 : 128);  // reduction depth the kernel covers (zero-padded)
   int occ = 0;
-  if (gemm_occupancy(kEpiSoftmax, p, &occ) != hipSuccess || occ <= 0) return CF_EHIP;
+  if (gemm_occupancy(epi, p, &occ) != hipSuccess || occ <= 0) return CF_EHIP;
   p.occupancy = occ;
   const int64_t cap = (int64_t)occ * di->cus;
-  const int64_t tn = (N + 127) / 128, tm = (M + 127) / 128;
-  if (tm > kMaxJoins) return CF_EUNSUPPORTED;
+  const int64_t tn = (N + p.bn - 1) / p.bn, tm = (M + 127) / 128;
+  // one join word per row block (two for the back-to-back GEMM)
+  if ((epi == kEpiSoftmaxGemm ? 2 : 1) * tm > kMaxJoins) return CF_EUNSUPPORTED;
   int64_t S = std::max<int64_t>(1, std::min<int64_t>(tn, cap / tm));
   const int64_t C = (tn + S - 1) / S;
   S = (tn + C - 1) / C;
@@ -224,9 +231,27 @@ static cf_status plan_gemm_strips(int64_t M, int64_t N, int64_t K, DevInfo* di, 
   p.grid = (int)std::min<int64_t>(units, cap);
   p.rounds = (int)((units + p.grid - 1) / p.grid);
   if (p.rounds > kMaxRounds) return CF_EUNSUPPORTED;
+  // the back-to-back GEMM's strips wait for each other's partial outputs:
+  // with several strips per row block they must all be resident (one round)
+  if (epi == kEpiSoftmaxGemm && S > 1 && p.rounds > 1) return CF_EOCCUPANCY;
   p.leader = true;
   *pl = p;
   return CF_OK;
+}
+
+// Workspace of the back-to-back GEMM past the header and join words: strip
+// statistics (M x strips float2), row statistics (M float2), partial outputs
+// (M x strips x 128 floats).
+struct B2bLayout {
+  size_t stats = 0, finals = 0, opart = 0, total = 0;
+};
+static B2bLayout b2b_layout(const GemmPlan& p, int64_t M) {
+  B2bLayout L;
+  L.stats = kPartialsOff;
+  L.finals = align_up(L.stats + (size_t)M * p.strips * 8, 256);
+  L.opart = align_up(L.finals + (size_t)M * 8, 256);
+  L.total = align_up(L.opart + (size_t)M * p.strips * 128 * 4, 256);
+  return L;
 }
 
 // the k_gemm_ln2 configuration without pipelining (8 waves, 256 x 256 tiles)
@@ -242,7 +267,7 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   const int dalgo = (epi == kEpiSoftmax && K <= 128) ? 2 : 1;
   p.algo = epi == kEpiStoreF32 ? 0 : (int)env_int("CF_GEMM_ALGO", dalgo);
   if (p.algo == 2 && (epi != kEpiSoftmax || K > 128)) return CF_EUNSUPPORTED;
-  if (p.algo == 2) return plan_gemm_strips(M, N, K, di, &p, pl);
+  if (p.algo == 2) return plan_gemm_strips(kEpiSoftmax, M, N, K, di, &p, pl);
   // Default tiles (measured on MI355X): 128x128 at two workgroups per CU for
   // the plain GEMM and the overlapped epilogues, 64x512 for the round-based
   // epilogues.
@@ -308,10 +333,15 @@ size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N) {
 
 void record_gemm_plan(const char* name, int epi, const GemmPlan& p, int64_t M, int64_t N, int64_t K) {
   const bool ov = p.algo >= 1 && epi != kEpiStoreF32;
-  const char* kernel = p.algo == 2 ? "k_gemm_sm3" : (ov ? (epi == kEpiLN ? "k_gemm_ln2" : "k_gemm_sm2") : "k_gemm");
+  const char* kernel = epi == kEpiSoftmaxGemm
+                           ? "k_gemm_sm3<B2B>"
+                           : (p.algo == 2 ? "k_gemm_sm3" : (ov ? (epi == kEpiLN ? "k_gemm_ln2" : "k_gemm_sm2") : "k_gemm"));
   const bool single = ln_one_at_a_time(epi, p);
-  const char* sched =
-      p.algo == 2 ? "strips" : (ov ? (epi == kEpiLN ? (single ? "one-tile-at-a-time" : "pipelined") : "two-sweep") : "rounds");
+  const char* sched = epi == kEpiSoftmaxGemm
+                          ? "strips, back-to-back"
+                          : (p.algo == 2 ? "strips"
+                                         : (ov ? (epi == kEpiLN ? (single ? "one-tile-at-a-time" : "pipelined") : "two-sweep")
+                                               : "rounds"));
   char buf[512];
   snprintf(buf, sizeof buf,
            "{\"call\":\"%s\",\"M\":%lld,\"N\":%lld,\"K\":%lld,\"kernel\":\"%s\",\"tile\":[%d,%d,%d],"
@@ -388,6 +418,14 @@ size_t cf_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2) {
       if (plan_gemm(op == CF_OP_GEMM_LN ? kEpiLN : kEpiSoftmax, op == CF_OP_GEMM_LN, d0, d1, d2, &p) != CF_OK)
         return (size_t)-1;
       return gemm_ws_bytes(p, d0, d1);
+    }
+    case CF_OP_GEMM_SOFTMAX_GEMM: {
+      if (d2 <= 0 || d2 > 128) return (size_t)-1;
+      DevInfo* di = nullptr;
+      if (dev_info(&di) != CF_OK) return (size_t)-1;
+      GemmPlan p;
+      if (plan_gemm_strips(kEpiSoftmaxGemm, d0, d1, d2, di, &p, &p) != CF_OK) return (size_t)-1;
+      return b2b_layout(p, d0).total;
     }
   }
   return (size_t)-1;
@@ -466,6 +504,54 @@ cf_status cf_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scale, cf_bf
   return run_gemm("cf_gemm_softmax", kEpiSoftmax, false, a, ws, ws_bytes, stream);
 }
 
+static cf_status check_b2b_args(const cf_bf16* Q, const cf_bf16* K, const cf_bf16* V, float scale, cf_bf16* O,
+                                int64_t M, int64_t N, int64_t D, int64_t Dv) {
+  if (!Q || !K || !V || !O || !(scale == scale) || scale - scale != 0.0f) return CF_EINVAL;
+  cf_status s = check_gemm_shape(M, N, D);
+  if (s != CF_OK) return s;
+  if (Dv <= 0) return CF_EINVAL;
+  if (D > 128 || Dv > 128 || Dv % 8 != 0) return CF_EUNSUPPORTED;
+  // V and O through 32-bit buffer offsets (with a 128-key block of slack)
+  if ((N + 128) * Dv * 2 >= (int64_t)1 << 31 || M * Dv * 2 >= (int64_t)1 << 31) return CF_EUNSUPPORTED;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return CF_EALIGN;
+  const size_t ob = (size_t)M * Dv * 2;
+  if (overlap(O, ob, Q, (size_t)M * D * 2) || overlap(O, ob, K, (size_t)N * D * 2) ||
+      overlap(O, ob, V, (size_t)N * Dv * 2))
+    return CF_EINVAL;
+  return CF_OK;
+}
+
+cf_status cf_gemm_softmax_gemm(const cf_bf16* Q, const cf_bf16* K, const cf_bf16* V, float scale, cf_bf16* O,
+                               int64_t M, int64_t N, int64_t D, int64_t Dv, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  cf_status s = check_b2b_args(Q, K, V, scale, O, M, N, D, Dv);
+  if (s != CF_OK) return s;
+  DevInfo* di = nullptr;
+  s = dev_info(&di);
+  if (s != CF_OK) return s;
+  GemmPlan p;
+  s = plan_gemm_strips(kEpiSoftmaxGemm, M, N, D, di, &p, &p);
+  if (s != CF_OK) return s;
+  const B2bLayout L = b2b_layout(p, M);
+  if (!ws || ws_bytes < L.total) return CF_EWORKSPACE;
+  if (M * p.strips * 128 * 4 >= (int64_t)1 << 32) return CF_EUNSUPPORTED;
+  char* base = static_cast<char*>(ws);
+  GemmArgs a{};
+  a.A = Q; a.B = K; a.V = V; a.scale = scale; a.Y = O;
+  a.M = M; a.N = N; a.K = D; a.Dv = Dv;
+  a.err = reinterpret_cast<uint32_t*>(base);
+  a.joins = reinterpret_cast<uint64_t*>(base + kHeader);
+  a.partials = reinterpret_cast<float*>(base + L.stats);
+  a.finals = reinterpret_cast<float*>(base + L.finals);
+  a.opart = reinterpret_cast<float*>(base + L.opart);
+  a.tiles_n = (int)((N + p.bn - 1) / p.bn);
+  a.tiles_m = (int)((M + p.bm - 1) / p.bm);
+  a.agg_leader = 1;
+  a.strips = p.strips;
+  record_gemm_plan("cf_gemm_softmax_gemm", kEpiSoftmaxGemm, p, M, N, D);
+  return launch_gemm(kEpiSoftmaxGemm, p, a, stream) == hipSuccess ? CF_OK : CF_EHIP;
+}
+
 // ------------------------------------------------------------ unfused chains
 // Workspace: fp32 intermediates, placed after the header and the join words
 // (which they never touch, so one zero-filled workspace serves fused and
@@ -485,6 +571,10 @@ size_t cf_unfused_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2) {
     case CF_OP_STITCH_POW_BCAST_ADD: n = 3 * vec + 3 * full; break;
     case CF_OP_GEMM_LN: n = d2 > 0 ? 4 * vec + 3 * full : (size_t)-1; break;
     case CF_OP_GEMM_SOFTMAX: n = d2 > 0 ? 2 * vec + 3 * full : (size_t)-1; break;
+    case CF_OP_GEMM_SOFTMAX_GEMM:  // + S bf16 [M x N] + the second product fp32 [M x (Dv <= 128)]
+      n = d2 > 0 ? 2 * vec + 3 * full + align_up((size_t)d0 * d1 * 2, 256) + align_up((size_t)d0 * 128 * 4, 256)
+                 : (size_t)-1;
+      break;
   }
   return n == (size_t)-1 ? n : kPartialsOff + n;
 }
@@ -639,6 +729,35 @@ cf_status cf_unfused_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scal
   CF_TRY(u_bcast_col(B0, sv, B1, M, N, 1, stream));   // y = e / s
   CF_TRY(u_cast_bf16(B1, S, M * N, stream));
   g_last_plan = "{\"call\":\"cf_unfused_gemm_softmax\",\"kernels\":8}";
+  return CF_OK;
+}
+
+cf_status cf_unfused_gemm_softmax_gemm(const cf_bf16* Q, const cf_bf16* K, const cf_bf16* V, float scale,
+                                       cf_bf16* O, int64_t M, int64_t N, int64_t D, int64_t Dv, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  cf_status s = check_b2b_args(Q, K, V, scale, O, M, N, D, Dv);
+  if (s != CF_OK) return s;
+  if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_GEMM_SOFTMAX_GEMM, M, N, D)) return CF_EWORKSPACE;
+  const size_t vec = align_up((size_t)M * 4, 256), full = align_up((size_t)M * N * 4, 256);
+  char* w = unfused_base(ws);
+  cf_bf16* S = reinterpret_cast<cf_bf16*>(w + 2 * vec + 3 * full);
+  float* Z = reinterpret_cast<float*>(w + 2 * vec + 3 * full + align_up((size_t)M * N * 2, 256));
+  // S = softmax(scale * Q.K^T) through the 8-kernel chain (its own buffers
+  // come first in the same workspace), then O = S.V and the cast
+  s = cf_unfused_gemm_softmax(Q, K, scale, S, M, N, D, ws, ws_bytes, stream);
+  if (s != CF_OK) return s;
+  s = check_gemm_shape(M, Dv, N);
+  if (s != CF_OK) return s;
+  GemmPlan p;
+  s = plan_gemm(kEpiStoreF32, true, M, Dv, N, &p);
+  if (s != CF_OK) return s;
+  GemmArgs a{};
+  a.A = S; a.B = V; a.Z = Z; a.M = M; a.N = Dv; a.K = N;
+  a.tiles_n = (int)((Dv + p.bn - 1) / p.bn);
+  a.tiles_m = (int)((M + p.bm - 1) / p.bm);
+  CF_TRY(launch_gemm(kEpiStoreF32, p, a, stream));
+  CF_TRY(u_cast_bf16(Z, O, M * Dv, stream));
+  g_last_plan = "{\"call\":\"cf_unfused_gemm_softmax_gemm\",\"kernels\":10}";
   return CF_OK;
 }
 

@@ -1141,11 +1141,26 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 //   the strip is computed again, normalised and stored as bf16.
 // The strip is recomputed rather than held across the wait: with a short
 // reduction dimension the second pass costs less than the exchange it hides.
+//
+// B2B: the softmax tile is not stored but multiplied by V, back to back
+// ([ComFuse] "B2BGEMM": S = F(P) per tile, eq. 3; partial products over the
+// contraction dimension, eq. 4; their sum at commit, eq. 5).  In sweep 2 the
+// ring alternates the tile's K block (first MatMul) and V block (second
+// MatMul), one shared buffer for both weights as the page describes.  The
+// normalised tile goes from the accumulator straight into bf16 operand
+// fragments: a lane holds 16 consecutive keys of its row, so the second
+// MatMul's k-order is permuted to match (k-slots 0-7 take keys 0-7 of lanes
+// 0-31 and keys 16-23 of lanes 32-63, and so on), and V's transposed
+// fragment reads use the same permutation.  The strip's partial output
+// (128 rows x 128 columns, fp32) goes to the workspace; after the row block's
+// second join every strip sums its share of the rows over the strips in
+// strip order and stores O.
 constexpr int kSmBM = 128, kSmBN = 128, kSmBK = 128;
 
-template <int KS, int MINB>
+template <int KS, int MINB, bool B2B = false>
 __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
-  constexpr int BM = kSmBM, BN = kSmBN, BK = kSmBK;
+  // B2B: 64-key tiles (the output accumulator needs the registers)
+  constexpr int BM = kSmBM, BN = B2B ? 64 : kSmBN, BK = kSmBK;
   constexpr int CB = BN / 32;  // KS: 16-deep k-steps covering the reduction dimension
   constexpr int SLOT = BN * BK * 2;  // one K tile: BN keys x BK dims
   constexpr int LB = SLOT / 4096;    // 16-byte direct loads per lane per tile
@@ -1153,6 +1168,8 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
   __shared__ __align__(16) char s1[SLOT];
   __shared__ uint32_t gens[kMaxRounds];
   __shared__ int last;
+  __shared__ uint32_t gen2;
+  __shared__ __align__(16) char sqb[B2B ? kSmBM * kSmBK * 2 : 16];  // B2B sweep 2: the strip's Q rows
 
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
@@ -1175,18 +1192,23 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
   // direct loads of K tile j (keys j*BN .., all dims) into a slot.  The
   // lane's byte offset within a tile is fixed (kOOB past the reduction
   // dimension); keys past N fall outside the buffer's range and read zero.
-  uint32_t koff[LB];
+  // Load q puts key 16q + kl (kl = 4w + lane/16) at chunk lane % 16; the
+  // sigma swizzle of that row depends on q only through q & 1, so two
+  // per-lane offsets serve every load (plus 16q keys, uniform).
+  static_assert(BK == 128, "16 keys per 4 KB load, 16 chunks per row");
+  uint32_t koff[2];
+  {
+    const int kl = 4 * w + (lane >> 4), pc = lane & 15;
 #pragma unroll
-  for (int q = 0; q < LB; ++q) {
-    const int o = (q * 4 + w) * 1024 + lane * 16;
-    const int key = o / (BK * 2), pc = (o % (BK * 2)) / 16;
-    const int gk = 8 * swz_sigma<BK>(key, pc);
-    koff[q] = gk < D ? (uint32_t)(key * D + gk) * 2u : kOOB;
+    for (int par = 0; par < 2; ++par) {
+      const int gk = 8 * swz_sigma<BK>(kl + 16 * par, pc);
+      koff[par] = gk < D ? (uint32_t)(kl * D + gk) * 2u : kOOB;
+    }
   }
   auto load_tile = [&](char* slot, int j) {
     const uint32_t base = (uint32_t)(j * BN) * (uint32_t)D * 2u;
 #pragma unroll
-    for (int q = 0; q < LB; ++q) g2l16(rB, slot + (q * 4 + w) * 1024, koff[q] + base);
+    for (int q = 0; q < LB; ++q) g2l16(rB, slot + (q * 4 + w) * 1024, koff[q & 1] + base + (uint32_t)(32 * q * D));
   };
   // strip u's first tile, and the tile that follows tile j of strip u
   auto strip_first = [&](int u) { return (u % S) * C; };
@@ -1360,31 +1382,252 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
     }
   }
 
-  // ------------------------------------------------ sweep 2: normalise, store
-  i = 0;
-  for (int u = g; u < units; u += G, ++i) {
-    const int rowblk = u / S, m0 = rowblk * BM;
-    bf16x8_t qf[KS];
-    load_q(m0, qf);
-    if (t == 0) wait_generation(a.joins + rowblk, gens[i], a.err);
-    __syncthreads();
-    const int row = m0 + w * 32 + l32;
-    const float2 fs = row < M ? ld_dev2(F + row) : make_float2(0.0f, 0.0f);
-    for (int j = strip_first(u); j < strip_end(u); ++j) {
-      f32x16 acc[CB];
-      step(2, u, j, qf, acc);
+  if constexpr (!B2B) {
+    // ------------------------------------------------ sweep 2: normalise, store
+    i = 0;
+    for (int u = g; u < units; u += G, ++i) {
+      const int rowblk = u / S, m0 = rowblk * BM;
+      bf16x8_t qf[KS];
+      load_q(m0, qf);
+      if (t == 0) wait_generation(a.joins + rowblk, gens[i], a.err);
+      __syncthreads();
+      const int row = m0 + w * 32 + l32;
+      const float2 fs = row < M ? ld_dev2(F + row) : make_float2(0.0f, 0.0f);
+      for (int j = strip_first(u); j < strip_end(u); ++j) {
+        f32x16 acc[CB];
+        step(2, u, j, qf, acc);
+  #pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+  #pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int col = j * BN + cb * 32 + 16 * hl + 8 * h;
+            float o[8];
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * h + e], sc, -fs.x)) * fs.y;
+            const u32x4 pk = {cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]), cvt_bf16x2(o[4], o[5]),
+                              cvt_bf16x2(o[6], o[7])};
+            bst16(rY, (row < M && col < N) ? (uint32_t)(row * N + col) * 2u : kOOB, pk);
+          }
+      }
+    }
+  } else {
+    // ---------------------------------------------- sweep 2: S.V, commit O
+    constexpr int DV = 128, NB = DV / 32;  // output columns held (zero past Dv)
+    static_assert(BN * DV * 2 == SLOT, "a V block fills one ring slot");
+    const int Dv = (int)a.Dv;
+    const __amdgpu_buffer_rsrc_t rV = rsrc(a.V, (uint32_t)(a.N * a.Dv * 2));
+    const __amdgpu_buffer_rsrc_t rOp = rsrc(a.opart, (uint32_t)(a.M * S * DV * 4));
+    const __amdgpu_buffer_rsrc_t rO = rsrc(a.Y, (uint32_t)(a.M * a.Dv * 2));
+    // direct loads of V block j (keys j*BN .., all columns): rows of 256
+    // bytes, 64-byte segments XORed by key % 4 for the transposed reads
+    // (load q: key 16q + 4w + lane/16, whose XOR term is the same for every q)
+    uint32_t voff;
+    {
+      const int kl = 4 * w + (lane >> 4), col = (((lane & 15) * 16) ^ nn_mask(kl)) / 2;
+      voff = col < Dv ? (uint32_t)(kl * Dv + col) * 2u : kOOB;
+    }
+    auto load_v = [&](char* slot, int j) {
+      const uint32_t base = (uint32_t)(j * BN) * (uint32_t)Dv * 2u;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+      for (int q = 0; q < LB; ++q) g2l16(rV, slot + (q * 4 + w) * 1024, voff + base + (uint32_t)(32 * q * Dv));
+    };
+    // V fragment for key block cb, half q, column block nb: 8 consecutive
+    // (permuted) keys of one column, gathered by two transposed reads.  The
+    // lane reads key k = cb*32 + 16*(lane/32) + 8q + 4hh + e and column
+    // n = nb*32 + c (e, c from the lane): k % 4 = e, so the segment XOR is
+    // (nb ^ e) * 64 and the byte offset splits into a per-lane base per nb
+    // plus a constant
+    uint32_t vb[NB];
+    {
+      const int G = lane >> 4, L = lane & 15, e = L >> 2, cc = L & 3;
+      const int clow = 2 * (16 * (cc & 1) + 8 * (G & 1) + 4 * (cc >> 1));  // < 64
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int col = j * BN + cb * 32 + 16 * hl + 8 * h;
-          float o[8];
+      for (int nb = 0; nb < NB; ++nb) vb[nb] = (uint32_t)((16 * (G >> 1) + e) * (DV * 2) + ((nb ^ e) << 6) + clow);
+    }
+    auto vfrag = [&](const char* slot, int cb, int q, int nb) -> bf16x8_t {
+      bf16x4_t h[2];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * h + e], sc, -fs.x)) * fs.y;
-          const u32x4 pk = {cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]), cvt_bf16x2(o[4], o[5]),
-                            cvt_bf16x2(o[6], o[7])};
-          bst16(rY, (row < M && col < N) ? (uint32_t)(row * N + col) * 2u : kOOB, pk);
+      for (int hh = 0; hh < 2; ++hh)
+        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4_t*)(slot + vb[nb] + (cb * 32 + 8 * q + 4 * hh) * (DV * 2)));
+      return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // S = 2^(P*sc - M) / L of tile j (zero on keys past N) into bf16
+    // fragments, one 32-key block at a time, each followed by its MFMAs
+    auto mma_sv = [&](const char* slot, const f32x16 (&acc)[CB], float2 fs, int j, f32x16 (&oacc)[NB]) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        bf16x8_t sf[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const bool ok = j * BN + cb * 32 + 16 * hl + 8 * q < N;
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            y[e] = ok ? __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * q + e], sc, -fs.x)) * fs.y : 0.0f;
+          const u32x4 pk = {cvt_bf16x2(y[0], y[1]), cvt_bf16x2(y[2], y[3]), cvt_bf16x2(y[4], y[5]),
+                            cvt_bf16x2(y[6], y[7])};
+          sf[q] = __builtin_bit_cast(bf16x8_t, pk);
         }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          bf16x8_t vf[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) vf[nb] = vfrag(slot, cb, q, nb);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[nb], sf[q], oacc[nb], 0, 0, 0);
+        }
+      }
+    };
+    // The strip's Q rows sit in LDS for this sweep (registers go to the
+    // output accumulator): row r's 16-byte chunk c at r*256 + 16*(c ^ r%16),
+    // so 16 lanes reading 16 rows at one chunk hit 16 distinct bank slots.
+    static_assert(BK == 128, "one 256-byte LDS row per Q row");
+    auto load_q_lds = [&](int m0) {
+#pragma unroll
+      for (int q = 0; q < BM * BK * 2 / 4096; ++q) {
+        const int o = (q * 4 + w) * 1024 + lane * 16;
+        const int r = o / 256, c = ((o % 256) / 16) ^ (r & 15);
+        g2l16(rA, sqb + (q * 4 + w) * 1024, (m0 + r < M && 8 * c < D) ? (uint32_t)((m0 + r) * D + 8 * c) * 2u : kOOB);
+      }
+    };
+    // first MatMul of one tile with Q from LDS: step ks+1's K and Q fragments
+    // are read before step ks's MFMAs issue
+    auto mma_tile_q = [&](const char* slot, f32x16 (&acc)[CB]) {
+      const int qr = w * 32 + l32;
+      const char* qrow = sqb + qr * 256;
+      bf16x8_t kf[2][CB], qv[2];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int key = cb * 32 + sigma(l32);
+        kf[0][cb] = *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz_sigma<BK>(key, hl));
+      }
+      qv[0] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * (hl ^ (qr & 15)));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int cur = ks & 1;
+        if (ks + 1 < KS) {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            const int key = cb * 32 + sigma(l32);
+            kf[cur ^ 1][cb] =
+                *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz_sigma<BK>(key, 2 * (ks + 1) + hl));
+          }
+          qv[cur ^ 1] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ((2 * (ks + 1) + hl) ^ (qr & 15)));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][cb], qv[cur], acc[cb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    i = 0;
+    for (int u = g; u < units; u += G, ++i) {
+      const int rowblk = u / S, m0 = rowblk * BM, su = u % S;
+      if (t == 0) wait_generation(a.joins + rowblk, gens[i], a.err);
+      __syncthreads();  // also: every wave is done with the previous strip's Q
+      load_q_lds(m0);
+      const int row = m0 + w * 32 + l32;
+      const float2 fs = row < M ? ld_dev2(F + row) : make_float2(0.0f, 0.0f);
+      f32x16 oacc[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.0f;
+      for (int j = strip_first(u); j < strip_end(u); ++j) {
+        // K block j is in stage st: prefetch V block j, first MatMul
+        f32x16 acc[CB];
+        wait_vm<0>();
+        __syncthreads();
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
+        if (st & 1) {
+          load_v(s0, j);
+          mma_tile_q(s1, acc);
+        } else {
+          load_v(s1, j);
+          mma_tile_q(s0, acc);
+        }
+        ++st;
+        // V block j is in stage st: prefetch the next K block, normalise and
+        // run the second MatMul
+        wait_vm<0>();
+        __syncthreads();
+        int nj = 0;
+        const bool more = next_tile(2, u, j, &nj);
+        if (st & 1) {
+          if (more) load_tile(s0, nj);
+          mma_sv(s1, acc, fs, j, oacc);
+        } else {
+          if (more) load_tile(s1, nj);
+          mma_sv(s0, acc, fs, j, oacc);
+        }
+        ++st;
+      }
+      // this lane's output row, columns nb*32 + 16*hl + [0, 16)
+      if (S == 1) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int col = nb * 32 + 16 * hl + 8 * h;
+            const u32x4 pk = {cvt_bf16x2(oacc[nb][8 * h], oacc[nb][8 * h + 1]),
+                              cvt_bf16x2(oacc[nb][8 * h + 2], oacc[nb][8 * h + 3]),
+                              cvt_bf16x2(oacc[nb][8 * h + 4], oacc[nb][8 * h + 5]),
+                              cvt_bf16x2(oacc[nb][8 * h + 6], oacc[nb][8 * h + 7])};
+            bst16(rO, (row < M && col < Dv) ? (uint32_t)(row * Dv + col) * 2u : kOOB, pk);
+          }
+        continue;
+      }
+      // publish the strip's partial output, join the row block's strips
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const int col = nb * 32 + 16 * hl + 4 * c4;
+          const u32x4 v = {__float_as_uint(oacc[nb][4 * c4]), __float_as_uint(oacc[nb][4 * c4 + 1]),
+                           __float_as_uint(oacc[nb][4 * c4 + 2]), __float_as_uint(oacc[nb][4 * c4 + 3])};
+          bst16_dev(rOp, row < M ? (uint32_t)(((row * S + su) * DV + col) * 4) : kOOB, v);
+        }
+      wait_stores();
+      __syncthreads();
+      uint64_t* jw2 = a.joins + a.tiles_m + rowblk;
+      if (t == 0) {
+        const uint64_t old = __hip_atomic_fetch_add(jw2, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)old == (uint32_t)(S - 1))
+          __hip_atomic_fetch_add(jw2, (1ull << 32) - (uint64_t)S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gen2 = (uint32_t)(old >> 32);
+      }
+      __syncthreads();
+      if (t == 0) wait_generation(jw2, gen2, a.err);
+      __syncthreads();
+      // strip su sums rows [su*R, su*R + R) of the block over the strips, in
+      // strip order, 8 columns per item
+      const int R = (BM + S - 1) / S;
+      for (int it = t; it < R * (DV / 8); it += kThreads) {
+        const int r = su * R + it / (DV / 8), c8 = (it % (DV / 8)) * 8;
+        const int orow = m0 + r;
+        if (r >= BM || orow >= M || c8 >= Dv) continue;
+        float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        for (int sk = 0; sk < S; sk += 8) {
+          u32x4 v[8][2];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              v[k][h] = bld16_dev(rOp, sk + k < S ? (uint32_t)(((orow * S + sk + k) * DV + c8 + 4 * h) * 4) : kOOB);
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (sk + k < S)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) o[e] += __uint_as_float(v[k][e >> 2][e & 3]);
+        }
+        const u32x4 pk = {cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]), cvt_bf16x2(o[4], o[5]),
+                          cvt_bf16x2(o[6], o[7])};
+        bst16(rO, (uint32_t)(orow * Dv + c8) * 2u, pk);
+      }
     }
   }
 }
@@ -1786,6 +2029,13 @@ static hipError_t gemm_dispatch(int epi, const GemmPlan& pl, const GemmArgs& a, 
   if (epi == kEpiLN) {
     if (!pl.nn) return hipErrorInvalidConfiguration;
     return pl.algo == 1 ? launch_gemm_overlap<kEpiLN>(pl, a, st, occ) : launch_gemm_t<kEpiLN, true>(pl, a, st, occ);
+  }
+  if (epi == kEpiSoftmaxGemm) {
+    if (pl.nn || pl.algo != 2) return hipErrorInvalidConfiguration;
+    auto kfn = pl.bk <= 32 ? k_gemm_sm3<2, 2, true> : (pl.bk <= 64 ? k_gemm_sm3<4, 2, true> : k_gemm_sm3<8, 2, true>);
+    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kfn, kThreads, 0);
+    hipLaunchKernelGGL(kfn, dim3(pl.grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
   }
   if (epi == kEpiSoftmax) {
     if (pl.nn) return hipErrorInvalidConfiguration;

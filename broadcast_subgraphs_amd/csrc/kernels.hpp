@@ -42,7 +42,7 @@ hipError_t launch_rows(int op, const RowPlan& pl, const RowArgs& a, hipStream_t 
 hipError_t rows_split_occupancy(int op, const RowPlan& pl, int* per_cu);
 
 // ----------------------------------------------------------------- GEMM
-enum GemmEpi { kEpiStoreF32 = 0, kEpiLN = 1, kEpiSoftmax = 2 };
+enum GemmEpi { kEpiStoreF32 = 0, kEpiLN = 1, kEpiSoftmax = 2, kEpiSoftmaxGemm = 3 };
 
 struct GemmArgs {
   const uint16_t* A;   // [M x K] bf16 (GEMM left operand; Q for softmax)
@@ -65,6 +65,9 @@ struct GemmArgs {
   int agg_leader;      // 0: every member reads all partials; 1: last arriver combines
   int strips;          // strip softmax: strips per row block
   int sw_a, sw_b;      // LN: per-round tile blocks per XCD (sw_a row x sw_b column splits; 0 = linear)
+  const uint16_t* V;   // softmax-GEMM: second operand [N x Dv] bf16 (Y is then O [M x Dv])
+  int64_t Dv;
+  float* opart;        // softmax-GEMM: per-strip partial outputs, M * strips * 128 floats
 };
 
 struct GemmPlan {

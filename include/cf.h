@@ -65,7 +65,8 @@ enum {
   CF_OP_STITCH_LAYERNORM = 2,     /* d0 = rows, d1 = cols            */
   CF_OP_STITCH_POW_BCAST_ADD = 3, /* d0 = rows, d1 = cols            */
   CF_OP_GEMM_LN = 4,              /* d0 = M, d1 = N, d2 = K          */
-  CF_OP_GEMM_SOFTMAX = 5          /* d0 = M, d1 = N, d2 = D          */
+  CF_OP_GEMM_SOFTMAX = 5,         /* d0 = M, d1 = N, d2 = D          */
+  CF_OP_GEMM_SOFTMAX_GEMM = 6     /* d0 = M, d1 = N, d2 = D (any Dv <= 128) */
 };
 
 /* Workspace bytes the fused call needs for this shape on the current device
@@ -142,6 +143,20 @@ cf_status cf_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scale, cf_bf
                           int64_t M, int64_t N, int64_t D, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* O = softmax(scale * Q.K^T) . V: two MatMuls back to back, the row softmax
+ * between them, S never written.  Q [M x D], K [N x D] (both D contiguous),
+ * V [N x Dv] (Dv contiguous), O [M x Dv]; scale finite; D <= 128,
+ * 8 <= Dv <= 128 with Dv % 8 == 0.  The S tile feeds the second MatMul from
+ * registers; partial outputs over the contraction dimension N are summed in
+ * a fixed order before the commit, so results are deterministic.
+ * [ComFuse] B2BGEMM (eq. 3: S_tile = F(P_tile); eq. 4: partial products
+ * S_tile.W2_tile over the contraction dimension; eq. 5: their sum at the
+ * commit; one circular buffer shared by the W1 and W2 tiles), with F the
+ * cross-tile softmax of the Stage-Stream Execution Model. */
+cf_status cf_gemm_softmax_gemm(const cf_bf16* Q, const cf_bf16* K, const cf_bf16* V, float scale,
+                               cf_bf16* O, int64_t M, int64_t N, int64_t D, int64_t Dv,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Unfused baselines: the same subgraphs as one kernel per operator, with     */
 /* fp32 intermediates in the workspace (in HBM) and broadcasts folded into    */
@@ -169,6 +184,11 @@ cf_status cf_unfused_gemm_ln(const cf_bf16* A, const cf_bf16* W, const float* bi
 cf_status cf_unfused_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scale, cf_bf16* S,
                                   int64_t M, int64_t N, int64_t D, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
+/* The softmax chain above writes S (bf16, [M x N]) to the workspace; a plain
+ * GEMM S.V (fp32 out) and a cast then produce O. */
+cf_status cf_unfused_gemm_softmax_gemm(const cf_bf16* Q, const cf_bf16* K, const cf_bf16* V,
+                                       float scale, cf_bf16* O, int64_t M, int64_t N, int64_t D,
+                                       int64_t Dv, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Graph replay of a captured sequence of calls (used to time the unfused     */

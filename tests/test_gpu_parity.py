@@ -214,6 +214,96 @@ def test_gemm_softmax_zero_q_is_exact():
     assert np.array_equal(g, np.full((M, N), 2.0 ** -13, np.float32))
 
 
+# Back-to-back GEMM with the softmax between: ragged tails on every axis, a
+# single strip per row (one 64-key tile), several strips per row block, and
+# the full 8192 x 8192 x 128 x 128 workload.
+B2B_SHAPES = [(300, 264, 72, 40), (512, 1024, 128, 128), (17, 8, 8, 8), (130, 40, 32, 16),
+              (1000, 2056, 128, 64), (8192, 8192, 128, 128)]
+
+
+def _b2b_run(d, M, N, D, Dv, unfused=False, ws=None):
+    O = torch.full((M, Dv), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = cf.cf_gemm_softmax_gemm(dbf16(d["q_bits"]), dbf16(d["k_bits"]), dbf16(d["v_bits"]), d["scale"], O,
+                                 ws=ws, unfused=unfused)
+    if not unfused:
+        check_ws(ws)
+    return host(O)
+
+
+@pytest.mark.parametrize("M,N,D,Dv", B2B_SHAPES)
+def test_gemm_softmax_gemm(M, N, D, Dv):
+    d = gen.gemm_softmax_gemm_inputs(seed=6, M=M, N=N, D=D, Dv=Dv)
+    g = _b2b_run(d, M, N, D, Dv)
+    o = oracle.gemm_softmax_gemm(d["q"], d["k"], d["v"], d["scale"])
+    err = rownorm_err(g, o)
+    assert err <= TOL_BF16, (err, cf.last_plan())
+
+
+def test_gemm_softmax_gemm_plan_uses_strips():
+    """The 8192-row workload runs several strips per row block in one round, and
+    a 40-key row runs one strip (the direct commit)."""
+    d = gen.gemm_softmax_gemm_inputs(seed=6, M=1024, N=8192, D=128, Dv=128)
+    _b2b_run(d, 1024, 8192, 128, 128)
+    p = json.loads(cf.last_plan())
+    assert p["kernel"] == "k_gemm_sm3<B2B>" and p["row_group"] > 1 and p["rounds"] == 1, p
+    d = gen.gemm_softmax_gemm_inputs(seed=6, M=130, N=40, D=32, Dv=16)
+    _b2b_run(d, 130, 40, 32, 16)
+    assert json.loads(cf.last_plan())["row_group"] == 1, cf.last_plan()
+
+
+def test_gemm_softmax_gemm_unfused():
+    M, N, D, Dv = 512, 1024, 128, 128
+    d = gen.gemm_softmax_gemm_inputs(seed=6, M=M, N=N, D=D, Dv=Dv)
+    g = _b2b_run(d, M, N, D, Dv, unfused=True)
+    o = oracle.gemm_softmax_gemm(d["q"], d["k"], d["v"], d["scale"])
+    assert rownorm_err(g, o) <= TOL_BF16
+
+
+def test_gemm_softmax_gemm_negative_scale_and_zero_q():
+    M, N, D, Dv = 256, 1000, 64, 96
+    d = gen.gemm_softmax_gemm_inputs(seed=7, M=M, N=N, D=D, Dv=Dv)
+    d["scale"] = -abs(d["scale"])
+    o = oracle.gemm_softmax_gemm(d["q"], d["k"], d["v"], d["scale"])
+    assert rownorm_err(_b2b_run(d, M, N, D, Dv), o) <= TOL_BF16, cf.last_plan()
+    d["q_bits"] = np.zeros_like(d["q_bits"])
+    d["q"] = np.zeros_like(d["q"])
+    o = oracle.gemm_softmax_gemm(d["q"], d["k"], d["v"], d["scale"])
+    assert rownorm_err(_b2b_run(d, M, N, D, Dv), o) <= TOL_BF16, cf.last_plan()
+
+
+def test_gemm_softmax_gemm_deterministic_on_one_workspace():
+    """Fixed strip order in the partial-output sum: repeated calls (one workspace)
+    give identical bits, also after a plain softmax call used the same join words."""
+    M, N, D, Dv = 1024, 8192, 128, 128
+    d = gen.gemm_softmax_gemm_inputs(seed=8, M=M, N=N, D=D, Dv=Dv)
+    need = max(cf.cf_workspace_bytes(cf.CF_OP_GEMM_SOFTMAX_GEMM, M, N, D),
+               cf.cf_workspace_bytes(cf.CF_OP_GEMM_SOFTMAX, M, N, D))
+    ws = cf.Workspace(need)
+    a = _b2b_run(d, M, N, D, Dv, ws=ws)
+    S = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    cf.cf_gemm_softmax(dbf16(d["q_bits"]), dbf16(d["k_bits"]), d["scale"], S, ws=ws)
+    b = _b2b_run(d, M, N, D, Dv, ws=ws)
+    assert np.array_equal(a, b)
+
+
+def test_gemm_softmax_gemm_rejects():
+    q = torch.zeros((64, 32), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((64, 32), dtype=torch.bfloat16, device="cuda")
+    v12 = torch.zeros((64, 12), dtype=torch.bfloat16, device="cuda")
+    o12 = torch.zeros((64, 12), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(cf.CFError) as e:
+        cf.cf_gemm_softmax_gemm(q, k, v12, 0.1, o12)
+    assert e.value.status == cf.CF_EUNSUPPORTED
+    v = torch.zeros((64, 16), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(cf.CFError) as e:
+        cf.cf_gemm_softmax_gemm(q, k, v, 0.1, v[:, :16])  # O aliases V
+    assert e.value.status == cf.CF_EINVAL
+    q136 = torch.zeros((64, 136), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(cf.CFError) as e:
+        cf.cf_gemm_softmax_gemm(q136, q136, v, 0.1, torch.zeros((64, 16), dtype=torch.bfloat16, device="cuda"))
+    assert e.value.status == cf.CF_EUNSUPPORTED
+
+
 # Every GEMM epilogue schedule the planner can pick (forced through its
 # CF_GEMM_ALGO override): 0 one join per round, 1 joins overlapped with
 # MainLoops, 2 softmax by strips.
