@@ -5,7 +5,9 @@ path) on its workload, inputs resident in HBM.  Each call is bracketed by HIP
 events on the stream it runs on, with a 512 MiB cache-evicting read sweep
 before it (outside the events) so every call reads its inputs from HBM.  The headline
 line reports the tall-skinny LayerNorm workload (750000 x 32 fp32); the other
-four workloads are reported under "per_config" in the same line.
+four workloads are reported under "per_config" in the same line, and so is the
+back-to-back GEMM with the softmax between (8192 x 8192 x 128 x 128), which is
+timed per kernel but is not part of the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
                        [--no-unfused] [--no-cpu] [--calibrate-copy]
@@ -42,6 +44,7 @@ KERNEL_SOURCES = {
     "pow_bcast_add_softmax_64x30000": ("stitch.hip", "dev.hpp"),
     "gemm_ln_4096x4096x1024": ("gemm.hip", "dev.hpp"),
     "gemm_softmax_8192x8192x128": ("gemm.hip", "dev.hpp"),
+    "gemm_softmax_gemm_8192x8192x128x128": ("gemm.hip", "dev.hpp"),
 }
 
 
@@ -131,9 +134,20 @@ class Workload:
             scale = d["scale"]
             call = lambda b, ws, u: cf.cf_gemm_softmax(b["Q"], b["K"], scale, b["S"], ws=ws, unfused=u)
             self.op, self.dims = cf.CF_OP_GEMM_SOFTMAX, (M, N, D)
+        elif name == "gemm_softmax_gemm_8192x8192x128x128":
+            M, N, D, Dv = 8192, 8192, 128, 128
+            d = gen.gemm_softmax_gemm_inputs(seed=6)
+            self.inp = d
+            bufs = {"Q": dbf(d["q_bits"]), "K": dbf(d["k_bits"]), "V": dbf(d["v_bits"]),
+                    "Y": torch.empty(M, Dv, dtype=torch.bfloat16, device=dev)}
+            self.bytes = 2 * (M * D + N * D + N * Dv + M * Dv)
+            self.flops = 2 * M * N * D + 2 * M * N * Dv
+            scale = d["scale"]
+            call = lambda b, ws, u: cf.cf_gemm_softmax_gemm(b["Q"], b["K"], b["V"], scale, b["Y"], ws=ws, unfused=u)
+            self.op, self.dims = cf.CF_OP_GEMM_SOFTMAX_GEMM, (M, N, D)
         else:
             raise ValueError(name)
-        self.bound = "mfma" if name == "gemm_ln_4096x4096x1024" else "hbm"
+        self.bound = "mfma" if name in ("gemm_ln_4096x4096x1024", "gemm_softmax_gemm_8192x8192x128x128") else "hbm"
         nb = cf.cf_workspace_bytes(self.op, *self.dims)
         self.ws = cf.Workspace(nb) if nb else None
         self.uws = None
@@ -154,11 +168,15 @@ class Workload:
             return oracle.pow_bcast_add_softmax(d["x"], d["v"], 1.5)
         if self.name == "gemm_ln_4096x4096x1024":
             return oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"], d["beta"], 1e-5)
+        if self.name == "gemm_softmax_gemm_8192x8192x128x128":
+            return oracle.gemm_softmax_gemm(d["q"], d["k"], d["v"], d["scale"])
         return oracle.gemm_softmax(d["q"], d["k"], d["scale"])
 
 
 WORKLOAD_NAMES = ["softmax_256x1024", "layernorm_750000x32", "pow_bcast_add_softmax_64x30000",
                   "gemm_ln_4096x4096x1024", "gemm_softmax_8192x8192x128"]
+# measured per kernel (and unfused) but outside the step
+EXTRA_NAMES = ["gemm_softmax_gemm_8192x8192x128x128"]
 
 
 def main():
@@ -201,8 +219,9 @@ def main():
                           "launches": args.warmup + args.steps}))
         return
 
-    names = [args.only] if args.only else WORKLOAD_NAMES
-    wl = [Workload(n, torch, cf, gen) for n in names]
+    names = [args.only] if args.only else WORKLOAD_NAMES + EXTRA_NAMES
+    wl_all = [Workload(n, torch, cf, gen) for n in names]
+    wl = [w for w in wl_all if w.name not in EXTRA_NAMES or args.only]  # the step
     torch.cuda.synchronize()
 
     def run_step(w, fn, ws, ev=None):
@@ -239,7 +258,7 @@ def main():
     # one pair of HIP events on the launch stream, five times
     per = {}
     cs = torch.cuda.Stream()
-    for w in wl:
+    for w in wl_all:
         with torch.cuda.stream(cs):
             cs.synchronize()
             cf.cf_graph_begin()
@@ -268,20 +287,21 @@ def main():
             ent["TFLOPs"] = round(w.flops / t / 1e6, 1)
             ent["frac_mfma_peak"] = round(w.flops / t / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)
         ent["bound"] = w.bound
+        ent["in_step"] = w in wl
         ent["plan"] = None
         per[w.name] = ent
     # plans (one extra untimed call each)
-    for w in wl:
+    for w in wl_all:
         w.fused(w.ws)
         per[w.name]["plan"] = json.loads(cf.last_plan())
     torch.cuda.synchronize()
-    for w in wl:
+    for w in wl_all:
         if w.ws is not None:
             assert w.ws.error_word() == 0, f"{w.name}: a cross-workgroup wait gave up"
 
     # ---- unfused baselines, stream-launched and graph-replayed
     if not args.no_unfused:
-        for w in wl:
+        for w in wl_all:
             w.uws = cf.Workspace(cf.cf_unfused_workspace_bytes(w.op, *w.dims))
             ks = max(3, min(args.steps, 10))
             for _ in range(2):

@@ -204,22 +204,23 @@ cf_status run_rows(const char* name, int op, const float* x, float* y, float* y_
 // Strip softmax: 128 x 128 tiles; each row block's column tiles are cut into
 // S strips of C consecutive tiles (no strip empty), one per resident
 // workgroup where the rows allow.
-// Strips (softmax, and the softmax between two GEMMs): 128-row units of
-// contiguous column tiles (128 columns; 64 for the back-to-back GEMM, whose
-// output accumulator needs the registers).
+// Strips (softmax, and the softmax between two GEMMs): row-block units of
+// contiguous column tiles, 128 x 128 tiles at two workgroups per CU for the
+// softmax, 256 rows x 64 keys at one 8-wave workgroup per CU for the
+// back-to-back GEMM (its output accumulator needs the registers).
 static cf_status plan_gemm_strips(int epi, int64_t M, int64_t N, int64_t K, DevInfo* di, GemmPlan* p0,
                                   GemmPlan* pl) {
   GemmPlan p = *p0;
   p.algo = 2;
   p.nn = 0;
-  p.bm = 128;
-  p.bn = epi == kEpiSoftmaxGemm ? 64 : 128;
+  p.bm = epi == kEpiSoftmaxGemm ? kB2bBM : 128;
+  p.bn = epi == kEpiSoftmaxGemm ? kB2bBN : 128;
   p.bk = K <= 32 ? 32 : (K <= 64 ? 64 : 128);  // reduction depth the kernel covers (zero-padded)
   int occ = 0;
   if (gemm_occupancy(epi, p, &occ) != hipSuccess || occ <= 0) return CF_EHIP;
   p.occupancy = occ;
   const int64_t cap = (int64_t)occ * di->cus;
-  const int64_t tn = (N + p.bn - 1) / p.bn, tm = (M + 127) / 128;
+  const int64_t tn = (N + p.bn - 1) / p.bn, tm = (M + p.bm - 1) / p.bm;
   // one join word per row block (two for the back-to-back GEMM)
   if ((epi == kEpiSoftmaxGemm ? 2 : 1) * tm > kMaxJoins) return CF_EUNSUPPORTED;
   int64_t S = std::max<int64_t>(1, std::min<int64_t>(tn, cap / tm));
@@ -240,8 +241,8 @@ static cf_status plan_gemm_strips(int epi, int64_t M, int64_t N, int64_t K, DevI
 }
 
 // Workspace of the back-to-back GEMM past the header and join words: strip
-// statistics (M x strips float2), row statistics (M float2), partial outputs
-// (M x strips x 128 floats).
+// row maxima (M x strips float2), row maxima (M float2), partial outputs
+// (strips x M x 128 floats) and their row sums (strips x M float2).
 struct B2bLayout {
   size_t stats = 0, finals = 0, opart = 0, total = 0;
 };
@@ -250,7 +251,7 @@ static B2bLayout b2b_layout(const GemmPlan& p, int64_t M) {
   L.stats = kPartialsOff;
   L.finals = align_up(L.stats + (size_t)M * p.strips * 8, 256);
   L.opart = align_up(L.finals + (size_t)M * 8, 256);
-  L.total = align_up(L.opart + (size_t)M * p.strips * 128 * 4, 256);
+  L.total = align_up(L.opart + (size_t)M * p.strips * (128 * 4 + 8), 256);
   return L;
 }
 
@@ -334,7 +335,7 @@ size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N) {
 void record_gemm_plan(const char* name, int epi, const GemmPlan& p, int64_t M, int64_t N, int64_t K) {
   const bool ov = p.algo >= 1 && epi != kEpiStoreF32;
   const char* kernel = epi == kEpiSoftmaxGemm
-                           ? "k_gemm_sm3<B2B>"
+                           ? "k_gemm_b2b"
                            : (p.algo == 2 ? "k_gemm_sm3" : (ov ? (epi == kEpiLN ? "k_gemm_ln2" : "k_gemm_sm2") : "k_gemm"));
   const bool single = ln_one_at_a_time(epi, p);
   const char* sched = epi == kEpiSoftmaxGemm
@@ -348,7 +349,8 @@ void record_gemm_plan(const char* name, int epi, const GemmPlan& p, int64_t M, i
            "\"layout\":\"%s\",\"tiles\":%d,\"row_group\":%lld,\"grid\":%d,\"block\":%d,\"occupancy\":%d,"
            "\"rounds\":%d,\"aggregation\":\"%s\",\"schedule\":\"%s\",\"xcd_block\":[%d,%d]}",
            name, (long long)M, (long long)N, (long long)K, kernel, p.bm, p.bn, p.bk, p.nn ? "NN" : "NT", p.tiles,
-           p.algo == 2 ? (long long)p.strips : (long long)((N + p.bn - 1) / p.bn), p.grid, single ? 512 : 256,
+           p.algo == 2 ? (long long)p.strips : (long long)((N + p.bn - 1) / p.bn), p.grid,
+           (single || epi == kEpiSoftmaxGemm) ? 512 : 256,
            p.occupancy, p.rounds,
            (ov || p.leader) ? (epi == kEpiLN && p.algo == 1 ? "peer-to-peer" : "leader") : "peer-to-peer", sched,
            p.sw_a, p.sw_b);

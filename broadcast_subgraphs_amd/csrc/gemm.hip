@@ -1141,26 +1141,11 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 //   the strip is computed again, normalised and stored as bf16.
 // The strip is recomputed rather than held across the wait: with a short
 // reduction dimension the second pass costs less than the exchange it hides.
-//
-// B2B: the softmax tile is not stored but multiplied by V, back to back
-// ([ComFuse] "B2BGEMM": S = F(P) per tile, eq. 3; partial products over the
-// contraction dimension, eq. 4; their sum at commit, eq. 5).  In sweep 2 the
-// ring alternates the tile's K block (first MatMul) and V block (second
-// MatMul), one shared buffer for both weights as the page describes.  The
-// normalised tile goes from the accumulator straight into bf16 operand
-// fragments: a lane holds 16 consecutive keys of its row, so the second
-// MatMul's k-order is permuted to match (k-slots 0-7 take keys 0-7 of lanes
-// 0-31 and keys 16-23 of lanes 32-63, and so on), and V's transposed
-// fragment reads use the same permutation.  The strip's partial output
-// (128 rows x 128 columns, fp32) goes to the workspace; after the row block's
-// second join every strip sums its share of the rows over the strips in
-// strip order and stores O.
 constexpr int kSmBM = 128, kSmBN = 128, kSmBK = 128;
 
-template <int KS, int MINB, bool B2B = false>
+template <int KS, int MINB>
 __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
-  // B2B: 64-key tiles (the output accumulator needs the registers)
-  constexpr int BM = kSmBM, BN = B2B ? 64 : kSmBN, BK = kSmBK;
+  constexpr int BM = kSmBM, BN = kSmBN, BK = kSmBK;
   constexpr int CB = BN / 32;  // KS: 16-deep k-steps covering the reduction dimension
   constexpr int SLOT = BN * BK * 2;  // one K tile: BN keys x BK dims
   constexpr int LB = SLOT / 4096;    // 16-byte direct loads per lane per tile
@@ -1168,8 +1153,6 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
   __shared__ __align__(16) char s1[SLOT];
   __shared__ uint32_t gens[kMaxRounds];
   __shared__ int last;
-  __shared__ uint32_t gen2;
-  __shared__ __align__(16) char sqb[B2B ? kSmBM * kSmBK * 2 : 16];  // B2B sweep 2: the strip's Q rows
 
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
@@ -1382,252 +1365,430 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
     }
   }
 
-  if constexpr (!B2B) {
-    // ------------------------------------------------ sweep 2: normalise, store
-    i = 0;
-    for (int u = g; u < units; u += G, ++i) {
-      const int rowblk = u / S, m0 = rowblk * BM;
-      bf16x8_t qf[KS];
-      load_q(m0, qf);
-      if (t == 0) wait_generation(a.joins + rowblk, gens[i], a.err);
-      __syncthreads();
-      const int row = m0 + w * 32 + l32;
-      const float2 fs = row < M ? ld_dev2(F + row) : make_float2(0.0f, 0.0f);
-      for (int j = strip_first(u); j < strip_end(u); ++j) {
-        f32x16 acc[CB];
-        step(2, u, j, qf, acc);
-  #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-  #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int col = j * BN + cb * 32 + 16 * hl + 8 * h;
-            float o[8];
-  #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * h + e], sc, -fs.x)) * fs.y;
-            const u32x4 pk = {cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]), cvt_bf16x2(o[4], o[5]),
-                              cvt_bf16x2(o[6], o[7])};
-            bst16(rY, (row < M && col < N) ? (uint32_t)(row * N + col) * 2u : kOOB, pk);
-          }
+  // ------------------------------------------------ sweep 2: normalise, store
+  i = 0;
+  for (int u = g; u < units; u += G, ++i) {
+    const int rowblk = u / S, m0 = rowblk * BM;
+    bf16x8_t qf[KS];
+    load_q(m0, qf);
+    if (t == 0) wait_generation(a.joins + rowblk, gens[i], a.err);
+    __syncthreads();
+    const int row = m0 + w * 32 + l32;
+    const float2 fs = row < M ? ld_dev2(F + row) : make_float2(0.0f, 0.0f);
+    for (int j = strip_first(u); j < strip_end(u); ++j) {
+      f32x16 acc[CB];
+      step(2, u, j, qf, acc);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = j * BN + cb * 32 + 16 * hl + 8 * h;
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * h + e], sc, -fs.x)) * fs.y;
+          const u32x4 pk = {cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]), cvt_bf16x2(o[4], o[5]),
+                            cvt_bf16x2(o[6], o[7])};
+          bst16(rY, (row < M && col < N) ? (uint32_t)(row * N + col) * 2u : kOOB, pk);
+        }
+    }
+  }
+}
+
+
+// Back-to-back GEMM with the row softmax between, O = softmax(scale Q.K^T).V
+// ([ComFuse] "B2BGEMM": S_tile = F(P_tile), eq. 3; partial products
+// S_tile.W2_tile over the contraction dimension, eq. 4; their sum at the
+// commit, eq. 5; the W1 and W2 tiles share one circular buffer).  F is the
+// cross-tile row softmax; its 1/sum factor is one scalar per row, so it
+// commutes with the second MatMul and is applied at the commit:
+//   Sweep 1: the row max of the scaled scores over the strip's K blocks
+//   (MFMA and one max per score); the last strip of a row block to arrive
+//   merges the block's strip maxima in order and publishes them.
+//   Sweep 2: K block j (first MatMul, P = Q.K_j^T), then V block j: the tile
+//   2^(P*sc - max) goes from the accumulator straight into bf16 operand
+//   fragments and meets V_j in the second MatMul; its row sums accumulate
+//   beside.  A lane holds 16 consecutive keys of its row, so the second
+//   MatMul's k-order is permuted to match (k-slots 0-7 take keys 0-7 of lanes
+//   0-31 and keys 16-23 of lanes 32-63, and so on) and V's transposed
+//   fragment reads follow it.
+//   Commit: each strip publishes its partial output and row sums (the tile
+//   goes through LDS so every store writes whole 1 KB runs); after the row
+//   block's second join every strip sums its share of the rows over the
+//   strips, in strip order, divides by the summed row sums and stores O.
+// One workgroup of 8 waves per CU (32 rows per wave, 256-row strips): the
+// strip's Q rows sit in LDS for both sweeps, and the K / V blocks (64 keys)
+// stream through an NS-slot ring with NS - 1 blocks in flight, each slot its
+// own LDS object so the compiler can tell the slot being read from the ones
+// being filled.
+template <int KS, int NS>
+__global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
+  constexpr int BM = kB2bBM, BN = kB2bBN, BK = kB2bBK, NW = kB2bWaves, THREADS = kB2bThreads;
+  constexpr int CB = BN / 32;            // 32-key blocks per tile
+  constexpr int DV = 128, NB = DV / 32;  // output columns held (zero past Dv)
+  constexpr int SLOT = BN * BK * 2;      // one K block (BN keys x BK dims) or V block (BN keys x DV)
+  constexpr int LPS = SLOT / (NW * 1024);  // 16-byte direct loads per lane per block
+  static_assert(SLOT == BN * DV * 2 && LPS * NW * 1024 == SLOT && BK == 128, "block shapes");
+  static_assert(NS >= 2 && NS <= 6 && (NS - 2) * LPS < 64, "ring depth");
+  __shared__ __align__(16) char sq[BM * BK * 2];  // the strip's Q rows
+  __shared__ __align__(16) char r0[SLOT];
+  __shared__ __align__(16) char r1[SLOT];
+  __shared__ __align__(16) char r2[NS > 2 ? SLOT : 16];
+  __shared__ __align__(16) char r3[NS > 3 ? SLOT : 16];
+  __shared__ __align__(16) char r4[NS > 4 ? SLOT : 16];
+  __shared__ __align__(16) char r5[NS > 5 ? SLOT : 16];
+  __shared__ uint32_t gens[kMaxRounds];
+  __shared__ int last;
+  __shared__ uint32_t gen2;
+  char* const ring_all[6] = {r0, r1, r2, r3, r4, r5};
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int M = (int)a.M, N = (int)a.N, D = (int)a.K, Dv = (int)a.Dv;
+  const int G = (int)gridDim.x;
+  const int g = (int)xcd_local_id(blockIdx.x, (uint32_t)G);
+  const int T = a.tiles_n;        // 64-key tiles per row
+  const int S = a.strips;         // strips per row block
+  const int C = (T + S - 1) / S;  // tiles per strip
+  const int units = a.tiles_m * S;
+  if (g >= units) return;
+  const __amdgpu_buffer_rsrc_t rA = rsrc(a.A, (uint32_t)(a.M * a.K * 2));
+  const __amdgpu_buffer_rsrc_t rB = rsrc(a.B, (uint32_t)(a.N * a.K * 2));
+  const __amdgpu_buffer_rsrc_t rV = rsrc(a.V, (uint32_t)(a.N * a.Dv * 2));
+  const __amdgpu_buffer_rsrc_t rO = rsrc(a.Y, (uint32_t)(a.M * a.Dv * 2));
+  // partial outputs, strip-major: [S][M][DV] fp32, then row sums [S][M] float2
+  const __amdgpu_buffer_rsrc_t rOp = rsrc(a.opart, (uint32_t)(a.M * S * DV * 4));
+  float2* const Lp = reinterpret_cast<float2*>(a.opart + (size_t)a.M * S * DV);
+  const float sc = a.scale * kLog2e;
+  float2* P = reinterpret_cast<float2*>(a.partials);
+  float2* F = reinterpret_cast<float2*>(a.finals);
+
+  // Direct loads: load q of a block puts key 32q + kl (kl = 4w + lane/16 <
+  // 32) at 16-byte chunk lane % 16 of that key's 256-byte row; the row's
+  // swizzle (sigma rows for K, 64-byte segments for V) does not depend on q,
+  // so one per-lane offset serves every load.  Columns past D (K) or Dv (V)
+  // and keys past N read zero.
+  uint32_t koff, voff;
+  {
+    const int kl = 4 * w + (lane >> 4), pc = lane & 15;
+    const int gk = 8 * swz_sigma<BK>(kl, pc);
+    koff = gk < D ? (uint32_t)(kl * D + gk) * 2u : kOOB;
+    const int col = ((pc * 16) ^ nn_mask(kl)) / 2;
+    voff = col < Dv ? (uint32_t)(kl * Dv + col) * 2u : kOOB;
+  }
+  auto load_k = [&](char* slot, int j) {
+    const uint32_t base = (uint32_t)(j * BN) * (uint32_t)D * 2u;
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) g2l16(rB, slot + (q * NW + w) * 1024, koff + base + (uint32_t)(64 * q * D));
+  };
+  auto load_v = [&](char* slot, int j) {
+    const uint32_t base = (uint32_t)(j * BN) * (uint32_t)Dv * 2u;
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) g2l16(rV, slot + (q * NW + w) * 1024, voff + base + (uint32_t)(64 * q * Dv));
+  };
+  // The strip's Q rows: row r's 16-byte chunk c at r*256 + 16*(c ^ r%16), so
+  // 16 lanes reading 16 rows at one chunk hit 16 distinct bank slots.
+  auto load_q = [&](int m0) {
+#pragma unroll
+    for (int q = 0; q < BM * BK * 2 / (NW * 1024); ++q) {
+      const int o = (q * NW + w) * 1024 + lane * 16;
+      const int r = o / 256, c = ((o % 256) / 16) ^ (r & 15);
+      g2l16(rA, sq + (q * NW + w) * 1024, (m0 + r < M && 8 * c < D) ? (uint32_t)((m0 + r) * D + 8 * c) * 2u : kOOB);
+    }
+  };
+  // First MatMul of one tile: acc[cb] += K rows (sigma-permuted) x Q rows;
+  // step ks+1's K and Q fragments are read before step ks's MFMAs issue
+  const int qr = w * 32 + l32;
+  auto mma_qk = [&](const char* slot, f32x16 (&acc)[CB]) {
+    const char* qrow = sq + qr * 256;
+    bf16x8_t kf[2][CB], qv[2];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int key = cb * 32 + sigma(l32);
+      kf[0][cb] = *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz_sigma<BK>(key, hl));
+    }
+    qv[0] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * (hl ^ (qr & 15)));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int key = cb * 32 + sigma(l32);
+          kf[cur ^ 1][cb] =
+              *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz_sigma<BK>(key, 2 * (ks + 1) + hl));
+        }
+        qv[cur ^ 1] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ((2 * (ks + 1) + hl) ^ (qr & 15)));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][cb], qv[cur], acc[cb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // V fragment for key block cb, half q, column block nb: 8 consecutive
+  // (permuted) keys of one column by two transposed reads.  The lane reads
+  // key k = cb*32 + 16*(lane/32) + 8q + 4hh + e, column n = nb*32 + c (e, c
+  // from the lane): k % 4 = e, so the segment XOR is (nb ^ e) * 64 and the
+  // byte offset is a per-lane base per nb plus a constant.
+  uint32_t vb[NB];
+  {
+    const int Gq = lane >> 4, L = lane & 15, e = L >> 2, cc = L & 3;
+    const int clow = 2 * (16 * (cc & 1) + 8 * (Gq & 1) + 4 * (cc >> 1));  // < 64
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) vb[nb] = (uint32_t)((16 * (Gq >> 1) + e) * (DV * 2) + ((nb ^ e) << 6) + clow);
+  }
+  auto vfrag = [&](const char* slot, int cb, int q, int nb) -> bf16x8_t {
+    bf16x4_t h[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4_t*)(slot + vb[nb] + (cb * 32 + 8 * q + 4 * hh) * (DV * 2)));
+    return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // E = 2^(P*sc - max) of tile j (zero on keys past N) into bf16 fragments,
+  // one 32-key block at a time, each followed by its MFMAs; the lane's share
+  // of its row sum accumulates in fp32
+  auto mma_ev = [&](const char* slot, const f32x16 (&acc)[CB], float mrow, int j, f32x16 (&oacc)[NB], float& lsum) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      bf16x8_t sf[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const bool ok = j * BN + cb * 32 + 16 * hl + 8 * q < N;
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = ok ? __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * q + e], sc, -mrow)) : 0.0f;
+        lsum += ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
+        const u32x4 pk = {cvt_bf16x2(y[0], y[1]), cvt_bf16x2(y[2], y[3]), cvt_bf16x2(y[4], y[5]),
+                          cvt_bf16x2(y[6], y[7])};
+        sf[q] = __builtin_bit_cast(bf16x8_t, pk);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        bf16x8_t vf[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) vf[nb] = vfrag(slot, cb, q, nb);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[nb], sf[q], oacc[nb], 0, 0, 0);
       }
     }
-  } else {
-    // ---------------------------------------------- sweep 2: S.V, commit O
-    constexpr int DV = 128, NB = DV / 32;  // output columns held (zero past Dv)
-    static_assert(BN * DV * 2 == SLOT, "a V block fills one ring slot");
-    const int Dv = (int)a.Dv;
-    const __amdgpu_buffer_rsrc_t rV = rsrc(a.V, (uint32_t)(a.N * a.Dv * 2));
-    const __amdgpu_buffer_rsrc_t rOp = rsrc(a.opart, (uint32_t)(a.M * S * DV * 4));
-    const __amdgpu_buffer_rsrc_t rO = rsrc(a.Y, (uint32_t)(a.M * a.Dv * 2));
-    // direct loads of V block j (keys j*BN .., all columns): rows of 256
-    // bytes, 64-byte segments XORed by key % 4 for the transposed reads
-    // (load q: key 16q + 4w + lane/16, whose XOR term is the same for every q)
-    uint32_t voff;
-    {
-      const int kl = 4 * w + (lane >> 4), col = (((lane & 15) * 16) ^ nn_mask(kl)) / 2;
-      voff = col < Dv ? (uint32_t)(kl * Dv + col) * 2u : kOOB;
-    }
-    auto load_v = [&](char* slot, int j) {
-      const uint32_t base = (uint32_t)(j * BN) * (uint32_t)Dv * 2u;
+  };
+  // One segment of the block stream (one strip in one sweep): nst blocks,
+  // block b in slot b % NS.  Before block b computes, the blocks issued after
+  // it may still be in flight (vmcnt, in order), a barrier publishes block b
+  // and retires block b - 1's slot, and block b + NS - 1 is issued into it.
+  // The caller's loads issued before the segment (the Q rows) are older than
+  // every block, so block 0's wait covers them.
+  auto segment = [&](int nst, auto&& issue, auto&& compute) {
 #pragma unroll
-      for (int q = 0; q < LB; ++q) g2l16(rV, slot + (q * 4 + w) * 1024, voff + base + (uint32_t)(32 * q * Dv));
-    };
-    // V fragment for key block cb, half q, column block nb: 8 consecutive
-    // (permuted) keys of one column, gathered by two transposed reads.  The
-    // lane reads key k = cb*32 + 16*(lane/32) + 8q + 4hh + e and column
-    // n = nb*32 + c (e, c from the lane): k % 4 = e, so the segment XOR is
-    // (nb ^ e) * 64 and the byte offset splits into a per-lane base per nb
-    // plus a constant
-    uint32_t vb[NB];
-    {
-      const int G = lane >> 4, L = lane & 15, e = L >> 2, cc = L & 3;
-      const int clow = 2 * (16 * (cc & 1) + 8 * (G & 1) + 4 * (cc >> 1));  // < 64
+    for (int b = 0; b < NS - 1; ++b)
+      if (b < nst) issue(b, ring_all[b]);
+    for (int b0 = 0; b0 < nst; b0 += NS) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vb[nb] = (uint32_t)((16 * (G >> 1) + e) * (DV * 2) + ((nb ^ e) << 6) + clow);
-    }
-    auto vfrag = [&](const char* slot, int cb, int q, int nb) -> bf16x8_t {
-      bf16x4_t h[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4_t*)(slot + vb[nb] + (cb * 32 + 8 * q + 4 * hh) * (DV * 2)));
-      return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    // S = 2^(P*sc - M) / L of tile j (zero on keys past N) into bf16
-    // fragments, one 32-key block at a time, each followed by its MFMAs
-    auto mma_sv = [&](const char* slot, const f32x16 (&acc)[CB], float2 fs, int j, f32x16 (&oacc)[NB]) {
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        bf16x8_t sf[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const bool ok = j * BN + cb * 32 + 16 * hl + 8 * q < N;
-          float y[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            y[e] = ok ? __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * q + e], sc, -fs.x)) * fs.y : 0.0f;
-          const u32x4 pk = {cvt_bf16x2(y[0], y[1]), cvt_bf16x2(y[2], y[3]), cvt_bf16x2(y[4], y[5]),
-                            cvt_bf16x2(y[6], y[7])};
-          sf[q] = __builtin_bit_cast(bf16x8_t, pk);
-        }
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          bf16x8_t vf[NB];
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) vf[nb] = vfrag(slot, cb, q, nb);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[nb], sf[q], oacc[nb], 0, 0, 0);
-        }
-      }
-    };
-    // The strip's Q rows sit in LDS for this sweep (registers go to the
-    // output accumulator): row r's 16-byte chunk c at r*256 + 16*(c ^ r%16),
-    // so 16 lanes reading 16 rows at one chunk hit 16 distinct bank slots.
-    static_assert(BK == 128, "one 256-byte LDS row per Q row");
-    auto load_q_lds = [&](int m0) {
-#pragma unroll
-      for (int q = 0; q < BM * BK * 2 / 4096; ++q) {
-        const int o = (q * 4 + w) * 1024 + lane * 16;
-        const int r = o / 256, c = ((o % 256) / 16) ^ (r & 15);
-        g2l16(rA, sqb + (q * 4 + w) * 1024, (m0 + r < M && 8 * c < D) ? (uint32_t)((m0 + r) * D + 8 * c) * 2u : kOOB);
-      }
-    };
-    // first MatMul of one tile with Q from LDS: step ks+1's K and Q fragments
-    // are read before step ks's MFMAs issue
-    auto mma_tile_q = [&](const char* slot, f32x16 (&acc)[CB]) {
-      const int qr = w * 32 + l32;
-      const char* qrow = sqb + qr * 256;
-      bf16x8_t kf[2][CB], qv[2];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int key = cb * 32 + sigma(l32);
-        kf[0][cb] = *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz_sigma<BK>(key, hl));
-      }
-      qv[0] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * (hl ^ (qr & 15)));
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int cur = ks & 1;
-        if (ks + 1 < KS) {
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            const int key = cb * 32 + sigma(l32);
-            kf[cur ^ 1][cb] =
-                *reinterpret_cast<const bf16x8_t*>(slot + key * (BK * 2) + 16 * swz_sigma<BK>(key, 2 * (ks + 1) + hl));
-          }
-          qv[cur ^ 1] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * ((2 * (ks + 1) + hl) ^ (qr & 15)));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cur][cb], qv[cur], acc[cb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    i = 0;
-    for (int u = g; u < units; u += G, ++i) {
-      const int rowblk = u / S, m0 = rowblk * BM, su = u % S;
-      if (t == 0) wait_generation(a.joins + rowblk, gens[i], a.err);
-      __syncthreads();  // also: every wave is done with the previous strip's Q
-      load_q_lds(m0);
-      const int row = m0 + w * 32 + l32;
-      const float2 fs = row < M ? ld_dev2(F + row) : make_float2(0.0f, 0.0f);
-      f32x16 oacc[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.0f;
-      for (int j = strip_first(u); j < strip_end(u); ++j) {
-        // K block j is in stage st: prefetch V block j, first MatMul
-        f32x16 acc[CB];
-        wait_vm<0>();
+      for (int i = 0; i < NS; ++i) {
+        const int b = b0 + i;
+        if (b >= nst) break;
+        wait_vm_n(min(NS - 2, nst - 1 - b) * LPS);
         __syncthreads();
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
-        if (st & 1) {
-          load_v(s0, j);
-          mma_tile_q(s1, acc);
-        } else {
-          load_v(s1, j);
-          mma_tile_q(s0, acc);
-        }
-        ++st;
-        // V block j is in stage st: prefetch the next K block, normalise and
-        // run the second MatMul
-        wait_vm<0>();
-        __syncthreads();
-        int nj = 0;
-        const bool more = next_tile(2, u, j, &nj);
-        if (st & 1) {
-          if (more) load_tile(s0, nj);
-          mma_sv(s1, acc, fs, j, oacc);
-        } else {
-          if (more) load_tile(s1, nj);
-          mma_sv(s0, acc, fs, j, oacc);
-        }
-        ++st;
+        if (b + NS - 1 < nst) issue(b + NS - 1, ring_all[(i + NS - 1) % NS]);
+        compute(b, ring_all[i]);
       }
-      // this lane's output row, columns nb*32 + 16*hl + [0, 16)
-      if (S == 1) {
+    }
+  };
+  auto strip_first = [&](int u) { return (u % S) * C; };
+  auto strip_len = [&](int u) { return min(T, (u % S) * C + C) - (u % S) * C; };
+
+  // ------------------------------------------------ sweep 1: row maxima
+  int i = 0;
+  int qloaded = -1;  // row block whose Q rows are in LDS
+  for (int u = g; u < units; u += G, ++i) {
+    const int rowblk = u / S, m0 = rowblk * BM, j0 = strip_first(u);
+    __syncthreads();  // every wave is done with the LDS of the previous segment
+    if (qloaded != rowblk) load_q(m0);
+    qloaded = rowblk;
+    // the max of the scaled scores from the raw ones (scaling is monotone),
+    // over the lane's valid 8-key chunks
+    float mx = -INFINITY, mn = INFINITY;
+    segment(
+        strip_len(u), [&](int b, char* slot) { load_k(slot, j0 + b); },
+        [&](int b, const char* slot) {
+          const int j = j0 + b;
+          f32x16 acc[CB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+          for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int col = nb * 32 + 16 * hl + 8 * h;
-            const u32x4 pk = {cvt_bf16x2(oacc[nb][8 * h], oacc[nb][8 * h + 1]),
-                              cvt_bf16x2(oacc[nb][8 * h + 2], oacc[nb][8 * h + 3]),
-                              cvt_bf16x2(oacc[nb][8 * h + 4], oacc[nb][8 * h + 5]),
-                              cvt_bf16x2(oacc[nb][8 * h + 6], oacc[nb][8 * h + 7])};
-            bst16(rO, (row < M && col < Dv) ? (uint32_t)(row * Dv + col) * 2u : kOOB, pk);
+            for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
+          mma_qk(slot, acc);
+          const int c0 = j * BN + 16 * hl;
+#pragma unroll
+          for (int q = 0; q < 2 * CB; ++q) {
+            if (c0 + (q >> 1) * 32 + 8 * (q & 1) < N) {
+#pragma unroll
+              for (int k = 0; k < 8; ++k) {
+                const float v = acc[q >> 1][8 * (q & 1) + k];
+                mx = fmaxf(mx, v);
+                mn = fminf(mn, v);
+              }
+            }
           }
-        continue;
-      }
-      // publish the strip's partial output, join the row block's strips
+        });
+    float m = mx == -INFINITY ? -INFINITY : (sc >= 0.0f ? mx * sc : mn * sc);  // base-2 domain
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    const int row = m0 + qr;
+    if (hl == 0 && row < M) st_dev2(P + (size_t)row * S + (u % S), make_float2(m, 0.0f));
+    wait_stores();
+    __syncthreads();
+    uint64_t* jw = a.joins + rowblk;
+    if (t == 0) {
+      const uint64_t old = __hip_atomic_fetch_add(jw, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = ((uint32_t)old == (uint32_t)(S - 1)) ? 1 : 0;
+      gens[i] = (uint32_t)(old >> 32);
+    }
+    __syncthreads();
+    if (last) {
+      // the block's row maxima over its strips, all loads in flight
+      if (t < BM && m0 + t < M) {
+        const float2* Pr = P + (size_t)(m0 + t) * S;
+        float mm = -INFINITY;
+        for (int k0 = 0; k0 < S; k0 += 8) {
+          float2 v[8];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+          for (int k = 0; k < 8; ++k) v[k] = k0 + k < S ? ld_dev2(Pr + k0 + k) : make_float2(-INFINITY, 0.0f);
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          const int col = nb * 32 + 16 * hl + 4 * c4;
-          const u32x4 v = {__float_as_uint(oacc[nb][4 * c4]), __float_as_uint(oacc[nb][4 * c4 + 1]),
-                           __float_as_uint(oacc[nb][4 * c4 + 2]), __float_as_uint(oacc[nb][4 * c4 + 3])};
-          bst16_dev(rOp, row < M ? (uint32_t)(((row * S + su) * DV + col) * 4) : kOOB, v);
+          for (int k = 0; k < 8; ++k) mm = fmaxf(mm, v[k].x);
         }
+        st_dev2(F + m0 + t, make_float2(mm, 0.0f));
+      }
       wait_stores();
       __syncthreads();
-      uint64_t* jw2 = a.joins + a.tiles_m + rowblk;
-      if (t == 0) {
-        const uint64_t old = __hip_atomic_fetch_add(jw2, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((uint32_t)old == (uint32_t)(S - 1))
-          __hip_atomic_fetch_add(jw2, (1ull << 32) - (uint64_t)S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        gen2 = (uint32_t)(old >> 32);
-      }
-      __syncthreads();
-      if (t == 0) wait_generation(jw2, gen2, a.err);
-      __syncthreads();
-      // strip su sums rows [su*R, su*R + R) of the block over the strips, in
-      // strip order, 8 columns per item
-      const int R = (BM + S - 1) / S;
-      for (int it = t; it < R * (DV / 8); it += kThreads) {
-        const int r = su * R + it / (DV / 8), c8 = (it % (DV / 8)) * 8;
-        const int orow = m0 + r;
-        if (r >= BM || orow >= M || c8 >= Dv) continue;
-        float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-        for (int sk = 0; sk < S; sk += 8) {
-          u32x4 v[8][2];
+      if (t == 0) __hip_atomic_fetch_add(jw, (1ull << 32) - (uint64_t)S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // ------------------------------------------------ sweep 2: S.V, commit O
+  i = 0;
+  for (int u = g; u < units; u += G, ++i) {
+    const int rowblk = u / S, m0 = rowblk * BM, su = u % S, j0 = strip_first(u);
+    __syncthreads();
+    if (qloaded != rowblk) load_q(m0);
+    qloaded = rowblk;
+    if (t == 0) wait_generation(a.joins + rowblk, gens[i], a.err);
+    __syncthreads();
+    const int row = m0 + qr;
+    const float mrow = row < M ? ld_dev2(F + row).x : 0.0f;
+    f32x16 oacc[NB];
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-              v[k][h] = bld16_dev(rOp, sk + k < S ? (uint32_t)(((orow * S + sk + k) * DV + c8 + 4 * h) * 4) : kOOB);
+      for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.0f;
+    float lsum = 0.0f;
+    f32x16 acc[CB];
+    // blocks alternate: 2b is K block j0 + b, 2b + 1 is V block j0 + b
+    segment(
+        2 * strip_len(u),
+        [&](int b, char* slot) {
+          if (b & 1)
+            load_v(slot, j0 + (b >> 1));
+          else
+            load_k(slot, j0 + (b >> 1));
+        },
+        [&](int b, const char* slot) {
+          if (b & 1) {
+            mma_ev(slot, acc, mrow, j0 + (b >> 1), oacc, lsum);
+          } else {
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (sk + k < S)
+            for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-              for (int e = 0; e < 8; ++e) o[e] += __uint_as_float(v[k][e >> 2][e & 3]);
+              for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
+            mma_qk(slot, acc);
+          }
+        });
+    lsum += __shfl_xor(lsum, 32, kWave);  // the row's sum over the strip
+    // this lane's output row, columns nb*32 + 16*hl + [0, 16)
+    if (S == 1) {
+      const float inv = 1.0f / lsum;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = nb * 32 + 16 * hl + 8 * h;
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = oacc[nb][8 * h + e] * inv;
+          const u32x4 pk = {cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]), cvt_bf16x2(o[4], o[5]),
+                            cvt_bf16x2(o[6], o[7])};
+          bst16(rO, (row < M && col < Dv) ? (uint32_t)(row * Dv + col) * 2u : kOOB, pk);
         }
-        const u32x4 pk = {cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]), cvt_bf16x2(o[4], o[5]),
-                          cvt_bf16x2(o[6], o[7])};
-        bst16(rO, (uint32_t)(orow * Dv + c8) * 2u, pk);
+      continue;
+    }
+    // publish the strip's partial output through LDS (now idle): wave w's 32
+    // rows go to a 16 KB region of its own (Q rows for waves 0-3, ring slots
+    // for waves 4-7), 16-byte chunk k of row r at r*512 + 16*(k ^ r), then
+    // back out as whole rows, 1 KB per store instruction
+    __syncthreads();  // every wave is done with the ring and the Q rows
+    char* const stage = w < 4 ? sq + w * 16384 : ring_all[w - 4];
+    static_assert(NS >= 4 && SLOT == 16384 && BM * BK * 2 == 4 * 16384, "one 16 KB staging region per wave");
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int k4 = nb * 8 + 4 * hl + c4;  // 16-byte chunk index of columns 4*k4 .. +3
+        const float4 v = make_float4(oacc[nb][4 * c4], oacc[nb][4 * c4 + 1], oacc[nb][4 * c4 + 2], oacc[nb][4 * c4 + 3]);
+        *reinterpret_cast<float4*>(stage + l32 * 512 + 16 * (k4 ^ l32)) = v;
       }
+    if (hl == 0 && row < M) st_dev2(Lp + (size_t)su * M + row, make_float2(lsum, 0.0f));
+    __syncthreads();
+#pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int idx = it * 64 + lane, r = idx >> 5, k4 = idx & 31;
+      const int orow = m0 + w * 32 + r;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * 512 + 16 * (k4 ^ r));
+      bst16_dev(rOp, orow < M ? (uint32_t)((((size_t)su * M + orow) * DV + 4 * k4) * 4) : kOOB, v);
+    }
+    wait_stores();
+    __syncthreads();
+    uint64_t* jw2 = a.joins + a.tiles_m + rowblk;
+    if (t == 0) {
+      const uint64_t old = __hip_atomic_fetch_add(jw2, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((uint32_t)old == (uint32_t)(S - 1))
+        __hip_atomic_fetch_add(jw2, (1ull << 32) - (uint64_t)S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      gen2 = (uint32_t)(old >> 32);
+    }
+    __syncthreads();
+    if (t == 0) wait_generation(jw2, gen2, a.err);
+    __syncthreads();
+    // strip su sums rows [su*R, su*R + R) of the block over the strips, in
+    // strip order, 8 columns per item, and divides by the summed row sums
+    const int R = (BM + S - 1) / S;
+    for (int it = t; it < R * (DV / 8); it += THREADS) {
+      const int r = su * R + it / (DV / 8), c8 = (it % (DV / 8)) * 8;
+      const int orow = m0 + r;
+      if (r >= BM || orow >= M || c8 >= Dv) continue;
+      float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      float ls = 0.0f;
+      for (int sk = 0; sk < S; sk += 8) {
+        u32x4 v[8][2];
+        float2 lv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            v[k][h] = bld16_dev(rOp, sk + k < S ? (uint32_t)((((size_t)(sk + k) * M + orow) * DV + c8 + 4 * h) * 4) : kOOB);
+          lv[k] = sk + k < S ? ld_dev2(Lp + (size_t)(sk + k) * M + orow) : make_float2(0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (sk + k < S) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += __uint_as_float(v[k][e >> 2][e & 3]);
+            ls += lv[k].x;
+          }
+      }
+      const float inv = 1.0f / ls;
+      const u32x4 pk = {cvt_bf16x2(o[0] * inv, o[1] * inv), cvt_bf16x2(o[2] * inv, o[3] * inv),
+                        cvt_bf16x2(o[4] * inv, o[5] * inv), cvt_bf16x2(o[6] * inv, o[7] * inv)};
+      bst16(rO, (uint32_t)(orow * Dv + c8) * 2u, pk);
     }
   }
 }
@@ -2032,9 +2193,9 @@ static hipError_t gemm_dispatch(int epi, const GemmPlan& pl, const GemmArgs& a, 
   }
   if (epi == kEpiSoftmaxGemm) {
     if (pl.nn || pl.algo != 2) return hipErrorInvalidConfiguration;
-    auto kfn = pl.bk <= 32 ? k_gemm_sm3<2, 2, true> : (pl.bk <= 64 ? k_gemm_sm3<4, 2, true> : k_gemm_sm3<8, 2, true>);
-    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kfn, kThreads, 0);
-    hipLaunchKernelGGL(kfn, dim3(pl.grid), dim3(kThreads), 0, st, a);
+    auto kfn = pl.bk <= 32 ? k_gemm_b2b<2, 4> : (pl.bk <= 64 ? k_gemm_b2b<4, 4> : k_gemm_b2b<8, 4>);
+    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kfn, kB2bThreads, 0);
+    hipLaunchKernelGGL(kfn, dim3(pl.grid), dim3(kB2bThreads), 0, st, a);
     return hipGetLastError();
   }
   if (epi == kEpiSoftmax) {

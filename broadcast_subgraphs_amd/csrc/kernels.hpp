@@ -44,6 +44,10 @@ hipError_t rows_split_occupancy(int op, const RowPlan& pl, int* per_cu);
 // ----------------------------------------------------------------- GEMM
 enum GemmEpi { kEpiStoreF32 = 0, kEpiLN = 1, kEpiSoftmax = 2, kEpiSoftmaxGemm = 3 };
 
+// Back-to-back GEMM kernel shape: 256-row strips of 64-key tiles, one 8-wave
+// workgroup per CU, the reduction dimension up to 128.
+constexpr int kB2bBM = 256, kB2bBN = 64, kB2bBK = 128, kB2bWaves = 8, kB2bThreads = kB2bWaves * 64;
+
 struct GemmArgs {
   const uint16_t* A;   // [M x K] bf16 (GEMM left operand; Q for softmax)
   const uint16_t* B;   // NN: W [K x N]; NT: K [N x K] (bf16)

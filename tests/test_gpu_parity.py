@@ -245,7 +245,7 @@ def test_gemm_softmax_gemm_plan_uses_strips():
     d = gen.gemm_softmax_gemm_inputs(seed=6, M=1024, N=8192, D=128, Dv=128)
     _b2b_run(d, 1024, 8192, 128, 128)
     p = json.loads(cf.last_plan())
-    assert p["kernel"] == "k_gemm_sm3<B2B>" and p["row_group"] > 1 and p["rounds"] == 1, p
+    assert p["kernel"] == "k_gemm_b2b" and p["row_group"] > 1 and p["rounds"] == 1, p
     d = gen.gemm_softmax_gemm_inputs(seed=6, M=130, N=40, D=32, Dv=16)
     _b2b_run(d, 130, 40, 32, 16)
     assert json.loads(cf.last_plan())["row_group"] == 1, cf.last_plan()
