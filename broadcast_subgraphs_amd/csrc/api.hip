@@ -221,7 +221,7 @@ static cf_status plan_gemm_strips(int epi, int64_t M, int64_t N, int64_t K, DevI
   p.occupancy = occ;
   const int64_t cap = (int64_t)occ * di->cus;
   const int64_t tn = (N + p.bn - 1) / p.bn, tm = (M + p.bm - 1) / p.bm;
-  // one join word per row block (two for the back-to-back GEMM)
+  // one join word per row block (the back-to-back GEMM's is its second block of words)
   if ((epi == kEpiSoftmaxGemm ? 2 : 1) * tm > kMaxJoins) return CF_EUNSUPPORTED;
   int64_t S = std::max<int64_t>(1, std::min<int64_t>(tn, cap / tm));
   const int64_t C = (tn + S - 1) / S;
@@ -240,17 +240,15 @@ static cf_status plan_gemm_strips(int epi, int64_t M, int64_t N, int64_t K, DevI
   return CF_OK;
 }
 
-// Workspace of the back-to-back GEMM past the header and join words: strip
-// row maxima (M x strips float2), row maxima (M float2), partial outputs
-// (strips x M x 128 floats) and their row sums (strips x M float2).
+// Workspace of the back-to-back GEMM past the header and join words: the
+// strips' partial outputs (strips x M x 128 floats), then their per-row
+// (max, sum) pairs (strips x M float2).
 struct B2bLayout {
-  size_t stats = 0, finals = 0, opart = 0, total = 0;
+  size_t opart = 0, total = 0;
 };
 static B2bLayout b2b_layout(const GemmPlan& p, int64_t M) {
   B2bLayout L;
-  L.stats = kPartialsOff;
-  L.finals = align_up(L.stats + (size_t)M * p.strips * 8, 256);
-  L.opart = align_up(L.finals + (size_t)M * 8, 256);
+  L.opart = kPartialsOff;
   L.total = align_up(L.opart + (size_t)M * p.strips * (128 * 4 + 8), 256);
   return L;
 }
@@ -543,8 +541,6 @@ cf_status cf_gemm_softmax_gemm(const cf_bf16* Q, const cf_bf16* K, const cf_bf16
   a.M = M; a.N = N; a.K = D; a.Dv = Dv;
   a.err = reinterpret_cast<uint32_t*>(base);
   a.joins = reinterpret_cast<uint64_t*>(base + kHeader);
-  a.partials = reinterpret_cast<float*>(base + L.stats);
-  a.finals = reinterpret_cast<float*>(base + L.finals);
   a.opart = reinterpret_cast<float*>(base + L.opart);
   a.tiles_n = (int)((N + p.bn - 1) / p.bn);
   a.tiles_m = (int)((M + p.bm - 1) / p.bm);

@@ -1399,27 +1399,26 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
 // ([ComFuse] "B2BGEMM": S_tile = F(P_tile), eq. 3; partial products
 // S_tile.W2_tile over the contraction dimension, eq. 4; their sum at the
 // commit, eq. 5; the W1 and W2 tiles share one circular buffer).  F is the
-// cross-tile row softmax; its 1/sum factor is one scalar per row, so it
-// commutes with the second MatMul and is applied at the commit:
-//   Sweep 1: the row max of the scaled scores over the strip's K blocks
-//   (MFMA and one max per score); the last strip of a row block to arrive
-//   merges the block's strip maxima in order and publishes them.
-//   Sweep 2: K block j (first MatMul, P = Q.K_j^T), then V block j: the tile
-//   2^(P*sc - max) goes from the accumulator straight into bf16 operand
-//   fragments and meets V_j in the second MatMul; its row sums accumulate
-//   beside.  A lane holds 16 consecutive keys of its row, so the second
-//   MatMul's k-order is permuted to match (k-slots 0-7 take keys 0-7 of lanes
-//   0-31 and keys 16-23 of lanes 32-63, and so on) and V's transposed
-//   fragment reads follow it.
-//   Commit: each strip publishes its partial output and row sums (the tile
-//   goes through LDS so every store writes whole 1 KB runs); after the row
-//   block's second join every strip sums its share of the rows over the
-//   strips, in strip order, divides by the summed row sums and stores O.
+// cross-tile row softmax.  A workgroup owns a strip (a row block's run of
+// 64-key tiles) and merges F's row statistics online, tile by tile, as the
+// pages' statistics exchange does between workgroups: per tile, K block j
+// (first MatMul, P = Q.K_j^T), then V block j, where the row max rises to
+// include the tile (the output accumulator and the row sum are scaled by
+// 2^(old max - new max)), the tile 2^(P*sc - max) goes from the accumulator
+// straight into bf16 operand fragments and meets V_j in the second MatMul,
+// and its row sums accumulate beside.  A lane holds 16 consecutive keys of
+// its row, so the second MatMul's k-order is permuted to match (k-slots 0-7
+// take keys 0-7 of lanes 0-31 and keys 16-23 of lanes 32-63, and so on) and
+// V's transposed fragment reads follow it.
+// Commit: each strip publishes its partial output with its (max, sum) per
+// row (the tile goes through LDS so every store writes whole 1 KB runs);
+// after the row block's join every strip sums its share of the rows over the
+// strips, in strip order, each weighted by 2^(strip max - block max), divides
+// by the equally weighted sums and stores O.  Exact in real arithmetic.
 // One workgroup of 8 waves per CU (32 rows per wave, 256-row strips): the
-// strip's Q rows sit in LDS for both sweeps, and the K / V blocks (64 keys)
-// stream through an NS-slot ring with NS - 1 blocks in flight, each slot its
-// own LDS object so the compiler can tell the slot being read from the ones
-// being filled.
+// strip's Q rows sit in LDS, and the K / V blocks stream through an NS-slot
+// ring with NS - 1 blocks in flight, each slot its own LDS object so the
+// compiler can tell the slot being read from the ones being filled.
 template <int KS, int NS>
 __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
   constexpr int BM = kB2bBM, BN = kB2bBN, BK = kB2bBK, NW = kB2bWaves, THREADS = kB2bThreads;
@@ -1436,8 +1435,6 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
   __shared__ __align__(16) char r3[NS > 3 ? SLOT : 16];
   __shared__ __align__(16) char r4[NS > 4 ? SLOT : 16];
   __shared__ __align__(16) char r5[NS > 5 ? SLOT : 16];
-  __shared__ uint32_t gens[kMaxRounds];
-  __shared__ int last;
   __shared__ uint32_t gen2;
   char* const ring_all[6] = {r0, r1, r2, r3, r4, r5};
 
@@ -1456,12 +1453,10 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rB = rsrc(a.B, (uint32_t)(a.N * a.K * 2));
   const __amdgpu_buffer_rsrc_t rV = rsrc(a.V, (uint32_t)(a.N * a.Dv * 2));
   const __amdgpu_buffer_rsrc_t rO = rsrc(a.Y, (uint32_t)(a.M * a.Dv * 2));
-  // partial outputs, strip-major: [S][M][DV] fp32, then row sums [S][M] float2
+  // partial outputs, strip-major: [S][M][DV] fp32, then (max, sum) [S][M] float2
   const __amdgpu_buffer_rsrc_t rOp = rsrc(a.opart, (uint32_t)(a.M * S * DV * 4));
   float2* const Lp = reinterpret_cast<float2*>(a.opart + (size_t)a.M * S * DV);
   const float sc = a.scale * kLog2e;
-  float2* P = reinterpret_cast<float2*>(a.partials);
-  float2* F = reinterpret_cast<float2*>(a.finals);
 
   // Direct loads: load q of a block puts key 32q + kl (kl = 4w + lane/16 <
   // 32) at 16-byte chunk lane % 16 of that key's 256-byte row; the row's
@@ -1546,20 +1541,53 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
           (lds_bf16x4_t*)(slot + vb[nb] + (cb * 32 + 8 * q + 4 * hh) * (DV * 2)));
     return __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  // E = 2^(P*sc - max) of tile j (zero on keys past N) into bf16 fragments,
-  // one 32-key block at a time, each followed by its MFMAs; the lane's share
-  // of its row sum accumulates in fp32
-  auto mma_ev = [&](const char* slot, const f32x16 (&acc)[CB], float mrow, int j, f32x16 (&oacc)[NB], float& lsum) {
+  // Tile j of the strip: the row's reference max m moves only when the tile
+  // exceeds it by more than 2^8 (both lanes of a row agree: one exchange);
+  // then oacc and l are scaled by 2^(m_old - m_new).  Exponents stay at most
+  // 2^8 (bf16 and fp32 hold them), and the result is the same in real
+  // arithmetic whichever reference is used.  Then E = 2^(P*sc - m) (zero on
+  // keys past N) into bf16 fragments, one 32-key block at a time, each
+  // followed by its MFMAs; the lane's share of the row sum accumulates in fp32
+  auto mma_ev = [&](const char* slot, const f32x16 (&acc)[CB], float& m, int j, f32x16 (&oacc)[NB], float& l) {
+    float tx = sc >= 0.0f ? -INFINITY : INFINITY;  // max (or min) of the raw scores
+    if (sc >= 0.0f) {
+#pragma unroll
+      for (int q = 0; q < 2 * CB; ++q)
+        if (j * BN + (q >> 1) * 32 + 16 * hl + 8 * (q & 1) < N)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) tx = fmaxf(tx, acc[q >> 1][8 * (q & 1) + e]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2 * CB; ++q)
+        if (j * BN + (q >> 1) * 32 + 16 * hl + 8 * (q & 1) < N)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) tx = fminf(tx, acc[q >> 1][8 * (q & 1) + e]);
+    }
+    float tm = (tx == INFINITY || tx == -INFINITY) ? -INFINITY : tx * sc;  // base-2 domain
+    tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
+    if (tm > m + 8.0f) {  // raise the reference (the first valid tile always does)
+      const float corr = __builtin_amdgcn_exp2f(m - tm);  // 0 while m = -inf
+      l *= corr;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[nb][r] *= corr;
+      m = tm;
+    }
+    // (m = -inf only before the row's first key: then E is zero; the MFMAs
+    // below always run for the whole wave)
+    const bool live = m != -INFINITY;
+    const float mn = live ? m : 0.0f;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       bf16x8_t sf[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const bool ok = j * BN + cb * 32 + 16 * hl + 8 * q < N;
+        const bool ok = live && j * BN + cb * 32 + 16 * hl + 8 * q < N;
         float y[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = ok ? __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * q + e], sc, -mrow)) : 0.0f;
-        lsum += ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
+        for (int e = 0; e < 8; ++e) y[e] = ok ? __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * q + e], sc, -mn)) : 0.0f;
+        l += ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
         const u32x4 pk = {cvt_bf16x2(y[0], y[1]), cvt_bf16x2(y[2], y[3]), cvt_bf16x2(y[4], y[5]),
                           cvt_bf16x2(y[6], y[7])};
         sf[q] = __builtin_bit_cast(bf16x8_t, pk);
@@ -1574,16 +1602,17 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
       }
     }
   };
-  // One segment of the block stream (one strip in one sweep): nst blocks,
-  // block b in slot b % NS.  Before block b computes, the blocks issued after
-  // it may still be in flight (vmcnt, in order), a barrier publishes block b
-  // and retires block b - 1's slot, and block b + NS - 1 is issued into it.
-  // The caller's loads issued before the segment (the Q rows) are older than
-  // every block, so block 0's wait covers them.
-  auto segment = [&](int nst, auto&& issue, auto&& compute) {
+  // The strip's block stream: nst blocks, block x in slot x % NS.  Before
+  // block b computes, the blocks issued after it may still be in flight
+  // (vmcnt, in order); a barrier publishes block b and retires block b - 1's
+  // slot, and block b + NS - 1 is issued into it.  Loads issued before the
+  // stream (the Q rows) are older than every block, so block 0's wait covers
+  // them.  NS is even, so a block's parity (K or V) is known once unrolled.
+  static_assert(NS % 2 == 0, "K / V parity fixed per unrolled step");
+  auto stream = [&](int nst, auto&& issue, auto&& compute) {
 #pragma unroll
-    for (int b = 0; b < NS - 1; ++b)
-      if (b < nst) issue(b, ring_all[b]);
+    for (int x = 0; x < NS - 1; ++x)
+      if (x < nst) issue(x, ring_all[x]);
     for (int b0 = 0; b0 < nst; b0 += NS) {
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
@@ -1592,91 +1621,22 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
         wait_vm_n(min(NS - 2, nst - 1 - b) * LPS);
         __syncthreads();
         if (b + NS - 1 < nst) issue(b + NS - 1, ring_all[(i + NS - 1) % NS]);
-        compute(b, ring_all[i]);
+        compute((i & 1) != 0, b, ring_all[i]);
       }
     }
   };
   auto strip_first = [&](int u) { return (u % S) * C; };
   auto strip_len = [&](int u) { return min(T, (u % S) * C + C) - (u % S) * C; };
 
-  // ------------------------------------------------ sweep 1: row maxima
-  int i = 0;
+  // ------------------------------------------------ the strips
   int qloaded = -1;  // row block whose Q rows are in LDS
-  for (int u = g; u < units; u += G, ++i) {
-    const int rowblk = u / S, m0 = rowblk * BM, j0 = strip_first(u);
-    __syncthreads();  // every wave is done with the LDS of the previous segment
-    if (qloaded != rowblk) load_q(m0);
-    qloaded = rowblk;
-    // the max of the scaled scores from the raw ones (scaling is monotone),
-    // over the lane's valid 8-key chunks
-    float mx = -INFINITY, mn = INFINITY;
-    segment(
-        strip_len(u), [&](int b, char* slot) { load_k(slot, j0 + b); },
-        [&](int b, const char* slot) {
-          const int j = j0 + b;
-          f32x16 acc[CB];
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
-          mma_qk(slot, acc);
-          const int c0 = j * BN + 16 * hl;
-#pragma unroll
-          for (int q = 0; q < 2 * CB; ++q) {
-            if (c0 + (q >> 1) * 32 + 8 * (q & 1) < N) {
-#pragma unroll
-              for (int k = 0; k < 8; ++k) {
-                const float v = acc[q >> 1][8 * (q & 1) + k];
-                mx = fmaxf(mx, v);
-                mn = fminf(mn, v);
-              }
-            }
-          }
-        });
-    float m = mx == -INFINITY ? -INFINITY : (sc >= 0.0f ? mx * sc : mn * sc);  // base-2 domain
-    m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    const int row = m0 + qr;
-    if (hl == 0 && row < M) st_dev2(P + (size_t)row * S + (u % S), make_float2(m, 0.0f));
-    wait_stores();
-    __syncthreads();
-    uint64_t* jw = a.joins + rowblk;
-    if (t == 0) {
-      const uint64_t old = __hip_atomic_fetch_add(jw, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = ((uint32_t)old == (uint32_t)(S - 1)) ? 1 : 0;
-      gens[i] = (uint32_t)(old >> 32);
-    }
-    __syncthreads();
-    if (last) {
-      // the block's row maxima over its strips, all loads in flight
-      if (t < BM && m0 + t < M) {
-        const float2* Pr = P + (size_t)(m0 + t) * S;
-        float mm = -INFINITY;
-        for (int k0 = 0; k0 < S; k0 += 8) {
-          float2 v[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) v[k] = k0 + k < S ? ld_dev2(Pr + k0 + k) : make_float2(-INFINITY, 0.0f);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) mm = fmaxf(mm, v[k].x);
-        }
-        st_dev2(F + m0 + t, make_float2(mm, 0.0f));
-      }
-      wait_stores();
-      __syncthreads();
-      if (t == 0) __hip_atomic_fetch_add(jw, (1ull << 32) - (uint64_t)S, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-
-  // ------------------------------------------------ sweep 2: S.V, commit O
-  i = 0;
-  for (int u = g; u < units; u += G, ++i) {
+  for (int u = g; u < units; u += G) {
     const int rowblk = u / S, m0 = rowblk * BM, su = u % S, j0 = strip_first(u);
-    __syncthreads();
+    __syncthreads();  // every wave is done with the LDS of the previous strip
     if (qloaded != rowblk) load_q(m0);
     qloaded = rowblk;
-    if (t == 0) wait_generation(a.joins + rowblk, gens[i], a.err);
-    __syncthreads();
     const int row = m0 + qr;
-    const float mrow = row < M ? ld_dev2(F + row).x : 0.0f;
+    float m = -INFINITY;  // running row max, base-2 domain
     f32x16 oacc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -1684,18 +1644,18 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
       for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.0f;
     float lsum = 0.0f;
     f32x16 acc[CB];
-    // blocks alternate: 2b is K block j0 + b, 2b + 1 is V block j0 + b
-    segment(
+    // blocks alternate: 2x is K block j0 + x, 2x + 1 is V block j0 + x
+    stream(
         2 * strip_len(u),
-        [&](int b, char* slot) {
-          if (b & 1)
-            load_v(slot, j0 + (b >> 1));
+        [&](int x, char* slot) {
+          if (x & 1)
+            load_v(slot, j0 + (x >> 1));
           else
-            load_k(slot, j0 + (b >> 1));
+            load_k(slot, j0 + (x >> 1));
         },
-        [&](int b, const char* slot) {
-          if (b & 1) {
-            mma_ev(slot, acc, mrow, j0 + (b >> 1), oacc, lsum);
+        [&](bool odd, int x, const char* slot) {
+          if (odd) {
+            mma_ev(slot, acc, m, j0 + (x >> 1), oacc, lsum);
           } else {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb)
@@ -1704,7 +1664,7 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
             mma_qk(slot, acc);
           }
         });
-    lsum += __shfl_xor(lsum, 32, kWave);  // the row's sum over the strip
+    lsum += __shfl_xor(lsum, 32, kWave);  // the row's sum over the strip (relative to m)
     // this lane's output row, columns nb*32 + 16*hl + [0, 16)
     if (S == 1) {
       const float inv = 1.0f / lsum;
@@ -1737,7 +1697,7 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
         const float4 v = make_float4(oacc[nb][4 * c4], oacc[nb][4 * c4 + 1], oacc[nb][4 * c4 + 2], oacc[nb][4 * c4 + 3]);
         *reinterpret_cast<float4*>(stage + l32 * 512 + 16 * (k4 ^ l32)) = v;
       }
-    if (hl == 0 && row < M) st_dev2(Lp + (size_t)su * M + row, make_float2(lsum, 0.0f));
+    if (hl == 0 && row < M) st_dev2(Lp + (size_t)su * M + row, make_float2(m, lsum));
     __syncthreads();
 #pragma unroll 4
     for (int it = 0; it < 16; ++it) {
@@ -1759,14 +1719,16 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
     if (t == 0) wait_generation(jw2, gen2, a.err);
     __syncthreads();
     // strip su sums rows [su*R, su*R + R) of the block over the strips, in
-    // strip order, 8 columns per item, and divides by the summed row sums
+    // strip order, merging (max, sum, output) online: each strip weighted by
+    // 2^(its max - the running max), the running terms rescaled when the max
+    // rises; 8 columns per item, every load of 8 strips in flight at once
     const int R = (BM + S - 1) / S;
     for (int it = t; it < R * (DV / 8); it += THREADS) {
       const int r = su * R + it / (DV / 8), c8 = (it % (DV / 8)) * 8;
       const int orow = m0 + r;
       if (r >= BM || orow >= M || c8 >= Dv) continue;
       float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-      float ls = 0.0f;
+      float mb = -INFINITY, ls = 0.0f;
       for (int sk = 0; sk < S; sk += 8) {
         u32x4 v[8][2];
         float2 lv[8];
@@ -1775,15 +1737,23 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
 #pragma unroll
           for (int h = 0; h < 2; ++h)
             v[k][h] = bld16_dev(rOp, sk + k < S ? (uint32_t)((((size_t)(sk + k) * M + orow) * DV + c8 + 4 * h) * 4) : kOOB);
-          lv[k] = sk + k < S ? ld_dev2(Lp + (size_t)(sk + k) * M + orow) : make_float2(0.0f, 0.0f);
+          lv[k] = sk + k < S ? ld_dev2(Lp + (size_t)(sk + k) * M + orow) : make_float2(-INFINITY, 0.0f);
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (sk + k < S) {
+        for (int k = 0; k < 8; ++k) {
+          if (lv[k].x == -INFINITY) continue;  // a strip with no key (or past S)
+          if (lv[k].x > mb) {
+            const float sdn = __builtin_amdgcn_exp2f(mb - lv[k].x);  // 0 while mb = -inf
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] += __uint_as_float(v[k][e >> 2][e & 3]);
-            ls += lv[k].x;
+            for (int e = 0; e < 8; ++e) o[e] *= sdn;
+            ls *= sdn;
+            mb = lv[k].x;
           }
+          const float wgt = __builtin_amdgcn_exp2f(lv[k].x - mb);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = fmaf(wgt, __uint_as_float(v[k][e >> 2][e & 3]), o[e]);
+          ls = fmaf(wgt, lv[k].y, ls);
+        }
       }
       const float inv = 1.0f / ls;
       const u32x4 pk = {cvt_bf16x2(o[0] * inv, o[1] * inv), cvt_bf16x2(o[2] * inv, o[3] * inv),
