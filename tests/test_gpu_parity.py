@@ -271,6 +271,36 @@ def test_gemm_softmax_gemm_negative_scale_and_zero_q():
     assert rownorm_err(_b2b_run(d, M, N, D, Dv), o) <= TOL_BF16, cf.last_plan()
 
 
+def _b2b_inputs_from(q32, k32, v32, scale):
+    qb, kb, vb = (gen.f32_to_bf16_bits(np.ascontiguousarray(x, np.float32)) for x in (q32, k32, v32))
+    return {"q_bits": qb, "q": gen.bf16_bits_to_f32(qb), "k_bits": kb, "k": gen.bf16_bits_to_f32(kb),
+            "v_bits": vb, "v": gen.bf16_bits_to_f32(vb), "scale": float(np.float32(scale))}
+
+
+def test_gemm_softmax_gemm_rising_max():
+    """Key magnitudes ramp up along the row, with a large scale: each row's max
+    grows by far more than 2^8 across a strip's tiles, so the running reference
+    moves (and the accumulator is rescaled) mid-strip, and the strips' maxima
+    differ widely at the commit."""
+    M, N, D, Dv = 512, 4096, 64, 64
+    ramp = (1.0 + 6.0 * np.arange(N) / N).astype(np.float32)
+    d = _b2b_inputs_from(gen.normal(11, 0, (M, D)), gen.normal(11, 1, (N, D)) * ramp[:, None],
+                         gen.normal(11, 2, (N, Dv)), 0.5)
+    g = _b2b_run(d, M, N, D, Dv)
+    o = oracle.gemm_softmax_gemm(d["q"], d["k"], d["v"], d["scale"])
+    assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
+
+
+def test_gemm_softmax_gemm_zero_scale_is_the_mean():
+    """scale = 0: every weight is 1/N, so each output row is the column mean of V."""
+    M, N, D, Dv = 256, 2048, 32, 32
+    d = gen.gemm_softmax_gemm_inputs(seed=12, M=M, N=N, D=D, Dv=Dv)
+    d["scale"] = 0.0
+    g = _b2b_run(d, M, N, D, Dv)
+    o = np.repeat(d["v"].astype(np.float64).mean(axis=0)[None, :], M, axis=0)
+    assert rownorm_err(g, o) <= TOL_BF16
+
+
 def test_gemm_softmax_gemm_deterministic_on_one_workspace():
     """Fixed strip order in the partial-output sum: repeated calls (one workspace)
     give identical bits, also after a plain softmax call used the same join words."""
