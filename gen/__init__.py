@@ -10,9 +10,11 @@ from .inputs import (  # noqa: F401
     gemm_ln_inputs,
     gemm_softmax_gemm_inputs,
     gemm_softmax_inputs,
+    layernorm_affine_inputs,
     layernorm_inputs,
     normal,
     pow_bcast_add_inputs,
+    rmsnorm_inputs,
     softmax_inputs,
     uniform,
     WORKLOADS,

@@ -26,6 +26,8 @@ WORKLOADS = {
     "gemm_ln_4096x4096x1024": dict(M=4096, N=4096, K=1024),
     "gemm_softmax_8192x8192x128": dict(M=8192, N=8192, D=128),
     "gemm_softmax_gemm_8192x8192x128x128": dict(M=8192, N=8192, D=128, Dv=128),
+    "rmsnorm_750000x32": dict(rows=750000, cols=32),
+    "layernorm_affine_750000x32": dict(rows=750000, cols=32),
 }
 
 
@@ -74,6 +76,25 @@ def softmax_inputs(seed: int = 1, rows: int = 256, cols: int = 1024) -> dict:
 def layernorm_inputs(seed: int = 2, rows: int = 750000, cols: int = 32) -> dict:
     """Tall-skinny LayerNorm (no affine) workload: X fp32 [rows x cols] ~ U(-1, 1)."""
     return {"x": uniform(seed, 0, (rows, cols), -1.0, 1.0)}
+
+
+def rmsnorm_inputs(seed: int = 7, rows: int = 750000, cols: int = 32) -> dict:
+    """RMSNorm workload: X fp32 [rows x cols] ~ U(-1, 1), gain fp32 [cols] = 1 + N(0, 0.1), eps = 1e-5."""
+    return {
+        "x": uniform(seed, 0, (rows, cols), -1.0, 1.0),
+        "gamma": (np.float64(1.0) + normal(seed, 1, (cols,), std=0.1).astype(np.float64)).astype(np.float32),
+        "eps": 1e-5,
+    }
+
+
+def layernorm_affine_inputs(seed: int = 8, rows: int = 750000, cols: int = 32) -> dict:
+    """Affine LayerNorm workload: X fp32 [rows x cols] ~ U(-1, 1), gamma = 1 + N(0, 0.1), beta ~ N(0, 0.1)."""
+    return {
+        "x": uniform(seed, 0, (rows, cols), -1.0, 1.0),
+        "gamma": (np.float64(1.0) + normal(seed, 1, (cols,), std=0.1).astype(np.float64)).astype(np.float32),
+        "beta": normal(seed, 2, (cols,), std=0.1),
+        "eps": 1e-5,
+    }
 
 
 def pow_bcast_add_inputs(seed: int = 3, rows: int = 64, cols: int = 30000) -> dict:

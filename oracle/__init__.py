@@ -20,7 +20,9 @@ from .subgraphs import (  # noqa: F401
     gemm_ln,
     gemm_softmax,
     gemm_softmax_gemm,
+    layernorm_affine_rows,
     layernorm_rows,
     pow_bcast_add_softmax,
+    rmsnorm_rows,
     softmax_rows,
 )

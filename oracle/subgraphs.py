@@ -14,6 +14,9 @@ its reason in the design notes):
     before the softmax.
   * The back-to-back product takes its second operand V row-major [N x Dv]
     (keys by output columns): O = S.V with S the scaled row softmax above.
+  * RMSNorm divides by the root of the mean square (over the row length) plus
+    eps; its gain gamma, like LayerNorm's gamma and beta, is a length-cols
+    row-vector broadcast, and a missing gain is 1.
 """
 from __future__ import annotations
 
@@ -111,3 +114,31 @@ def gemm_softmax_gemm(q, k, v, scale: float) -> np.ndarray:
     """
     s = gemm_softmax(q, k, scale)
     return ops.matmul(s, ops.f64(v))
+
+
+def layernorm_affine_rows(x, gamma, beta, eps: float = 1e-5) -> np.ndarray:
+    """LayerNorm followed by its affine map: LayerNorm(x) * gamma + beta per row.
+
+    ComFuse, Frontend / Fusion Spec IR: LayerNorm among the stage DAGs the
+    recursive split covers, and 1-D parameters as row-vector broadcasts (Phi
+    patterns); the affine map is the output stage after the two reductions.
+    """
+    n = layernorm_rows(x, eps)
+    return ops.add_rowvec(ops.mul_rowvec(n, ops.f64(gamma)), ops.f64(beta))
+
+
+def rmsnorm_rows(x, gamma=None, eps: float = 1e-5) -> np.ndarray:
+    """RMSNorm: square -> row sum -> mean -> rsqrt(ms + eps) -> multiply (-> times gamma).
+
+    ComFuse, Stage-Stream Execution Model: one reduction stage whose broadcast
+    result scales the original values held from the first stage (bypass path);
+    the gain is a row-vector broadcast (Phi patterns).  ``gamma`` None means 1.
+    """
+    x = ops.f64(x)
+    n = x.shape[1]
+    ms = ops.rowsum(ops.map_square(x)) / np.float64(n)
+    r = ops.map_rsqrt_eps(ms, eps)
+    y = ops.mul_colvec(x, r)
+    if gamma is not None:
+        y = ops.mul_rowvec(y, ops.f64(gamma))
+    return y

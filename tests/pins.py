@@ -293,4 +293,54 @@ def pin_b2b_one_hot():
     _close(o, v[[3, 0, 7, 5]], 1e-12, 1e-12, what="B2B one-hot")
 
 
+# ------------------------------------------------------- RMSNorm, affine LayerNorm
+
+def _bf_rmsnorm(rows, eps, gamma=None):
+    out = []
+    for row in rows:
+        n = len(row)
+        ms = math.fsum(v * v for v in row) / n
+        r = 1.0 / math.sqrt(ms + eps)
+        out.append([v * r * (gamma[j] if gamma is not None else 1.0) for j, v in enumerate(row)])
+    return out
+
+
+def pin_rmsnorm_brute_force():
+    for (m, n) in [(3, 5), (2, 32), (4, 1)]:
+        rng = _rng(70 + n)
+        x, g = rng.normal(size=(m, n)), 1.0 + 0.1 * rng.normal(size=n)
+        _close(oracle.rmsnorm_rows(x, g, 1e-5), _bf_rmsnorm(x.tolist(), 1e-5, g.tolist()), 1e-13, 1e-15,
+               what=f"RMSNorm brute {m,n}")
+        _close(oracle.rmsnorm_rows(x, None, 1e-5), _bf_rmsnorm(x.tolist(), 1e-5), 1e-13, 1e-15,
+               what=f"RMSNorm brute no gain {m,n}")
+
+
+def pin_rmsnorm_closed_forms():
+    """Constant row c: y = c / sqrt(c^2 + eps).  Any row: mean(y^2) = ms / (ms + eps) (no gain).
+    A row and its negation map to negated outputs (no centering)."""
+    c, eps = 0.75, 1e-5
+    y = oracle.rmsnorm_rows(np.full((2, 16), c), None, eps)
+    _close(y, np.full((2, 16), c / math.sqrt(c * c + eps)), 1e-15, what="RMSNorm constant row")
+    x = _rng(72).uniform(-1, 1, size=(6, 32))
+    ms = np.mean(x * x, axis=1)
+    _close(np.mean(oracle.rmsnorm_rows(x, None, eps) ** 2, axis=1), ms / (ms + eps), 1e-13, what="RMSNorm mean square")
+    _close(oracle.rmsnorm_rows(-x, None, eps), -oracle.rmsnorm_rows(x, None, eps), 0.0, 0.0, what="RMSNorm odd")
+
+
+def pin_layernorm_affine_brute_force():
+    for (m, n) in [(3, 6), (2, 32)]:
+        rng = _rng(74 + n)
+        x, g, b = rng.normal(size=(m, n)), 1.0 + 0.1 * rng.normal(size=n), 0.1 * rng.normal(size=n)
+        nrm = _bf_layernorm(x.tolist(), 1e-5)
+        yb = [[nrm[i][j] * g[j] + b[j] for j in range(n)] for i in range(m)]
+        _close(oracle.layernorm_affine_rows(x, g, b, 1e-5), yb, 1e-13, 1e-15, what=f"affine LN brute {m,n}")
+
+
+def pin_layernorm_affine_constant_row():
+    """A constant row normalises to 0, so the output is beta."""
+    b = _rng(76).normal(size=12)
+    y = oracle.layernorm_affine_rows(np.full((3, 12), -2.5), _rng(77).normal(size=12), b, 1e-5)
+    assert np.array_equal(y, np.repeat(b[None, :], 3, axis=0)), "affine LN constant row is not beta"
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

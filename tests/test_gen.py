@@ -53,3 +53,7 @@ def test_workload_shapes():
     assert d["q_bits"].shape == (8, 4) and d["k_bits"].shape == (16, 4) and d["v_bits"].shape == (16, 12)
     assert np.array_equal(gen.bf16_bits_to_f32(d["v_bits"]), d["v"])
     assert d["scale"] == float(np.float32(0.5))
+    d = gen.rmsnorm_inputs(rows=5, cols=7)
+    assert d["x"].shape == (5, 7) and d["gamma"].shape == (7,) and d["x"].dtype == np.float32
+    d = gen.layernorm_affine_inputs(rows=5, cols=7)
+    assert d["gamma"].shape == (7,) and d["beta"].shape == (7,)

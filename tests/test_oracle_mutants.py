@@ -54,6 +54,18 @@ def _b2b_unnormalized(q, k, v, scale):
     return ops.matmul(np.exp(s - s.max(axis=1)[:, None]), ops.f64(v))
 
 
+def _rms_centered(x, gamma=None, eps=1e-5):
+    x = ops.f64(x)
+    c = ops.sub_colvec(x, ops.rowsum(x) / x.shape[1])
+    y = ops.mul_colvec(c, ops.map_rsqrt_eps(ops.rowsum(ops.map_square(c)) / x.shape[1], eps))
+    return y if gamma is None else ops.mul_rowvec(y, ops.f64(gamma))
+
+
+def _ln_affine_beta_scaled(x, gamma, beta, eps=1e-5):
+    n = subgraphs.layernorm_rows(x, eps)
+    return ops.mul_rowvec(ops.add_rowvec(n, ops.f64(beta)), ops.f64(gamma))
+
+
 def _pow_row_broadcast(x, v, p=1.5):
     x = ops.f64(x)
     pv = ops.map_pow(ops.f64(v), p)
@@ -99,6 +111,8 @@ MUTANTS = {
     "pow_row_broadcast": (subgraphs, "pow_bcast_add_softmax", _pow_row_broadcast),
     "b2b_softmax_over_wrong_axis": (subgraphs, "gemm_softmax_gemm", _b2b_softmax_over_keys_axis0),
     "b2b_unnormalized": (subgraphs, "gemm_softmax_gemm", _b2b_unnormalized),
+    "rmsnorm_centers": (subgraphs, "rmsnorm_rows", _rms_centered),
+    "ln_affine_beta_scaled": (subgraphs, "layernorm_affine_rows", _ln_affine_beta_scaled),
 }
 
 
