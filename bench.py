@@ -5,9 +5,10 @@ path) on its workload, inputs resident in HBM.  Each call is bracketed by HIP
 events on the stream it runs on, with a 512 MiB cache-evicting read sweep
 before it (outside the events) so every call reads its inputs from HBM.  The headline
 line reports the tall-skinny LayerNorm workload (750000 x 32 fp32); the other
-four workloads are reported under "per_config" in the same line, and so is the
-back-to-back GEMM with the softmax between (8192 x 8192 x 128 x 128), which is
-timed per kernel but is not part of the step.
+four workloads are reported under "per_config" in the same line, and so are
+the back-to-back GEMM with the softmax between (8192 x 8192 x 128 x 128),
+RMSNorm and affine LayerNorm (750000 x 32 fp32), which are timed per kernel
+but are not part of the step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
                        [--no-unfused] [--no-cpu] [--calibrate-copy]
@@ -45,6 +46,8 @@ KERNEL_SOURCES = {
     "gemm_ln_4096x4096x1024": ("gemm.hip", "dev.hpp"),
     "gemm_softmax_8192x8192x128": ("gemm.hip", "dev.hpp"),
     "gemm_softmax_gemm_8192x8192x128x128": ("gemm.hip", "dev.hpp"),
+    "rmsnorm_750000x32": ("stitch.hip", "dev.hpp"),
+    "layernorm_affine_750000x32": ("stitch.hip", "dev.hpp"),
 }
 
 
@@ -145,6 +148,22 @@ class Workload:
             scale = d["scale"]
             call = lambda b, ws, u: cf.cf_gemm_softmax_gemm(b["Q"], b["K"], b["V"], scale, b["Y"], ws=ws, unfused=u)
             self.op, self.dims = cf.CF_OP_GEMM_SOFTMAX_GEMM, (M, N, D)
+        elif name == "rmsnorm_750000x32":
+            d = gen.rmsnorm_inputs(seed=7)
+            self.inp = d
+            bufs = {"X": d32(d["x"]), "G": d32(d["gamma"]), "Y": torch.empty(750000, 32, device=dev)}
+            self.bytes, self.flops = 2 * d["x"].nbytes + d["gamma"].nbytes, 0
+            call = lambda b, ws, u: cf.cf_stitch_rmsnorm(b["X"], b["G"], b["Y"], 1e-5, ws=ws, unfused=u)
+            self.op, self.dims = cf.CF_OP_STITCH_RMSNORM, (750000, 32, 0)
+        elif name == "layernorm_affine_750000x32":
+            d = gen.layernorm_affine_inputs(seed=8)
+            self.inp = d
+            bufs = {"X": d32(d["x"]), "G": d32(d["gamma"]), "B": d32(d["beta"]),
+                    "Y": torch.empty(750000, 32, device=dev)}
+            self.bytes, self.flops = 2 * d["x"].nbytes + d["gamma"].nbytes + d["beta"].nbytes, 0
+            call = lambda b, ws, u: cf.cf_stitch_layernorm_affine(b["X"], b["G"], b["B"], b["Y"], 1e-5, ws=ws,
+                                                                  unfused=u)
+            self.op, self.dims = cf.CF_OP_STITCH_LAYERNORM_AFFINE, (750000, 32, 0)
         else:
             raise ValueError(name)
         self.bound = "mfma" if name in ("gemm_ln_4096x4096x1024", "gemm_softmax_gemm_8192x8192x128x128") else "hbm"
@@ -170,13 +189,17 @@ class Workload:
             return oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"], d["beta"], 1e-5)
         if self.name == "gemm_softmax_gemm_8192x8192x128x128":
             return oracle.gemm_softmax_gemm(d["q"], d["k"], d["v"], d["scale"])
+        if self.name == "rmsnorm_750000x32":
+            return oracle.rmsnorm_rows(d["x"], d["gamma"], 1e-5)
+        if self.name == "layernorm_affine_750000x32":
+            return oracle.layernorm_affine_rows(d["x"], d["gamma"], d["beta"], 1e-5)
         return oracle.gemm_softmax(d["q"], d["k"], d["scale"])
 
 
 WORKLOAD_NAMES = ["softmax_256x1024", "layernorm_750000x32", "pow_bcast_add_softmax_64x30000",
                   "gemm_ln_4096x4096x1024", "gemm_softmax_8192x8192x128"]
 # measured per kernel (and unfused) but outside the step
-EXTRA_NAMES = ["gemm_softmax_gemm_8192x8192x128x128"]
+EXTRA_NAMES = ["gemm_softmax_gemm_8192x8192x128x128", "rmsnorm_750000x32", "layernorm_affine_750000x32"]
 
 
 def main():

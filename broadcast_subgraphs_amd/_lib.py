@@ -18,7 +18,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "cf.h")
 
 CF_OK, CF_EINVAL, CF_EUNSUPPORTED, CF_EALIGN, CF_EWORKSPACE, CF_EOCCUPANCY, CF_EHIP = range(7)
 (CF_OP_STITCH_SOFTMAX, CF_OP_STITCH_LAYERNORM, CF_OP_STITCH_POW_BCAST_ADD, CF_OP_GEMM_LN, CF_OP_GEMM_SOFTMAX,
- CF_OP_GEMM_SOFTMAX_GEMM) = 1, 2, 3, 4, 5, 6
+ CF_OP_GEMM_SOFTMAX_GEMM, CF_OP_STITCH_LAYERNORM_AFFINE, CF_OP_STITCH_RMSNORM) = 1, 2, 3, 4, 5, 6, 7, 8
 
 _lib = None
 _lock = threading.Lock()
@@ -37,12 +37,16 @@ _SIGS = {
     "cf_stitch_softmax": (_ST, [_P, _P, _I64, _I64, _P, _SZ, _P]),
     "cf_stitch_layernorm": (_ST, [_P, _P, _I64, _I64, _F, _P, _SZ, _P]),
     "cf_stitch_pow_bcast_add": (_ST, [_P, _P, _F, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "cf_stitch_layernorm_affine": (_ST, [_P, _P, _P, _P, _I64, _I64, _F, _P, _SZ, _P]),
+    "cf_stitch_rmsnorm": (_ST, [_P, _P, _P, _I64, _I64, _F, _P, _SZ, _P]),
     "cf_gemm_ln": (_ST, [_P, _P, _P, _P, _P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_gemm_softmax": (_ST, [_P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_gemm_softmax_gemm": (_ST, [_P, _P, _P, _F, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_unfused_stitch_softmax": (_ST, [_P, _P, _I64, _I64, _P, _SZ, _P]),
     "cf_unfused_stitch_layernorm": (_ST, [_P, _P, _I64, _I64, _F, _P, _SZ, _P]),
     "cf_unfused_stitch_pow_bcast_add": (_ST, [_P, _P, _F, _P, _P, _I64, _I64, _P, _SZ, _P]),
+    "cf_unfused_stitch_layernorm_affine": (_ST, [_P, _P, _P, _P, _I64, _I64, _F, _P, _SZ, _P]),
+    "cf_unfused_stitch_rmsnorm": (_ST, [_P, _P, _P, _I64, _I64, _F, _P, _SZ, _P]),
     "cf_unfused_gemm_ln": (_ST, [_P, _P, _P, _P, _P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_unfused_gemm_softmax": (_ST, [_P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_unfused_gemm_softmax_gemm": (_ST, [_P, _P, _P, _F, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
@@ -250,6 +254,36 @@ def cf_gemm_softmax(Q, K, scale, S, ws=None, stream=None, unfused=False):
     p, n, w = _ws_args(CF_OP_GEMM_SOFTMAX, M, N, D, ws, Q.device, st, unfused)
     name = "cf_unfused_gemm_softmax" if unfused else "cf_gemm_softmax"
     _check(name, getattr(lib(), name)(_ptr(Q), _ptr(K), float(scale), _ptr(S), M, N, D, p, n, st))
+    return w
+
+
+def cf_stitch_layernorm_affine(x, gamma, beta, y, eps=1e-5, ws=None, stream=None, unfused=False):
+    """x, y [rows, cols], gamma, beta [cols]: fp32 tensors; y = LayerNorm(x) * gamma + beta."""
+    torch = _torch()
+    _need(x, torch.float32, "x", 2)
+    _need(y, torch.float32, "y", 2)
+    _need(gamma, torch.float32, "gamma", 1)
+    _need(beta, torch.float32, "beta", 1)
+    rows, cols = x.shape
+    st = _stream(stream)
+    p, n, w = _ws_args(CF_OP_STITCH_LAYERNORM_AFFINE, rows, cols, 0, ws, x.device, st, unfused)
+    name = "cf_unfused_stitch_layernorm_affine" if unfused else "cf_stitch_layernorm_affine"
+    _check(name, getattr(lib(), name)(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, cols, float(eps), p, n, st))
+    return w
+
+
+def cf_stitch_rmsnorm(x, gamma, y, eps=1e-5, ws=None, stream=None, unfused=False):
+    """x, y [rows, cols] fp32, gamma [cols] fp32 or None (gain 1); y = x * rsqrt(mean(x^2) + eps) * gamma."""
+    torch = _torch()
+    _need(x, torch.float32, "x", 2)
+    _need(y, torch.float32, "y", 2)
+    if gamma is not None:
+        _need(gamma, torch.float32, "gamma", 1)
+    rows, cols = x.shape
+    st = _stream(stream)
+    p, n, w = _ws_args(CF_OP_STITCH_RMSNORM, rows, cols, 0, ws, x.device, st, unfused)
+    name = "cf_unfused_stitch_rmsnorm" if unfused else "cf_stitch_rmsnorm"
+    _check(name, getattr(lib(), name)(_ptr(x), _ptr(gamma), _ptr(y), rows, cols, float(eps), p, n, st))
     return w
 
 

@@ -170,14 +170,19 @@ void record_rows_plan(const char* name, const RowPlan& p, int64_t rows, int64_t 
 }
 
 cf_status run_rows(const char* name, int op, const float* x, float* y, float* y_pre, const float* v, float pw,
-                   float eps, int64_t rows, int64_t cols, void* ws, size_t ws_bytes, hipStream_t st) {
+                   float eps, int64_t rows, int64_t cols, void* ws, size_t ws_bytes, hipStream_t st,
+                   const float* gamma, const float* beta) {
   if (!x || !y || rows <= 0 || cols <= 0) return CF_EINVAL;
   if (op == kPowSoftmax && !v) return CF_EINVAL;
-  if (op == kLayerNorm && !(eps >= 0.0f)) return CF_EINVAL;
+  if (is_norm(op) && !(eps >= 0.0f)) return CF_EINVAL;
+  if (op == kLayerNormAffine && (!gamma || !beta)) return CF_EINVAL;
   const size_t bytes = (size_t)rows * cols * sizeof(float);
   if (overlap(x, bytes, y, bytes)) return CF_EINVAL;
   if (y_pre && (overlap(y_pre, bytes, y, bytes) || overlap(y_pre, bytes, x, bytes))) return CF_EINVAL;
-  const bool vec_ok = aligned16(x) && aligned16(y) && (!y_pre || aligned16(y_pre));
+  const size_t vbytes = (size_t)cols * sizeof(float);
+  if ((gamma && overlap(y, bytes, gamma, vbytes)) || (beta && overlap(y, bytes, beta, vbytes))) return CF_EINVAL;
+  const bool vec_ok = aligned16(x) && aligned16(y) && (!y_pre || aligned16(y_pre)) && (!gamma || aligned16(gamma)) &&
+                      (!beta || aligned16(beta));
   RowPlan p;
   cf_status s = plan_rows(op, rows, cols, vec_ok, &p);
   if (s != CF_OK) return s;
@@ -185,6 +190,7 @@ cf_status run_rows(const char* name, int op, const float* x, float* y, float* y_
   if (need > 0 && (!ws || ws_bytes < need)) return CF_EWORKSPACE;
   RowArgs a{};
   a.x = x; a.y = y; a.y_pre = y_pre; a.v = v; a.p = pw; a.eps = eps;
+  a.gamma = gamma; a.beta = beta;
   a.rows = rows; a.cols = cols;
   if (need > 0) {
     const WsLayout L = ws_layout(rows * p.split * 4);
@@ -402,8 +408,14 @@ size_t cf_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2) {
   switch (op) {
     case CF_OP_STITCH_SOFTMAX:
     case CF_OP_STITCH_LAYERNORM:
-    case CF_OP_STITCH_POW_BCAST_ADD: {
-      const int rop = op == CF_OP_STITCH_SOFTMAX ? kSoftmax : (op == CF_OP_STITCH_LAYERNORM ? kLayerNorm : kPowSoftmax);
+    case CF_OP_STITCH_POW_BCAST_ADD:
+    case CF_OP_STITCH_LAYERNORM_AFFINE:
+    case CF_OP_STITCH_RMSNORM: {
+      const int rop = op == CF_OP_STITCH_SOFTMAX          ? kSoftmax
+                      : op == CF_OP_STITCH_LAYERNORM      ? kLayerNorm
+                      : op == CF_OP_STITCH_POW_BCAST_ADD  ? kPowSoftmax
+                      : op == CF_OP_STITCH_LAYERNORM_AFFINE ? kLayerNormAffine
+                                                            : kRmsNorm;
       RowPlan p;
       if (plan_rows(rop, d0, d1, true, &p) != CF_OK) return (size_t)-1;
       const size_t a = rows_ws_bytes(p, d0);
@@ -433,18 +445,32 @@ size_t cf_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2) {
 
 cf_status cf_stitch_softmax(const float* x, float* y, int64_t rows, int64_t cols, void* ws, size_t ws_bytes,
                             hipStream_t stream) {
-  return run_rows("cf_stitch_softmax", kSoftmax, x, y, nullptr, nullptr, 0.f, 0.f, rows, cols, ws, ws_bytes, stream);
+  return run_rows("cf_stitch_softmax", kSoftmax, x, y, nullptr, nullptr, 0.f, 0.f, rows, cols, ws, ws_bytes, stream,
+                  nullptr, nullptr);
 }
 
 cf_status cf_stitch_layernorm(const float* x, float* y, int64_t rows, int64_t cols, float eps, void* ws,
                               size_t ws_bytes, hipStream_t stream) {
   return run_rows("cf_stitch_layernorm", kLayerNorm, x, y, nullptr, nullptr, 0.f, eps, rows, cols, ws, ws_bytes,
-                  stream);
+                  stream, nullptr, nullptr);
 }
 
 cf_status cf_stitch_pow_bcast_add(const float* x, const float* v, float p, float* y, float* y_pre, int64_t rows,
                                   int64_t cols, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return run_rows("cf_stitch_pow_bcast_add", kPowSoftmax, x, y, y_pre, v, p, 0.f, rows, cols, ws, ws_bytes, stream);
+  return run_rows("cf_stitch_pow_bcast_add", kPowSoftmax, x, y, y_pre, v, p, 0.f, rows, cols, ws, ws_bytes, stream,
+                  nullptr, nullptr);
+}
+
+cf_status cf_stitch_layernorm_affine(const float* x, const float* gamma, const float* beta, float* y, int64_t rows,
+                                     int64_t cols, float eps, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_rows("cf_stitch_layernorm_affine", kLayerNormAffine, x, y, nullptr, nullptr, 0.f, eps, rows, cols, ws,
+                  ws_bytes, stream, gamma, beta);
+}
+
+cf_status cf_stitch_rmsnorm(const float* x, const float* gamma, float* y, int64_t rows, int64_t cols, float eps,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_rows("cf_stitch_rmsnorm", kRmsNorm, x, y, nullptr, nullptr, 0.f, eps, rows, cols, ws, ws_bytes, stream,
+                  gamma, nullptr);
 }
 
 static cf_status run_gemm(const char* name, int epi, bool nn, GemmArgs a, void* ws, size_t ws_bytes,
@@ -567,6 +593,8 @@ size_t cf_unfused_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2) {
     case CF_OP_STITCH_SOFTMAX: n = 2 * vec + 2 * full; break;
     case CF_OP_STITCH_LAYERNORM: n = 4 * vec + 2 * full; break;
     case CF_OP_STITCH_POW_BCAST_ADD: n = 3 * vec + 3 * full; break;
+    case CF_OP_STITCH_LAYERNORM_AFFINE: n = 4 * vec + 3 * full; break;
+    case CF_OP_STITCH_RMSNORM: n = 3 * vec + 2 * full; break;
     case CF_OP_GEMM_LN: n = d2 > 0 ? 4 * vec + 3 * full : (size_t)-1; break;
     case CF_OP_GEMM_SOFTMAX: n = d2 > 0 ? 2 * vec + 3 * full : (size_t)-1; break;
     case CF_OP_GEMM_SOFTMAX_GEMM:  // + S bf16 [M x N] + the second product fp32 [M x (Dv <= 128)]
@@ -647,6 +675,45 @@ cf_status cf_unfused_stitch_pow_bcast_add(const float* x, const float* v, float 
   CF_TRY(u_map(v, pv, rows, 2, p, 0.f, stream));
   CF_TRY(u_bcast_col(x, pv, Y, rows, cols, 3, stream));
   return unfused_softmax_chain(Y, y, rows, cols, chain, stream);
+}
+
+cf_status cf_unfused_stitch_layernorm_affine(const float* x, const float* gamma, const float* beta, float* y,
+                                             int64_t rows, int64_t cols, float eps, void* ws, size_t ws_bytes,
+                                             hipStream_t stream) {
+  if (!x || !y || !gamma || !beta || rows <= 0 || cols <= 0 || !(eps >= 0.f)) return CF_EINVAL;
+  if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_STITCH_LAYERNORM_AFFINE, rows, cols, 0)) return CF_EWORKSPACE;
+  char* w = unfused_base(ws);
+  const size_t vec = align_up((size_t)rows * 4, 256), full = align_up((size_t)rows * cols * 4, 256);
+  float* n = reinterpret_cast<float*>(w + 4 * vec + 2 * full);
+  CF_TRY(unfused_ln_chain(x, n, rows, cols, eps, w, stream));          // 7 kernels
+  float* t = reinterpret_cast<float*>(w + 4 * vec);                     // the chain's first full buffer, free now
+  CF_TRY(u_bcast_row(n, gamma, t, rows, cols, 2, stream));              // * gamma
+  CF_TRY(u_bcast_row(t, beta, y, rows, cols, 3, stream));               // + beta
+  g_last_plan = "{\"call\":\"cf_unfused_stitch_layernorm_affine\",\"kernels\":9}";
+  return CF_OK;
+}
+
+cf_status cf_unfused_stitch_rmsnorm(const float* x, const float* gamma, float* y, int64_t rows, int64_t cols, float eps,
+                                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!x || !y || rows <= 0 || cols <= 0 || !(eps >= 0.f)) return CF_EINVAL;
+  if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_STITCH_RMSNORM, rows, cols, 0)) return CF_EWORKSPACE;
+  char* w = unfused_base(ws);
+  const size_t vec = align_up((size_t)rows * 4, 256), full = align_up((size_t)rows * cols * 4, 256);
+  float* ss = reinterpret_cast<float*>(w);
+  float* r = reinterpret_cast<float*>(w + vec);
+  float* q = reinterpret_cast<float*>(w + 3 * vec);
+  float* t = reinterpret_cast<float*>(w + 3 * vec + full);
+  CF_TRY(u_map(x, q, rows * cols, 1, 0.f, 0.f, stream));              // square
+  CF_TRY(u_rowreduce(q, ss, rows, cols, 0, stream));                  // row sum
+  CF_TRY(u_map(ss, r, rows, 3, eps, 1.0f / (float)cols, stream));     // rsqrt(ss / n + eps)
+  if (gamma) {
+    CF_TRY(u_bcast_col(x, r, t, rows, cols, 2, stream));              // x * r
+    CF_TRY(u_bcast_row(t, gamma, y, rows, cols, 2, stream));          // * gamma
+  } else {
+    CF_TRY(u_bcast_col(x, r, y, rows, cols, 2, stream));
+  }
+  g_last_plan = "{\"call\":\"cf_unfused_stitch_rmsnorm\",\"kernels\":5}";
+  return CF_OK;
 }
 
 cf_status cf_unfused_gemm_ln(const cf_bf16* A, const cf_bf16* W, const float* bias, const cf_bf16* R,

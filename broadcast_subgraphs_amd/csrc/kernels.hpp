@@ -8,13 +8,18 @@
 
 namespace cf {
 
-enum RowOp { kSoftmax = 0, kLayerNorm = 1, kPowSoftmax = 2 };
+enum RowOp { kSoftmax = 0, kLayerNorm = 1, kPowSoftmax = 2, kLayerNormAffine = 3, kRmsNorm = 4 };
+// LayerNorm (with or without its affine map) and RMSNorm: one reduction
+// family; RMSNorm is the LayerNorm stage chain with the mean held at 0.
+constexpr bool is_norm(int op) { return op == kLayerNorm || op == kLayerNormAffine || op == kRmsNorm; }
 
 struct RowArgs {
   const float* x;
   float* y;
   float* y_pre;     // pow-softmax only, nullable
   const float* v;   // pow-softmax only
+  const float* gamma;  // affine LayerNorm: [cols]; RMSNorm: [cols] or null (gain 1)
+  const float* beta;   // affine LayerNorm: [cols]
   float p;
   float eps;
   int64_t rows;

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(BLOCK) void k_rows(RowArgs a) {
           load_frag<W>(x[r][v], xr + c0);
         } else {
 #pragma unroll
-          for (int e = 0; e < W; ++e) x[r][v][e] = (OP == kLayerNorm) ? 0.0f : -INFINITY;
+          for (int e = 0; e < W; ++e) x[r][v][e] = is_norm(OP) ? 0.0f : -INFINITY;
         }
       }
     }
@@ -187,17 +187,44 @@ __global__ __launch_bounds__(BLOCK) void k_rows(RowArgs a) {
           }
         }
       }
-    } else {  // kLayerNorm
+    } else {  // the norms: LayerNorm (affine or not), RMSNorm (mean held at 0)
       const float inv_n = 1.0f / (float)cols;
+      // gain / bias fragments of the lane's columns, loaded beside x (one round trip)
+      constexpr bool GAIN = OP == kLayerNormAffine || OP == kRmsNorm, BIAS = OP == kLayerNormAffine;
+      float gv[NV][W], bv[NV][W];
+      if constexpr (GAIN) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const int64_t c0 = (int64_t)(v * LPR + q) * W;
+          if (a.gamma != nullptr && c0 < cols) {
+            load_frag<W>(gv[v], a.gamma + c0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < W; ++e) gv[v][e] = 1.0f;
+          }
+          if constexpr (BIAS) {
+            if (c0 < cols) {
+              load_frag<W>(bv[v], a.beta + c0);
+            } else {
+#pragma unroll
+              for (int e = 0; e < W; ++e) bv[v][e] = 0.0f;
+            }
+          }
+        }
+      }
       float mu[RPI];
 #pragma unroll
       for (int r = 0; r < RPI; ++r) {
-        float s = 0.0f;
+        if constexpr (OP == kRmsNorm) {
+          mu[r] = 0.0f;
+        } else {
+          float s = 0.0f;
 #pragma unroll
-        for (int v = 0; v < NV; ++v)
+          for (int v = 0; v < NV; ++v)
 #pragma unroll
-          for (int e = 0; e < W; ++e) s += x[r][v][e];
-        mu[r] = row_reduce<OpSum, LPR, BLOCK>(s, red, slot, group, wave_in_row) * inv_n;
+            for (int e = 0; e < W; ++e) s += x[r][v][e];
+          mu[r] = row_reduce<OpSum, LPR, BLOCK>(s, red, slot, group, wave_in_row) * inv_n;
+        }
       }
       float rs[RPI];
 #pragma unroll
@@ -226,7 +253,12 @@ __global__ __launch_bounds__(BLOCK) void k_rows(RowArgs a) {
           const int64_t c0 = (int64_t)(v * LPR + q) * W;
           if (c0 < cols) {
 #pragma unroll
-            for (int e = 0; e < W; ++e) x[r][v][e] *= rs[r];
+            for (int e = 0; e < W; ++e) {
+              float o = x[r][v][e] * rs[r];
+              if constexpr (GAIN) o *= gv[v][e];
+              if constexpr (BIAS) o += bv[v][e];
+              x[r][v][e] = o;
+            }
             store_frag<W>(a.y + row * cols + c0, x[r][v]);
           }
         }
@@ -271,7 +303,7 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
         load_frag<W>(x[v], xr + c0);
       } else {
 #pragma unroll
-        for (int e = 0; e < W; ++e) x[v][e] = (OP == kLayerNorm) ? 0.0f : -INFINITY;
+        for (int e = 0; e < W; ++e) x[v][e] = is_norm(OP) ? 0.0f : -INFINITY;
       }
     }
 
@@ -313,13 +345,16 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
       part0 = m;
       part1 = l;
     } else {
-      float sx = 0.0f;
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-#pragma unroll
-        for (int e = 0; e < W; ++e) sx += x[v][e];
       const float n_loc = cend > cbeg ? (float)(cend - cbeg) : 0.0f;
-      const float mean_loc = row_reduce<OpSum, kBlock>(sx, red, slot, 0, wave_in_row) / fmaxf(n_loc, 1.0f);
+      float mean_loc = 0.0f;  // RMSNorm: the mean is held at 0 throughout
+      if constexpr (OP != kRmsNorm) {
+        float sx = 0.0f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+          for (int e = 0; e < W; ++e) sx += x[v][e];
+        mean_loc = row_reduce<OpSum, kBlock>(sx, red, slot, 0, wave_in_row) / fmaxf(n_loc, 1.0f);
+      }
       float sq = 0.0f;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
@@ -393,12 +428,26 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
       }
       const float rs = rsqrtf(M2 / (float)cols + a.eps);
       const float shift = part1 - mean;  // this member's values are x - mean_loc
+      constexpr bool GAIN = OP == kLayerNormAffine || OP == kRmsNorm, BIAS = OP == kLayerNormAffine;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         const int64_t c0 = cbeg + (int64_t)(v * kBlock + t) * W;
         if (c0 < cend) {
+          float gv[W], bv[W];
+          if (GAIN && a.gamma != nullptr) {
+            load_frag<W>(gv, a.gamma + c0);
+          } else {
 #pragma unroll
-          for (int e = 0; e < W; ++e) x[v][e] = (x[v][e] + shift) * rs;
+            for (int e = 0; e < W; ++e) gv[e] = 1.0f;
+          }
+          if (BIAS) {
+            load_frag<W>(bv, a.beta + c0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < W; ++e) bv[e] = 0.0f;
+          }
+#pragma unroll
+          for (int e = 0; e < W; ++e) x[v][e] = fmaf((x[v][e] + shift) * rs, gv[e], bv[e]);
           store_frag<W>(a.y + row * cols + c0, x[v]);
         }
       }
@@ -447,15 +496,20 @@ static hipError_t launch_rows_w(const RowPlan& pl, const RowArgs& a, hipStream_t
   return hipErrorInvalidConfiguration;
 }
 
-hipError_t launch_rows(int op, const RowPlan& pl, const RowArgs& a, hipStream_t st) {
-  if (pl.w == 4) {
-    if (op == kSoftmax) return launch_rows_w<kSoftmax, 4>(pl, a, st);
-    if (op == kLayerNorm) return launch_rows_w<kLayerNorm, 4>(pl, a, st);
-    return launch_rows_w<kPowSoftmax, 4>(pl, a, st);
+template <int W>
+static hipError_t launch_rows_op(int op, const RowPlan& pl, const RowArgs& a, hipStream_t st) {
+  switch (op) {
+    case kSoftmax: return launch_rows_w<kSoftmax, W>(pl, a, st);
+    case kLayerNorm: return launch_rows_w<kLayerNorm, W>(pl, a, st);
+    case kPowSoftmax: return launch_rows_w<kPowSoftmax, W>(pl, a, st);
+    case kLayerNormAffine: return launch_rows_w<kLayerNormAffine, W>(pl, a, st);
+    case kRmsNorm: return launch_rows_w<kRmsNorm, W>(pl, a, st);
   }
-  if (op == kSoftmax) return launch_rows_w<kSoftmax, 1>(pl, a, st);
-  if (op == kLayerNorm) return launch_rows_w<kLayerNorm, 1>(pl, a, st);
-  return launch_rows_w<kPowSoftmax, 1>(pl, a, st);
+  return hipErrorInvalidConfiguration;
+}
+
+hipError_t launch_rows(int op, const RowPlan& pl, const RowArgs& a, hipStream_t st) {
+  return pl.w == 4 ? launch_rows_op<4>(op, pl, a, st) : launch_rows_op<1>(op, pl, a, st);
 }
 
 // Occupancy (resident workgroups per CU) of the split kernel for a plan.
@@ -466,6 +520,7 @@ hipError_t rows_split_occupancy(int op, const RowPlan& pl, int* per_cu) {
 #define CF_OCC_NV(OPV, WV) CF_OCC(OPV, 1, WV) CF_OCC(OPV, 2, WV) CF_OCC(OPV, 4, WV) CF_OCC(OPV, 8, WV) CF_OCC(OPV, 16, WV)
   CF_OCC_NV(kSoftmax, 4) CF_OCC_NV(kLayerNorm, 4) CF_OCC_NV(kPowSoftmax, 4)
   CF_OCC_NV(kSoftmax, 1) CF_OCC_NV(kLayerNorm, 1) CF_OCC_NV(kPowSoftmax, 1)
+  CF_OCC_NV(kLayerNormAffine, 4) CF_OCC_NV(kRmsNorm, 4) CF_OCC_NV(kLayerNormAffine, 1) CF_OCC_NV(kRmsNorm, 1)
 #undef CF_OCC_NV
 #undef CF_OCC
   return hipErrorInvalidConfiguration;

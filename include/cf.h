@@ -66,7 +66,9 @@ enum {
   CF_OP_STITCH_POW_BCAST_ADD = 3, /* d0 = rows, d1 = cols            */
   CF_OP_GEMM_LN = 4,              /* d0 = M, d1 = N, d2 = K          */
   CF_OP_GEMM_SOFTMAX = 5,         /* d0 = M, d1 = N, d2 = D          */
-  CF_OP_GEMM_SOFTMAX_GEMM = 6     /* d0 = M, d1 = N, d2 = D (any Dv <= 128) */
+  CF_OP_GEMM_SOFTMAX_GEMM = 6,    /* d0 = M, d1 = N, d2 = D (any Dv <= 128) */
+  CF_OP_STITCH_LAYERNORM_AFFINE = 7, /* d0 = rows, d1 = cols         */
+  CF_OP_STITCH_RMSNORM = 8        /* d0 = rows, d1 = cols            */
 };
 
 /* Workspace bytes the fused call needs for this shape on the current device
@@ -115,6 +117,24 @@ cf_status cf_stitch_layernorm(const float* x, float* y, int64_t rows, int64_t co
 cf_status cf_stitch_pow_bcast_add(const float* x, const float* v, float p, float* y, float* y_pre,
                                   int64_t rows, int64_t cols, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/* y = LayerNorm(x) * gamma + beta over each row (population variance, eps
+ * inside the root); gamma, beta fp32 [cols], row-vector broadcasts, not
+ * NULL, not overlapping y.  Same planning and rules as cf_stitch_layernorm.
+ * [ComFuse] Frontend / Fusion Spec IR (LayerNorm among the stage DAGs the
+ * split at reduction nodes covers; 1-D parameters as row-vector broadcasts,
+ * the Phi patterns). */
+cf_status cf_stitch_layernorm_affine(const float* x, const float* gamma, const float* beta, float* y,
+                                     int64_t rows, int64_t cols, float eps, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
+/* y = x * rsqrt(mean(x^2) + eps) * gamma over each row (mean over cols);
+ * gamma fp32 [cols] or NULL (gain 1); eps >= 0.  One reduction stage whose
+ * broadcast result scales the values held from the first stage.  Same
+ * planning and rules as cf_stitch_layernorm.  [ComFuse] Stage-Stream
+ * Execution Model (bypass path), Frontend / Fusion Spec IR (Phi patterns). */
+cf_status cf_stitch_rmsnorm(const float* x, const float* gamma, float* y, int64_t rows, int64_t cols,
+                            float eps, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* GEMM with a stitched epilogue across output tiles (bf16 in, fp32          */
@@ -177,6 +197,12 @@ cf_status cf_unfused_stitch_layernorm(const float* x, float* y, int64_t rows, in
 cf_status cf_unfused_stitch_pow_bcast_add(const float* x, const float* v, float p, float* y,
                                           float* y_pre, int64_t rows, int64_t cols, void* ws,
                                           size_t ws_bytes, hipStream_t stream);
+cf_status cf_unfused_stitch_layernorm_affine(const float* x, const float* gamma, const float* beta,
+                                             float* y, int64_t rows, int64_t cols, float eps, void* ws,
+                                             size_t ws_bytes, hipStream_t stream);
+cf_status cf_unfused_stitch_rmsnorm(const float* x, const float* gamma, float* y, int64_t rows,
+                                    int64_t cols, float eps, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
 cf_status cf_unfused_gemm_ln(const cf_bf16* A, const cf_bf16* W, const float* bias,
                              const cf_bf16* R, const float* gamma, const float* beta, float eps,
                              cf_bf16* Y, int64_t M, int64_t N, int64_t K, void* ws,

@@ -111,6 +111,50 @@ def test_layernorm_constant_rows_are_zero():
 
 # -------------------------------------------------------- pow-broadcast-add
 
+# RMSNorm and affine LayerNorm: every row plan (packed rows, 4-byte
+# fragments for ragged rows, one row per workgroup, one wide row per
+# workgroup, rows split across workgroups) and the full 750000 x 32 shape.
+NORM_SHAPES = [(750000, 32), (1, 1), (5, 3), (1000, 32), (999, 36), (7, 100), (3, 1024), (4, 5000),
+               (2, 30000), (3, 70001)]
+
+
+@pytest.mark.parametrize("rows,cols", NORM_SHAPES)
+def test_layernorm_affine(rows, cols):
+    d = gen.layernorm_affine_inputs(seed=8, rows=rows, cols=cols)
+    y = empty_f32(rows, cols)
+    cf.cf_stitch_layernorm_affine(d32(d["x"]), d32(d["gamma"]), d32(d["beta"]), y, d["eps"])
+    o = oracle.layernorm_affine_rows(d["x"], d["gamma"], d["beta"], d["eps"])
+    err = rownorm_err(host(y), o)
+    assert err <= TOL_F32, (err, cf.last_plan())
+
+
+@pytest.mark.parametrize("gain", [True, False])
+@pytest.mark.parametrize("rows,cols", NORM_SHAPES)
+def test_rmsnorm(rows, cols, gain):
+    d = gen.rmsnorm_inputs(seed=7, rows=rows, cols=cols)
+    g = d["gamma"] if gain else None
+    y = empty_f32(rows, cols)
+    cf.cf_stitch_rmsnorm(d32(d["x"]), d32(g) if gain else None, y, d["eps"])
+    o = oracle.rmsnorm_rows(d["x"], g, d["eps"])
+    err = rownorm_err(host(y), o)
+    assert err <= TOL_F32, (err, cf.last_plan())
+
+
+def test_norms_unfused_and_misaligned():
+    rows, cols = 1000, 36
+    d = gen.layernorm_affine_inputs(seed=8, rows=rows, cols=cols)
+    y = empty_f32(rows, cols)
+    cf.cf_stitch_layernorm_affine(d32(d["x"]), d32(d["gamma"]), d32(d["beta"]), y, d["eps"], unfused=True)
+    assert rownorm_err(host(y), oracle.layernorm_affine_rows(d["x"], d["gamma"], d["beta"], d["eps"])) <= TOL_F32
+    y = empty_f32(rows, cols, misalign=True)
+    cf.cf_stitch_rmsnorm(d32(d["x"]), d32(d["gamma"]), y, d["eps"])
+    assert json.loads(cf.last_plan())["frag_floats"] == 1
+    assert rownorm_err(host(y), oracle.rmsnorm_rows(d["x"], d["gamma"], d["eps"])) <= TOL_F32
+    y = empty_f32(rows, cols)
+    cf.cf_stitch_rmsnorm(d32(d["x"]), None, y, d["eps"], unfused=True)
+    assert rownorm_err(host(y), oracle.rmsnorm_rows(d["x"], None, d["eps"])) <= TOL_F32
+
+
 POW_SHAPES = [(64, 30000), (3, 5), (7, 9), (64, 1024), (5, 20001), (1000, 32), (130, 8)]
 
 
