@@ -7,6 +7,7 @@ its arrays without sharing any of each other's code.
 from .inputs import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    gemm_act_inputs,
     gemm_ln_inputs,
     gemm_softmax_gemm_inputs,
     gemm_softmax_inputs,

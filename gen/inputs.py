@@ -28,6 +28,7 @@ WORKLOADS = {
     "gemm_softmax_gemm_8192x8192x128x128": dict(M=8192, N=8192, D=128, Dv=128),
     "rmsnorm_750000x32": dict(rows=750000, cols=32),
     "layernorm_affine_750000x32": dict(rows=750000, cols=32),
+    "gemm_gelu_4096x4096x1024": dict(M=4096, N=4096, K=1024),
 }
 
 
@@ -131,6 +132,14 @@ def gemm_ln_inputs(seed: int = 4, M: int = 4096, N: int = 4096, K: int = 1024, r
     else:
         out["r_bits"], out["r"] = None, None
     return out
+
+
+def gemm_act_inputs(seed: int = 9, M: int = 4096, N: int = 4096, K: int = 1024) -> dict:
+    """GEMM + bias + activation workload: A bf16 [M x K] ~ N(0, 1); W bf16 [K x N] ~ N(0, 0.02);
+    bias fp32 [N] ~ N(0, 0.1) (the GEMM + LayerNorm workload's operands without the residual)."""
+    a_bits, a = _bf16(normal(seed, 0, (M, K)))
+    w_bits, w = _bf16(normal(seed, 1, (K, N), std=0.02))
+    return {"a_bits": a_bits, "a": a, "w_bits": w_bits, "w": w, "bias": normal(seed, 2, (N,), std=0.1)}
 
 
 def gemm_softmax_inputs(seed: int = 5, M: int = 8192, N: int = 8192, D: int = 128) -> dict:

@@ -17,6 +17,8 @@ routines or brute force in ``tests/test_oracle_pins.py``; none is unpinned.
 """
 from . import ops  # noqa: F401
 from .subgraphs import (  # noqa: F401
+    ACTIVATIONS,
+    gemm_act,
     gemm_ln,
     gemm_softmax,
     gemm_softmax_gemm,

@@ -134,3 +134,18 @@ def matmul(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     """Z_ij = sum_k a_ik b_kj in float64 (library dgemm as one step)."""
     assert a.ndim == 2 and b.ndim == 2 and a.shape[1] == b.shape[0]
     return a @ b
+
+
+def map_relu(x: np.ndarray) -> np.ndarray:
+    return np.maximum(x, 0.0)
+
+
+def map_gelu_tanh(x: np.ndarray) -> np.ndarray:
+    """0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), the tanh form of GELU."""
+    c = np.sqrt(np.float64(2.0) / np.pi)
+    return 0.5 * x * (1.0 + np.tanh(c * (x + 0.044715 * x * x * x)))
+
+
+def map_silu(x: np.ndarray) -> np.ndarray:
+    """x * sigmoid(x) = x / (1 + exp(-x))."""
+    return x / (1.0 + np.exp(-x))

@@ -14,6 +14,7 @@ its reason in the design notes):
     before the softmax.
   * The back-to-back product takes its second operand V row-major [N x Dv]
     (keys by output columns): O = S.V with S the scaled row softmax above.
+  * The activation epilogue's GELU is the tanh form; SiLU is x * sigmoid(x).
   * RMSNorm divides by the root of the mean square (over the row length) plus
     eps; its gain gamma, like LayerNorm's gamma and beta, is a length-cols
     row-vector broadcast, and a missing gain is 1.
@@ -142,3 +143,22 @@ def rmsnorm_rows(x, gamma=None, eps: float = 1e-5) -> np.ndarray:
     if gamma is not None:
         y = ops.mul_rowvec(y, ops.f64(gamma))
     return y
+
+
+# activation name -> the ops function that computes it (looked up per call)
+ACTIVATIONS = {"none": None, "relu": "map_relu", "gelu_tanh": "map_gelu_tanh", "silu": "map_silu",
+               "square": "map_square"}
+
+
+def gemm_act(a, w, bias, act: str) -> np.ndarray:
+    """Y = act(A.W + bias): a GEMM with a unary-activation epilogue, per output element.
+
+    ComFuse, Stage-Stream Execution Model (Fig. 3: x = alpha * Acc + Bias, alpha = 1)
+    followed by one elementwise stage; Frontend / Fusion Spec IR names
+    activations and squares among the epilogue operators.  ``bias`` may be None.
+    """
+    z = ops.matmul(ops.f64(a), ops.f64(w))
+    if bias is not None:
+        z = ops.add_rowvec(z, ops.f64(bias))
+    name = ACTIVATIONS[act]
+    return z if name is None else getattr(ops, name)(z)

@@ -343,4 +343,47 @@ def pin_layernorm_affine_constant_row():
     assert np.array_equal(y, np.repeat(b[None, :], 3, axis=0)), "affine LN constant row is not beta"
 
 
+# ------------------------------------------------------- GEMM + activation
+
+def _bf_act(v, act):
+    if act == "none":
+        return v
+    if act == "relu":
+        return v if v > 0 else 0.0
+    if act == "gelu_tanh":
+        return 0.5 * v * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (v + 0.044715 * v ** 3)))
+    if act == "silu":
+        return v / (1.0 + math.exp(-v))
+    return v * v
+
+
+def pin_gemm_act_brute_force():
+    for act in ["none", "relu", "gelu_tanh", "silu", "square"]:
+        for (m, n, k) in [(3, 5, 4), (2, 7, 3)]:
+            rng = _rng(80 + m + n)
+            a, w, b = rng.normal(size=(m, k)), rng.normal(size=(k, n)), rng.normal(size=n)
+            z = _bf_matmul(a.tolist(), w.tolist())
+            yb = [[_bf_act(z[i][j] + b[j], act) for j in range(n)] for i in range(m)]
+            _close(oracle.gemm_act(a, w, b, act), yb, 1e-13, 1e-14, what=f"GEMM+{act} brute {m,n,k}")
+            y0 = [[_bf_act(z[i][j], act) for j in range(n)] for i in range(m)]
+            _close(oracle.gemm_act(a, w, None, act), y0, 1e-13, 1e-14, what=f"GEMM+{act} brute no bias")
+
+
+def pin_gemm_act_closed_forms():
+    """Values the definitions fix: GELU and SiLU of 0 are 0 and tend to x for large x and to 0
+    for large negative x; SiLU(x) - SiLU(-x) = x; ReLU(x) - ReLU(-x) = x; square of a ones GEMM is K^2."""
+    x = np.array([[0.0, 30.0, -30.0, 1.5]])
+    eye = np.eye(4)
+    g = oracle.gemm_act(x, eye, None, "gelu_tanh")
+    _close(g, [[0.0, 30.0, 0.0, g[0, 3]]], 0.0, 1e-12, what="GELU limits")
+    s = oracle.gemm_act(x, eye, None, "silu")
+    _close(s[0, :3], [0.0, 30.0, 0.0], 0.0, 1e-11, what="SiLU limits")
+    v = _rng(82).normal(size=(3, 6))
+    for act in ["silu", "relu"]:
+        d = oracle.gemm_act(v, np.eye(6), None, act) - oracle.gemm_act(-v, np.eye(6), None, act)
+        _close(d, v, 1e-14, 1e-15, what=f"{act} odd part")
+    _close(oracle.gemm_act(np.ones((2, 9)), np.ones((9, 3)), None, "square"), np.full((2, 3), 81.0), 0.0, 0.0,
+           what="square of ones")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

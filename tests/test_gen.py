@@ -57,3 +57,5 @@ def test_workload_shapes():
     assert d["x"].shape == (5, 7) and d["gamma"].shape == (7,) and d["x"].dtype == np.float32
     d = gen.layernorm_affine_inputs(rows=5, cols=7)
     assert d["gamma"].shape == (7,) and d["beta"].shape == (7,)
+    d = gen.gemm_act_inputs(M=16, N=24, K=8)
+    assert d["a_bits"].shape == (16, 8) and d["w_bits"].shape == (8, 24) and d["bias"].shape == (24,)

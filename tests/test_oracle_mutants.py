@@ -112,6 +112,9 @@ MUTANTS = {
     "b2b_softmax_over_wrong_axis": (subgraphs, "gemm_softmax_gemm", _b2b_softmax_over_keys_axis0),
     "b2b_unnormalized": (subgraphs, "gemm_softmax_gemm", _b2b_unnormalized),
     "rmsnorm_centers": (subgraphs, "rmsnorm_rows", _rms_centered),
+    "gelu_erf_constant_dropped": (ops, "map_gelu_tanh", lambda x: 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * x))),
+    "silu_sign": (ops, "map_silu", lambda x: x / (1.0 + np.exp(x))),
+    "relu_is_abs": (ops, "map_relu", lambda x: np.abs(x)),
     "ln_affine_beta_scaled": (subgraphs, "layernorm_affine_rows", _ln_affine_beta_scaled),
 }
 
