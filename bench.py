@@ -48,6 +48,7 @@ KERNEL_SOURCES = {
     "gemm_softmax_gemm_8192x8192x128x128": ("gemm.hip", "dev.hpp"),
     "rmsnorm_750000x32": ("stitch.hip", "dev.hpp"),
     "layernorm_affine_750000x32": ("stitch.hip", "dev.hpp"),
+    "gemm_gelu_4096x4096x1024": ("gemm.hip", "dev.hpp"),
 }
 
 
@@ -164,9 +165,20 @@ class Workload:
             call = lambda b, ws, u: cf.cf_stitch_layernorm_affine(b["X"], b["G"], b["B"], b["Y"], 1e-5, ws=ws,
                                                                   unfused=u)
             self.op, self.dims = cf.CF_OP_STITCH_LAYERNORM_AFFINE, (750000, 32, 0)
+        elif name == "gemm_gelu_4096x4096x1024":
+            M, N, K = 4096, 4096, 1024
+            d = gen.gemm_act_inputs(seed=9)
+            self.inp = d
+            bufs = {"A": dbf(d["a_bits"]), "W": dbf(d["w_bits"]), "bias": d32(d["bias"]),
+                    "Y": torch.empty(M, N, dtype=torch.bfloat16, device=dev)}
+            self.bytes = 2 * (M * K + K * N + M * N) + 4 * N
+            self.flops = 2 * M * N * K
+            call = lambda b, ws, u: cf.cf_gemm_act(b["A"], b["W"], b["bias"], "gelu_tanh", b["Y"], ws=ws, unfused=u)
+            self.op, self.dims = cf.CF_OP_GEMM_ACT, (M, N, K)
         else:
             raise ValueError(name)
-        self.bound = "mfma" if name in ("gemm_ln_4096x4096x1024", "gemm_softmax_gemm_8192x8192x128x128") else "hbm"
+        self.bound = "mfma" if name in ("gemm_ln_4096x4096x1024", "gemm_softmax_gemm_8192x8192x128x128",
+                                        "gemm_gelu_4096x4096x1024") else "hbm"
         nb = cf.cf_workspace_bytes(self.op, *self.dims)
         self.ws = cf.Workspace(nb) if nb else None
         self.uws = None
@@ -193,13 +205,16 @@ class Workload:
             return oracle.rmsnorm_rows(d["x"], d["gamma"], 1e-5)
         if self.name == "layernorm_affine_750000x32":
             return oracle.layernorm_affine_rows(d["x"], d["gamma"], d["beta"], 1e-5)
+        if self.name == "gemm_gelu_4096x4096x1024":
+            return oracle.gemm_act(d["a"], d["w"], d["bias"], "gelu_tanh")
         return oracle.gemm_softmax(d["q"], d["k"], d["scale"])
 
 
 WORKLOAD_NAMES = ["softmax_256x1024", "layernorm_750000x32", "pow_bcast_add_softmax_64x30000",
                   "gemm_ln_4096x4096x1024", "gemm_softmax_8192x8192x128"]
 # measured per kernel (and unfused) but outside the step
-EXTRA_NAMES = ["gemm_softmax_gemm_8192x8192x128x128", "rmsnorm_750000x32", "layernorm_affine_750000x32"]
+EXTRA_NAMES = ["gemm_softmax_gemm_8192x8192x128x128", "rmsnorm_750000x32", "layernorm_affine_750000x32",
+               "gemm_gelu_4096x4096x1024"]
 
 
 def main():

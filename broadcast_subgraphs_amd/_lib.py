@@ -18,7 +18,10 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "cf.h")
 
 CF_OK, CF_EINVAL, CF_EUNSUPPORTED, CF_EALIGN, CF_EWORKSPACE, CF_EOCCUPANCY, CF_EHIP = range(7)
 (CF_OP_STITCH_SOFTMAX, CF_OP_STITCH_LAYERNORM, CF_OP_STITCH_POW_BCAST_ADD, CF_OP_GEMM_LN, CF_OP_GEMM_SOFTMAX,
- CF_OP_GEMM_SOFTMAX_GEMM, CF_OP_STITCH_LAYERNORM_AFFINE, CF_OP_STITCH_RMSNORM) = 1, 2, 3, 4, 5, 6, 7, 8
+ CF_OP_GEMM_SOFTMAX_GEMM, CF_OP_STITCH_LAYERNORM_AFFINE, CF_OP_STITCH_RMSNORM, CF_OP_GEMM_ACT) = range(1, 10)
+CF_ACT_NONE, CF_ACT_RELU, CF_ACT_GELU_TANH, CF_ACT_SILU, CF_ACT_SQUARE = range(5)
+ACT_IDS = {"none": CF_ACT_NONE, "relu": CF_ACT_RELU, "gelu_tanh": CF_ACT_GELU_TANH, "silu": CF_ACT_SILU,
+           "square": CF_ACT_SQUARE}
 
 _lib = None
 _lock = threading.Lock()
@@ -42,6 +45,7 @@ _SIGS = {
     "cf_gemm_ln": (_ST, [_P, _P, _P, _P, _P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_gemm_softmax": (_ST, [_P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_gemm_softmax_gemm": (_ST, [_P, _P, _P, _F, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
+    "cf_gemm_act": (_ST, [_P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_unfused_stitch_softmax": (_ST, [_P, _P, _I64, _I64, _P, _SZ, _P]),
     "cf_unfused_stitch_layernorm": (_ST, [_P, _P, _I64, _I64, _F, _P, _SZ, _P]),
     "cf_unfused_stitch_pow_bcast_add": (_ST, [_P, _P, _F, _P, _P, _I64, _I64, _P, _SZ, _P]),
@@ -50,6 +54,7 @@ _SIGS = {
     "cf_unfused_gemm_ln": (_ST, [_P, _P, _P, _P, _P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_unfused_gemm_softmax": (_ST, [_P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_unfused_gemm_softmax_gemm": (_ST, [_P, _P, _P, _F, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
+    "cf_unfused_gemm_act": (_ST, [_P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_graph_begin": (_ST, [_P]),
     "cf_graph_end": (_ST, [_P, ctypes.POINTER(_P)]),
     "cf_graph_launch": (_ST, [_P, _P]),
@@ -298,6 +303,23 @@ def cf_gemm_softmax_gemm(Q, K, V, scale, O, ws=None, stream=None, unfused=False)
     p, n, w = _ws_args(CF_OP_GEMM_SOFTMAX_GEMM, M, N, D, ws, Q.device, st, unfused)
     name = "cf_unfused_gemm_softmax_gemm" if unfused else "cf_gemm_softmax_gemm"
     _check(name, getattr(lib(), name)(_ptr(Q), _ptr(K), _ptr(V), float(scale), _ptr(O), M, N, D, Dv, p, n, st))
+    return w
+
+
+def cf_gemm_act(A, W, bias, act, Y, ws=None, stream=None, unfused=False):
+    """A [M,K], W [K,N], Y [M,N]: bf16 tensors; bias fp32 [N] or None; act a CF_ACT_* id or its name."""
+    torch = _torch()
+    for t, nm in ((A, "A"), (W, "W"), (Y, "Y")):
+        _need(t, torch.bfloat16, nm, 2)
+    if bias is not None:
+        _need(bias, torch.float32, "bias", 1)
+    act_id = ACT_IDS[act] if isinstance(act, str) else int(act)
+    M, K = A.shape
+    N = W.shape[1]
+    st = _stream(stream)
+    p, n, w = _ws_args(CF_OP_GEMM_ACT, M, N, K, ws, A.device, st, unfused)
+    name = "cf_unfused_gemm_act" if unfused else "cf_gemm_act"
+    _check(name, getattr(lib(), name)(_ptr(A), _ptr(W), _ptr(bias), act_id, _ptr(Y), M, N, K, p, n, st))
     return w
 
 

@@ -270,14 +270,19 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   p.nn = nn ? 1 : 0;
   // softmax with a reduction dimension of at most 128 runs by strips
   const int dalgo = (epi == kEpiSoftmax && K <= 128) ? 2 : 1;
-  p.algo = epi == kEpiStoreF32 ? 0 : (int)env_int("CF_GEMM_ALGO", dalgo);
+  const bool plain = epi == kEpiStoreF32 || epi == kEpiAct;  // tiles independent of each other
+  p.algo = plain ? 0 : (int)env_int("CF_GEMM_ALGO", dalgo);
   if (p.algo == 2 && (epi != kEpiSoftmax || K > 128)) return CF_EUNSUPPORTED;
   if (p.algo == 2) return plan_gemm_strips(kEpiSoftmax, M, N, K, di, &p, pl);
   // Default tiles (measured on MI355X): 128x128 at two workgroups per CU for
   // the plain GEMM and the overlapped epilogues, 64x512 for the round-based
   // epilogues.
-  const int dflt = (epi == kEpiStoreF32 || p.algo == 1) ? 3 : 4;
-  p.cfg = (int)env_int(epi == kEpiSoftmax ? "CF_GEMM_SOFTMAX_CFG" : (epi == kEpiLN ? "CF_GEMM_LN_CFG" : "CF_GEMM_CFG"), dflt);
+  const int dflt = (plain || p.algo == 1) ? 3 : 4;
+  p.cfg = (int)env_int(epi == kEpiSoftmax ? "CF_GEMM_SOFTMAX_CFG"
+                       : epi == kEpiLN     ? "CF_GEMM_LN_CFG"
+                       : epi == kEpiAct    ? "CF_GEMM_ACT_CFG"
+                                           : "CF_GEMM_CFG",
+                       dflt);
   if (!gemm_tile_config(epi, p.algo, p.cfg, &p.bm, &p.bn, &p.bk)) return CF_EUNSUPPORTED;
   const int64_t tn = (N + p.bn - 1) / p.bn, tm = (M + p.bm - 1) / p.bm;
   p.tiles = (int)(tn * tm);
@@ -285,7 +290,7 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   if (gemm_occupancy(epi, p, &occ) != hipSuccess || occ <= 0) return CF_EHIP;
   p.occupancy = occ;
   const int64_t cap = (int64_t)occ * di->cus;
-  if (epi == kEpiStoreF32) {
+  if (plain) {
     p.grid = (int)std::min<int64_t>(p.tiles, std::max<int64_t>(cap, 1) * 4);
   } else if (p.algo == 1) {
     // one join word per row block; every workgroup resident.  Pipelined
@@ -337,7 +342,8 @@ size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N) {
 }
 
 void record_gemm_plan(const char* name, int epi, const GemmPlan& p, int64_t M, int64_t N, int64_t K) {
-  const bool ov = p.algo >= 1 && epi != kEpiStoreF32;
+  const bool plain = epi == kEpiStoreF32 || epi == kEpiAct;
+  const bool ov = p.algo >= 1 && !plain;
   const char* kernel = epi == kEpiSoftmaxGemm
                            ? "k_gemm_b2b"
                            : (p.algo == 2 ? "k_gemm_sm3" : (ov ? (epi == kEpiLN ? "k_gemm_ln2" : "k_gemm_sm2") : "k_gemm"));
@@ -346,7 +352,7 @@ void record_gemm_plan(const char* name, int epi, const GemmPlan& p, int64_t M, i
                           ? "strips, back-to-back"
                           : (p.algo == 2 ? "strips"
                                          : (ov ? (epi == kEpiLN ? (single ? "one-tile-at-a-time" : "pipelined") : "two-sweep")
-                                               : "rounds"));
+                                               : (plain ? "independent-tiles" : "rounds")));
   char buf[512];
   snprintf(buf, sizeof buf,
            "{\"call\":\"%s\",\"M\":%lld,\"N\":%lld,\"K\":%lld,\"kernel\":\"%s\",\"tile\":[%d,%d,%d],"
@@ -356,7 +362,8 @@ void record_gemm_plan(const char* name, int epi, const GemmPlan& p, int64_t M, i
            p.algo == 2 ? (long long)p.strips : (long long)((N + p.bn - 1) / p.bn), p.grid,
            (single || epi == kEpiSoftmaxGemm) ? 512 : 256,
            p.occupancy, p.rounds,
-           (ov || p.leader) ? (epi == kEpiLN && p.algo == 1 ? "peer-to-peer" : "leader") : "peer-to-peer", sched,
+           plain ? "none" : ((ov || p.leader) ? (epi == kEpiLN && p.algo == 1 ? "peer-to-peer" : "leader") : "peer-to-peer"),
+           sched,
            p.sw_a, p.sw_b);
   g_last_plan = buf;
 }
@@ -438,6 +445,12 @@ size_t cf_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2) {
       GemmPlan p;
       if (plan_gemm_strips(kEpiSoftmaxGemm, d0, d1, d2, di, &p, &p) != CF_OK) return (size_t)-1;
       return b2b_layout(p, d0).total;
+    }
+    case CF_OP_GEMM_ACT: {
+      if (d2 <= 0) return (size_t)-1;
+      GemmPlan p;
+      if (plan_gemm(kEpiAct, true, d0, d1, d2, &p) != CF_OK) return (size_t)-1;
+      return 0;  // the tiles are independent: no partials, no joins
     }
   }
   return (size_t)-1;
@@ -576,6 +589,37 @@ cf_status cf_gemm_softmax_gemm(const cf_bf16* Q, const cf_bf16* K, const cf_bf16
   return launch_gemm(kEpiSoftmaxGemm, p, a, stream) == hipSuccess ? CF_OK : CF_EHIP;
 }
 
+static cf_status check_act_args(const cf_bf16* A, const cf_bf16* W, const float* bias, int act, cf_bf16* Y,
+                                int64_t M, int64_t N, int64_t K) {
+  if (!A || !W || !Y || act < CF_ACT_NONE || act > CF_ACT_SQUARE) return CF_EINVAL;
+  cf_status s = check_gemm_shape(M, N, K);
+  if (s != CF_OK) return s;
+  if (!aligned16(A) || !aligned16(W) || !aligned16(Y) || (bias && !aligned16(bias))) return CF_EALIGN;
+  const size_t yb = (size_t)M * N * 2;
+  if (overlap(Y, yb, A, (size_t)M * K * 2) || overlap(Y, yb, W, (size_t)K * N * 2) ||
+      (bias && overlap(Y, yb, bias, (size_t)N * 4)))
+    return CF_EINVAL;
+  return CF_OK;
+}
+
+cf_status cf_gemm_act(const cf_bf16* A, const cf_bf16* W, const float* bias, int act, cf_bf16* Y, int64_t M,
+                      int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  cf_status s = check_act_args(A, W, bias, act, Y, M, N, K);
+  if (s != CF_OK) return s;
+  GemmPlan p;
+  s = plan_gemm(kEpiAct, true, M, N, K, &p);
+  if (s != CF_OK) return s;
+  GemmArgs a{};
+  a.A = A; a.B = W; a.bias = bias; a.act = act; a.Y = Y;
+  a.M = M; a.N = N; a.K = K;
+  a.tiles_n = (int)((N + p.bn - 1) / p.bn);
+  a.tiles_m = (int)((M + p.bm - 1) / p.bm);
+  record_gemm_plan("cf_gemm_act", kEpiAct, p, M, N, K);
+  return launch_gemm(kEpiAct, p, a, stream) == hipSuccess ? CF_OK : CF_EHIP;
+}
+
 // ------------------------------------------------------------ unfused chains
 // Workspace: fp32 intermediates, placed after the header and the join words
 // (which they never touch, so one zero-filled workspace serves fused and
@@ -597,6 +641,7 @@ size_t cf_unfused_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2) {
     case CF_OP_STITCH_RMSNORM: n = 3 * vec + 2 * full; break;
     case CF_OP_GEMM_LN: n = d2 > 0 ? 4 * vec + 3 * full : (size_t)-1; break;
     case CF_OP_GEMM_SOFTMAX: n = d2 > 0 ? 2 * vec + 3 * full : (size_t)-1; break;
+    case CF_OP_GEMM_ACT: n = d2 > 0 ? 2 * full : (size_t)-1; break;
     case CF_OP_GEMM_SOFTMAX_GEMM:  // + S bf16 [M x N] + the second product fp32 [M x (Dv <= 128)]
       n = d2 > 0 ? 2 * vec + 3 * full + align_up((size_t)d0 * d1 * 2, 256) + align_up((size_t)d0 * 128 * 4, 256)
                  : (size_t)-1;
@@ -823,6 +868,44 @@ cf_status cf_unfused_gemm_softmax_gemm(const cf_bf16* Q, const cf_bf16* K, const
   CF_TRY(launch_gemm(kEpiStoreF32, p, a, stream));
   CF_TRY(u_cast_bf16(Z, O, M * Dv, stream));
   g_last_plan = "{\"call\":\"cf_unfused_gemm_softmax_gemm\",\"kernels\":10}";
+  return CF_OK;
+}
+
+cf_status cf_unfused_gemm_act(const cf_bf16* A, const cf_bf16* W, const float* bias, int act, cf_bf16* Y,
+                               int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes, hipStream_t stream) {
+  cf_status s = check_act_args(A, W, bias, act, Y, M, N, K);
+  if (s != CF_OK) return s;
+  if (!ws || ws_bytes < cf_unfused_workspace_bytes(CF_OP_GEMM_ACT, M, N, K)) return CF_EWORKSPACE;
+  const size_t full = align_up((size_t)M * N * 4, 256);
+  char* w = unfused_base(ws);
+  float* B0 = reinterpret_cast<float*>(w);
+  float* B1 = reinterpret_cast<float*>(w + full);
+  GemmPlan p;
+  s = plan_gemm(kEpiStoreF32, true, M, N, K, &p);
+  if (s != CF_OK) return s;
+  GemmArgs a{};
+  a.A = A; a.B = W; a.Z = B0; a.M = M; a.N = N; a.K = K;
+  a.tiles_n = (int)((N + p.bn - 1) / p.bn);
+  a.tiles_m = (int)((M + p.bm - 1) / p.bm);
+  CF_TRY(launch_gemm(kEpiStoreF32, p, a, stream));  // Z = A.W
+  int kernels = 2;
+  float* cur = B0;
+  if (bias) {
+    CF_TRY(u_bcast_row(B0, bias, B1, M, N, 3, stream));  // u = Z + bias
+    cur = B1;
+    ++kernels;
+  }
+  static const int kMapOp[] = {-1, 5, 6, 7, 1};  // relu, gelu_tanh, silu, square
+  if (act != CF_ACT_NONE) {
+    float* out = cur == B0 ? B1 : B0;
+    CF_TRY(u_map(cur, out, M * N, kMapOp[act], 0.f, 0.f, stream));  // y = act(u)
+    cur = out;
+    ++kernels;
+  }
+  CF_TRY(u_cast_bf16(cur, Y, M * N, stream));
+  char buf[96];
+  snprintf(buf, sizeof buf, "{\"call\":\"cf_unfused_gemm_act\",\"kernels\":%d}", kernels);
+  g_last_plan = buf;
   return CF_OK;
 }
 

@@ -492,8 +492,37 @@ constexpr int gemm_lds_bytes() {
   constexpr int ring = (BM + BN) * BK * 2;  // slot 0 (slot 1 is its own object)
   // bf16 tile + red (2 x 4 x BM floats) + pub (BM float4) + parts (256 float4) + stat (BM float2) + flags
   constexpr int epi = EPI == kEpiStoreF32 ? BM * BN * 4 / 4
+                      : EPI == kEpiAct    ? BM * BN * 2 + BN * 4  // bf16 tile + bias slice
                                           : BM * BN * 2 + 32 * BM + 16 * BM + 16 * 256 + 8 * BM + 64 + 3 * BN * 4;
   return ring > epi ? ring : epi;
+}
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// Unary activations of the activation epilogue, in fp32.  Both sigmoid-gated
+// forms use 1 / (1 + 2^t): the tanh-form GELU 0.5 u (1 + tanh z), with
+// z = sqrt(2/pi) (u + 0.044715 u^3), equals u * sigmoid(2 z) because
+// 1 + tanh z = 2 / (1 + e^(-2z)); SiLU is u * sigmoid(u).  For t past the
+// exp2 range the gate is 1 / inf = 0 (or 1 / 1 = 1), the exact limits.
+constexpr float kGeluT1 = -2.302208198144325f;    // -2 sqrt(2/pi) log2(e)
+constexpr float kGeluT3 = -0.1029432395800235f;   // the same times 0.044715
+template <int ACT>
+__device__ __forceinline__ float act_fn(float u) {
+  if constexpr (ACT == kActRelu) {
+    return fmaxf(u, 0.0f);
+  } else if constexpr (ACT == kActGeluTanh) {
+    const float t = u * fmaf(kGeluT3, u * u, kGeluT1);
+    return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+  } else if constexpr (ACT == kActSilu) {
+    return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * u));
+  } else if constexpr (ACT == kActSquare) {
+    return u * u;
+  } else {
+    return u;
+  }
 }
 
 }  // namespace
@@ -578,6 +607,59 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
             st4_stream(a.Z + row * a.N + col, *reinterpret_cast<const float4*>(ot + rr * BN + 4 * (c ^ (rr & 15))));
         }
         __syncthreads();
+      }
+    } else if constexpr (EPI == kEpiAct) {
+      // y = act(acc + bias_j) per element: no cross-tile dependency.  The bias
+      // slice goes to LDS (zero past N or without bias), the bf16 results to
+      // the LDS output tile, then whole row segments out.
+      uint16_t* tile16 = reinterpret_cast<uint16_t*>(lds);
+      float* vec = reinterpret_cast<float*>(lds + BM * BN * 2);
+      for (int id = t; id < BN / 4; id += kThreads) {
+        const int64_t gn = n0 + 4 * id;
+        reinterpret_cast<float4*>(vec)[id] = (a.bias != nullptr && gn < a.N)
+                                                 ? *reinterpret_cast<const float4*>(a.bias + gn)
+                                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      __syncthreads();
+      auto finish = [&](auto actc) {
+        constexpr int ACT = decltype(actc)::value;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int cl0 = wn * WN + cb * 32 + 16 * hl;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float4 b0 = *reinterpret_cast<const float4*>(vec + cl0 + 8 * h);
+            const float4 b1 = *reinterpret_cast<const float4*>(vec + cl0 + 8 * h + 4);
+            const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+              const int rl = wm * WM + rb * 32 + l32;
+              float o[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) o[e] = act_fn<ACT>(acc[rb][cb][8 * h + e] + bb[e]);
+              const u32x4 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                                pack_bf16x2(o[6], o[7])};
+              *reinterpret_cast<u32x4*>(tile16 + rl * BN + 8 * eswz(rl, cl0 / 8 + h)) = pk;
+            }
+          }
+        }
+      };
+      switch (a.act) {
+        case kActRelu: finish(IntC<kActRelu>{}); break;
+        case kActGeluTanh: finish(IntC<kActGeluTanh>{}); break;
+        case kActSilu: finish(IntC<kActSilu>{}); break;
+        case kActSquare: finish(IntC<kActSquare>{}); break;
+        default: finish(IntC<kActNone>{}); break;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < BM * C16 / kThreads; ++j) {
+        const int id = j * kThreads + t;
+        const int rr = id / C16, c = id % C16;
+        const int64_t row = m0 + rr, col = n0 + 8 * c;
+        if (row < a.M && col < a.N)
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tile16 + rr * BN + 8 * eswz(rr, c)),
+                                      reinterpret_cast<u32x4*>(a.Y + row * a.N + col));
       }
     } else {
       // LDS carve-up (the ring is free): output / residual tile, then scratch.
@@ -2101,6 +2183,8 @@ bool gemm_tile_config(int epi, int algo, int cfg, int* bm, int* bn, int* bk) {
   const TileCfg* t = ln2 ? kLnCfgs : kCfgs;
   const int n = ln2 ? (int)(sizeof(kLnCfgs) / sizeof(kLnCfgs[0])) : (int)(sizeof(kCfgs) / sizeof(kCfgs[0]));
   if (cfg < 0 || cfg >= n) return false;
+  // the round-based epilogue kernels exist for tiles of at most 128 x 256
+  if (!ln2 && epi != kEpiStoreF32 && t[cfg].bm * t[cfg].bn > 128 * 256) return false;
   *bm = t[cfg].bm;
   *bn = t[cfg].bn;
   *bk = t[cfg].bk;
@@ -2160,6 +2244,10 @@ static hipError_t gemm_dispatch(int epi, const GemmPlan& pl, const GemmArgs& a, 
   if (epi == kEpiLN) {
     if (!pl.nn) return hipErrorInvalidConfiguration;
     return pl.algo == 1 ? launch_gemm_overlap<kEpiLN>(pl, a, st, occ) : launch_gemm_t<kEpiLN, true>(pl, a, st, occ);
+  }
+  if (epi == kEpiAct) {
+    if (!pl.nn || pl.algo != 0) return hipErrorInvalidConfiguration;
+    return launch_gemm_t<kEpiAct, true>(pl, a, st, occ);
   }
   if (epi == kEpiSoftmaxGemm) {
     if (pl.nn || pl.algo != 2) return hipErrorInvalidConfiguration;

@@ -68,7 +68,17 @@ enum {
   CF_OP_GEMM_SOFTMAX = 5,         /* d0 = M, d1 = N, d2 = D          */
   CF_OP_GEMM_SOFTMAX_GEMM = 6,    /* d0 = M, d1 = N, d2 = D (any Dv <= 128) */
   CF_OP_STITCH_LAYERNORM_AFFINE = 7, /* d0 = rows, d1 = cols         */
-  CF_OP_STITCH_RMSNORM = 8        /* d0 = rows, d1 = cols            */
+  CF_OP_STITCH_RMSNORM = 8,       /* d0 = rows, d1 = cols            */
+  CF_OP_GEMM_ACT = 9              /* d0 = M, d1 = N, d2 = K          */
+};
+
+/* Unary activations of cf_gemm_act (fp32, applied to u = A.W + bias). */
+enum {
+  CF_ACT_NONE = 0,      /* y = u                                            */
+  CF_ACT_RELU = 1,      /* y = max(u, 0)                                    */
+  CF_ACT_GELU_TANH = 2, /* y = 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))) */
+  CF_ACT_SILU = 3,      /* y = u / (1 + exp(-u))                            */
+  CF_ACT_SQUARE = 4     /* y = u * u                                        */
 };
 
 /* Workspace bytes the fused call needs for this shape on the current device
@@ -177,6 +187,22 @@ cf_status cf_gemm_softmax_gemm(const cf_bf16* Q, const cf_bf16* K, const cf_bf16
                                cf_bf16* O, int64_t M, int64_t N, int64_t D, int64_t Dv,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Y = act(A.W + bias) per element.  A [M x K], W [K x N] (N contiguous),
+ * bias fp32 [N] (row-vector broadcast, 16-byte aligned) or NULL (no bias),
+ * act one of CF_ACT_* (anything else: CF_EINVAL), Y [M x N] not overlapping
+ * A, W or bias.  The accumulator goes through bias and activation in
+ * registers and leaves as bf16; every output element belongs to one tile, so
+ * the tiles never wait on each other and the call needs no workspace
+ * (cf_workspace_bytes returns 0; ws may be NULL and is not touched).
+ * [ComFuse] Frontend / Fusion Spec IR (1-D parameters become row-vector
+ * broadcasts, unary functions such as activations and squares become
+ * computation nodes) and Stage-Stream Execution Model (Fig. 3: x = alpha*Acc
+ * + Bias, here alpha = 1); [sass2mlir] "Epilogue fusion" (consumer math in the
+ * producer's registers; one owner per output element). */
+cf_status cf_gemm_act(const cf_bf16* A, const cf_bf16* W, const float* bias, int act, cf_bf16* Y,
+                      int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Unfused baselines: the same subgraphs as one kernel per operator, with     */
 /* fp32 intermediates in the workspace (in HBM) and broadcasts folded into    */
@@ -215,6 +241,11 @@ cf_status cf_unfused_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scal
 cf_status cf_unfused_gemm_softmax_gemm(const cf_bf16* Q, const cf_bf16* K, const cf_bf16* V,
                                        float scale, cf_bf16* O, int64_t M, int64_t N, int64_t D,
                                        int64_t Dv, void* ws, size_t ws_bytes, hipStream_t stream);
+/* A plain GEMM (fp32 out), the bias add (skipped without bias), the
+ * activation (skipped for CF_ACT_NONE) and the cast, one kernel each. */
+cf_status cf_unfused_gemm_act(const cf_bf16* A, const cf_bf16* W, const float* bias, int act,
+                              cf_bf16* Y, int64_t M, int64_t N, int64_t K, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Graph replay of a captured sequence of calls (used to time the unfused     */

@@ -378,6 +378,110 @@ def test_gemm_softmax_gemm_rejects():
     assert e.value.status == cf.CF_EUNSUPPORTED
 
 
+# ------------------------------------------------ GEMM + unary activation
+
+ACTS = ["none", "relu", "gelu_tanh", "silu", "square"]
+GEMM_ACT_SHAPES = [(300, 264, 72), (17, 8, 8), (512, 1024, 256), (129, 136, 1032), (8300, 4096, 64)]
+
+
+def act_err(g, o):
+    """max_ij |g - o| / (2^-8 |o_ij| + 2^-12 max|o|): at most 1 passes.
+
+    bf16 rounding to nearest moves a value by at most 2^-9 of itself; the
+    2^-12 max|o| floor covers the fp32 accumulation and the activation's
+    fp32 evaluation near zero crossings."""
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    assert g.shape == o.shape
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    floor = 2.0 ** -12 * max(float(np.max(np.abs(o))), 1e-30)
+    return float(np.max(np.abs(g - o) / (2.0 ** -8 * np.abs(o) + floor)))
+
+
+def _gemm_act_run(d, M, N, act, bias=True, unfused=False):
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = cf.cf_gemm_act(dbf16(d["a_bits"]), dbf16(d["w_bits"]), d32(d["bias"]) if bias else None, act, Y,
+                        unfused=unfused)
+    check_ws(ws)
+    return host(Y)
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("M,N,K", GEMM_ACT_SHAPES)
+def test_gemm_act(M, N, K, act):
+    d = gen.gemm_act_inputs(seed=9, M=M, N=N, K=K)
+    g = _gemm_act_run(d, M, N, act)
+    o = oracle.gemm_act(d["a"], d["w"], d["bias"], act)
+    assert act_err(g, o) <= 1.0, (act_err(g, o), cf.last_plan())
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "silu"])
+def test_gemm_act_full_size(act):
+    M, N, K = 4096, 4096, 1024
+    d = gen.gemm_act_inputs(seed=9, M=M, N=N, K=K)
+    g = _gemm_act_run(d, M, N, act)
+    plan = json.loads(cf.last_plan())
+    assert plan["kernel"] == "k_gemm" and plan["schedule"] == "independent-tiles", plan
+    o = oracle.gemm_act(d["a"], d["w"], d["bias"], act)
+    assert act_err(g, o) <= 1.0, act_err(g, o)
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_gemm_act_no_bias_and_unfused(act):
+    M, N, K = 300, 264, 72
+    d = gen.gemm_act_inputs(seed=19, M=M, N=N, K=K)
+    o = oracle.gemm_act(d["a"], d["w"], None, act)
+    assert act_err(_gemm_act_run(d, M, N, act, bias=False), o) <= 1.0
+    assert act_err(_gemm_act_run(d, M, N, act, bias=False, unfused=True), o) <= 1.0
+    o = oracle.gemm_act(d["a"], d["w"], d["bias"], act)
+    assert act_err(_gemm_act_run(d, M, N, act, unfused=True), o) <= 1.0
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_gemm_act_ones_are_exact(act):
+    """A = W = 1, bias = 0: every u is K = 1024, and act(1024) is a bf16 value
+    (1024, or 2^20 for the square): the output is exact.  For the gated forms
+    the gate's exponent is far below the exp2 range, so the gate is 1."""
+    M, N, K = 256, 512, 1024
+    one = gen.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    d = {"a_bits": np.full((M, K), one, np.uint16), "w_bits": np.full((K, N), one, np.uint16),
+         "bias": np.zeros(N, np.float32)}
+    g = _gemm_act_run(d, M, N, act)
+    want = float(K) ** 2 if act == "square" else float(K)
+    assert np.all(g == want)
+
+
+@pytest.mark.parametrize("cfg", range(1, 6))
+def test_gemm_act_every_tile_config(monkeypatch, cfg):
+    monkeypatch.setenv("CF_GEMM_ACT_CFG", str(cfg))
+    M, N, K = 300, 264, 72
+    d = gen.gemm_act_inputs(seed=29, M=M, N=N, K=K)
+    g = _gemm_act_run(d, M, N, "gelu_tanh")
+    o = oracle.gemm_act(d["a"], d["w"], d["bias"], "gelu_tanh")
+    assert act_err(g, o) <= 1.0, cf.last_plan()
+
+
+def test_gemm_act_rejects():
+    A = torch.zeros((64, 32), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((32, 64), dtype=torch.bfloat16, device="cuda")
+    Y = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros(65, dtype=torch.float32, device="cuda")
+    assert cf.cf_workspace_bytes(cf.CF_OP_GEMM_ACT, 64, 64, 32) == 0
+    with pytest.raises(cf.CFError) as e:
+        cf.cf_gemm_act(A, W, b[:64], 5, Y)  # no such activation
+    assert e.value.status == cf.CF_EINVAL
+    with pytest.raises(cf.CFError) as e:
+        cf.cf_gemm_act(A, W, b[1:], "relu", Y)  # bias not 16-byte aligned
+    assert e.value.status == cf.CF_EALIGN
+    with pytest.raises(cf.CFError) as e:
+        cf.cf_gemm_act(A, A, b[:64], "relu", A)  # Y aliases A
+    assert e.value.status == cf.CF_EINVAL
+    W12 = torch.zeros((32, 12), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(cf.CFError) as e:
+        cf.cf_gemm_act(A, W12, None, "relu", torch.zeros((64, 12), dtype=torch.bfloat16, device="cuda"))
+    assert e.value.status == cf.CF_EUNSUPPORTED
+
+
 # Every GEMM epilogue schedule the planner can pick (forced through its
 # CF_GEMM_ALGO override): 0 one join per round, 1 joins overlapped with
 # MainLoops, 2 softmax by strips.
