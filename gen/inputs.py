@@ -134,12 +134,21 @@ def gemm_ln_inputs(seed: int = 4, M: int = 4096, N: int = 4096, K: int = 1024, r
     return out
 
 
-def gemm_act_inputs(seed: int = 9, M: int = 4096, N: int = 4096, K: int = 1024) -> dict:
+def gemm_act_inputs(seed: int = 9, M: int = 4096, N: int = 4096, K: int = 1024, positive: bool = False) -> dict:
     """GEMM + bias + activation workload: A bf16 [M x K] ~ N(0, 1); W bf16 [K x N] ~ N(0, 0.02);
-    bias fp32 [N] ~ N(0, 0.1) (the GEMM + LayerNorm workload's operands without the residual)."""
-    a_bits, a = _bf16(normal(seed, 0, (M, K)))
-    w_bits, w = _bf16(normal(seed, 1, (K, N), std=0.02))
-    return {"a_bits": a_bits, "a": a, "w_bits": w_bits, "w": w, "bias": normal(seed, 2, (N,), std=0.1)}
+    bias fp32 [N] ~ N(0, 0.1) (the GEMM + LayerNorm workload's operands without the residual).
+
+    ``positive``: A ~ U(0.5, 1.5), W ~ U(0, 0.02), bias ~ U(0, 0.1) instead, so every entry of
+    A.W + bias is positive (the domain of an rsqrt epilogue)."""
+    if positive:
+        a_bits, a = _bf16(uniform(seed, 0, (M, K), 0.5, 1.5))
+        w_bits, w = _bf16(uniform(seed, 1, (K, N), 0.0, 0.02))
+        bias = uniform(seed, 2, (N,), 0.0, 0.1)
+    else:
+        a_bits, a = _bf16(normal(seed, 0, (M, K)))
+        w_bits, w = _bf16(normal(seed, 1, (K, N), std=0.02))
+        bias = normal(seed, 2, (N,), std=0.1)
+    return {"a_bits": a_bits, "a": a, "w_bits": w_bits, "w": w, "bias": bias}
 
 
 def gemm_softmax_inputs(seed: int = 5, M: int = 8192, N: int = 8192, D: int = 128) -> dict:

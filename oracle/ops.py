@@ -146,6 +146,11 @@ def map_gelu_tanh(x: np.ndarray) -> np.ndarray:
     return 0.5 * x * (1.0 + np.tanh(c * (x + 0.044715 * x * x * x)))
 
 
+def map_rsqrt(x: np.ndarray) -> np.ndarray:
+    """1 / sqrt(x), no eps (inf at 0, nan below)."""
+    return 1.0 / np.sqrt(x)
+
+
 def map_silu(x: np.ndarray) -> np.ndarray:
     """x * sigmoid(x) = x / (1 + exp(-x))."""
     return x / (1.0 + np.exp(-x))

@@ -14,7 +14,8 @@ its reason in the design notes):
     before the softmax.
   * The back-to-back product takes its second operand V row-major [N x Dv]
     (keys by output columns): O = S.V with S the scaled row softmax above.
-  * The activation epilogue's GELU is the tanh form; SiLU is x * sigmoid(x).
+  * The activation epilogue's GELU is the tanh form; SiLU is x * sigmoid(x);
+    its rsqrt is 1/sqrt(u) with no eps (the norms' eps belongs to their stage).
   * RMSNorm divides by the root of the mean square (over the row length) plus
     eps; its gain gamma, like LayerNorm's gamma and beta, is a length-cols
     row-vector broadcast, and a missing gain is 1.
@@ -147,7 +148,7 @@ def rmsnorm_rows(x, gamma=None, eps: float = 1e-5) -> np.ndarray:
 
 # activation name -> the ops function that computes it (looked up per call)
 ACTIVATIONS = {"none": None, "relu": "map_relu", "gelu_tanh": "map_gelu_tanh", "silu": "map_silu",
-               "square": "map_square"}
+               "square": "map_square", "rsqrt": "map_rsqrt"}
 
 
 def gemm_act(a, w, bias, act: str) -> np.ndarray:
@@ -155,7 +156,8 @@ def gemm_act(a, w, bias, act: str) -> np.ndarray:
 
     ComFuse, Stage-Stream Execution Model (Fig. 3: x = alpha * Acc + Bias, alpha = 1)
     followed by one elementwise stage; Frontend / Fusion Spec IR names
-    activations and squares among the epilogue operators.  ``bias`` may be None.
+    activations, rsqrt and squares among the unary operators that become
+    computation nodes.  ``bias`` may be None.
     """
     z = ops.matmul(ops.f64(a), ops.f64(w))
     if bias is not None:

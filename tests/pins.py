@@ -354,6 +354,8 @@ def _bf_act(v, act):
         return 0.5 * v * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (v + 0.044715 * v ** 3)))
     if act == "silu":
         return v / (1.0 + math.exp(-v))
+    if act == "rsqrt":
+        return 1.0 / math.sqrt(v)
     return v * v
 
 
@@ -384,6 +386,24 @@ def pin_gemm_act_closed_forms():
         _close(d, v, 1e-14, 1e-15, what=f"{act} odd part")
     _close(oracle.gemm_act(np.ones((2, 9)), np.ones((9, 3)), None, "square"), np.full((2, 3), 81.0), 0.0, 0.0,
            what="square of ones")
+
+
+def pin_gemm_act_rsqrt():
+    """rsqrt epilogue: brute force on positive operands (every u > 0), and closed forms:
+    a ones GEMM with K = 9 gives 1/3, with K = 4 exactly 0.5; a diagonal GEMM gives 1/sqrt of
+    each entry (0.25 -> 2, 16 -> 0.25)."""
+    for (m, n, k) in [(3, 5, 4), (2, 7, 3)]:
+        rng = _rng(90 + m + n)
+        a, w, b = rng.uniform(0.5, 1.5, (m, k)), rng.uniform(0.1, 1.0, (k, n)), rng.uniform(0.0, 1.0, n)
+        z = _bf_matmul(a.tolist(), w.tolist())
+        yb = [[_bf_act(z[i][j] + b[j], "rsqrt") for j in range(n)] for i in range(m)]
+        _close(oracle.gemm_act(a, w, b, "rsqrt"), yb, 1e-13, 1e-14, what=f"GEMM+rsqrt brute {m,n,k}")
+    _close(oracle.gemm_act(np.ones((2, 9)), np.ones((9, 3)), None, "rsqrt"), np.full((2, 3), 1.0 / 3.0), 0.0,
+           0.0, what="rsqrt of a ones GEMM, K = 9")
+    _close(oracle.gemm_act(np.ones((1, 4)), np.ones((4, 2)), np.zeros(2), "rsqrt"), [[0.5, 0.5]], 0.0, 0.0,
+           what="rsqrt of a ones GEMM, K = 4")
+    _close(oracle.gemm_act(np.array([[0.25, 16.0]]), np.eye(2), None, "rsqrt"), [[2.0, 0.25]], 0.0, 0.0,
+           what="rsqrt of a diagonal GEMM")
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

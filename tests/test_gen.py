@@ -59,3 +59,9 @@ def test_workload_shapes():
     assert d["gamma"].shape == (7,) and d["beta"].shape == (7,)
     d = gen.gemm_act_inputs(M=16, N=24, K=8)
     assert d["a_bits"].shape == (16, 8) and d["w_bits"].shape == (8, 24) and d["bias"].shape == (24,)
+
+
+def test_gemm_act_positive_inputs_are_positive():
+    d = gen.gemm_act_inputs(M=16, N=24, K=8, positive=True)
+    assert d["a"].min() >= 0.5 and d["w"].min() >= 0.0 and d["bias"].min() >= 0.0
+    assert d["a"].max() <= 1.5 and d["w"].max() <= 0.02

@@ -115,6 +115,8 @@ MUTANTS = {
     "gelu_erf_constant_dropped": (ops, "map_gelu_tanh", lambda x: 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * x))),
     "silu_sign": (ops, "map_silu", lambda x: x / (1.0 + np.exp(x))),
     "relu_is_abs": (ops, "map_relu", lambda x: np.abs(x)),
+    "rsqrt_is_sqrt": (ops, "map_rsqrt", lambda x: np.sqrt(x)),
+    "rsqrt_with_eps": (ops, "map_rsqrt", lambda x: 1.0 / np.sqrt(x + 1e-5)),
     "ln_affine_beta_scaled": (subgraphs, "layernorm_affine_rows", _ln_affine_beta_scaled),
 }
 
