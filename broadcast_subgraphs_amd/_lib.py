@@ -19,9 +19,9 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "cf.h")
 CF_OK, CF_EINVAL, CF_EUNSUPPORTED, CF_EALIGN, CF_EWORKSPACE, CF_EOCCUPANCY, CF_EHIP = range(7)
 (CF_OP_STITCH_SOFTMAX, CF_OP_STITCH_LAYERNORM, CF_OP_STITCH_POW_BCAST_ADD, CF_OP_GEMM_LN, CF_OP_GEMM_SOFTMAX,
  CF_OP_GEMM_SOFTMAX_GEMM, CF_OP_STITCH_LAYERNORM_AFFINE, CF_OP_STITCH_RMSNORM, CF_OP_GEMM_ACT) = range(1, 10)
-CF_ACT_NONE, CF_ACT_RELU, CF_ACT_GELU_TANH, CF_ACT_SILU, CF_ACT_SQUARE = range(5)
+CF_ACT_NONE, CF_ACT_RELU, CF_ACT_GELU_TANH, CF_ACT_SILU, CF_ACT_SQUARE, CF_ACT_RSQRT = range(6)
 ACT_IDS = {"none": CF_ACT_NONE, "relu": CF_ACT_RELU, "gelu_tanh": CF_ACT_GELU_TANH, "silu": CF_ACT_SILU,
-           "square": CF_ACT_SQUARE}
+           "square": CF_ACT_SQUARE, "rsqrt": CF_ACT_RSQRT}
 
 _lib = None
 _lock = threading.Lock()

@@ -591,7 +591,7 @@ cf_status cf_gemm_softmax_gemm(const cf_bf16* Q, const cf_bf16* K, const cf_bf16
 
 static cf_status check_act_args(const cf_bf16* A, const cf_bf16* W, const float* bias, int act, cf_bf16* Y,
                                 int64_t M, int64_t N, int64_t K) {
-  if (!A || !W || !Y || act < CF_ACT_NONE || act > CF_ACT_SQUARE) return CF_EINVAL;
+  if (!A || !W || !Y || act < CF_ACT_NONE || act > CF_ACT_RSQRT) return CF_EINVAL;
   cf_status s = check_gemm_shape(M, N, K);
   if (s != CF_OK) return s;
   if (!aligned16(A) || !aligned16(W) || !aligned16(Y) || (bias && !aligned16(bias))) return CF_EALIGN;
@@ -895,7 +895,7 @@ cf_status cf_unfused_gemm_act(const cf_bf16* A, const cf_bf16* W, const float* b
     cur = B1;
     ++kernels;
   }
-  static const int kMapOp[] = {-1, 5, 6, 7, 1};  // relu, gelu_tanh, silu, square
+  static const int kMapOp[] = {-1, 5, 6, 7, 1, 8};  // relu, gelu_tanh, silu, square, rsqrt
   if (act != CF_ACT_NONE) {
     float* out = cur == B0 ? B1 : B0;
     CF_TRY(u_map(cur, out, M * N, kMapOp[act], 0.f, 0.f, stream));  // y = act(u)

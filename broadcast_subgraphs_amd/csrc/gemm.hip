@@ -520,6 +520,8 @@ __device__ __forceinline__ float act_fn(float u) {
     return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * u));
   } else if constexpr (ACT == kActSquare) {
     return u * u;
+  } else if constexpr (ACT == kActRsqrt) {
+    return __builtin_amdgcn_rsqf(u);
   } else {
     return u;
   }
@@ -649,6 +651,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm(GemmArgs a) {
         case kActGeluTanh: finish(IntC<kActGeluTanh>{}); break;
         case kActSilu: finish(IntC<kActSilu>{}); break;
         case kActSquare: finish(IntC<kActSquare>{}); break;
+        case kActRsqrt: finish(IntC<kActRsqrt>{}); break;
         default: finish(IntC<kActNone>{}); break;
       }
       __syncthreads();

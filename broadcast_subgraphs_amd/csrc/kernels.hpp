@@ -50,7 +50,7 @@ hipError_t rows_split_occupancy(int op, const RowPlan& pl, int* per_cu);
 enum GemmEpi { kEpiStoreF32 = 0, kEpiLN = 1, kEpiSoftmax = 2, kEpiSoftmaxGemm = 3, kEpiAct = 4 };
 
 // unary activations of the activation epilogue (the same ids as the C-ABI's CF_ACT_*)
-enum ActId { kActNone = 0, kActRelu = 1, kActGeluTanh = 2, kActSilu = 3, kActSquare = 4 };
+enum ActId { kActNone = 0, kActRelu = 1, kActGeluTanh = 2, kActSilu = 3, kActSquare = 4, kActRsqrt = 5 };
 
 // Back-to-back GEMM kernel shape: 256-row strips of 64-key tiles, one 8-wave
 // workgroup per CU, the reduction dimension up to 128.
@@ -113,7 +113,7 @@ hipError_t u_bcast_col(const float* x, const float* c, float* y, int64_t rows, i
 // y = x (op) r[col]  for op: 2 mul, 3 add
 hipError_t u_bcast_row(const float* x, const float* r, float* y, int64_t rows, int64_t cols, int op, hipStream_t st);
 // y = f(x) elementwise: 0 exp, 1 square, 2 pow(x, p), 3 rsqrt(x/n + eps) , 4 scale(x, p),
-// 5 relu, 6 tanh-form gelu, 7 silu
+// 5 relu, 6 tanh-form gelu, 7 silu, 8 rsqrt(x)
 hipError_t u_map(const float* x, float* y, int64_t n, int op, float p, float q, hipStream_t st);
 hipError_t u_add_bf16(const float* x, const uint16_t* r, float* y, int64_t n, hipStream_t st);
 hipError_t u_cast_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t st);

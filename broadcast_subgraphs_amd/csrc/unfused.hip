@@ -81,6 +81,7 @@ __global__ __launch_bounds__(kB) void u_k_map(const float* x, float* y, int64_t 
       case 5: r = fmaxf(v, 0.0f); break;
       case 6: r = 0.5f * v * (1.0f + tanhf(0.7978845608028654f * (v + 0.044715f * v * v * v))); break;
       case 7: r = v / (1.0f + expf(-v)); break;
+      case 8: r = 1.0f / sqrtf(v); break;
       default: r = v * p; break;
     }
     y[i] = r;

@@ -78,7 +78,8 @@ enum {
   CF_ACT_RELU = 1,      /* y = max(u, 0)                                    */
   CF_ACT_GELU_TANH = 2, /* y = 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))) */
   CF_ACT_SILU = 3,      /* y = u / (1 + exp(-u))                            */
-  CF_ACT_SQUARE = 4     /* y = u * u                                        */
+  CF_ACT_SQUARE = 4,    /* y = u * u                                        */
+  CF_ACT_RSQRT = 5      /* y = 1 / sqrt(u) (inf at 0, NaN below; no eps)   */
 };
 
 /* Workspace bytes the fused call needs for this shape on the current device
@@ -195,7 +196,7 @@ cf_status cf_gemm_softmax_gemm(const cf_bf16* Q, const cf_bf16* K, const cf_bf16
  * the tiles never wait on each other and the call needs no workspace
  * (cf_workspace_bytes returns 0; ws may be NULL and is not touched).
  * [ComFuse] Frontend / Fusion Spec IR (1-D parameters become row-vector
- * broadcasts, unary functions such as activations and squares become
+ * broadcasts, unary functions such as activations, rsqrt and squares become
  * computation nodes) and Stage-Stream Execution Model (Fig. 3: x = alpha*Acc
  * + Bias, here alpha = 1); [sass2mlir] "Epilogue fusion" (consumer math in the
  * producer's registers; one owner per output element). */

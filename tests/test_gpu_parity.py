@@ -380,7 +380,7 @@ def test_gemm_softmax_gemm_rejects():
 
 # ------------------------------------------------ GEMM + unary activation
 
-ACTS = ["none", "relu", "gelu_tanh", "silu", "square"]
+ACTS = ["none", "relu", "gelu_tanh", "silu", "square", "rsqrt"]
 GEMM_ACT_SHAPES = [(300, 264, 72), (17, 8, 8), (512, 1024, 256), (129, 136, 1032), (8300, 4096, 64)]
 
 
@@ -406,19 +406,24 @@ def _gemm_act_run(d, M, N, act, bias=True, unfused=False):
     return host(Y)
 
 
+def _act_inputs(act, seed, M, N, K):
+    # rsqrt is defined on positive values: its operands make every A.W + bias positive
+    return gen.gemm_act_inputs(seed=seed, M=M, N=N, K=K, positive=act == "rsqrt")
+
+
 @pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("M,N,K", GEMM_ACT_SHAPES)
 def test_gemm_act(M, N, K, act):
-    d = gen.gemm_act_inputs(seed=9, M=M, N=N, K=K)
+    d = _act_inputs(act, 9, M, N, K)
     g = _gemm_act_run(d, M, N, act)
     o = oracle.gemm_act(d["a"], d["w"], d["bias"], act)
     assert act_err(g, o) <= 1.0, (act_err(g, o), cf.last_plan())
 
 
-@pytest.mark.parametrize("act", ["gelu_tanh", "silu"])
+@pytest.mark.parametrize("act", ["gelu_tanh", "silu", "rsqrt"])
 def test_gemm_act_full_size(act):
     M, N, K = 4096, 4096, 1024
-    d = gen.gemm_act_inputs(seed=9, M=M, N=N, K=K)
+    d = _act_inputs(act, 9, M, N, K)
     g = _gemm_act_run(d, M, N, act)
     plan = json.loads(cf.last_plan())
     assert plan["kernel"] == "k_gemm" and plan["schedule"] == "independent-tiles", plan
@@ -429,7 +434,7 @@ def test_gemm_act_full_size(act):
 @pytest.mark.parametrize("act", ACTS)
 def test_gemm_act_no_bias_and_unfused(act):
     M, N, K = 300, 264, 72
-    d = gen.gemm_act_inputs(seed=19, M=M, N=N, K=K)
+    d = _act_inputs(act, 19, M, N, K)
     o = oracle.gemm_act(d["a"], d["w"], None, act)
     assert act_err(_gemm_act_run(d, M, N, act, bias=False), o) <= 1.0
     assert act_err(_gemm_act_run(d, M, N, act, bias=False, unfused=True), o) <= 1.0
@@ -440,14 +445,14 @@ def test_gemm_act_no_bias_and_unfused(act):
 @pytest.mark.parametrize("act", ACTS)
 def test_gemm_act_ones_are_exact(act):
     """A = W = 1, bias = 0: every u is K = 1024, and act(1024) is a bf16 value
-    (1024, or 2^20 for the square): the output is exact.  For the gated forms
-    the gate's exponent is far below the exp2 range, so the gate is 1."""
+    (1024, 2^20 for the square, 2^-5 for rsqrt): the output is exact.  For the
+    gated forms the gate's exponent is far below the exp2 range, so the gate is 1."""
     M, N, K = 256, 512, 1024
     one = gen.f32_to_bf16_bits(np.ones(1, np.float32))[0]
     d = {"a_bits": np.full((M, K), one, np.uint16), "w_bits": np.full((K, N), one, np.uint16),
          "bias": np.zeros(N, np.float32)}
     g = _gemm_act_run(d, M, N, act)
-    want = float(K) ** 2 if act == "square" else float(K)
+    want = {"square": float(K) ** 2, "rsqrt": 1.0 / 32.0}.get(act, float(K))
     assert np.all(g == want)
 
 
@@ -468,7 +473,7 @@ def test_gemm_act_rejects():
     b = torch.zeros(65, dtype=torch.float32, device="cuda")
     assert cf.cf_workspace_bytes(cf.CF_OP_GEMM_ACT, 64, 64, 32) == 0
     with pytest.raises(cf.CFError) as e:
-        cf.cf_gemm_act(A, W, b[:64], 5, Y)  # no such activation
+        cf.cf_gemm_act(A, W, b[:64], 6, Y)  # no such activation
     assert e.value.status == cf.CF_EINVAL
     with pytest.raises(cf.CFError) as e:
         cf.cf_gemm_act(A, W, b[1:], "relu", Y)  # bias not 16-byte aligned
