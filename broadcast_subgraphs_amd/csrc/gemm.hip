@@ -2154,6 +2154,108 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
   }
 }
 
+// GEMM + unary activation on large tiles, one workgroup of NWAVES waves per
+// CU walking tiles XCD-locally.  The tiles are independent (each output
+// element has one owner), so there is no join; while a tile's epilogue runs,
+// the first NS-1 stages of the workgroup's next tile are already in flight.
+// The tile's bias slice goes to LDS with one direct load issued before the
+// MainLoop (double-buffered by tile parity, so the next tile's slice never
+// overwrites one still being read); its completion is covered by the
+// MainLoop's own waits, which retire every load issued before the last stage.
+// Lane (rb, cb) results are 16 consecutive columns of one row; each lane
+// writes its 32-byte row segment as two 16-byte stores (L2 merges the halves).
+template <int BM, int BN, int BK, int WGM, int NWAVES, int NS>
+__global__ __launch_bounds__(NWAVES * 64, 1) void k_gemm_act2(GemmArgs a) {
+  using RG = Ring<BM, BN, BK, true, NWAVES>;
+  constexpr int WGN = NWAVES / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int RB = WM / 32, CB = WN / 32;
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && WGM * WGN == NWAVES, "wave tile");
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  static_assert(BN * 4 <= 64 * 16, "one wave load carries the bias slice");
+  __shared__ __align__(16) char s0[RG::STAGE_BYTES];
+  __shared__ __align__(16) char s1[RG::STAGE_BYTES];
+  __shared__ __align__(16) char s2[NS > 2 ? RG::STAGE_BYTES : 16];
+  __shared__ __align__(16) char s3[NS > 3 ? RG::STAGE_BYTES : 16];
+  __shared__ __align__(16) float bias_sl[2][BN];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int M = (int)a.M, N = (int)a.N;
+  const int KT = (int)((a.K + BK - 1) / BK);
+  const int G = (int)gridDim.x;
+  const int g = (int)xcd_local_id(blockIdx.x, (uint32_t)G);
+  const int T = a.tiles_n;
+  const int tiles = a.tiles_m * T;
+  if (g >= tiles) return;
+  const __amdgpu_buffer_rsrc_t rA = rsrc(a.A, (uint32_t)(a.M * a.K * 2));
+  const __amdgpu_buffer_rsrc_t rB = rsrc(a.B, (uint32_t)(a.N * a.K * 2));
+  const __amdgpu_buffer_rsrc_t rY = rsrc(a.Y, (uint32_t)(a.M * a.N * 2));
+  const __amdgpu_buffer_rsrc_t rBias = rsrc(a.bias, a.bias ? (uint32_t)(a.N * 4) : 0u);  // no bias: reads zero
+  const RG rg(a);
+  char* const all_slots[4] = {s0, s1, s2, s3};
+  char* sl[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) sl[q] = all_slots[q];
+  bool staged = false;  // the tile's first stages are already in the ring
+  int par = 0;
+
+  for (int tile = g; tile < tiles; tile += G, par ^= 1) {
+    const int next = tile + G < tiles ? tile + G : -1;
+    const int m0 = (tile / T) * BM, n0 = (tile % T) * BN;
+    f32x16 acc[RB][CB];
+    zero_acc(acc);
+    if (!staged) {
+      __syncthreads();  // every wave is done with the ring
+      prologue_ns<BM, BN, BK, true, NWAVES, NS>(rg, rA, rB, sl, m0, n0, KT);
+    }
+    if (w == 0 && lane * 4 < BN) {
+      const int c = n0 + lane * 4;  // N % 8 == 0: a chunk is wholly inside or past N
+      g2l16(rBias, bias_sl[par], c < N ? (uint32_t)c * 4u : kOOB);  // lane i fills bytes [16i, 16i + 16)
+    }
+    const bool pre = next >= 0 && KT % NS == 0;
+    main_loop_ns<BM, BN, BK, true, RB, CB, NWAVES, NS>(rg, rA, rB, sl, m0, n0, pre, (next / T) * BM,
+                                                       (next % T) * BN, acc, KT, wm, wn);
+    staged = pre;
+    const float* bsl = bias_sl[par];
+    auto finish = [&](auto actc) {
+      constexpr int ACT = decltype(actc)::value;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int cl0 = wn * WN + cb * 32 + 16 * hl;
+        const int col = n0 + cl0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float4 b0 = *reinterpret_cast<const float4*>(bsl + cl0 + 8 * h);
+          const float4 b1 = *reinterpret_cast<const float4*>(bsl + cl0 + 8 * h + 4);
+          const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const int row = m0 + wm * WM + rb * 32 + l32;
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = act_fn<ACT>(acc[rb][cb][8 * h + e] + bb[e]);
+            const u32x4 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                              pack_bf16x2(o[6], o[7])};
+            const int cc = col + 8 * h;
+            bst16(rY, (row < M && cc < N) ? (uint32_t)(row * N + cc) * 2u : kOOB, pk);
+          }
+        }
+      }
+    };
+    switch (a.act) {
+      case kActRelu: finish(IntC<kActRelu>{}); break;
+      case kActGeluTanh: finish(IntC<kActGeluTanh>{}); break;
+      case kActSilu: finish(IntC<kActSilu>{}); break;
+      case kActSquare: finish(IntC<kActSquare>{}); break;
+      case kActRsqrt: finish(IntC<kActRsqrt>{}); break;
+      default: finish(IntC<kActNone>{}); break;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- dispatch
 
 struct TileCfg {
@@ -2181,7 +2283,21 @@ static const TileCfg kLnCfgs[] = {
     {128, 128, 32},  // 6: 2x2 waves of 64x64, 2-slot ring 32 KB, 2 WG/CU, pipelined
 };
 
+static const TileCfg kActCfgs[] = {
+    {256, 256, 64},  // 0: 8 waves of 128x64, 2-slot ring, 1 WG/CU
+    {256, 256, 32},  // 1: 8 waves of 128x64, 4-slot ring, 1 WG/CU
+    {256, 128, 64},  // 2: 8 waves of 64x64, 2-slot ring, 1 WG/CU
+    {256, 128, 64},  // 3: 8 waves of 64x64, 3-slot ring, 1 WG/CU
+};
+
 bool gemm_tile_config(int epi, int algo, int cfg, int* bm, int* bn, int* bk) {
+  if (epi == kEpiAct && algo == 1) {
+    if (cfg < 0 || cfg >= (int)(sizeof(kActCfgs) / sizeof(kActCfgs[0]))) return false;
+    *bm = kActCfgs[cfg].bm;
+    *bn = kActCfgs[cfg].bn;
+    *bk = kActCfgs[cfg].bk;
+    return true;
+  }
   const bool ln2 = epi == kEpiLN && algo == 1;
   const TileCfg* t = ln2 ? kLnCfgs : kCfgs;
   const int n = ln2 ? (int)(sizeof(kLnCfgs) / sizeof(kLnCfgs[0])) : (int)(sizeof(kCfgs) / sizeof(kCfgs[0]));
@@ -2249,8 +2365,20 @@ static hipError_t gemm_dispatch(int epi, const GemmPlan& pl, const GemmArgs& a, 
     return pl.algo == 1 ? launch_gemm_overlap<kEpiLN>(pl, a, st, occ) : launch_gemm_t<kEpiLN, true>(pl, a, st, occ);
   }
   if (epi == kEpiAct) {
-    if (!pl.nn || pl.algo != 0) return hipErrorInvalidConfiguration;
-    return launch_gemm_t<kEpiAct, true>(pl, a, st, occ);
+    if (!pl.nn) return hipErrorInvalidConfiguration;
+    if (pl.algo == 0) return launch_gemm_t<kEpiAct, true>(pl, a, st, occ);
+    auto go = [&](auto kfn, int threads) -> hipError_t {
+      if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kfn, threads, 0);
+      hipLaunchKernelGGL(kfn, dim3(pl.grid), dim3(threads), 0, st, a);
+      return hipGetLastError();
+    };
+    switch (pl.cfg) {
+      case 0: return go(k_gemm_act2<256, 256, 64, 2, 8, 2>, 512);  // 8 waves of 128x64, 2-slot ring 128 KB
+      case 1: return go(k_gemm_act2<256, 256, 32, 2, 8, 4>, 512);  // 8 waves of 128x64, 4-slot ring 128 KB
+      case 2: return go(k_gemm_act2<256, 128, 64, 4, 8, 2>, 512);  // 8 waves of 64x64, 2-slot ring 96 KB
+      case 3: return go(k_gemm_act2<256, 128, 64, 4, 8, 3>, 512);  // 8 waves of 64x64, 3-slot ring 144 KB
+    }
+    return hipErrorInvalidConfiguration;
   }
   if (epi == kEpiSoftmaxGemm) {
     if (pl.nn || pl.algo != 2) return hipErrorInvalidConfiguration;

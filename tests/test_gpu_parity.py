@@ -411,9 +411,11 @@ def _act_inputs(act, seed, M, N, K):
     return gen.gemm_act_inputs(seed=seed, M=M, N=N, K=K, positive=act == "rsqrt")
 
 
+@pytest.mark.parametrize("algo", [0, 1])
 @pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("M,N,K", GEMM_ACT_SHAPES)
-def test_gemm_act(M, N, K, act):
+def test_gemm_act(monkeypatch, M, N, K, act, algo):
+    monkeypatch.setenv("CF_GEMM_ACT_ALGO", str(algo))
     d = _act_inputs(act, 9, M, N, K)
     g = _gemm_act_run(d, M, N, act)
     o = oracle.gemm_act(d["a"], d["w"], d["bias"], act)
@@ -426,7 +428,7 @@ def test_gemm_act_full_size(act):
     d = _act_inputs(act, 9, M, N, K)
     g = _gemm_act_run(d, M, N, act)
     plan = json.loads(cf.last_plan())
-    assert plan["kernel"] == "k_gemm" and plan["schedule"] == "independent-tiles", plan
+    assert plan["kernel"] == "k_gemm_act2" and plan["schedule"] == "independent-tiles", plan
     o = oracle.gemm_act(d["a"], d["w"], d["bias"], act)
     assert act_err(g, o) <= 1.0, act_err(g, o)
 
@@ -458,12 +460,45 @@ def test_gemm_act_ones_are_exact(act):
 
 @pytest.mark.parametrize("cfg", range(1, 6))
 def test_gemm_act_every_tile_config(monkeypatch, cfg):
+    """The round-based kernel (128-wide tiles, two workgroups per CU) in every tile configuration."""
+    monkeypatch.setenv("CF_GEMM_ACT_ALGO", "0")
     monkeypatch.setenv("CF_GEMM_ACT_CFG", str(cfg))
     M, N, K = 300, 264, 72
     d = gen.gemm_act_inputs(seed=29, M=M, N=N, K=K)
     g = _gemm_act_run(d, M, N, "gelu_tanh")
     o = oracle.gemm_act(d["a"], d["w"], d["bias"], "gelu_tanh")
     assert act_err(g, o) <= 1.0, cf.last_plan()
+
+
+ACT2_SHAPES = [(300, 264, 72), (17, 8, 8), (129, 136, 1032), (4133, 8192, 128), (4133, 4096, 192)]
+
+
+@pytest.mark.parametrize("cfg", range(4))
+@pytest.mark.parametrize("M,N,K", ACT2_SHAPES)
+def test_gemm_act_large_tiles(monkeypatch, cfg, M, N, K):
+    """The large-tile kernel (one 8-wave workgroup per CU) in every ring
+    configuration: ragged edges, more tiles than workgroups (the next tile's
+    first stages prefetched during the epilogue when the stage count allows),
+    and each activation across the configurations."""
+    monkeypatch.setenv("CF_GEMM_ACT_ALGO", "1")
+    monkeypatch.setenv("CF_GEMM_ACT_CFG", str(cfg))
+    act = ACTS[(cfg + K) % len(ACTS)]
+    d = _act_inputs(act, 39, M, N, K)
+    g = _gemm_act_run(d, M, N, act)
+    plan = json.loads(cf.last_plan())
+    assert plan["kernel"] == "k_gemm_act2", plan
+    o = oracle.gemm_act(d["a"], d["w"], d["bias"], act)
+    assert act_err(g, o) <= 1.0, (act, act_err(g, o), plan)
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_gemm_act_large_tiles_full_size_no_bias(monkeypatch, act):
+    monkeypatch.setenv("CF_GEMM_ACT_ALGO", "1")
+    M, N, K = 4096, 4096, 1024
+    d = _act_inputs(act, 49, M, N, K)
+    g = _gemm_act_run(d, M, N, act, bias=act != "none")
+    o = oracle.gemm_act(d["a"], d["w"], d["bias"] if act != "none" else None, act)
+    assert act_err(g, o) <= 1.0, act_err(g, o)
 
 
 def test_gemm_act_rejects():
