@@ -15,7 +15,7 @@ stitched kernels reach the same values (up to rounding) by a faster route.
 Parity status: every function is pinned by closed forms, invariants, library
 routines or brute force in ``tests/test_oracle_pins.py``; none is unpinned.
 """
-from . import ops  # noqa: F401
+from . import graph, ops  # noqa: F401
 from .subgraphs import (  # noqa: F401
     ACTIVATIONS,
     gemm_act,

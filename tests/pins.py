@@ -406,4 +406,58 @@ def pin_gemm_act_rsqrt():
            what="rsqrt of a diagonal GEMM")
 
 
+def pin_graph_families_match_subgraphs():
+    """The captured graph of every stage DAG, evaluated node by node, gives the subgraph oracle's
+    values, with operands of add and mul in either order."""
+    from oracle import graph
+    from tests import graphs
+    rng = _rng(100)
+    rows, cols, k = 5, 12, 7
+    x = rng.normal(size=(rows, cols))
+    g, bt = 1.0 + 0.1 * rng.normal(size=cols), 0.1 * rng.normal(size=cols)
+    v = rng.uniform(0.1, 2.0, rows)
+    a, w, bias, r = rng.normal(size=(rows, k)), rng.normal(size=(k, cols)), rng.normal(size=cols), \
+        rng.normal(size=(rows, cols))
+    kk = rng.normal(size=(cols, k))
+    ap, wp, bp = np.abs(a) + 0.5, np.abs(w), np.abs(bias)
+    for cm in (False, True):
+        cases = [
+            (graphs.softmax(), [x], oracle.softmax_rows(x)),
+            (graphs.layernorm(cols, 1e-5, False, cm), [x], oracle.layernorm_rows(x, 1e-5)),
+            (graphs.layernorm(cols, 1e-5, True, cm), [x, g, bt], oracle.layernorm_affine_rows(x, g, bt, 1e-5)),
+            (graphs.rmsnorm(cols, 1e-5, False, cm), [x], oracle.rmsnorm_rows(x, None, 1e-5)),
+            (graphs.rmsnorm(cols, 1e-5, True, cm), [x, g], oracle.rmsnorm_rows(x, g, 1e-5)),
+            (graphs.pow_softmax(1.5, cm), [x, v], oracle.pow_bcast_add_softmax(x, v, 1.5)[0]),
+            (graphs.gemm_ln(cols, 1e-5, True, cm), [a, w, bias, r, g, bt], oracle.gemm_ln(a, w, bias, r, g, bt, 1e-5)),
+            (graphs.gemm_ln(cols, 1e-5, False, cm), [a, w, bias, None, g, bt],
+             oracle.gemm_ln(a, w, bias, None, g, bt, 1e-5)),
+            (graphs.gemm_softmax(0.3, cm), [a, kk], oracle.gemm_softmax(a, kk, 0.3)),
+        ]
+        for act in oracle.ACTIVATIONS:
+            aa, ww, bb = (ap, wp, bp) if act == "rsqrt" else (a, w, bias)
+            cases.append((graphs.gemm_act(act, True, cm), [aa, ww, bb], oracle.gemm_act(aa, ww, bb, act)))
+            cases.append((graphs.gemm_act(act, False, cm), [aa, ww], oracle.gemm_act(aa, ww, None, act)))
+        for (nodes, t), args, want in cases:
+            _close(graph.evaluate(nodes, t, args), want, 1e-12, 1e-14, what=f"graph of {nodes[t][0]} (commuted={cm})")
+
+
+def pin_graph_brute_force():
+    """A graph outside the stage DAGs, every broadcast kind and a per-row computation, against loops:
+    y_ij = (x_ij - v_i) * r_j / 2 + 3 max_l x_il;  z_ij = sum_l a_il b_jl (the transposed MatMul)."""
+    from oracle import graph
+    rng = _rng(101)
+    x, v, r = rng.normal(size=(4, 6)), rng.normal(size=4), rng.normal(size=6)
+    nodes = [("input", -1, -1, 0, 0, 0.0), ("colvec", -1, -1, 0, 1, 0.0), ("rowvec", -1, -1, 0, 2, 0.0),
+             ("const", -1, -1, 0, -1, 2.0), ("sub", 0, 1, 0, -1, 0.0), ("mul", 4, 2, 0, -1, 0.0),
+             ("div", 5, 3, 0, -1, 0.0), ("rowmax", 0, -1, 0, -1, 0.0), ("const", -1, -1, 0, -1, 3.0),
+             ("mul", 7, 8, 0, -1, 0.0), ("add", 6, 9, 0, -1, 0.0)]
+    xs, vs, rs = x.tolist(), v.tolist(), r.tolist()
+    want = [[(xs[i][j] - vs[i]) * rs[j] / 2.0 + 3.0 * max(xs[i]) for j in range(6)] for i in range(4)]
+    _close(graph.evaluate(nodes, 10, [x, v, r]), want, 1e-14, 1e-15, what="graph brute force")
+    a, b = rng.normal(size=(3, 5)), rng.normal(size=(4, 5))
+    nodes = [("operand", -1, -1, 0, 0, 0.0), ("operand", -1, -1, 0, 1, 0.0), ("matmul", 0, 1, 1, -1, 0.0)]
+    want = [[math.fsum(a[i, l] * b[j, l] for l in range(5)) for j in range(4)] for i in range(3)]
+    _close(graph.evaluate(nodes, 2, [a, b]), want, 1e-13, 1e-15, what="graph transposed MatMul")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -7,8 +7,16 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import ops, subgraphs
+from oracle import graph, ops, subgraphs
 from tests import pins
+
+
+def _graph_as_tile_swapped(kind, v, rows, cols):
+    if kind == "row":
+        return ops.bcast_row(v, rows)
+    if kind == "vec":
+        return ops.bcast_col(v, cols)
+    return graph.np.full((rows, cols), v) if kind == "scalar" else v
 
 
 def _ln_sample_variance(x, eps=1e-5):
@@ -118,6 +126,11 @@ MUTANTS = {
     "rsqrt_is_sqrt": (ops, "map_rsqrt", lambda x: np.sqrt(x)),
     "rsqrt_with_eps": (ops, "map_rsqrt", lambda x: 1.0 / np.sqrt(x + 1e-5)),
     "ln_affine_beta_scaled": (subgraphs, "layernorm_affine_rows", _ln_affine_beta_scaled),
+    "graph_broadcast_axes_swapped": (graph, "_as_tile", _graph_as_tile_swapped),
+    "graph_div_is_mul": (graph, "_BINARY", {"add": ops.add, "sub": ops.sub, "mul": ops.mul, "div": ops.mul}),
+    "graph_sub_reversed": (graph, "_BINARY", {"add": ops.add, "sub": lambda x, y: y - x, "mul": ops.mul,
+                                              "div": ops.div}),
+    "graph_silu_is_relu": (graph, "_UNARY", {**graph._UNARY, "silu": "map_relu"}),
 }
 
 
