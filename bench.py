@@ -374,9 +374,46 @@ def main():
             del w.uws
             torch.cuda.empty_cache()
 
+    # ---- Fusion Spec IR: the headline subgraph as a captured graph, lowered,
+    # matched and launched; host cost of building the spec and of one launch
+    # against the direct entry point, and the launched kernel's bits
+    spec_info = None
+    head = next((w for w in wl if w.name == HEADLINE), wl[0])
+    if head.name == "layernorm_750000x32":
+        g = cf.Graph()
+        x = g.input(0)
+        mu = g.op("div", g.op("rowsum", x), g.const(32))
+        c = g.op("sub", x, mu)
+        var = g.op("div", g.op("rowsum", g.op("square", c)), g.const(32))
+        y = g.op("mul", c, g.op("rsqrt", g.op("add", var, g.const(1e-5))))
+        t0 = time.perf_counter()
+        nb = 200
+        for _ in range(nb):
+            spec = cf.Spec(g, y, 750000, 32)
+        build_us = (time.perf_counter() - t0) / nb * 1e6
+        b0 = head.sets[0]
+        out = torch.empty_like(b0["Y"])
+        spec.launch([b0["X"]], out, ws=head.ws)
+        head.fused(head.ws)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(out, b0["Y"]))
+        nl = 200
+        t0 = time.perf_counter()
+        for _ in range(nl):
+            spec.launch([b0["X"]], out, ws=head.ws)
+        t_spec = (time.perf_counter() - t0) / nl * 1e6
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(nl):
+            head.fused(head.ws)
+        t_direct = (time.perf_counter() - t0) / nl * 1e6
+        torch.cuda.synchronize()
+        spec_info = {"match": spec.describe()["match"]["call"], "build_host_us": round(build_us, 2),
+                     "launch_host_us": round(t_spec, 2), "direct_launch_host_us": round(t_direct, 2),
+                     "bitwise_equal_to_direct": same}
+
     # ---- CPU baseline: the oracle, on rank 0, on a bounded sample
     cpu = None
-    head = next((w for w in wl if w.name == HEADLINE), wl[0])
     if not args.no_cpu:
         import oracle
         reps, t_cpu = 0, 0.0
@@ -434,6 +471,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_config": per,
+        "spec_ir": spec_info,
         "source_hash": cur_hash,
     }
     print(json.dumps(line))

@@ -15,6 +15,7 @@ import threading
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcf.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "cf.h")
+HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_HERE), "include", "cf_spec.h")]
 
 CF_OK, CF_EINVAL, CF_EUNSUPPORTED, CF_EALIGN, CF_EWORKSPACE, CF_EOCCUPANCY, CF_EHIP = range(7)
 (CF_OP_STITCH_SOFTMAX, CF_OP_STITCH_LAYERNORM, CF_OP_STITCH_POW_BCAST_ADD, CF_OP_GEMM_LN, CF_OP_GEMM_SOFTMAX,
@@ -31,6 +32,17 @@ _I64 = ctypes.c_int64
 _F = ctypes.c_float
 _SZ = ctypes.c_size_t
 _ST = ctypes.c_int
+
+class GNode(ctypes.Structure):
+    """cf_gnode: one node of a captured graph (include/cf_spec.h)."""
+    _fields_ = [("op", ctypes.c_int32), ("in0", ctypes.c_int32), ("in1", ctypes.c_int32),
+                ("attr", ctypes.c_int32), ("slot", ctypes.c_int32), ("value", ctypes.c_double)]
+
+
+# cf_gop codes by name
+G_OPS = {name: i for i, name in enumerate(
+    ["input", "operand", "matmul", "rowvec", "colvec", "tensor", "const", "add", "sub", "mul", "div", "pow",
+     "exp", "square", "rsqrt", "relu", "gelu_tanh", "silu", "rowsum", "rowmax"])}
 
 _SIGS = {
     "cf_workspace_bytes": (_SZ, [ctypes.c_int, _I64, _I64, _I64]),
@@ -61,6 +73,12 @@ _SIGS = {
     "cf_graph_destroy": (_ST, [_P]),
     "cf_util_fill_f32": (_ST, [_P, _I64, _F, _P]),
     "cf_util_copy_f32": (_ST, [_P, _P, _I64, _P]),
+    "cf_spec_build": (_ST, [ctypes.POINTER(GNode), ctypes.c_int, ctypes.c_int, _I64, _I64, _I64,
+                            ctypes.POINTER(_P)]),
+    "cf_spec_describe": (ctypes.c_int, [_P, ctypes.c_char_p, _SZ]),
+    "cf_spec_workspace_bytes": (_SZ, [_P]),
+    "cf_spec_launch": (_ST, [_P, ctypes.POINTER(_P), ctypes.c_int, _P, _P, _SZ, _P]),
+    "cf_spec_free": (None, [_P]),
 }
 
 
@@ -71,9 +89,11 @@ class CFError(RuntimeError):
 
 
 def header_functions() -> list[str]:
-    """Names of every function the C header declares."""
-    with open(HEADER_PATH) as f:
-        txt = f.read()
+    """Names of every function the C headers declare."""
+    txt = ""
+    for path in HEADER_PATHS:
+        with open(path) as f:
+            txt += f.read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b(cf_[a-z0-9_]+)\s*\(", txt)))
 
@@ -355,3 +375,87 @@ def cf_util_fill_f32(p, value=0.0, stream=None):
 
 def cf_util_copy_f32(src, dst, stream=None):
     _check("cf_util_copy_f32", lib().cf_util_copy_f32(_ptr(src), _ptr(dst), src.numel(), _stream(stream)))
+
+
+# ------------------------------------------------------------- Fusion Spec IR
+
+class Graph:
+    """A captured graph as plain node tuples (op name, in0, in1, attr, slot, value).
+
+    Each builder method appends one node and returns its index.  Placeholders
+    name the slot of their tensor in the argument list given at launch."""
+
+    def __init__(self):
+        self.nodes = []
+
+    def _add(self, op, a=-1, b=-1, attr=0, slot=-1, value=0.0):
+        self.nodes.append((op, a, b, attr, slot, float(value)))
+        return len(self.nodes) - 1
+
+    def input(self, slot):
+        return self._add("input", slot=slot)
+
+    def operand(self, slot):
+        return self._add("operand", slot=slot)
+
+    def rowvec(self, slot):
+        return self._add("rowvec", slot=slot)
+
+    def colvec(self, slot):
+        return self._add("colvec", slot=slot)
+
+    def tensor(self, slot):
+        return self._add("tensor", slot=slot)
+
+    def const(self, value):
+        return self._add("const", value=value)
+
+    def matmul(self, a, b, nt=False):
+        return self._add("matmul", a, b, attr=1 if nt else 0)
+
+    def op(self, name, a, b=-1):
+        return self._add(name, a, b)
+
+
+class Spec:
+    """cf_spec_build over a Graph; launch() enqueues the kernel it matched."""
+
+    def __init__(self, graph, terminal, rows, cols, k=0):
+        """graph: a Graph, or a list of its node tuples."""
+        nodes = graph.nodes if hasattr(graph, "nodes") else list(graph)
+        arr = (GNode * max(1, len(nodes)))()
+        for i, (op, a, b, attr, slot, value) in enumerate(nodes):
+            arr[i] = GNode(G_OPS[op], a, b, attr, slot, value)
+        h = _P()
+        self._h = None
+        _check("cf_spec_build", lib().cf_spec_build(arr, len(nodes), terminal, rows, cols, k, ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.cf_spec_free(self._h)
+            self._h = None
+
+    def describe(self) -> dict:
+        import json
+        n = lib().cf_spec_describe(self._h, None, 0)
+        buf = ctypes.create_string_buffer(n + 1)
+        lib().cf_spec_describe(self._h, buf, n + 1)
+        return json.loads(buf.value.decode())
+
+    def workspace_bytes(self) -> int:
+        return int(lib().cf_spec_workspace_bytes(self._h))
+
+    def launch(self, args, out, ws=None, stream=None):
+        """args: tensors by slot (None where unused); out: the output tensor."""
+        st = _stream(stream)
+        nb = self.workspace_bytes()
+        if nb == ctypes.c_size_t(-1).value:
+            raise CFError("cf_spec_workspace_bytes", CF_EUNSUPPORTED)
+        if ws is None:
+            ws = _workspace(nb, out.device, st)
+        ptrs = (_P * max(1, len(args)))(*[None if t is None else t.data_ptr() for t in args])
+        _check("cf_spec_launch", lib().cf_spec_launch(self._h, ptrs, len(args), _ptr(out),
+                                                      None if ws is None else ws.ptr(),
+                                                      0 if ws is None else ws.nbytes, st))
+        return ws

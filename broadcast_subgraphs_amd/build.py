@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcf.so")
-SOURCES = ["api.hip", "stitch.hip", "gemm.hip", "unfused.hip"]
+SOURCES = ["api.hip", "stitch.hip", "gemm.hip", "unfused.hip", "spec.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

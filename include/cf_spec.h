@@ -1,0 +1,118 @@
+/*
+ * cf_spec.h -- Fusion Spec IR front end of libcf.so: a captured epilogue or
+ * memory-intensive subgraph in, a launchable stitched kernel out.
+ *
+ * [ComFuse] Frontend / Fusion Spec IR (eq. 9: G_epi --Phi--> S --Psi--> T;
+ * eq. 10: S = <N, E, tau, A, C>).  The caller describes the subgraph as a
+ * list of raw operator nodes (cf_gnode).  cf_spec_build applies Phi: a
+ * top-down traversal from the root (the MatMul, or the 2-D input of a
+ * memory-intensive subgraph) that maps
+ *   - a binary operator to a broadcast node for each operand that is not a
+ *     full tile plus one computation node,
+ *   - a constant to a scalar broadcast node,
+ *   - a 1-D placeholder to a row-vector broadcast (or, for the per-row
+ *     vectors of [AStitch] "What people did before", a column broadcast)
+ *     and an entry of the runtime parameter table A,
+ *   - a unary function to a computation node,
+ *   - a row reduction to a split: the nodes after it form a nested S (C)
+ *     whose entry points are a placeholder for the reduction's statistic
+ *     and placeholders for the tensors from before the reduction that the
+ *     later nodes still read (the passthrough of LayerNorm's x - mean).
+ * Psi here does not generate code: it walks S structurally into a canonical
+ * form and matches it against the stage DAGs the library's precompiled
+ * kernels implement, binding the graph's constants and placeholders to the
+ * kernel's arguments.  A graph outside Phi's pattern set, or whose S matches
+ * no kernel, is refused with CF_EUNSUPPORTED and nothing else happens (the
+ * caller falls back to its own path): a spec that builds computes exactly
+ * the graph's semantics.
+ *
+ * Accepted forms (operand order of ADD and MUL is free; association is not):
+ *   softmax        e = exp(x - rowmax(x)); y = e / rowsum(e)
+ *   LayerNorm      mu = rowsum(x) / cols; c = x - mu;
+ *                  y = c * rsqrt(rowsum(square(c)) / cols + eps)   [* gamma + beta]
+ *   RMSNorm        y = x * rsqrt(rowsum(square(x)) / cols + eps)   [* gamma]
+ *   pow-softmax    softmax(x + pow(v, p)), v a per-row vector
+ *   GEMM+LN        the LayerNorm form on u = (A.W + bias) [+ R], with gamma, beta
+ *   GEMM+softmax   the softmax form on A.B^T * scale
+ *   GEMM+act       act(A.W [+ bias]), act one of RELU, GELU_TANH, SILU, SQUARE,
+ *                  RSQRT, or none (the MatMul, or MatMul + bias, is the output)
+ * Constants: the row length in a mean must equal cols; eps >= 0, p, scale
+ * are bound as arguments.
+ */
+#ifndef CF_SPEC_H
+#define CF_SPEC_H
+
+#include "cf.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Operator kinds of a captured graph node. */
+typedef enum cf_gop {
+  CF_G_INPUT = 0,     /* 2-D fp32 input [rows x cols] of a memory-intensive subgraph      */
+  CF_G_OPERAND = 1,   /* 2-D bf16 MatMul operand placeholder                             */
+  CF_G_MATMUL = 2,    /* in0 . in1 (attr 0: in1 is [K x cols]; attr 1: in1 is [cols x K]) */
+  CF_G_ROWVEC = 3,    /* 1-D fp32 placeholder of length cols (row-vector broadcast)      */
+  CF_G_COLVEC = 4,    /* 1-D fp32 placeholder of length rows (one value per row)         */
+  CF_G_TENSOR = 5,    /* 2-D bf16 placeholder [rows x cols] added elementwise (residual) */
+  CF_G_CONST = 6,     /* scalar constant `value`                                         */
+  CF_G_ADD = 7,
+  CF_G_SUB = 8,
+  CF_G_MUL = 9,
+  CF_G_DIV = 10,
+  CF_G_POW = 11,      /* in0 ^ in1 (in1 a constant)                                      */
+  CF_G_EXP = 12,
+  CF_G_SQUARE = 13,
+  CF_G_RSQRT = 14,
+  CF_G_RELU = 15,
+  CF_G_GELU_TANH = 16,
+  CF_G_SILU = 17,
+  CF_G_ROWSUM = 18,   /* reduction over the row: one value per row                       */
+  CF_G_ROWMAX = 19
+} cf_gop;
+
+/* One node of the captured graph.  Inputs refer to earlier nodes (-1 when
+ * unused).  Placeholders (INPUT, OPERAND, ROWVEC, COLVEC, TENSOR) name the
+ * index of their device pointer in the `args` array of cf_spec_launch. */
+typedef struct cf_gnode {
+  int32_t op;
+  int32_t in0, in1;
+  int32_t attr;  /* MATMUL: operand layout (see CF_G_MATMUL) */
+  int32_t slot;  /* placeholders: index into args[] */
+  double value;  /* CONST */
+} cf_gnode;
+
+typedef struct cf_spec cf_spec;
+
+/* Phi then Psi for the graph nodes[0..n) with output node `terminal`, for
+ * output rows x cols (and reduction depth k for a MatMul root, else 0).
+ * Host-only (no device call).  On success *out receives a spec owned by the
+ * caller (free with cf_spec_free).  CF_EINVAL: malformed graph (bad index,
+ * cycle, missing input).  CF_EUNSUPPORTED: outside Phi's patterns, or no
+ * kernel implements its S. */
+cf_status cf_spec_build(const cf_gnode* nodes, int n, int terminal, int64_t rows, int64_t cols, int64_t k,
+                        cf_spec** out);
+
+/* JSON description of S (levels, node categories, edges, tau, parameter
+ * table A, nesting C) and of Psi's match (kernel, bound constants and
+ * arguments), NUL-terminated and truncated to n.  Returns the full length. */
+int cf_spec_describe(const cf_spec* s, char* buf, size_t n);
+
+/* Workspace bytes the matched kernel needs (cf_workspace_bytes of its op). */
+size_t cf_spec_workspace_bytes(const cf_spec* s);
+
+/* Enqueue the matched kernel: args[slot] are the device pointers of the
+ * graph's placeholders, out the terminal's output (fp32 for a
+ * memory-intensive subgraph, bf16 for a MatMul root).  Same rules, errors
+ * and workspace contract as the entry point it dispatches to. */
+cf_status cf_spec_launch(const cf_spec* s, const void* const* args, int nargs, void* out, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+void cf_spec_free(cf_spec* s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CF_SPEC_H */
