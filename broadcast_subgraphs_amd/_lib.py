@@ -79,6 +79,11 @@ _SIGS = {
     "cf_spec_workspace_bytes": (_SZ, [_P]),
     "cf_spec_launch": (_ST, [_P, ctypes.POINTER(_P), ctypes.c_int, _P, _P, _SZ, _P]),
     "cf_spec_free": (None, [_P]),
+    "cf_auto_build": (_ST, [ctypes.POINTER(GNode), ctypes.c_int, ctypes.c_int, _I64, _I64, ctypes.POINTER(_P)]),
+    "cf_auto_describe": (ctypes.c_int, [_P, ctypes.c_char_p, _SZ]),
+    "cf_auto_source": (ctypes.c_int, [_P, ctypes.c_char_p, _SZ]),
+    "cf_auto_launch": (_ST, [_P, ctypes.POINTER(_P), ctypes.c_int, _P, _P]),
+    "cf_auto_free": (None, [_P]),
 }
 
 
@@ -459,3 +464,46 @@ class Spec:
                                                       None if ws is None else ws.ptr(),
                                                       0 if ws is None else ws.nbytes, st))
         return ws
+
+
+def _gnodes(graph):
+    nodes = graph.nodes if hasattr(graph, "nodes") else list(graph)
+    arr = (GNode * max(1, len(nodes)))()
+    for i, (op, a, b, attr, slot, value) in enumerate(nodes):
+        arr[i] = GNode(G_OPS[op], a, b, attr, slot, value)
+    return arr, len(nodes)
+
+
+class Auto:
+    """cf_auto_build over a Graph (or its node tuples): a generated stitched kernel."""
+
+    def __init__(self, graph, terminal, rows, cols):
+        arr, n = _gnodes(graph)
+        h = _P()
+        self._h = None
+        _check("cf_auto_build", lib().cf_auto_build(arr, n, terminal, rows, cols, ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.cf_auto_free(self._h)
+            self._h = None
+
+    def _text(self, fn) -> str:
+        n = fn(self._h, None, 0)
+        buf = ctypes.create_string_buffer(n + 1)
+        fn(self._h, buf, n + 1)
+        return buf.value.decode()
+
+    def describe(self) -> dict:
+        import json
+        return json.loads(self._text(lib().cf_auto_describe))
+
+    def source(self) -> str:
+        return self._text(lib().cf_auto_source)
+
+    def launch(self, args, out, stream=None):
+        """args: fp32 tensors by slot (None where unused); out: fp32 [rows, cols]."""
+        st = _stream(stream)
+        ptrs = (_P * max(1, len(args)))(*[None if t is None else t.data_ptr() for t in args])
+        _check("cf_auto_launch", lib().cf_auto_launch(self._h, ptrs, len(args), _ptr(out), st))

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcf.so")
-SOURCES = ["api.hip", "stitch.hip", "gemm.hip", "unfused.hip", "spec.cpp"]
+SOURCES = ["api.hip", "stitch.hip", "gemm.hip", "unfused.hip", "spec.cpp", "auto.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -34,12 +34,13 @@ FLAGS = [
     "-Rpass-analysis=kernel-resource-usage",
     "-I", os.path.join(ROOT, "include"),
 ]
+LIBS = ["-lhiprtc"]  # the runtime compiler for automatically stitched kernels
 
 
 def build(verbose: bool = False) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp, *LIBS]
     proc = subprocess.run(cmd, cwd=CSRC, capture_output=True, text=True)
     report = os.path.join(PKG, "libcf.resources.txt")
     with open(report, "w") as f:

@@ -111,6 +111,51 @@ cf_status cf_spec_launch(const cf_spec* s, const void* const* args, int nargs, v
 
 void cf_spec_free(cf_spec* s);
 
+/* ------------------------------------------------------------------------ */
+/* Automatic stitching of an arbitrary memory-intensive graph.                */
+/*                                                                            */
+/* [AStitch] "Making it automatic" (dominant ops, index propagation, merging  */
+/* of dominants, passive block-locality check), "Four stitching schemes"      */
+/* (where each value lives), "Adaptive thread mapping".  For graphs outside   */
+/* Psi's kernel set: the scheduler finds the dominants (row reductions,       */
+/* expensive ops whose per-row result feeds a broadcast, the output),         */
+/* propagates the row-fragment thread mapping from them through the           */
+/* one-to-one ops, merges them into one stitched group, decides per edge      */
+/* whether the value stays in the thread's registers (Local) or crosses       */
+/* waves through LDS (Regional), picks the mapping by the row length, and     */
+/* generates one HIP kernel for the group, compiled at build time with        */
+/* hiprtc for gfx950.                                                         */
+/*                                                                            */
+/* Accepted graphs: CF_G_INPUT placeholders (any number, fp32 [rows x cols]), */
+/* ROWVEC, COLVEC, CONST, the binary and unary operators, ROWSUM and ROWMAX;  */
+/* the terminal is a tile.  Rows of up to 32768 values (one workgroup per     */
+/* row at most); wider rows would need the Global scheme and are refused.     */
+/* ------------------------------------------------------------------------ */
+
+typedef struct cf_auto cf_auto;
+
+/* Schedule the graph, generate its kernel and compile it (host only: no
+ * device call).  CF_EINVAL: malformed graph; CF_EUNSUPPORTED: outside the
+ * accepted graphs; CF_EHIP: the runtime compiler failed. */
+cf_status cf_auto_build(const cf_gnode* nodes, int n, int terminal, int64_t rows, int64_t cols,
+                        cf_auto** out);
+
+/* JSON: dominants, merged groups, per-edge stitching scheme, thread mapping,
+ * parameters, generated source and code sizes.  Returns the full length. */
+int cf_auto_describe(const cf_auto* a, char* buf, size_t n);
+
+/* The generated HIP source.  Returns the full length. */
+int cf_auto_source(const cf_auto* a, char* buf, size_t n);
+
+/* Enqueue the generated kernel: args[slot] are the placeholders' device
+ * pointers, out the fp32 [rows x cols] output (not overlapping any input).
+ * Loads the code object on the current device at its first launch there.
+ * 16-byte aligned pointers and cols % 4 == 0 select the 16-byte-fragment
+ * variant, anything else the 4-byte one.  No workspace. */
+cf_status cf_auto_launch(cf_auto* a, const void* const* args, int nargs, float* out, hipStream_t stream);
+
+void cf_auto_free(cf_auto* a);
+
 #ifdef __cplusplus
 }
 #endif

@@ -96,3 +96,45 @@ def gemm_act(act, bias=True, commuted=False):
     if act != "none":
         u = b.add(act, u)
     return b.nodes, u
+
+
+# Graphs outside the library's stage DAGs (for the automatic stitcher).
+
+def silu_ln_scaled(cols):
+    """y = LayerNorm(silu(x) + b) * v_i, b a row vector (slot 1), v a per-row vector (slot 2)."""
+    b = B()
+    x = b.ph("input", 0)
+    u = b.add("add", b.add("silu", x), b.ph("rowvec", 1))
+    y = layernorm_chain(b, u, cols, 1e-5)
+    return b.nodes, b.add("mul", y, b.ph("colvec", 2))
+
+
+def softmax_temperature():
+    """softmax(x * t_i), t a per-row temperature (slot 1)."""
+    b = B()
+    return b.nodes, softmax_chain(b, b.add("mul", b.ph("input", 0), b.ph("colvec", 1)))
+
+
+def residual_ln(cols):
+    """LayerNorm(x + r) * gamma + beta with two fp32 inputs: x (0), r (1); gamma (2), beta (3)."""
+    b = B()
+    u = b.add("add", b.ph("input", 0), b.ph("input", 1))
+    return b.nodes, layernorm_chain(b, u, cols, 1e-5, True, g=2, bt=3)
+
+
+def gelu_centered():
+    """gelu(x) - rowmax(gelu(x)) + v_i^2 / 3 (v slot 1)."""
+    b = B()
+    gx = b.add("gelu_tanh", b.ph("input", 0))
+    d = b.add("sub", gx, b.add("rowmax", gx))
+    pv = b.add("div", b.add("pow", b.ph("colvec", 1), b.c(2.0)), b.c(3.0))
+    return b.nodes, b.add("add", d, pv)
+
+
+def rms_relu(cols):
+    """relu(RMSNorm(x) * g) with g a row vector (slot 1)."""
+    b = B()
+    x = b.ph("input", 0)
+    ms = b.add("div", b.add("rowsum", b.add("square", x)), b.c(cols))
+    y = b.add("mul", b.add("mul", x, b.add("rsqrt", b.add("add", ms, b.c(1e-6)))), b.ph("rowvec", 1))
+    return b.nodes, b.add("relu", y)

@@ -1,0 +1,69 @@
+"""Automatic stitching on the host (no GPU): the schedule, the thread mapping, the generated kernel
+(compiled with hiprtc for gfx950 here), and the graphs it refuses.
+
+[AStitch] "Making it automatic" (dominants, index propagation, merging, locality check), "Four
+stitching schemes", "Adaptive thread mapping".
+"""
+import pytest
+
+import broadcast_subgraphs_amd as cf
+from tests import graphs
+
+
+def auto(g, rows, cols):
+    nodes, t = g
+    return cf.Auto(nodes, t, rows, cols)
+
+
+@pytest.mark.parametrize("cols,lanes,frags,wg,waves", [
+    (32, 8, 1, 256, 1), (33, 8, 2, 256, 1), (5, 8, 1, 256, 1), (1024, 64, 4, 256, 1), (1000, 64, 4, 256, 1),
+    (4096, 256, 4, 256, 4), (30000, 1024, 8, 1024, 16), (32768, 1024, 8, 1024, 16)])
+def test_thread_mapping_follows_the_row_length(cols, lanes, frags, wg, waves):
+    d = auto(graphs.layernorm(cols), 100, cols).describe()
+    m = d["mapping"]
+    assert (m["lanes_per_row"], m["frags_per_lane"], m["workgroup"], m["waves_per_row"]) == (lanes, frags, wg, waves)
+    assert m["rows_per_workgroup"] == wg // lanes
+    assert lanes * frags * 4 >= cols
+    # reductions cross waves through LDS only when a row spans several waves
+    schemes = {e["scheme"] for e in d["edges"]}
+    assert schemes == ({"local", "regional"} if waves > 1 else {"local"})
+    assert d["kernels"] == 1 and d["code_bytes"] > 0
+
+
+def test_dominants_and_merge():
+    d = auto(graphs.pow_softmax(1.5), 64, 30000).describe()
+    kinds = [(x["op"], x["kind"]) for x in d["dominants"]]
+    # v^p is computed once per row and broadcast; the two reductions and the output
+    assert ("pow", "expensive_broadcast") in kinds
+    assert kinds.count(("rowmax", "reduce")) == 1 and kinds.count(("rowsum", "reduce")) == 1
+    assert kinds[-1][1] == "output"
+    assert len(d["groups"]) == 1 and sorted(d["groups"][0]["dominants"]) == sorted(x["node"] for x in d["dominants"])
+    assert [p["kind"] for p in d["params"]] == ["input", "colvec"]
+
+
+def test_generated_source_has_both_variants():
+    a = auto(graphs.softmax(), 256, 1024)
+    src = a.source()
+    assert "k_auto_vec" in src and "k_auto_scalar" in src
+    assert src.count("__shfl_xor") == 2 * 2 * 6  # two reductions of 64 lanes, in both variants
+
+
+def test_refusals():
+    with pytest.raises(cf.CFError) as e:
+        auto(graphs.gemm_act("relu"), 64, 64)  # a MatMul root takes the GEMM entry points
+    assert e.value.status == cf.CF_EUNSUPPORTED
+    with pytest.raises(cf.CFError) as e:
+        auto(graphs.layernorm(32769), 4, 32769)  # a row wider than one workgroup: the Global scheme
+    assert e.value.status == cf.CF_EUNSUPPORTED
+    b = graphs.B()
+    with pytest.raises(cf.CFError) as e:
+        auto((b.nodes, b.add("rowsum", b.ph("input", 0))), 4, 8)  # a per-row output
+    assert e.value.status == cf.CF_EUNSUPPORTED
+    b = graphs.B()
+    with pytest.raises(cf.CFError) as e:
+        auto((b.nodes, b.add("exp", b.ph("input", 99))), 4, 8)  # slot out of range
+    assert e.value.status == cf.CF_EINVAL
+    b = graphs.B()
+    with pytest.raises(cf.CFError) as e:
+        auto((b.nodes, b.add("exp", b.ph("rowvec", 0))), 4, 8)  # no input tile to drive the rows
+    assert e.value.status == cf.CF_EUNSUPPORTED

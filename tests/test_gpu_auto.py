@@ -1,0 +1,79 @@
+"""Automatically stitched kernels on the GPU against the graph oracle (oracle.graph.evaluate)."""
+import numpy as np
+import pytest
+import torch
+
+import broadcast_subgraphs_amd as cf
+import gen
+import oracle
+from tests import graphs
+from tests.test_gpu_parity import TOL_F32, d32, host, rownorm_err
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1000, 32), (999, 36), (5, 3), (7, 100), (33, 1024), (3, 5000), (4, 30000), (2, 32768), (4099, 33)]
+
+
+def _inputs(rows, cols, seed):
+    x = gen.normal(seed, 0, (rows, cols))
+    r = gen.normal(seed, 1, (rows, cols))
+    g = (1.0 + 0.1 * gen.normal(seed, 2, (cols,)).astype(np.float64)).astype(np.float32)
+    bt = gen.normal(seed, 3, (cols,), std=0.1)
+    v = gen.uniform(seed, 4, (rows,), 0.1, 2.0)
+    return x, r, g, bt, v
+
+
+def _cases(rows, cols, x, r, g, bt, v):
+    return [
+        ("softmax", graphs.softmax(), [x]),
+        ("layernorm", graphs.layernorm(cols), [x]),
+        ("layernorm_affine", graphs.layernorm(cols, 1e-5, True), [x, g, bt]),
+        ("rmsnorm_gain", graphs.rmsnorm(cols, 1e-5, True), [x, g]),
+        ("pow_softmax", graphs.pow_softmax(1.5), [x, v]),
+        ("silu_ln_scaled", graphs.silu_ln_scaled(cols), [x, bt, v]),
+        ("softmax_temperature", graphs.softmax_temperature(), [x, v]),
+        ("residual_ln", graphs.residual_ln(cols), [x, r, g, bt]),
+        ("gelu_centered", graphs.gelu_centered(), [x, v]),
+        ("rms_relu", graphs.rms_relu(cols), [x, g]),
+    ]
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+def test_auto_graphs(rows, cols):
+    x, r, g, bt, v = _inputs(rows, cols, 70 + cols % 17)
+    for name, (nodes, t), hargs in _cases(rows, cols, x, r, g, bt, v):
+        a = cf.Auto(nodes, t, rows, cols)
+        out = torch.full((rows, cols), float("nan"), device="cuda")
+        a.launch([d32(h) for h in hargs], out)
+        got = host(out)
+        want = oracle.graph.evaluate(nodes, t, hargs)
+        assert rownorm_err(got, want) <= TOL_F32, (name, a.describe()["mapping"])
+
+
+def test_auto_misaligned_takes_the_scalar_variant_and_repeats_bitwise():
+    rows, cols = 513, 64
+    x, r, g, bt, v = _inputs(rows, cols, 90)
+    nodes, t = graphs.residual_ln(cols)
+    a = cf.Auto(nodes, t, rows, cols)
+    buf = torch.full((rows * cols + 1,), float("nan"), device="cuda")
+    out = buf[1:].view(rows, cols)  # 4-byte aligned only
+    args = [d32(x), d32(r), d32(g), d32(bt)]
+    a.launch(args, out)
+    got = host(out)
+    assert rownorm_err(got, oracle.graph.evaluate(nodes, t, [x, r, g, bt])) <= TOL_F32
+    out2 = torch.empty((rows, cols), device="cuda")
+    a.launch(args, out2)
+    a.launch(args, out2)
+    assert np.array_equal(host(out2), got)  # the 16-byte variant computes the same bits
+
+
+def test_auto_launch_rejects_overlap_and_missing_args():
+    nodes, t = graphs.layernorm(32)
+    a = cf.Auto(nodes, t, 16, 32)
+    X = torch.zeros((16, 32), device="cuda")
+    with pytest.raises(cf.CFError) as e:
+        a.launch([X], X)
+    assert e.value.status == cf.CF_EINVAL
+    with pytest.raises(cf.CFError) as e:
+        a.launch([], torch.empty_like(X))
+    assert e.value.status == cf.CF_EINVAL
