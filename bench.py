@@ -49,6 +49,8 @@ KERNEL_SOURCES = {
     "rmsnorm_750000x32": ("stitch.hip", "dev.hpp"),
     "layernorm_affine_750000x32": ("stitch.hip", "dev.hpp"),
     "gemm_gelu_4096x4096x1024": ("gemm.hip", "dev.hpp"),
+    "auto_layernorm_750000x32": ("auto.cpp",),
+    "auto_silu_ln_scaled_750000x32": ("auto.cpp",),
 }
 
 
@@ -175,11 +177,34 @@ class Workload:
             self.flops = 2 * M * N * K
             call = lambda b, ws, u: cf.cf_gemm_act(b["A"], b["W"], b["bias"], "gelu_tanh", b["Y"], ws=ws, unfused=u)
             self.op, self.dims = cf.CF_OP_GEMM_ACT, (M, N, K)
+        elif name in ("auto_layernorm_750000x32", "auto_silu_ln_scaled_750000x32"):
+            # the same subgraph as a captured graph, stitched automatically into
+            # a generated kernel (and a graph outside the library's stage DAGs)
+            d = gen.layernorm_affine_inputs(seed=10)
+            v = gen.uniform(10, 5, (750000,), 0.1, 2.0)
+            self.inp = {"x": d["x"], "beta": d["beta"], "v": v}
+            g = cf.Graph()
+            x = g.input(0)
+            u = g.op("add", g.op("silu", x), g.rowvec(1)) if name.startswith("auto_silu") else x
+            mu = g.op("div", g.op("rowsum", u), g.const(32))
+            c = g.op("sub", u, mu)
+            var = g.op("div", g.op("rowsum", g.op("square", c)), g.const(32))
+            y = g.op("mul", c, g.op("rsqrt", g.op("add", var, g.const(1e-5))))
+            if name.startswith("auto_silu"):
+                y = g.op("mul", y, g.colvec(2))
+            self.graph = (g.nodes, y)
+            auto = cf.Auto(g, y, 750000, 32)
+            self.plan_auto = auto.describe()
+            bufs = {"X": d32(d["x"]), "B": d32(d["beta"]), "V": d32(v), "Y": torch.empty(750000, 32, device=dev)}
+            extra = 0 if name.startswith("auto_layernorm") else d["beta"].nbytes + v.nbytes
+            self.bytes, self.flops = 2 * d["x"].nbytes + extra, 0
+            call = lambda b, ws, u: auto.launch([b["X"], b["B"], b["V"]], b["Y"])
+            self.op, self.dims = None, (750000, 32, 0)
         else:
             raise ValueError(name)
         self.bound = "mfma" if name in ("gemm_ln_4096x4096x1024", "gemm_softmax_gemm_8192x8192x128x128",
                                         "gemm_gelu_4096x4096x1024") else "hbm"
-        nb = cf.cf_workspace_bytes(self.op, *self.dims)
+        nb = cf.cf_workspace_bytes(self.op, *self.dims) if self.op is not None else 0
         self.ws = cf.Workspace(nb) if nb else None
         self.uws = None
         self.copies = max(2, -(-ROTATE_BYTES // self.bytes))
@@ -188,6 +213,9 @@ class Workload:
         self.fused = lambda ws=None: call(self.sets[0], ws, False)
         self.unfused = lambda ws=None: call(self.sets[0], ws, True)
         self.out = self.sets[0]["Y"] if "Y" in bufs else self.sets[0]["S"]
+        if self.op is None:
+            call(self.sets[0], None, False)  # the code object loads here, not under graph capture
+            torch.cuda.synchronize()
 
     def oracle_once(self, oracle):
         d = self.inp
@@ -207,6 +235,8 @@ class Workload:
             return oracle.layernorm_affine_rows(d["x"], d["gamma"], d["beta"], 1e-5)
         if self.name == "gemm_gelu_4096x4096x1024":
             return oracle.gemm_act(d["a"], d["w"], d["bias"], "gelu_tanh")
+        if self.name.startswith("auto_"):
+            return oracle.graph.evaluate(self.graph[0], self.graph[1], [d["x"], d["beta"], d["v"]])
         return oracle.gemm_softmax(d["q"], d["k"], d["scale"])
 
 
@@ -214,7 +244,7 @@ WORKLOAD_NAMES = ["softmax_256x1024", "layernorm_750000x32", "pow_bcast_add_soft
                   "gemm_ln_4096x4096x1024", "gemm_softmax_8192x8192x128"]
 # measured per kernel (and unfused) but outside the step
 EXTRA_NAMES = ["gemm_softmax_gemm_8192x8192x128x128", "rmsnorm_750000x32", "layernorm_affine_750000x32",
-               "gemm_gelu_4096x4096x1024"]
+               "gemm_gelu_4096x4096x1024", "auto_layernorm_750000x32", "auto_silu_ln_scaled_750000x32"]
 
 
 def main():
@@ -331,7 +361,7 @@ def main():
     # plans (one extra untimed call each)
     for w in wl_all:
         w.fused(w.ws)
-        per[w.name]["plan"] = json.loads(cf.last_plan())
+        per[w.name]["plan"] = json.loads(cf.last_plan()) if w.op is not None else w.plan_auto
     torch.cuda.synchronize()
     for w in wl_all:
         if w.ws is not None:
@@ -340,6 +370,8 @@ def main():
     # ---- unfused baselines, stream-launched and graph-replayed
     if not args.no_unfused:
         for w in wl_all:
+            if w.op is None:
+                continue  # a generated kernel has no unfused twin
             w.uws = cf.Workspace(cf.cf_unfused_workspace_bytes(w.op, *w.dims))
             ks = max(3, min(args.steps, 10))
             for _ in range(2):
