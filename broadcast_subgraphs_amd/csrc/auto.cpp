@@ -62,6 +62,7 @@ struct cf_auto {
   std::vector<std::pair<int, int>> dominants;  // (node, kind)
   std::vector<Edge> edges;
   int lanes = 0, frags = 0, wg = 0, rows_per_wg = 0, waves_per_row = 0;
+  std::string name;  // generated kernel name prefix (unique per graph and mapping)
   std::string src;
   std::vector<char> code;
   std::mutex mu;
@@ -336,7 +337,7 @@ std::string generate(const cf_auto* A) {
        "__device__ __forceinline__ f4 ntld4(const f4* p) { return __builtin_nontemporal_load(p); }\n";
   for (int vec = 1; vec >= 0; --vec) {
     snprintf(b, sizeof b,
-             "extern \"C\" __global__ __launch_bounds__(%d) void k_auto_%s(AutoArgs a) {\n"
+             "extern \"C\" __global__ __launch_bounds__(%d) void %s_%s(AutoArgs a) {\n"
              "  const long rows = a.rows, cols = a.cols;\n"
              "  const int rl = threadIdx.x %% %d, rg = threadIdx.x / %d;\n"
              "  %s\n"
@@ -344,7 +345,7 @@ std::string generate(const cf_auto* A) {
              "    const long row = rb + rg;\n"
              "    const bool rok = row < rows;\n"
              "    {\n",
-             A->wg, vec ? "vec" : "scalar", A->lanes, A->lanes,
+             A->wg, A->name.c_str(), vec ? "vec" : "scalar", A->lanes, A->lanes,
              A->waves_per_row > 1 ? "__shared__ float red[2][16]; int slot = 0;" : "", A->rows_per_wg,
              A->rows_per_wg);
     s += b;
@@ -402,6 +403,23 @@ cf_status cf_auto_build(const cf_gnode* nodes, int n, int terminal, int64_t rows
   cf_status st = infer(A);
   if (st == CF_OK) st = schedule(A);
   if (st == CF_OK) {
+    // name: FNV-1a of the live graph and the mapping, so profiles tell generated kernels apart
+    uint64_t h = 1469598103934665603ull;
+    auto mix = [&](const void* p, size_t n) {
+      for (size_t i = 0; i < n; ++i) h = (h ^ static_cast<const unsigned char*>(p)[i]) * 1099511628211ull;
+    };
+    for (size_t i = 0; i < A->g.size(); ++i)
+      if (A->live[i]) {
+        const cf_gnode& q = A->g[i];
+        const int32_t f[5] = {q.op, q.in0, q.in1, q.attr, q.slot};
+        mix(f, sizeof f);
+        mix(&q.value, sizeof q.value);
+      }
+    const int m[2] = {A->lanes, A->frags};
+    mix(m, sizeof m);
+    char nm[32];
+    snprintf(nm, sizeof nm, "k_auto_%08x", (unsigned)(h ^ (h >> 32)));
+    A->name = nm;
     A->src = generate(A);
     st = compile(A);
   }
@@ -445,7 +463,8 @@ int cf_auto_describe(const cf_auto* A, char* buf, size_t n) {
     j += t;
     first = false;
   }
-  snprintf(t, sizeof t, "],\"kernels\":1,\"source_bytes\":%zu,\"code_bytes\":%zu}", A->src.size(), A->code.size());
+  snprintf(t, sizeof t, "],\"kernels\":1,\"kernel\":\"%s_vec\",\"source_bytes\":%zu,\"code_bytes\":%zu}",
+           A->name.c_str(), A->src.size(), A->code.size());
   j += t;
   if (buf && n > 0) {
     const size_t m = std::min(n - 1, j.size());
@@ -495,8 +514,8 @@ cf_status cf_auto_launch(cf_auto* A, const void* const* args, int nargs, float* 
       hipModule_t m = nullptr;
       if (hipModuleLoadData(&m, A->code.data()) != hipSuccess) return CF_EHIP;
       hipFunction_t fv = nullptr, fs = nullptr;
-      if (hipModuleGetFunction(&fv, m, "k_auto_vec") != hipSuccess ||
-          hipModuleGetFunction(&fs, m, "k_auto_scalar") != hipSuccess) {
+      if (hipModuleGetFunction(&fv, m, (A->name + "_vec").c_str()) != hipSuccess ||
+          hipModuleGetFunction(&fs, m, (A->name + "_scalar").c_str()) != hipSuccess) {
         (void)hipModuleUnload(m);
         return CF_EHIP;
       }

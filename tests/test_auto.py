@@ -44,7 +44,9 @@ def test_dominants_and_merge():
 def test_generated_source_has_both_variants():
     a = auto(graphs.softmax(), 256, 1024)
     src = a.source()
-    assert "k_auto_vec" in src and "k_auto_scalar" in src
+    name = a.describe()["kernel"]
+    assert name.startswith("k_auto_") and name.endswith("_vec")
+    assert name in src and name.replace("_vec", "_scalar") in src
     assert src.count("__shfl_xor") == 2 * 2 * 6  # two reductions of 64 lanes, in both variants
 
 
