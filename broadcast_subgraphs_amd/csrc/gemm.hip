@@ -2173,6 +2173,12 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void k_gemm_act2(GemmArgs a) {
   static_assert(WM % 32 == 0 && WN % 32 == 0 && WGM * WGN == NWAVES, "wave tile");
   static_assert(NS >= 2 && NS <= 4, "ring depth");
   static_assert(BN * 4 <= 64 * 16, "one wave load carries the bias slice");
+  constexpr int THREADS = NWAVES * 64;
+  constexpr int C16 = BN * 2 / 16;  // 16-byte chunks per bf16 output row
+  // output rows staged per chunk: the largest power of two (at most BM) whose rows fit one slot
+  constexpr int RC0 = RG::STAGE_BYTES / (BN * 2);
+  constexpr int RC = RC0 >= BM ? BM : (RC0 >= 128 ? 128 : (RC0 >= 64 ? 64 : 32));
+  static_assert(RC0 >= 32 && BM % RC == 0 && (RC * C16) % THREADS == 0 && C16 >= 16, "output staging");
   __shared__ __align__(16) char s0[RG::STAGE_BYTES];
   __shared__ __align__(16) char s1[RG::STAGE_BYTES];
   __shared__ __align__(16) char s2[NS > 2 ? RG::STAGE_BYTES : 16];
@@ -2220,29 +2226,49 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void k_gemm_act2(GemmArgs a) {
                                                        (next % T) * BN, acc, KT, wm, wn);
     staged = pre;
     const float* bsl = bias_sl[par];
+    // The results leave through the ring's last slot (free here: the next
+    // tile's prefetch fills the others) in chunks of RC whole rows, then as
+    // non-temporal 16-byte stores of whole row segments: one write per
+    // output line instead of two half-line writes from the lane layout.
+    uint16_t* const stg = reinterpret_cast<uint16_t*>(sl[NS - 1]);
+    __syncthreads();  // every wave is done reading the last slot
     auto finish = [&](auto actc) {
       constexpr int ACT = decltype(actc)::value;
+#pragma unroll 1
+      for (int q = 0; q < BM / RC; ++q) {
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int cl0 = wn * WN + cb * 32 + 16 * hl;
-        const int col = n0 + cl0;
+        for (int cb = 0; cb < CB; ++cb) {
+          const int cl0 = wn * WN + cb * 32 + 16 * hl;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float4 b0 = *reinterpret_cast<const float4*>(bsl + cl0 + 8 * h);
-          const float4 b1 = *reinterpret_cast<const float4*>(bsl + cl0 + 8 * h + 4);
-          const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+          for (int h = 0; h < 2; ++h) {
+            const float4 b0 = *reinterpret_cast<const float4*>(bsl + cl0 + 8 * h);
+            const float4 b1 = *reinterpret_cast<const float4*>(bsl + cl0 + 8 * h + 4);
+            const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            const int row = m0 + wm * WM + rb * 32 + l32;
-            float o[8];
+            for (int rb = 0; rb < RB; ++rb) {
+              const int rl = wm * WM + rb * 32;  // the wave's 32 rows of this block (uniform)
+              if (rl / RC != q) continue;
+              const int rr = rl - q * RC + l32;
+              float o[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = act_fn<ACT>(acc[rb][cb][8 * h + e] + bb[e]);
-            const u32x4 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                              pack_bf16x2(o[6], o[7])};
-            const int cc = col + 8 * h;
-            bst16(rY, (row < M && cc < N) ? (uint32_t)(row * N + cc) * 2u : kOOB, pk);
+              for (int e = 0; e < 8; ++e) o[e] = act_fn<ACT>(acc[rb][cb][8 * h + e] + bb[e]);
+              const u32x4 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                                pack_bf16x2(o[6], o[7])};
+              *reinterpret_cast<u32x4*>(stg + rr * BN + 8 * eswz(rr, cl0 / 8 + h)) = pk;
+            }
           }
         }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < RC * C16 / THREADS; ++j) {
+          const int id = j * THREADS + t;
+          const int rr = id / C16, c = id % C16;
+          const int row = m0 + q * RC + rr, col = n0 + 8 * c;
+          if (row < M && col < N)
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + rr * BN + 8 * eswz(rr, c)),
+                                        reinterpret_cast<u32x4*>(a.Y + (int64_t)row * N + col));
+        }
+        __syncthreads();
       }
     };
     switch (a.act) {
