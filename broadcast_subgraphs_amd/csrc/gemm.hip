@@ -1329,9 +1329,15 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
     return false;
   };
   // wait for stage st, free the other slot, prefetch the next stage into it,
-  // then run the tile from stage st's slot
-  auto step = [&](int sweep, int u, int j, const bf16x8_t (&qf)[KS], f32x16 (&acc)[CB]) {
-    wait_vm<0>();
+  // then run the tile from stage st's slot.  `stored`: the previous step
+  // issued the 8 output stores of its tile after this stage's prefetch; the
+  // vector-memory counter retires in issue order, so waiting down to those 8
+  // completes the prefetch while the stores keep draining under this tile's
+  // MainLoop (they must be done only by the wait one step later).
+  constexpr int kStoresPerTile = 2 * CB;
+  auto step = [&](int sweep, int u, int j, const bf16x8_t (&qf)[KS], f32x16 (&acc)[CB], bool stored) {
+    if (stored) wait_vm<kStoresPerTile>();
+    else wait_vm<0>();
     __syncthreads();
     int nj = 0;
     const bool more = next_tile(sweep, u, j, &nj);
@@ -1358,7 +1364,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
     float m = -INFINITY, l = 0.0f;  // running, base-2 domain, this lane's row
     for (int j = strip_first(u); j < strip_end(u); ++j) {
       f32x16 acc[CB];
-      step(1, u, j, qf, acc);
+      step(1, u, j, qf, acc, false);
       // 8-column chunks of this lane's row: chunk q = (cb, h) holds columns
       // j*BN + cb*32 + 16*hl + 8*h + [0, 8); it is valid or not as a whole
       const int c0 = j * BN + 16 * hl;
@@ -1462,7 +1468,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
     const float2 fs = row < M ? ld_dev2(F + row) : make_float2(0.0f, 0.0f);
     for (int j = strip_first(u); j < strip_end(u); ++j) {
       f32x16 acc[CB];
-      step(2, u, j, qf, acc);
+      step(2, u, j, qf, acc, j > strip_first(u));
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
