@@ -1641,7 +1641,21 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
   // followed by its MFMAs; the lane's share of the row sum accumulates in fp32
   auto mma_ev = [&](const char* slot, const f32x16 (&acc)[CB], float& m, int j, f32x16 (&oacc)[NB], float& l) {
     float tx = sc >= 0.0f ? -INFINITY : INFINITY;  // max (or min) of the raw scores
-    if (sc >= 0.0f) {
+    const bool whole = (j + 1) * BN <= N;           // every key of the tile is valid (uniform)
+    if (sc >= 0.0f && whole) {
+      // a tree over 8-value chunks: no long dependency chain
+      float cm[2 * CB];
+#pragma unroll
+      for (int q = 0; q < 2 * CB; ++q) {
+        const float* v = &acc[q >> 1][8 * (q & 1)];
+        cm[q] = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+      }
+#pragma unroll
+      for (int d = 1; d < 2 * CB; d *= 2)
+#pragma unroll
+        for (int q = 0; q + d < 2 * CB; q += 2 * d) cm[q] = fmaxf(cm[q], cm[q + d]);
+      tx = cm[0];
+    } else if (sc >= 0.0f) {
 #pragma unroll
       for (int q = 0; q < 2 * CB; ++q)
         if (j * BN + (q >> 1) * 32 + 16 * hl + 8 * (q & 1) < N)
@@ -1669,15 +1683,22 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
     // below always run for the whole wave)
     const bool live = m != -INFINITY;
     const float mn = live ? m : 0.0f;
+    // a whole tile of valid keys needs no per-chunk masking
+    const bool full = live && whole;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       bf16x8_t sf[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const bool ok = live && j * BN + cb * 32 + 16 * hl + 8 * q < N;
         float y[8];
+        if (full) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = ok ? __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * q + e], sc, -mn)) : 0.0f;
+          for (int e = 0; e < 8; ++e) y[e] = __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * q + e], sc, -mn));
+        } else {
+          const bool ok = live && j * BN + cb * 32 + 16 * hl + 8 * q < N;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = ok ? __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * q + e], sc, -mn)) : 0.0f;
+        }
         l += ((y[0] + y[1]) + (y[2] + y[3])) + ((y[4] + y[5]) + (y[6] + y[7]));
         const u32x4 pk = {cvt_bf16x2(y[0], y[1]), cvt_bf16x2(y[2], y[3]), cvt_bf16x2(y[4], y[5]),
                           cvt_bf16x2(y[6], y[7])};
