@@ -1647,7 +1647,9 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
       float cm[2 * CB];
 #pragma unroll
       for (int q = 0; q < 2 * CB; ++q) {
-        const float* v = &acc[q >> 1][8 * (q & 1)];
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = acc[q >> 1][8 * (q & 1) + e];
         cm[q] = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
       }
 #pragma unroll
