@@ -738,7 +738,10 @@ cf_status cf_unfused_stitch_layernorm_affine(const float* x, const float* gamma,
   char* w = unfused_base(ws);
   const size_t vec = align_up((size_t)rows * 4, 256), full = align_up((size_t)rows * cols * 4, 256);
   float* n = reinterpret_cast<float*>(w + 4 * vec + 2 * full);
-  CF_TRY(unfused_ln_chain(x, n, rows, cols, eps, w, stream));          // 7 kernels
+  {
+    const cf_status cs = unfused_ln_chain(x, n, rows, cols, eps, w, stream);  // 7 kernels
+    if (cs != CF_OK) return cs;
+  }
   float* t = reinterpret_cast<float*>(w + 4 * vec);                     // the chain's first full buffer, free now
   CF_TRY(u_bcast_row(n, gamma, t, rows, cols, 2, stream));              // * gamma
   CF_TRY(u_bcast_row(t, beta, y, rows, cols, 3, stream));               // + beta
