@@ -104,3 +104,29 @@ def test_product_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 txt = open(os.path.join(root, f)).read()
                 assert not re.search(r"\boracle\b", txt), f"{f} mentions the oracle"
+
+
+def test_spec_and_auto_validation_before_any_hip_call(L):
+    from broadcast_subgraphs_amd._lib import GNode
+    h = P()
+    # null graph, bad terminal, non-positive sizes
+    assert L.cf_spec_build(None, 1, 0, 4, 4, 0, ctypes.byref(h)) == cf.CF_EINVAL
+    nodes = (GNode * 2)(GNode(cf.G_OPS["input"], -1, -1, 0, 0, 0.0), GNode(cf.G_OPS["exp"], 0, -1, 0, -1, 0.0))
+    assert L.cf_spec_build(nodes, 2, 5, 4, 4, 0, ctypes.byref(h)) == cf.CF_EINVAL
+    assert L.cf_spec_build(nodes, 2, 1, 0, 4, 0, ctypes.byref(h)) == cf.CF_EINVAL
+    assert L.cf_spec_build(nodes, 2, 1, 4, 4, 0, None) == cf.CF_EINVAL
+    # a valid S that no kernel implements (exp alone) is refused, not launched
+    assert L.cf_spec_build(nodes, 2, 1, 4, 4, 0, ctypes.byref(h)) == cf.CF_EUNSUPPORTED
+    assert L.cf_auto_build(None, 1, 0, 4, 4, ctypes.byref(h)) == cf.CF_EINVAL
+    assert L.cf_auto_build(nodes, 2, 1, 4, 0, ctypes.byref(h)) == cf.CF_EINVAL
+    # a built generated kernel rejects a missing argument and a null output before touching the device
+    assert L.cf_auto_build(nodes, 2, 1, 4, 4, ctypes.byref(h)) == cf.CF_OK
+    try:
+        assert L.cf_auto_launch(h, None, 0, P(A16), None) == cf.CF_EINVAL
+        args = (P * 1)(P(B16))
+        assert L.cf_auto_launch(h, args, 1, None, None) == cf.CF_EINVAL
+        # the output overlapping an input
+        assert L.cf_auto_launch(h, args, 1, P(B16 + 16), None) == cf.CF_EINVAL
+    finally:
+        L.cf_auto_free(h)
+    assert L.cf_spec_launch(None, None, 0, P(A16), None, 0, None) == cf.CF_EINVAL
