@@ -734,3 +734,21 @@ def test_one_workspace_shared_by_every_op():
                 err = rownorm_err(host(y), oracle.pow_bcast_add_softmax(p["x"], p["v"], 1.5)[0])
             assert ws.error_word() == 0, f"step {step}: a join gave up"
             assert err <= TOL_F32, (step, err)
+
+
+def test_single_row_and_minimal_gemms(monkeypatch):
+    """One output row (and the smallest legal N, K) through every fused GEMM."""
+    for M, N, K in [(1, 8, 8), (1, 264, 72), (2, 136, 1032)]:
+        d = gen.gemm_ln_inputs(seed=71, M=M, N=N, K=K)
+        assert rownorm_err(_gemm_ln_run(d, M, N, K), oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"],
+                                                                   d["beta"], d["eps"])) <= TOL_BF16
+        q = gen.gemm_softmax_inputs(seed=72, M=M, N=N, D=K)
+        assert rownorm_err(_gemm_sm_run(q, M, N, K), oracle.gemm_softmax(q["q"], q["k"], q["scale"])) <= TOL_BF16
+        for algo in (0, 1):
+            monkeypatch.setenv("CF_GEMM_ACT_ALGO", str(algo))
+            g = gen.gemm_act_inputs(seed=73, M=M, N=N, K=K)
+            assert act_err(_gemm_act_run(g, M, N, "silu"), oracle.gemm_act(g["a"], g["w"], g["bias"], "silu")) <= 1.0
+        if K <= 128:
+            b = gen.gemm_softmax_gemm_inputs(seed=74, M=M, N=N, D=K, Dv=8)
+            assert rownorm_err(_b2b_run(b, M, N, K, 8), oracle.gemm_softmax_gemm(b["q"], b["k"], b["v"], b["scale"])) \
+                <= TOL_BF16
