@@ -250,8 +250,8 @@ EXTRA_NAMES = ["gemm_softmax_gemm_8192x8192x128x128", "rmsnorm_750000x32", "laye
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(the path shards by rows with no exchange, but no multi-GPU run is built)"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1 "
+                                   "(the path shards by rows with no exchange; no multi-GPU launch is provided)"}))
         sys.exit(2)
 
     import torch
