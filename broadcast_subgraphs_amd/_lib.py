@@ -82,7 +82,8 @@ _SIGS = {
     "cf_auto_build": (_ST, [ctypes.POINTER(GNode), ctypes.c_int, ctypes.c_int, _I64, _I64, ctypes.POINTER(_P)]),
     "cf_auto_describe": (ctypes.c_int, [_P, ctypes.c_char_p, _SZ]),
     "cf_auto_source": (ctypes.c_int, [_P, ctypes.c_char_p, _SZ]),
-    "cf_auto_launch": (_ST, [_P, ctypes.POINTER(_P), ctypes.c_int, _P, _P]),
+    "cf_auto_launch": (_ST, [_P, ctypes.POINTER(_P), ctypes.c_int, _P, _P, _SZ, _P]),
+    "cf_auto_workspace_bytes": (_SZ, [_P]),
     "cf_auto_free": (None, [_P]),
 }
 
@@ -502,8 +503,20 @@ class Auto:
     def source(self) -> str:
         return self._text(lib().cf_auto_source)
 
-    def launch(self, args, out, stream=None):
-        """args: fp32 tensors by slot (None where unused); out: fp32 [rows, cols]."""
+    def workspace_bytes(self) -> int:
+        return int(lib().cf_auto_workspace_bytes(self._h))
+
+    def launch(self, args, out, ws=None, stream=None):
+        """args: fp32 tensors by slot (None where unused); out: fp32 [rows, cols].  A workspace is
+        allocated and cached when the kernel needs one and none is given; returns it."""
         st = _stream(stream)
+        nb = self.workspace_bytes()
+        if nb == ctypes.c_size_t(-1).value:
+            raise CFError("cf_auto_workspace_bytes", CF_EHIP)
+        if ws is None:
+            ws = _workspace(nb, out.device, st)
         ptrs = (_P * max(1, len(args)))(*[None if t is None else t.data_ptr() for t in args])
-        _check("cf_auto_launch", lib().cf_auto_launch(self._h, ptrs, len(args), _ptr(out), st))
+        _check("cf_auto_launch", lib().cf_auto_launch(self._h, ptrs, len(args), _ptr(out),
+                                                      None if ws is None else ws.ptr(),
+                                                      0 if ws is None else ws.nbytes, st))
+        return ws

@@ -30,6 +30,9 @@ constexpr int kMaxSlots = 16;
 constexpr int kMaxDevices = 16;
 constexpr int kMaxFrags = 8;       // float4 fragments per lane
 constexpr int kMaxLanes = 1024;    // lanes per row (one workgroup)
+constexpr int kMaxMembers = 256;   // workgroups per row (Global scheme)
+constexpr int64_t kJoinWords = 16384;                 // the workspace's join-word region (after its 256-byte header)
+constexpr size_t kPartsOff = 256 + kJoinWords * 8;    // partials follow the join words
 
 enum Shape { kTile, kRowVal, kVec, kScalar };
 enum DomKind { kDomReduce, kDomExpensiveBcast, kDomOutput };
@@ -62,6 +65,8 @@ struct cf_auto {
   std::vector<std::pair<int, int>> dominants;  // (node, kind)
   std::vector<Edge> edges;
   int lanes = 0, frags = 0, wg = 0, rows_per_wg = 0, waves_per_row = 0;
+  bool global = false;  // a row spans `members` workgroups that join at every reduction
+  int members = 1, reductions = 0;
   std::string name;  // generated kernel name prefix (unique per graph and mapping)
   std::string src;
   std::vector<char> code;
@@ -154,8 +159,19 @@ cf_status schedule(cf_auto* A) {
   const int64_t c4 = (A->cols + 3) / 4;
   int lanes = 8;
   while (lanes < kMaxLanes && (int64_t)lanes * 4 < c4) lanes *= 2;
-  const int64_t frags = (c4 + lanes - 1) / lanes;
-  if (frags > kMaxFrags) return CF_EUNSUPPORTED;  // the row spans workgroups: Global scheme, not generated
+  int64_t frags = (c4 + lanes - 1) / lanes;
+  for (int i = 0; i < n; ++i) A->reductions += A->live[i] && is_reduce(g[i].op);
+  if (frags > kMaxFrags) {
+    // Global: the row is cut into slices of 256 lanes x 8 fragments, one
+    // workgroup each; the members of a row publish every reduction's partial,
+    // join and merge the partials in member order.
+    lanes = 256;
+    frags = kMaxFrags;
+    const int64_t members = (c4 + (int64_t)lanes * frags - 1) / ((int64_t)lanes * frags);
+    if (members > kMaxMembers) return CF_EUNSUPPORTED;
+    A->global = true;
+    A->members = (int)members;
+  }
   A->lanes = lanes;
   A->frags = (int)frags;
   A->wg = std::max(256, lanes);
@@ -173,7 +189,7 @@ cf_status schedule(cf_auto* A) {
     const int ni = is_binary(g[j].op) ? 2 : 1;
     for (int q = 0; q < ni; ++q) {
       const int i = q == 0 ? g[j].in0 : g[j].in1;
-      const int scheme = (is_reduce(g[i].op) && A->waves_per_row > 1) ? kRegional : kLocal;
+      const int scheme = !is_reduce(g[i].op) ? kLocal : A->global ? kGlobal : A->waves_per_row > 1 ? kRegional : kLocal;
       A->edges.push_back({i, j, scheme});
     }
   }
@@ -224,7 +240,8 @@ std::string body(const cf_auto* A, bool vec) {
   const cf_gnode* g = A->g.data();
   const int F = A->frags;
   std::string s;
-  char b[512];
+  char b[1024];
+  int kr = 0;  // reduction index within the row (Global partial buffers)
   auto loop = [&](const std::string& stmt) {
     s += "#pragma unroll\n      for (int f = 0; f < " + std::to_string(F) +
          "; ++f)\n#pragma unroll\n        for (int e = 0; e < 4; ++e) " + stmt + "\n";
@@ -240,7 +257,7 @@ std::string body(const cf_auto* A, bool vec) {
       if (vec) {
         snprintf(b, sizeof b,
                  "#pragma unroll\n      for (int f = 0; f < %d; ++f) {\n"
-                 "        const long c = 4L * (f * %d + rl);\n"
+                 "        const long c = c0 + 4L * (f * %d + rl);\n"
                  "        f4 q = {0.f, 0.f, 0.f, 0.f};\n"
                  "        if (%sc < cols) q = %s((const f4*)(%s + c));\n"
                  "        %s[f][0] = q.x; %s[f][1] = q.y; %s[f][2] = q.z; %s[f][3] = q.w;\n      }\n",
@@ -249,7 +266,7 @@ std::string body(const cf_auto* A, bool vec) {
       } else {
         snprintf(b, sizeof b,
                  "#pragma unroll\n      for (int f = 0; f < %d; ++f)\n#pragma unroll\n        for (int e = 0; e < 4; ++e) {\n"
-                 "          const long c = 4L * (f * %d + rl) + e;\n"
+                 "          const long c = c0 + 4L * (f * %d + rl) + e;\n"
                  "          %s[f][e] = (%sc < cols) ? (%s)[c] : 0.0f;\n        }\n",
                  F, A->lanes, ti.c_str(), row ? "rok && " : "", base.c_str());
       }
@@ -269,7 +286,7 @@ std::string body(const cf_auto* A, bool vec) {
       const std::string init = mx ? "-__builtin_inff()" : "0.0f";
       const std::string comb = mx ? "fmaxf" : "cf_add";
       s += "      float " + ri + " = " + init + ";\n";
-      snprintf(b, sizeof b, "{ if (4L * (f * %d + rl) + e < cols) %s = %s(%s, t%d[f][e]); }", A->lanes, ri.c_str(),
+      snprintf(b, sizeof b, "{ if (c0 + 4L * (f * %d + rl) + e < cols) %s = %s(%s, t%d[f][e]); }", A->lanes, ri.c_str(),
                comb.c_str(), ri.c_str(), g[i].in0);
       loop(b);
       for (int m = std::min(A->lanes, 64) / 2; m >= 1; m /= 2) {
@@ -288,6 +305,25 @@ std::string body(const cf_auto* A, bool vec) {
                  "      slot ^= 1;\n",
                  ri.c_str(), ri.c_str(), A->waves_per_row, ri.c_str(), comb.c_str(), ri.c_str());
         s += b;
+      }
+      if (A->global) {
+        // Global: publish this member's partial, join the row's members, merge
+        // every member's partial in member order (identical on every member)
+        snprintf(b, sizeof b,
+                 "      {\n"
+                 "        float* const pp = a.parts + ((rs * 2L + par) * %d + %d) * (long)S;\n"
+                 "        if (threadIdx.x == 0) {\n"
+                 "          cf_st_dev(pp + sl, %s);\n"
+                 "          __builtin_amdgcn_s_waitcnt(0);\n"
+                 "          cf_join(a.joins + rs, (unsigned)S, a.err);\n"
+                 "        }\n"
+                 "        __syncthreads();\n"
+                 "        %s = %s;\n"
+                 "        for (int q = 0; q < S; ++q) %s = %s(%s, cf_ld_dev(pp + q));\n"
+                 "      }\n",
+                 A->reductions, kr, ri.c_str(), ri.c_str(), init.c_str(), ri.c_str(), comb.c_str(), ri.c_str());
+        s += b;
+        ++kr;
       }
       continue;
     }
@@ -311,7 +347,7 @@ std::string body(const cf_auto* A, bool vec) {
   if (vec) {
     snprintf(b, sizeof b,
              "#pragma unroll\n      for (int f = 0; f < %d; ++f) {\n"
-             "        const long c = 4L * (f * %d + rl);\n"
+             "        const long c = c0 + 4L * (f * %d + rl);\n"
              "        if (rok && c < cols) {\n"
              "          const f4 q = {%s[f][0], %s[f][1], %s[f][2], %s[f][3]};\n"
              "          __builtin_nontemporal_store(q, (f4*)(a.out + row * cols + c));\n        }\n      }\n",
@@ -319,7 +355,7 @@ std::string body(const cf_auto* A, bool vec) {
   } else {
     snprintf(b, sizeof b,
              "#pragma unroll\n      for (int f = 0; f < %d; ++f)\n#pragma unroll\n        for (int e = 0; e < 4; ++e) {\n"
-             "          const long c = 4L * (f * %d + rl) + e;\n"
+             "          const long c = c0 + 4L * (f * %d + rl) + e;\n"
              "          if (rok && c < cols) a.out[row * cols + c] = %s[f][e];\n        }\n",
              F, A->lanes, to.c_str());
   }
@@ -332,22 +368,58 @@ std::string generate(const cf_auto* A) {
   char b[1024];
   s += "// generated: one stitched kernel for a memory-intensive graph\n"
        "typedef float f4 __attribute__((ext_vector_type(4)));\n"
-       "struct AutoArgs { const float* p[16]; float* out; long rows; long cols; };\n"
+       "struct AutoArgs { const float* p[16]; float* out; long rows; long cols; unsigned* err;\n"
+       "                  unsigned long long* joins; float* parts; int S; int RG; };\n"
+       "__device__ __forceinline__ void cf_st_dev(float* p, float v) {\n"
+       "  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n}\n"
+       "__device__ __forceinline__ float cf_ld_dev(const float* p) {\n"
+       "  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n}\n"
+       "// arrive on a generation-counted join word {generation:32 | arrivals:32}; the last\n"
+       "// of `m` members advances the generation; the others wait for it (capped spin)\n"
+       "__device__ __forceinline__ void cf_join(unsigned long long* j, unsigned m, unsigned* err) {\n"
+       "  const unsigned long long old = __hip_atomic_fetch_add(j, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n"
+       "  const unsigned gen0 = (unsigned)(old >> 32);\n"
+       "  if ((unsigned)old == m - 1) {\n"
+       "    __hip_atomic_fetch_add(j, (1ull << 32) - m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n"
+       "    return;\n  }\n"
+       "  for (unsigned it = 0; it < (1u << 20); ++it) {\n"
+       "    const unsigned long long w = __hip_atomic_load(j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n"
+       "    if ((unsigned)(w >> 32) != gen0) return;\n"
+       "    __builtin_amdgcn_s_sleep(1);\n  }\n"
+       "  __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n}\n"
        "__device__ __forceinline__ float cf_add(float x, float y) { return x + y; }\n"
        "__device__ __forceinline__ f4 ntld4(const f4* p) { return __builtin_nontemporal_load(p); }\n";
   for (int vec = 1; vec >= 0; --vec) {
-    snprintf(b, sizeof b,
-             "extern \"C\" __global__ __launch_bounds__(%d) void %s_%s(AutoArgs a) {\n"
-             "  const long rows = a.rows, cols = a.cols;\n"
-             "  const int rl = threadIdx.x %% %d, rg = threadIdx.x / %d;\n"
-             "  %s\n"
-             "  for (long rb = (long)blockIdx.x * %d; rb < rows; rb += (long)gridDim.x * %d) {\n"
-             "    const long row = rb + rg;\n"
-             "    const bool rok = row < rows;\n"
-             "    {\n",
-             A->wg, A->name.c_str(), vec ? "vec" : "scalar", A->lanes, A->lanes,
-             A->waves_per_row > 1 ? "__shared__ float red[2][16]; int slot = 0;" : "", A->rows_per_wg,
-             A->rows_per_wg);
+    if (A->global) {
+      // one row per group of S member workgroups; rows in rounds of RG groups
+      snprintf(b, sizeof b,
+               "extern \"C\" __global__ __launch_bounds__(%d) void %s_%s(AutoArgs a) {\n"
+               "  const long rows = a.rows, cols = a.cols;\n"
+               "  const int rl = threadIdx.x;\n"
+               "  __shared__ float red[2][16]; int slot = 0;\n"
+               "  const int S = a.S, sl = (int)blockIdx.x %% S;\n"
+               "  const long rs = (long)blockIdx.x / S;\n"
+               "  const long c0 = 4L * sl * %d;\n"
+               "  int par = 0;\n"
+               "  for (long row = rs; row < rows; row += a.RG, par ^= 1) {\n"
+               "    const bool rok = true;\n"
+               "    {\n",
+               A->wg, A->name.c_str(), vec ? "vec" : "scalar", A->lanes * A->frags);
+    } else {
+      snprintf(b, sizeof b,
+               "extern \"C\" __global__ __launch_bounds__(%d) void %s_%s(AutoArgs a) {\n"
+               "  const long rows = a.rows, cols = a.cols;\n"
+               "  const int rl = threadIdx.x %% %d, rg = threadIdx.x / %d;\n"
+               "  const long c0 = 0;\n"
+               "  %s\n"
+               "  for (long rb = (long)blockIdx.x * %d; rb < rows; rb += (long)gridDim.x * %d) {\n"
+               "    const long row = rb + rg;\n"
+               "    const bool rok = row < rows;\n"
+               "    {\n",
+               A->wg, A->name.c_str(), vec ? "vec" : "scalar", A->lanes, A->lanes,
+               A->waves_per_row > 1 ? "__shared__ float red[2][16]; int slot = 0;" : "", A->rows_per_wg,
+               A->rows_per_wg);
+    }
     s += b;
     s += body(A, vec != 0);
     s += "    }\n  }\n}\n";
@@ -435,11 +507,12 @@ int cf_auto_describe(const cf_auto* A, char* buf, size_t n) {
   if (!A) return -1;
   static const char* dk[] = {"reduce", "expensive_broadcast", "output"};
   static const char* sk[] = {"local", "regional", "global"};
-  char t[256];
+  char t[512];
   snprintf(t, sizeof t,
            "{\"rows\":%lld,\"cols\":%lld,\"mapping\":{\"lanes_per_row\":%d,\"frags_per_lane\":%d,\"workgroup\":%d,"
-           "\"rows_per_workgroup\":%d,\"waves_per_row\":%d},\"dominants\":[",
-           (long long)A->rows, (long long)A->cols, A->lanes, A->frags, A->wg, A->rows_per_wg, A->waves_per_row);
+           "\"rows_per_workgroup\":%d,\"waves_per_row\":%d,\"workgroups_per_row\":%d},\"dominants\":[",
+           (long long)A->rows, (long long)A->cols, A->lanes, A->frags, A->wg, A->rows_per_wg, A->waves_per_row,
+           A->members);
   std::string j = t;
   for (size_t d = 0; d < A->dominants.size(); ++d) {
     snprintf(t, sizeof t, "%s{\"node\":%d,\"op\":\"%s\",\"kind\":\"%s\"}", d ? "," : "", A->dominants[d].first,
@@ -484,12 +557,71 @@ int cf_auto_source(const cf_auto* A, char* buf, size_t n) {
   return (int)A->src.size();
 }
 
-cf_status cf_auto_launch(cf_auto* A, const void* const* args, int nargs, float* out, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Load the code object on the current device once; returns the device or -1.
+int ensure_loaded(cf_auto* A) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  std::lock_guard<std::mutex> lk(A->mu);
+  if (!A->mod[dev]) {
+    hipModule_t m = nullptr;
+    if (hipModuleLoadData(&m, A->code.data()) != hipSuccess) return -1;
+    hipFunction_t fv = nullptr, fs = nullptr;
+    if (hipModuleGetFunction(&fv, m, (A->name + "_vec").c_str()) != hipSuccess ||
+        hipModuleGetFunction(&fs, m, (A->name + "_scalar").c_str()) != hipSuccess) {
+      (void)hipModuleUnload(m);
+      return -1;
+    }
+    A->mod[dev] = m;
+    A->fn_vec[dev] = fv;
+    A->fn_scalar[dev] = fs;
+  }
+  return dev;
+}
+
+// Global scheme: rows per round (every member workgroup of a round resident
+// at once), or 0 if not even one row's members fit.
+cf_status global_rows_per_round(cf_auto* A, int dev, int64_t* rg) {
+  int occ = 0, cus = 0;
+  if (hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&occ, A->fn_vec[dev], A->wg, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return CF_EHIP;
+  int occ_s = 0;
+  if (hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&occ_s, A->fn_scalar[dev], A->wg, 0) != hipSuccess)
+    return CF_EHIP;
+  const int64_t cap = (int64_t)std::min(occ, occ_s) * cus;
+  *rg = std::min<int64_t>({A->rows, cap / A->members, kJoinWords});
+  return *rg >= 1 ? CF_OK : CF_EOCCUPANCY;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t cf_auto_workspace_bytes(cf_auto* A) {
+  if (!A) return (size_t)-1;
+  if (!A->global) return 0;
+  const int dev = ensure_loaded(A);
+  if (dev < 0) return (size_t)-1;
+  int64_t rg = 0;
+  if (global_rows_per_round(A, dev, &rg) != CF_OK) return (size_t)-1;
+  return kPartsOff + (size_t)rg * 2 * A->reductions * A->members * 4;
+}
+
+cf_status cf_auto_launch(cf_auto* A, const void* const* args, int nargs, float* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
   if (!A || !out || nargs < 0 || (nargs > 0 && !args)) return CF_EINVAL;
   struct {
     const float* p[kMaxSlots];
     float* out;
     long rows, cols;
+    unsigned* err;
+    unsigned long long* joins;
+    float* parts;
+    int S, RG;
   } ka{};
   const size_t tile_bytes = (size_t)A->rows * (size_t)A->cols * 4;
   bool vec = A->cols % 4 == 0 && aligned16(out);
@@ -503,31 +635,31 @@ cf_status cf_auto_launch(cf_auto* A, const void* const* args, int nargs, float* 
     if (op != CF_G_COLVEC) vec = vec && aligned16(args[s]);
     ka.p[s] = static_cast<const float*>(args[s]);
   }
+  if (A->global && (!ws || overlap(ws, ws_bytes, out, tile_bytes))) return !ws ? CF_EWORKSPACE : CF_EINVAL;
   ka.out = out;
   ka.rows = (long)A->rows;
   ka.cols = (long)A->cols;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CF_EHIP;
-  {
-    std::lock_guard<std::mutex> lk(A->mu);
-    if (!A->mod[dev]) {
-      hipModule_t m = nullptr;
-      if (hipModuleLoadData(&m, A->code.data()) != hipSuccess) return CF_EHIP;
-      hipFunction_t fv = nullptr, fs = nullptr;
-      if (hipModuleGetFunction(&fv, m, (A->name + "_vec").c_str()) != hipSuccess ||
-          hipModuleGetFunction(&fs, m, (A->name + "_scalar").c_str()) != hipSuccess) {
-        (void)hipModuleUnload(m);
-        return CF_EHIP;
-      }
-      A->mod[dev] = m;
-      A->fn_vec[dev] = fv;
-      A->fn_scalar[dev] = fs;
-    }
+  const int dev = ensure_loaded(A);
+  if (dev < 0) return CF_EHIP;
+  unsigned grid = 0;
+  if (A->global) {
+    int64_t rg = 0;
+    const cf_status st = global_rows_per_round(A, dev, &rg);
+    if (st != CF_OK) return st;
+    if (ws_bytes < kPartsOff + (size_t)rg * 2 * A->reductions * A->members * 4) return CF_EWORKSPACE;
+    char* base = static_cast<char*>(ws);
+    ka.err = reinterpret_cast<unsigned*>(base);
+    ka.joins = reinterpret_cast<unsigned long long*>(base + 256);
+    ka.parts = reinterpret_cast<float*>(base + kPartsOff);
+    ka.S = A->members;
+    ka.RG = (int)rg;
+    grid = (unsigned)(rg * A->members);
+  } else {
+    const int64_t blocks = (A->rows + A->rows_per_wg - 1) / A->rows_per_wg;
+    // a grid-stride launch of at most 32 workgroups of 256 lanes per CU (by lanes)
+    const int64_t cap = (int64_t)8192 * 256 / A->wg;
+    grid = (unsigned)std::min<int64_t>(blocks, cap);
   }
-  const int64_t blocks = (A->rows + A->rows_per_wg - 1) / A->rows_per_wg;
-  // a grid-stride launch of at most 32 workgroups of 256 lanes per CU (by lanes)
-  const int64_t cap = (int64_t)8192 * 256 / A->wg;
-  const unsigned grid = (unsigned)std::min<int64_t>(blocks, cap);
   void* params[] = {&ka};
   const hipError_t e = hipModuleLaunchKernel(vec ? A->fn_vec[dev] : A->fn_scalar[dev], grid, 1, 1, (unsigned)A->wg, 1,
                                              1, 0, stream, params, nullptr);

@@ -121,15 +121,17 @@ void cf_spec_free(cf_spec* s);
 /* expensive ops whose per-row result feeds a broadcast, the output),         */
 /* propagates the row-fragment thread mapping from them through the           */
 /* one-to-one ops, merges them into one stitched group, decides per edge      */
-/* whether the value stays in the thread's registers (Local) or crosses       */
-/* waves through LDS (Regional), picks the mapping by the row length, and     */
+/* whether the value stays in the thread's registers (Local), crosses waves   */
+/* through LDS (Regional) or crosses workgroups through global memory and a   */
+/* join (Global), picks the mapping by the row length, and                    */
 /* generates one HIP kernel for the group, compiled at build time with        */
 /* hiprtc for gfx950.                                                         */
 /*                                                                            */
 /* Accepted graphs: CF_G_INPUT placeholders (any number, fp32 [rows x cols]), */
 /* ROWVEC, COLVEC, CONST, the binary and unary operators, ROWSUM and ROWMAX;  */
-/* the terminal is a tile.  Rows of up to 32768 values (one workgroup per     */
-/* row at most); wider rows would need the Global scheme and are refused.     */
+/* the terminal is a tile.  Rows of up to 32768 values run one workgroup per  */
+/* row at most; wider rows (up to 256 x 8192 values) are cut into slices of   */
+/* 8192, one workgroup each, whose members join at every row reduction.       */
 /* ------------------------------------------------------------------------ */
 
 typedef struct cf_auto cf_auto;
@@ -147,12 +149,23 @@ int cf_auto_describe(const cf_auto* a, char* buf, size_t n);
 /* The generated HIP source.  Returns the full length. */
 int cf_auto_source(const cf_auto* a, char* buf, size_t n);
 
+/* Workspace bytes the generated kernel needs on the current device: 0 unless
+ * rows span workgroups (then the join words and partials of one round of
+ * co-resident rows).  Loads the code object on the device.  (size_t)-1 on
+ * failure. */
+size_t cf_auto_workspace_bytes(cf_auto* a);
+
 /* Enqueue the generated kernel: args[slot] are the placeholders' device
  * pointers, out the fp32 [rows x cols] output (not overlapping any input).
  * Loads the code object on the current device at its first launch there.
  * 16-byte aligned pointers and cols % 4 == 0 select the 16-byte-fragment
- * variant, anything else the 4-byte one.  No workspace. */
-cf_status cf_auto_launch(cf_auto* a, const void* const* args, int nargs, float* out, hipStream_t stream);
+ * variant, anything else the 4-byte one.  ws/ws_bytes: the workspace (same
+ * contract as cf.h's: zero-filled once, error word at byte 0), needed only
+ * when cf_auto_workspace_bytes is non-zero; CF_EOCCUPANCY when not even one
+ * row's workgroups can be resident.  Free the kernel (cf_auto_free) only
+ * after the work it enqueued has completed. */
+cf_status cf_auto_launch(cf_auto* a, const void* const* args, int nargs, float* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
 
 void cf_auto_free(cf_auto* a);
 

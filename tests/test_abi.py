@@ -122,11 +122,11 @@ def test_spec_and_auto_validation_before_any_hip_call(L):
     # a built generated kernel rejects a missing argument and a null output before touching the device
     assert L.cf_auto_build(nodes, 2, 1, 4, 4, ctypes.byref(h)) == cf.CF_OK
     try:
-        assert L.cf_auto_launch(h, None, 0, P(A16), None) == cf.CF_EINVAL
+        assert L.cf_auto_launch(h, None, 0, P(A16), None, 0, None) == cf.CF_EINVAL
         args = (P * 1)(P(B16))
-        assert L.cf_auto_launch(h, args, 1, None, None) == cf.CF_EINVAL
+        assert L.cf_auto_launch(h, args, 1, None, None, 0, None) == cf.CF_EINVAL
         # the output overlapping an input
-        assert L.cf_auto_launch(h, args, 1, P(B16 + 16), None) == cf.CF_EINVAL
+        assert L.cf_auto_launch(h, args, 1, P(B16 + 16), None, 0, None) == cf.CF_EINVAL
     finally:
         L.cf_auto_free(h)
     assert L.cf_spec_launch(None, None, 0, P(A16), None, 0, None) == cf.CF_EINVAL

@@ -55,7 +55,7 @@ def test_refusals():
         auto(graphs.gemm_act("relu"), 64, 64)  # a MatMul root takes the GEMM entry points
     assert e.value.status == cf.CF_EUNSUPPORTED
     with pytest.raises(cf.CFError) as e:
-        auto(graphs.layernorm(32769), 4, 32769)  # a row wider than one workgroup: the Global scheme
+        auto(graphs.layernorm(256 * 8192 + 1), 1, 256 * 8192 + 1)  # more than 256 member workgroups per row
     assert e.value.status == cf.CF_EUNSUPPORTED
     b = graphs.B()
     with pytest.raises(cf.CFError) as e:
@@ -69,3 +69,15 @@ def test_refusals():
     with pytest.raises(cf.CFError) as e:
         auto((b.nodes, b.add("exp", b.ph("rowvec", 0))), 4, 8)  # no input tile to drive the rows
     assert e.value.status == cf.CF_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("cols,members", [(32769, 5), (100000, 13), (1 << 20, 128)])
+def test_global_scheme_for_rows_wider_than_a_workgroup(cols, members):
+    """Rows of more than 32768 values: slices of 256 lanes x 8 fragments, one workgroup each, and
+    every reduction edge crosses workgroups (Global)."""
+    d = auto(graphs.softmax(), 3, cols).describe()
+    m = d["mapping"]
+    assert (m["lanes_per_row"], m["frags_per_lane"], m["workgroups_per_row"]) == (256, 8, members)
+    assert members * 256 * 8 * 4 >= cols > (members - 1) * 256 * 8 * 4
+    red_edges = [e for e in d["edges"] if e["scheme"] != "local"]
+    assert red_edges and all(e["scheme"] == "global" for e in red_edges)

@@ -11,7 +11,8 @@ from tests.test_gpu_parity import TOL_F32, d32, host, rownorm_err
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(1000, 32), (999, 36), (5, 3), (7, 100), (33, 1024), (3, 5000), (4, 30000), (2, 32768), (4099, 33)]
+SHAPES = [(1000, 32), (999, 36), (5, 3), (7, 100), (33, 1024), (3, 5000), (4, 30000), (2, 32768), (4099, 33),
+          (3, 32769), (2, 100000), (5, 70001), (600, 40000)]
 
 
 def _inputs(rows, cols, seed):
@@ -44,8 +45,10 @@ def test_auto_graphs(rows, cols):
     for name, (nodes, t), hargs in _cases(rows, cols, x, r, g, bt, v):
         a = cf.Auto(nodes, t, rows, cols)
         out = torch.full((rows, cols), float("nan"), device="cuda")
-        a.launch([d32(h) for h in hargs], out)
+        ws = a.launch([d32(h) for h in hargs], out)
         got = host(out)
+        if ws is not None:
+            assert ws.error_word() == 0, "a cross-workgroup wait gave up"
         want = oracle.graph.evaluate(nodes, t, hargs)
         assert rownorm_err(got, want) <= TOL_F32, (name, a.describe()["mapping"])
 
@@ -77,3 +80,23 @@ def test_auto_launch_rejects_overlap_and_missing_args():
     with pytest.raises(cf.CFError) as e:
         a.launch([], torch.empty_like(X))
     assert e.value.status == cf.CF_EINVAL
+
+
+def test_auto_global_rows_in_several_rounds_repeat_bitwise():
+    """More rows than one round of co-resident member workgroups: the row groups walk the rows,
+    the join words and partial buffers are reused round after round, and a second launch on the
+    same workspace gives the same bits (members merge partials in a fixed order)."""
+    rows, cols = 3000, 40000
+    x, r, g, bt, v = _inputs(rows, cols, 91)
+    nodes, t = graphs.layernorm(cols, 1e-5, True)
+    a = cf.Auto(nodes, t, rows, cols)
+    assert a.describe()["mapping"]["workgroups_per_row"] == 5
+    args = [d32(x), d32(g), d32(bt)]
+    out = torch.empty((rows, cols), device="cuda")
+    ws = a.launch(args, out)
+    first = host(out)
+    assert ws.error_word() == 0
+    assert rownorm_err(first, oracle.graph.evaluate(nodes, t, [x, g, bt])) <= TOL_F32
+    a.launch(args, out, ws=ws)
+    assert np.array_equal(host(out), first)
+    assert ws.error_word() == 0
