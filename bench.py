@@ -51,6 +51,7 @@ KERNEL_SOURCES = {
     "gemm_gelu_4096x4096x1024": ("gemm.hip", "dev.hpp"),
     "auto_layernorm_750000x32": ("auto.cpp",),
     "auto_silu_ln_scaled_750000x32": ("auto.cpp",),
+    "auto_softmax_512x65536": ("auto.cpp",),
 }
 
 
@@ -200,6 +201,23 @@ class Workload:
             self.bytes, self.flops = 2 * d["x"].nbytes + extra, 0
             call = lambda b, ws, u: auto.launch([b["X"], b["B"], b["V"]], b["Y"])
             self.op, self.dims = None, (750000, 32, 0)
+        elif name == "auto_softmax_512x65536":
+            # rows of 65536 values: the generated kernel's Global scheme (8 member
+            # workgroups per row joining at both reductions)
+            x = gen.softmax_inputs(seed=11, rows=512, cols=1 << 16)["x"]
+            self.inp = {"x": x}
+            g = cf.Graph()
+            xi = g.input(0)
+            e = g.op("exp", g.op("sub", xi, g.op("rowmax", xi)))
+            y = g.op("div", e, g.op("rowsum", e))
+            self.graph = (g.nodes, y)
+            auto = cf.Auto(g, y, 512, 1 << 16)
+            self.plan_auto = auto.describe()
+            bufs = {"X": d32(x), "Y": torch.empty(512, 1 << 16, device=dev)}
+            self.bytes, self.flops = 2 * x.nbytes, 0
+            auto_ws = cf.Workspace(auto.workspace_bytes())
+            call = lambda b, ws, u: auto.launch([b["X"]], b["Y"], ws=auto_ws)
+            self.op, self.dims = None, (512, 1 << 16, 0)
         else:
             raise ValueError(name)
         self.bound = "mfma" if name in ("gemm_ln_4096x4096x1024", "gemm_softmax_gemm_8192x8192x128x128",
@@ -235,6 +253,8 @@ class Workload:
             return oracle.layernorm_affine_rows(d["x"], d["gamma"], d["beta"], 1e-5)
         if self.name == "gemm_gelu_4096x4096x1024":
             return oracle.gemm_act(d["a"], d["w"], d["bias"], "gelu_tanh")
+        if self.name == "auto_softmax_512x65536":
+            return oracle.graph.evaluate(self.graph[0], self.graph[1], [d["x"]])
         if self.name.startswith("auto_"):
             return oracle.graph.evaluate(self.graph[0], self.graph[1], [d["x"], d["beta"], d["v"]])
         return oracle.gemm_softmax(d["q"], d["k"], d["scale"])
@@ -244,7 +264,8 @@ WORKLOAD_NAMES = ["softmax_256x1024", "layernorm_750000x32", "pow_bcast_add_soft
                   "gemm_ln_4096x4096x1024", "gemm_softmax_8192x8192x128"]
 # measured per kernel (and unfused) but outside the step
 EXTRA_NAMES = ["gemm_softmax_gemm_8192x8192x128x128", "rmsnorm_750000x32", "layernorm_affine_750000x32",
-               "gemm_gelu_4096x4096x1024", "auto_layernorm_750000x32", "auto_silu_ln_scaled_750000x32"]
+               "gemm_gelu_4096x4096x1024", "auto_layernorm_750000x32", "auto_silu_ln_scaled_750000x32",
+               "auto_softmax_512x65536"]
 
 
 def main():

@@ -307,8 +307,9 @@ std::string body(const cf_auto* A, bool vec) {
         s += b;
       }
       if (A->global) {
-        // Global: publish this member's partial, join the row's members, merge
-        // every member's partial in member order (identical on every member)
+        // Global: publish this member's partial, join the row's members, then
+        // one load per member into LDS and a fixed-order merge by the first
+        // wave (the same order, so the same bits, on every member)
         snprintf(b, sizeof b,
                  "      {\n"
                  "        float* const pp = a.parts + ((rs * 2L + par) * %d + %d) * (long)S;\n"
@@ -318,10 +319,19 @@ std::string body(const cf_auto* A, bool vec) {
                  "          cf_join(a.joins + rs, (unsigned)S, a.err);\n"
                  "        }\n"
                  "        __syncthreads();\n"
-                 "        %s = %s;\n"
-                 "        for (int q = 0; q < S; ++q) %s = %s(%s, cf_ld_dev(pp + q));\n"
+                 "        if (threadIdx.x < S) pm[threadIdx.x] = cf_ld_dev(pp + threadIdx.x);\n"
+                 "        __syncthreads();\n"
+                 "        if (threadIdx.x < 64) {\n"
+                 "          float v = %s;\n"
+                 "          for (int q = threadIdx.x; q < S; q += 64) v = %s(v, pm[q]);\n"
+                 "          for (int m = 32; m >= 1; m >>= 1) v = %s(v, __shfl_xor(v, m, 64));\n"
+                 "          if (threadIdx.x == 0) pm[256] = v;\n"
+                 "        }\n"
+                 "        __syncthreads();\n"
+                 "        %s = pm[256];\n"
+                 "        __syncthreads();\n"
                  "      }\n",
-                 A->reductions, kr, ri.c_str(), ri.c_str(), init.c_str(), ri.c_str(), comb.c_str(), ri.c_str());
+                 A->reductions, kr, ri.c_str(), init.c_str(), comb.c_str(), comb.c_str(), ri.c_str());
         s += b;
         ++kr;
       }
@@ -397,6 +407,7 @@ std::string generate(const cf_auto* A) {
                "  const long rows = a.rows, cols = a.cols;\n"
                "  const int rl = threadIdx.x;\n"
                "  __shared__ float red[2][16]; int slot = 0;\n"
+               "  __shared__ float pm[257];  // the members' partials, then their merge\n"
                "  const int S = a.S, sl = (int)blockIdx.x %% S;\n"
                "  const long rs = (long)blockIdx.x / S;\n"
                "  const long c0 = 4L * sl * %d;\n"
