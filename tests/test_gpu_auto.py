@@ -100,3 +100,30 @@ def test_auto_global_rows_in_several_rounds_repeat_bitwise():
     a.launch(args, out, ws=ws)
     assert np.array_equal(host(out), first)
     assert ws.error_word() == 0
+
+
+@pytest.mark.parametrize("name", ["layernorm_750000x32", "silu_ln_scaled_750000x32", "softmax_512x65536"])
+def test_auto_bench_workloads_at_full_size(name):
+    """The generated kernels the bench times, at the sizes it times them."""
+    if name == "softmax_512x65536":
+        rows, cols = 512, 1 << 16
+        x = gen.softmax_inputs(seed=11, rows=rows, cols=cols)["x"]
+        nodes, t = graphs.softmax()
+        hargs = [x]
+    else:
+        rows, cols = 750000, 32
+        d = gen.layernorm_affine_inputs(seed=10)
+        v = gen.uniform(10, 5, (rows,), 0.1, 2.0)
+        if name.startswith("silu"):
+            nodes, t = graphs.silu_ln_scaled(cols)
+            hargs = [d["x"], d["beta"], v]
+        else:
+            nodes, t = graphs.layernorm(cols)
+            hargs = [d["x"]]
+    a = cf.Auto(nodes, t, rows, cols)
+    out = torch.full((rows, cols), float("nan"), device="cuda")
+    ws = a.launch([d32(h) for h in hargs], out)
+    got = host(out)
+    if ws is not None:
+        assert ws.error_word() == 0
+    assert rownorm_err(got, oracle.graph.evaluate(nodes, t, hargs)) <= TOL_F32
