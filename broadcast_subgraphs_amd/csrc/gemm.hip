@@ -40,6 +40,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 
 constexpr int kThreads = 256;
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset beyond every range: reads zero
@@ -1573,14 +1577,25 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
     for (int q = 0; q < LPS; ++q) g2l16(rV, slot + (q * NW + w) * 1024, voff + base + (uint32_t)(64 * q * Dv));
   };
   // The strip's Q rows: row r's 16-byte chunk c at r*256 + 16*(c ^ r%16), so
-  // 16 lanes reading 16 rows at one chunk hit 16 distinct bank slots.
+  // 16 lanes reading 16 rows at one chunk hit 16 distinct bank slots.  Load q
+  // fills rows 32q + 4w + lane/16; the chunk and its swizzle do not depend on
+  // q, so one per-lane offset serves every load (no per-load address state to
+  // keep live).  Rows past M lie beyond the descriptor's range and read zero.
+  uint32_t qoff;
+  bool qok;
+  {
+    const int r = 4 * w + (lane >> 4), c = (lane & 15) ^ (r & 15);
+    qok = 8 * c < D;
+    qoff = (uint32_t)(r * D + 8 * c) * 2u;
+  }
   auto load_q = [&](int m0) {
+    uint32_t o = qoff + (uint32_t)m0 * (uint32_t)D * 2u;
+    // opaque, so the per-load sums are formed here and not hoisted out of
+    // the strip loop as eight live registers (which would spill)
+    asm volatile("" : "+v"(o));
 #pragma unroll
-    for (int q = 0; q < BM * BK * 2 / (NW * 1024); ++q) {
-      const int o = (q * NW + w) * 1024 + lane * 16;
-      const int r = o / 256, c = ((o % 256) / 16) ^ (r & 15);
-      g2l16(rA, sq + (q * NW + w) * 1024, (m0 + r < M && 8 * c < D) ? (uint32_t)((m0 + r) * D + 8 * c) * 2u : kOOB);
-    }
+    for (int q = 0; q < BM * BK * 2 / (NW * 1024); ++q)
+      g2l16(rA, sq + (q * NW + w) * 1024, qok ? o + (uint32_t)(64 * q * D) : kOOB);
   };
   // First MatMul of one tile: acc[cb] += K rows (sigma-permuted) x Q rows;
   // step ks+1's K and Q fragments are read before step ks's MFMAs issue
@@ -1801,15 +1816,18 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
     // for waves 4-7), 16-byte chunk k of row r at r*512 + 16*(k ^ r), then
     // back out as whole rows, 1 KB per store instruction
     __syncthreads();  // every wave is done with the ring and the Q rows
-    char* const stage = w < 4 ? sq + w * 16384 : ring_all[w - 4];
+    // (the region is picked at run time from separate LDS objects, so the
+    // pointer is cast back to the LDS address space: the stores and loads
+    // below are then LDS instructions with 32-bit addresses, not flat ones)
+    lds_char_t* const stage = (lds_char_t*)(w < 4 ? sq + w * 16384 : ring_all[w - 4]);
     static_assert(NS >= 4 && SLOT == 16384 && BM * BK * 2 == 4 * 16384, "one 16 KB staging region per wave");
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
         const int k4 = nb * 8 + 4 * hl + c4;  // 16-byte chunk index of columns 4*k4 .. +3
-        const float4 v = make_float4(oacc[nb][4 * c4], oacc[nb][4 * c4 + 1], oacc[nb][4 * c4 + 2], oacc[nb][4 * c4 + 3]);
-        *reinterpret_cast<float4*>(stage + l32 * 512 + 16 * (k4 ^ l32)) = v;
+        const f32x4 v = {oacc[nb][4 * c4], oacc[nb][4 * c4 + 1], oacc[nb][4 * c4 + 2], oacc[nb][4 * c4 + 3]};
+        *reinterpret_cast<lds_f32x4_t*>(stage + l32 * 512 + 16 * (k4 ^ l32)) = v;
       }
     if (hl == 0 && row < M) st_dev2(Lp + (size_t)su * M + row, make_float2(m, lsum));
     __syncthreads();
@@ -1817,7 +1835,7 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
     for (int it = 0; it < 16; ++it) {
       const int idx = it * 64 + lane, r = idx >> 5, k4 = idx & 31;
       const int orow = m0 + w * 32 + r;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * 512 + 16 * (k4 ^ r));
+      const u32x4 v = *reinterpret_cast<const lds_u32x4_t*>(stage + r * 512 + 16 * (k4 ^ r));
       bst16_dev(rOp, orow < M ? (uint32_t)((((size_t)su * M + orow) * DV + 4 * k4) * 4) : kOOB, v);
     }
     wait_stores();
