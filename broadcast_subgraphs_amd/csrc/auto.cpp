@@ -593,19 +593,30 @@ int ensure_loaded(cf_auto* A) {
   return dev;
 }
 
-// Global scheme: rows per round (every member workgroup of a round resident
-// at once), or 0 if not even one row's members fit.
-cf_status global_rows_per_round(cf_auto* A, int dev, int64_t* rg) {
+// Global scheme: rows per round for the kernel form that runs (vector or
+// scalar: their register use, and so their residency, differ), with every
+// member workgroup of a round resident at once; an error if not even one
+// row's members fit.
+cf_status global_rows_per_round(cf_auto* A, int dev, bool vec, int64_t* rg) {
   int occ = 0, cus = 0;
-  if (hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&occ, A->fn_vec[dev], A->wg, 0) != hipSuccess ||
+  if (hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&occ, vec ? A->fn_vec[dev] : A->fn_scalar[dev], A->wg, 0) !=
+          hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return CF_EHIP;
-  int occ_s = 0;
-  if (hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&occ_s, A->fn_scalar[dev], A->wg, 0) != hipSuccess)
-    return CF_EHIP;
-  const int64_t cap = (int64_t)std::min(occ, occ_s) * cus;
+  const int64_t cap = (int64_t)occ * cus;
   *rg = std::min<int64_t>({A->rows, cap / A->members, kJoinWords});
   return *rg >= 1 ? CF_OK : CF_EOCCUPANCY;
+}
+
+// Workspace bytes of a Global launch: the partials of the larger round of the
+// two kernel forms.
+cf_status global_ws_bytes(cf_auto* A, int dev, size_t* bytes) {
+  int64_t rv = 0, rs = 0;
+  cf_status st = global_rows_per_round(A, dev, true, &rv);
+  if (st == CF_OK) st = global_rows_per_round(A, dev, false, &rs);
+  if (st != CF_OK) return st;
+  *bytes = kPartsOff + (size_t)std::max(rv, rs) * 2 * A->reductions * A->members * 4;
+  return CF_OK;
 }
 
 }  // namespace
@@ -617,9 +628,8 @@ size_t cf_auto_workspace_bytes(cf_auto* A) {
   if (!A->global) return 0;
   const int dev = ensure_loaded(A);
   if (dev < 0) return (size_t)-1;
-  int64_t rg = 0;
-  if (global_rows_per_round(A, dev, &rg) != CF_OK) return (size_t)-1;
-  return kPartsOff + (size_t)rg * 2 * A->reductions * A->members * 4;
+  size_t bytes = 0;
+  return global_ws_bytes(A, dev, &bytes) == CF_OK ? bytes : (size_t)-1;
 }
 
 cf_status cf_auto_launch(cf_auto* A, const void* const* args, int nargs, float* out, void* ws, size_t ws_bytes,
@@ -655,9 +665,11 @@ cf_status cf_auto_launch(cf_auto* A, const void* const* args, int nargs, float* 
   unsigned grid = 0;
   if (A->global) {
     int64_t rg = 0;
-    const cf_status st = global_rows_per_round(A, dev, &rg);
+    size_t need = 0;
+    cf_status st = global_rows_per_round(A, dev, vec, &rg);
+    if (st == CF_OK) st = global_ws_bytes(A, dev, &need);
     if (st != CF_OK) return st;
-    if (ws_bytes < kPartsOff + (size_t)rg * 2 * A->reductions * A->members * 4) return CF_EWORKSPACE;
+    if (ws_bytes < need) return CF_EWORKSPACE;
     char* base = static_cast<char*>(ws);
     ka.err = reinterpret_cast<unsigned*>(base);
     ka.joins = reinterpret_cast<unsigned long long*>(base + 256);

@@ -102,6 +102,28 @@ def test_auto_global_rows_in_several_rounds_repeat_bitwise():
     assert ws.error_word() == 0
 
 
+def test_auto_global_scalar_form_matches_vector_form_bitwise():
+    """The Global scheme's two kernel forms hold different numbers of member workgroups at once,
+    so they walk the rows in rounds of different sizes; one workspace of workspace_bytes() serves
+    both, and each row's partials merge in member order either way, so the bits agree."""
+    rows, cols = 1500, 40000
+    x, r, g, bt, v = _inputs(rows, cols, 92)
+    nodes, t = graphs.layernorm(cols, 1e-5, True)
+    a = cf.Auto(nodes, t, rows, cols)
+    args = [d32(x), d32(g), d32(bt)]
+    ws = cf.Workspace(a.workspace_bytes())
+    buf = torch.full((rows * cols + 1,), float("nan"), device="cuda")
+    out_s = buf[1:].view(rows, cols)  # 4-byte aligned only: the scalar form
+    a.launch(args, out_s, ws=ws)
+    got_s = host(out_s)
+    assert ws.error_word() == 0
+    assert rownorm_err(got_s, oracle.graph.evaluate(nodes, t, [x, g, bt])) <= TOL_F32
+    out_v = torch.empty((rows, cols), device="cuda")
+    a.launch(args, out_v, ws=ws)
+    assert ws.error_word() == 0
+    assert np.array_equal(host(out_v), got_s)
+
+
 @pytest.mark.parametrize("name", ["layernorm_750000x32", "silu_ln_scaled_750000x32", "softmax_512x65536"])
 def test_auto_bench_workloads_at_full_size(name):
     """The generated kernels the bench times, at the sizes it times them."""
