@@ -268,6 +268,17 @@ EXTRA_NAMES = ["gemm_softmax_gemm_8192x8192x128x128", "rmsnorm_750000x32", "laye
                "auto_softmax_512x65536"]
 
 
+def shape_keys(w):
+    """The timed workload's sizes for the JSON line's config: rows x cols, or the GEMM's M, N, K."""
+    a, b, c = w.dims
+    if c:
+        return {"M": a, "N": b, "K": c}
+    keys = {"rows": a, "cols": b}
+    if "layernorm" in w.name or "rmsnorm" in w.name:
+        keys["eps"] = 1e-5
+    return keys
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -519,7 +530,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": head.name, "rows": 750000, "cols": 32, "eps": 1e-5,
+        "config": {"workload": head.name, **shape_keys(head),
                    "step": "one fused call per workload: " + ", ".join(w.name for w in wl)},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -31,8 +31,11 @@ constexpr int kMaxDevices = 16;
 constexpr int kMaxFrags = 8;       // float4 fragments per lane
 constexpr int kMaxLanes = 1024;    // lanes per row (one workgroup)
 constexpr int kMaxMembers = 256;   // workgroups per row (Global scheme)
-constexpr int64_t kJoinWords = 16384;                 // the workspace's join-word region (after its 256-byte header)
-constexpr size_t kPartsOff = 256 + kJoinWords * 8;    // partials follow the join words
+// Global-scheme workspace, in the library's fixed layout: the 256-byte header
+// (error word at 0), the join-word region (one 64-bit generation-counted word
+// per row group), then the tagged partial slots, 8 bytes each.
+constexpr int64_t kJoinWords = 16384;
+constexpr size_t kSlotsOff = 256 + kJoinWords * 8;
 
 enum Shape { kTile, kRowVal, kVec, kScalar };
 enum DomKind { kDomReduce, kDomExpensiveBcast, kDomOutput };
@@ -240,7 +243,7 @@ std::string body(const cf_auto* A, bool vec) {
   const cf_gnode* g = A->g.data();
   const int F = A->frags;
   std::string s;
-  char b[1024];
+  char b[4096];
   int kr = 0;  // reduction index within the row (Global partial buffers)
   auto loop = [&](const std::string& stmt) {
     s += "#pragma unroll\n      for (int f = 0; f < " + std::to_string(F) +
@@ -285,6 +288,15 @@ std::string body(const cf_auto* A, bool vec) {
       const bool mx = op == CF_G_ROWMAX;
       const std::string init = mx ? "-__builtin_inff()" : "0.0f";
       const std::string comb = mx ? "fmaxf" : "cf_add";
+      if (A->global && kr == 0) {
+        // Global, a launch's first row: the launch join the kernel arrived on
+        // before its first loads completes here, so no member reads a slot
+        // before every member has cleared its own
+        s += "      if (it_ == 0) {\n"
+             "        if (threadIdx.x == 0) cf_await(a.joins + rs, jold, (unsigned)S, a.err);\n"
+             "        __syncthreads();\n"
+             "      }\n";
+      }
       s += "      float " + ri + " = " + init + ";\n";
       snprintf(b, sizeof b, "{ if (c0 + 4L * (f * %d + rl) + e < cols) %s = %s(%s, t%d[f][e]); }", A->lanes, ri.c_str(),
                comb.c_str(), ri.c_str(), g[i].in0);
@@ -307,19 +319,16 @@ std::string body(const cf_auto* A, bool vec) {
         s += b;
       }
       if (A->global) {
-        // Global: publish this member's partial, join the row's members, then
-        // one load per member into LDS and a fixed-order merge by the first
-        // wave (the same order, so the same bits, on every member)
+        // Global: publish this member's partial in its tagged slot, take every
+        // member's slot once it carries this row's tag (the value arrives with
+        // the tag: no separate arrival or load), then a fixed-order merge by
+        // the first wave (the same order, so the same bits, on every member)
         snprintf(b, sizeof b,
                  "      {\n"
-                 "        float* const pp = a.parts + ((rs * 2L + par) * %d + %d) * (long)S;\n"
-                 "        if (threadIdx.x == 0) {\n"
-                 "          cf_st_dev(pp + sl, %s);\n"
-                 "          __builtin_amdgcn_s_waitcnt(0);\n"
-                 "          cf_join(a.joins + rs, (unsigned)S, a.err);\n"
-                 "        }\n"
-                 "        __syncthreads();\n"
-                 "        if (threadIdx.x < S) pm[threadIdx.x] = cf_ld_dev(pp + threadIdx.x);\n"
+                 "        unsigned long long* const pp = a.slots + ((rs * 2L + par) * %d + %d) * (long)S;\n"
+                 "        const unsigned tag = it_ + 1u;\n"
+                 "        if (threadIdx.x == 0) cf_put(pp + sl, tag, %s);\n"
+                 "        for (int q = threadIdx.x; q < S; q += (int)blockDim.x) pm[q] = cf_take(pp + q, tag, a.err);\n"
                  "        __syncthreads();\n"
                  "        if (threadIdx.x < 64) {\n"
                  "          float v = %s;\n"
@@ -375,19 +384,32 @@ std::string body(const cf_auto* A, bool vec) {
 
 std::string generate(const cf_auto* A) {
   std::string s;
-  char b[1024];
+  char b[4096];
   s += "// generated: one stitched kernel for a memory-intensive graph\n"
        "typedef float f4 __attribute__((ext_vector_type(4)));\n"
        "struct AutoArgs { const float* p[16]; float* out; long rows; long cols; unsigned* err;\n"
-       "                  unsigned long long* joins; float* parts; int S; int RG; };\n"
-       "__device__ __forceinline__ void cf_st_dev(float* p, float v) {\n"
-       "  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n}\n"
-       "__device__ __forceinline__ float cf_ld_dev(const float* p) {\n"
-       "  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n}\n"
-       "// arrive on a generation-counted join word {generation:32 | arrivals:32}; the last\n"
-       "// of `m` members advances the generation; the others wait for it (capped spin)\n"
-       "__device__ __forceinline__ void cf_join(unsigned long long* j, unsigned m, unsigned* err) {\n"
-       "  const unsigned long long old = __hip_atomic_fetch_add(j, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n"
+       "                  unsigned long long* joins; unsigned long long* slots; int S; int RG; };\n"
+       "// a tagged slot {tag:32 | value:32}: one 64-bit device-scope store publishes\n"
+       "// the value together with its tag, so a reader needs no other ordering\n"
+       "__device__ __forceinline__ void cf_put(unsigned long long* s, unsigned tag, float v) {\n"
+       "  __hip_atomic_store(s, ((unsigned long long)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,\n"
+       "                     __HIP_MEMORY_SCOPE_AGENT);\n}\n"
+       "// the slot's value once it carries `tag` (capped spin: on giving up, the\n"
+       "// error word is set and 0 returned, so the kernel still finishes)\n"
+       "__device__ __forceinline__ float cf_take(unsigned long long* s, unsigned tag, unsigned* err) {\n"
+       "  for (unsigned it = 0; it < (1u << 20); ++it) {\n"
+       "    const unsigned long long w = __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n"
+       "    if ((unsigned)(w >> 32) == tag) return __uint_as_float((unsigned)w);\n"
+       "    __builtin_amdgcn_s_sleep(1);\n  }\n"
+       "  __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n"
+       "  return 0.0f;\n}\n"
+       "// a generation-counted join word {generation:32 | arrivals:32}: arrive (the\n"
+       "// returned word is the arrival's), then await: the last of `m` members\n"
+       "// advances the generation, the others wait for it (capped spin)\n"
+       "__device__ __forceinline__ unsigned long long cf_arrive(unsigned long long* j) {\n"
+       "  return __hip_atomic_fetch_add(j, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n}\n"
+       "__device__ __forceinline__ void cf_await(unsigned long long* j, unsigned long long old, unsigned m,\n"
+       "                                         unsigned* err) {\n"
        "  const unsigned gen0 = (unsigned)(old >> 32);\n"
        "  if ((unsigned)old == m - 1) {\n"
        "    __hip_atomic_fetch_add(j, (1ull << 32) - m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n"
@@ -411,11 +433,26 @@ std::string generate(const cf_auto* A) {
                "  const int S = a.S, sl = (int)blockIdx.x %% S;\n"
                "  const long rs = (long)blockIdx.x / S;\n"
                "  const long c0 = 4L * sl * %d;\n"
+               "  unsigned it_ = 0;  // this launch's rows of the group so far (tags count from 1)\n"
+               "  // the launch join, before any load: this member clears its slots (both\n"
+               "  // parities, every reduction) and arrives; it awaits the others at its\n"
+               "  // first reduction, so the join overlaps the first row's loads.  No slot\n"
+               "  // read in this launch then holds a value from before it (this kernel's\n"
+               "  // or another op's sharing the workspace), and tags restart at 1\n"
+               "  unsigned long long jold = 0;\n"
+               "  if (threadIdx.x == 0) {\n"
+               "    for (int p = 0; p < 2; ++p)\n"
+               "      for (int k = 0; k < %d; ++k)\n"
+               "        __hip_atomic_store(a.slots + ((rs * 2L + p) * %d + k) * (long)S + sl, 0ull, __ATOMIC_RELAXED,\n"
+               "                           __HIP_MEMORY_SCOPE_AGENT);\n"
+               "    __builtin_amdgcn_s_waitcnt(0);\n"
+               "    jold = cf_arrive(a.joins + rs);\n"
+               "  }\n"
                "  int par = 0;\n"
-               "  for (long row = rs; row < rows; row += a.RG, par ^= 1) {\n"
+               "  for (long row = rs; row < rows; row += a.RG, par ^= 1, ++it_) {\n"
                "    const bool rok = true;\n"
                "    {\n",
-               A->wg, A->name.c_str(), vec ? "vec" : "scalar", A->lanes * A->frags);
+               A->wg, A->name.c_str(), vec ? "vec" : "scalar", A->lanes * A->frags, A->reductions, A->reductions);
     } else {
       snprintf(b, sizeof b,
                "extern \"C\" __global__ __launch_bounds__(%d) void %s_%s(AutoArgs a) {\n"
@@ -433,7 +470,8 @@ std::string generate(const cf_auto* A) {
     }
     s += b;
     s += body(A, vec != 0);
-    s += "    }\n  }\n}\n";
+    s += "    }\n  }\n";
+    s += "}\n";
   }
   return s;
 }
@@ -615,7 +653,7 @@ cf_status global_ws_bytes(cf_auto* A, int dev, size_t* bytes) {
   cf_status st = global_rows_per_round(A, dev, true, &rv);
   if (st == CF_OK) st = global_rows_per_round(A, dev, false, &rs);
   if (st != CF_OK) return st;
-  *bytes = kPartsOff + (size_t)std::max(rv, rs) * 2 * A->reductions * A->members * 4;
+  *bytes = kSlotsOff + (size_t)std::max(rv, rs) * 2 * A->reductions * A->members * 8;
   return CF_OK;
 }
 
@@ -641,7 +679,7 @@ cf_status cf_auto_launch(cf_auto* A, const void* const* args, int nargs, float* 
     long rows, cols;
     unsigned* err;
     unsigned long long* joins;
-    float* parts;
+    unsigned long long* slots;
     int S, RG;
   } ka{};
   const size_t tile_bytes = (size_t)A->rows * (size_t)A->cols * 4;
@@ -673,7 +711,7 @@ cf_status cf_auto_launch(cf_auto* A, const void* const* args, int nargs, float* 
     char* base = static_cast<char*>(ws);
     ka.err = reinterpret_cast<unsigned*>(base);
     ka.joins = reinterpret_cast<unsigned long long*>(base + 256);
-    ka.parts = reinterpret_cast<float*>(base + kPartsOff);
+    ka.slots = reinterpret_cast<unsigned long long*>(base + kSlotsOff);
     ka.S = A->members;
     ka.RG = (int)rg;
     grid = (unsigned)(rg * A->members);

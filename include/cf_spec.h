@@ -150,9 +150,12 @@ int cf_auto_describe(const cf_auto* a, char* buf, size_t n);
 int cf_auto_source(const cf_auto* a, char* buf, size_t n);
 
 /* Workspace bytes the generated kernel needs on the current device: 0 unless
- * rows span workgroups (then the join words and partials of one round of
- * co-resident rows).  Loads the code object on the device.  (size_t)-1 on
- * failure. */
+ * rows span workgroups.  Then, in cf.h's fixed workspace layout: the header
+ * and join-word region, followed by one 8-byte tagged partial slot per
+ * member, row reduction and row of two rounds of co-resident rows.  Every
+ * launch clears its slots and joins each row's members once before it reads
+ * any slot, so the workspace may serve any op in any order.  Loads the code
+ * object on the device.  (size_t)-1 on failure. */
 size_t cf_auto_workspace_bytes(cf_auto* a);
 
 /* Enqueue the generated kernel: args[slot] are the placeholders' device

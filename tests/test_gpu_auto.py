@@ -7,7 +7,7 @@ import broadcast_subgraphs_amd as cf
 import gen
 import oracle
 from tests import graphs
-from tests.test_gpu_parity import TOL_F32, d32, host, rownorm_err
+from tests.test_gpu_parity import TOL_F32, d32, dbf16, host, rownorm_err
 
 pytestmark = pytest.mark.gpu
 
@@ -122,6 +122,42 @@ def test_auto_global_scalar_form_matches_vector_form_bitwise():
     a.launch(args, out_v, ws=ws)
     assert ws.error_word() == 0
     assert np.array_equal(host(out_v), got_s)
+
+
+def test_auto_global_layouts_and_library_ops_share_a_workspace():
+    """Two generated kernels with different member counts per row (5 and 8) and a library op that
+    writes its own partials where the slots lie take turns on one workspace: each launch clears
+    its slots and joins each row's members before reading one, so what the others left behind
+    never passes for a fresh partial, and every repeat gives the first launch's bits."""
+    ka = (700, 40000)
+    kb = (300, 1 << 16)
+    xa = gen.normal(93, 0, ka)
+    xb = gen.softmax_inputs(seed=94, rows=kb[0], cols=kb[1])["x"]
+    na, ta = graphs.layernorm(ka[1])
+    nb, tb = graphs.softmax()
+    a = cf.Auto(na, ta, *ka)
+    b = cf.Auto(nb, tb, *kb)
+    assert a.describe()["mapping"]["workgroups_per_row"] == 5
+    assert b.describe()["mapping"]["workgroups_per_row"] == 8
+    q = gen.gemm_softmax_inputs(seed=96, M=512, N=1024, D=128)
+    ws = cf.Workspace(max(a.workspace_bytes(), b.workspace_bytes(),
+                          cf.cf_workspace_bytes(cf.CF_OP_GEMM_SOFTMAX, 512, 1024, 128)))
+    XA, XB = d32(xa), d32(xb)
+    oa, ob = torch.empty(ka, device="cuda"), torch.empty(kb, device="cuda")
+    a.launch([XA], oa, ws=ws)
+    first_a = host(oa)
+    assert rownorm_err(first_a, oracle.graph.evaluate(na, ta, [xa])) <= TOL_F32
+    b.launch([XB], ob, ws=ws)
+    first_b = host(ob)
+    assert rownorm_err(first_b, oracle.graph.evaluate(nb, tb, [xb])) <= TOL_F32
+    S = torch.empty((512, 1024), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        cf.cf_gemm_softmax(dbf16(q["q_bits"]), dbf16(q["k_bits"]), q["scale"], S, ws=ws)
+        for k, X, o, first in ((a, XA, oa, first_a), (b, XB, ob, first_b)):
+            o.fill_(float("nan"))
+            k.launch([X], o, ws=ws)
+            assert np.array_equal(host(o), first)
+            assert ws.error_word() == 0
 
 
 @pytest.mark.parametrize("name", ["layernorm_750000x32", "silu_ln_scaled_750000x32", "softmax_512x65536"])
