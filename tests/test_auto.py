@@ -81,3 +81,23 @@ def test_global_scheme_for_rows_wider_than_a_workgroup(cols, members):
     assert members * 256 * 8 * 4 >= cols > (members - 1) * 256 * 8 * 4
     red_edges = [e for e in d["edges"] if e["scheme"] != "local"]
     assert red_edges and all(e["scheme"] == "global" for e in red_edges)
+
+
+def test_global_source_exchanges_tagged_partials():
+    """Global scheme: each row reduction publishes the member's partial with one tagged store and
+    takes every member's slot by the row's tag; one generation-counted join per launch (arrived on
+    before the first loads, awaited at the first reduction) follows the clear of the member's
+    slots, so nothing written before the launch can carry a tag it waits for."""
+    src = auto(graphs.softmax(), 3, 100000).source()
+    assert src.count("cf_put(pp + sl, tag,") == 2 * 2  # two reductions, in both variants
+    assert src.count("cf_take(pp + q, tag,") == 2 * 2
+    assert src.count("const unsigned tag = it_ + 1u;") == 2 * 2
+    assert src.count("jold = cf_arrive(a.joins + rs)") == 2
+    assert src.count("cf_await(a.joins + rs, jold") == 2
+    for start in (0, src.index("_scalar(AutoArgs a)")):
+        clear = src.index("__hip_atomic_store(a.slots", start)
+        arrive = src.index("jold = cf_arrive", start)
+        loop = src.index("for (long row = rs", start)
+        first_take = src.index("cf_take(pp + q", start)
+        await_ = src.index("cf_await(a.joins + rs, jold", start)
+        assert clear < arrive < loop < await_ < first_take
