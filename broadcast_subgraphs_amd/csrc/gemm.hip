@@ -1511,9 +1511,10 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
 // strips, in strip order, each weighted by 2^(strip max - block max), divides
 // by the equally weighted sums and stores O.  Exact in real arithmetic.
 // One workgroup of 8 waves per CU (32 rows per wave, 256-row strips): the
-// strip's Q rows sit in LDS, and the K / V blocks stream through an NS-slot
-// ring with NS - 1 blocks in flight, each slot its own LDS object so the
-// compiler can tell the slot being read from the ones being filled.
+// strip's Q rows sit in LDS, and the K / V blocks stream through a 4-slot
+// ring that holds two tiles (one computed, the next in flight; one barrier
+// per tile), each slot its own LDS object so the compiler can tell the slot
+// being read from the ones being filled.
 template <int KS, int NS>
 __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
   constexpr int BM = kB2bBM, BN = kB2bBN, BK = kB2bBK, NW = kB2bWaves, THREADS = kB2bThreads;
@@ -1522,16 +1523,15 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
   constexpr int SLOT = BN * BK * 2;      // one K block (BN keys x BK dims) or V block (BN keys x DV)
   constexpr int LPS = SLOT / (NW * 1024);  // 16-byte direct loads per lane per block
   static_assert(SLOT == BN * DV * 2 && LPS * NW * 1024 == SLOT && BK == 128, "block shapes");
-  static_assert(NS >= 2 && NS <= 6 && (NS - 2) * LPS < 64, "ring depth");
+  static_assert(NS == 4, "two tiles of K and V blocks");
   __shared__ __align__(16) char sq[BM * BK * 2];  // the strip's Q rows
   __shared__ __align__(16) char r0[SLOT];
   __shared__ __align__(16) char r1[SLOT];
-  __shared__ __align__(16) char r2[NS > 2 ? SLOT : 16];
-  __shared__ __align__(16) char r3[NS > 3 ? SLOT : 16];
-  __shared__ __align__(16) char r4[NS > 4 ? SLOT : 16];
-  __shared__ __align__(16) char r5[NS > 5 ? SLOT : 16];
+  __shared__ __align__(16) char r2[SLOT];
+  __shared__ __align__(16) char r3[SLOT];
   __shared__ uint32_t gen2;
-  char* const ring_all[6] = {r0, r1, r2, r3, r4, r5};
+  // slot i of the ring (i is a constant wherever a block is computed on)
+  auto ring = [&](int i) -> char* { return i == 0 ? r0 : i == 1 ? r1 : i == 2 ? r2 : r3; };
 
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
@@ -1731,29 +1731,6 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
       }
     }
   };
-  // The strip's block stream: nst blocks, block x in slot x % NS.  Before
-  // block b computes, the blocks issued after it may still be in flight
-  // (vmcnt, in order); a barrier publishes block b and retires block b - 1's
-  // slot, and block b + NS - 1 is issued into it.  Loads issued before the
-  // stream (the Q rows) are older than every block, so block 0's wait covers
-  // them.  NS is even, so a block's parity (K or V) is known once unrolled.
-  static_assert(NS % 2 == 0, "K / V parity fixed per unrolled step");
-  auto stream = [&](int nst, auto&& issue, auto&& compute) {
-#pragma unroll
-    for (int x = 0; x < NS - 1; ++x)
-      if (x < nst) issue(x, ring_all[x]);
-    for (int b0 = 0; b0 < nst; b0 += NS) {
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        const int b = b0 + i;
-        if (b >= nst) break;
-        wait_vm_n(min(NS - 2, nst - 1 - b) * LPS);
-        __syncthreads();
-        if (b + NS - 1 < nst) issue(b + NS - 1, ring_all[(i + NS - 1) % NS]);
-        compute((i & 1) != 0, b, ring_all[i]);
-      }
-    }
-  };
   auto strip_first = [&](int u) { return (u % S) * C; };
   auto strip_len = [&](int u) { return min(T, (u % S) * C + C) - (u % S) * C; };
 
@@ -1773,26 +1750,32 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
       for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.0f;
     float lsum = 0.0f;
     f32x16 acc[CB];
-    // blocks alternate: 2x is K block j0 + x, 2x + 1 is V block j0 + x
-    stream(
-        2 * strip_len(u),
-        [&](int x, char* slot) {
-          if (x & 1)
-            load_v(slot, j0 + (x >> 1));
-          else
-            load_k(slot, j0 + (x >> 1));
-        },
-        [&](bool odd, int x, const char* slot) {
-          if (odd) {
-            mma_ev(slot, acc, m, j0 + (x >> 1), oacc, lsum);
-          } else {
+    // tile x of the strip: K block in slot 2(x % 2), V block in slot 2(x % 2) + 1.
+    // One barrier per tile publishes both blocks of tile x and retires tile
+    // x - 1's slots, into which tile x + 1 is issued at once (one tile ahead);
+    // the Q rows, issued before tile 0, are covered by its wait
+    const int len = strip_len(u);
+    load_k(ring(0), j0);
+    load_v(ring(1), j0);
+    for (int x0 = 0; x0 < len; x0 += 2) {
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
+      for (int h = 0; h < 2; ++h) {
+        const int x = x0 + h;
+        if (x >= len) break;
+        wait_vm<0>();
+        __syncthreads();
+        if (x + 1 < len) {
+          load_k(ring(2 * (h ^ 1)), j0 + x + 1);
+          load_v(ring(2 * (h ^ 1) + 1), j0 + x + 1);
+        }
 #pragma unroll
-              for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
-            mma_qk(slot, acc);
-          }
-        });
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[cb][r] = 0.0f;
+        mma_qk(ring(2 * h), acc);
+        mma_ev(ring(2 * h + 1), acc, m, j0 + x, oacc, lsum);
+      }
+    }
     lsum += __shfl_xor(lsum, 32, kWave);  // the row's sum over the strip (relative to m)
     // this lane's output row, columns nb*32 + 16*hl + [0, 16)
     if (S == 1) {
@@ -1819,7 +1802,7 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
     // (the region is picked at run time from separate LDS objects, so the
     // pointer is cast back to the LDS address space: the stores and loads
     // below are then LDS instructions with 32-bit addresses, not flat ones)
-    lds_char_t* const stage = (lds_char_t*)(w < 4 ? sq + w * 16384 : ring_all[w - 4]);
+    lds_char_t* const stage = (lds_char_t*)(w < 4 ? sq + w * 16384 : ring(w - 4));
     static_assert(NS >= 4 && SLOT == 16384 && BM * BK * 2 == 4 * 16384, "one 16 KB staging region per wave");
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
