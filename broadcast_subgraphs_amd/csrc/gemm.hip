@@ -1754,9 +1754,11 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
     // One barrier per tile publishes both blocks of tile x and retires tile
     // x - 1's slots, into which tile x + 1 is issued at once (one tile ahead);
     // the Q rows, issued before tile 0, are covered by its wait
-    const int len = strip_len(u);
-    load_k(ring(0), j0);
-    load_v(ring(1), j0);
+    const int len = strip_len(u);  // >= 1: the planner gives every strip a tile
+    if (len > 0) {
+      load_k(ring(0), j0);
+      load_v(ring(1), j0);
+    }
     for (int x0 = 0; x0 < len; x0 += 2) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
