@@ -259,10 +259,11 @@ def test_gemm_softmax_zero_q_is_exact():
 
 
 # Back-to-back GEMM with the softmax between: ragged tails on every axis, a
-# single strip per row (one 64-key tile), several strips per row block, and
-# the full 8192 x 8192 x 128 x 128 workload.
+# single strip per row (one 64-key tile), several strips per row block, strips
+# of an odd number of tiles (3 per strip with a ragged last tile; 3 per strip
+# with a last strip of 1), and the full 8192 x 8192 x 128 x 128 workload.
 B2B_SHAPES = [(300, 264, 72, 40), (512, 1024, 128, 128), (17, 8, 8, 8), (130, 40, 32, 16),
-              (1000, 2056, 128, 64), (8192, 8192, 128, 128)]
+              (1000, 2056, 128, 64), (8192, 1496, 128, 128), (4096, 2536, 96, 72), (8192, 8192, 128, 128)]
 
 
 def _b2b_run(d, M, N, D, Dv, unfused=False, ws=None):
