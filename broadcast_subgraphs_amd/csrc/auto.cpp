@@ -433,26 +433,33 @@ std::string generate(const cf_auto* A) {
                "  const int S = a.S, sl = (int)blockIdx.x %% S;\n"
                "  const long rs = (long)blockIdx.x / S;\n"
                "  const long c0 = 4L * sl * %d;\n"
-               "  unsigned it_ = 0;  // this launch's rows of the group so far (tags count from 1)\n"
-               "  // the launch join, before any load: this member clears its slots (both\n"
-               "  // parities, every reduction) and arrives; it awaits the others at its\n"
-               "  // first reduction, so the join overlaps the first row's loads.  No slot\n"
-               "  // read in this launch then holds a value from before it (this kernel's\n"
-               "  // or another op's sharing the workspace), and tags restart at 1\n"
-               "  unsigned long long jold = 0;\n"
-               "  if (threadIdx.x == 0) {\n"
-               "    for (int p = 0; p < 2; ++p)\n"
-               "      for (int k = 0; k < %d; ++k)\n"
-               "        __hip_atomic_store(a.slots + ((rs * 2L + p) * %d + k) * (long)S + sl, 0ull, __ATOMIC_RELAXED,\n"
-               "                           __HIP_MEMORY_SCOPE_AGENT);\n"
-               "    __builtin_amdgcn_s_waitcnt(0);\n"
-               "    jold = cf_arrive(a.joins + rs);\n"
-               "  }\n"
+               "  unsigned it_ = 0;  // this launch's rows of the group so far (tags count from 1)\n",
+               A->wg, A->name.c_str(), vec ? "vec" : "scalar", A->lanes * A->frags);
+      s += b;
+      if (A->reductions > 0) {
+        snprintf(b, sizeof b,
+                 "  // the launch join, before any load: this member clears its slots (both\n"
+                 "  // parities, every reduction) and arrives; it awaits the others at its\n"
+                 "  // first reduction, so the join overlaps the first row's loads.  No slot\n"
+                 "  // read in this launch then holds a value from before it (this kernel's\n"
+                 "  // or another op's sharing the workspace), and tags restart at 1\n"
+                 "  unsigned long long jold = 0;\n"
+                 "  if (threadIdx.x == 0) {\n"
+                 "    for (int p = 0; p < 2; ++p)\n"
+                 "      for (int k = 0; k < %d; ++k)\n"
+                 "        __hip_atomic_store(a.slots + ((rs * 2L + p) * %d + k) * (long)S + sl, 0ull, __ATOMIC_RELAXED,\n"
+                 "                           __HIP_MEMORY_SCOPE_AGENT);\n"
+                 "    __builtin_amdgcn_s_waitcnt(0);\n"
+                 "    jold = cf_arrive(a.joins + rs);\n"
+                 "  }\n",
+                 A->reductions, A->reductions);
+        s += b;
+      }
+      snprintf(b, sizeof b,
                "  int par = 0;\n"
                "  for (long row = rs; row < rows; row += a.RG, par ^= 1, ++it_) {\n"
                "    const bool rok = true;\n"
-               "    {\n",
-               A->wg, A->name.c_str(), vec ? "vec" : "scalar", A->lanes * A->frags, A->reductions, A->reductions);
+               "    {\n");
     } else {
       snprintf(b, sizeof b,
                "extern \"C\" __global__ __launch_bounds__(%d) void %s_%s(AutoArgs a) {\n"
@@ -663,7 +670,7 @@ extern "C" {
 
 size_t cf_auto_workspace_bytes(cf_auto* A) {
   if (!A) return (size_t)-1;
-  if (!A->global) return 0;
+  if (!A->global || A->reductions == 0) return 0;  // no cross-workgroup exchange
   const int dev = ensure_loaded(A);
   if (dev < 0) return (size_t)-1;
   size_t bytes = 0;
@@ -694,7 +701,8 @@ cf_status cf_auto_launch(cf_auto* A, const void* const* args, int nargs, float* 
     if (op != CF_G_COLVEC) vec = vec && aligned16(args[s]);
     ka.p[s] = static_cast<const float*>(args[s]);
   }
-  if (A->global && (!ws || overlap(ws, ws_bytes, out, tile_bytes))) return !ws ? CF_EWORKSPACE : CF_EINVAL;
+  const bool exch = A->global && A->reductions > 0;  // members exchange partials through ws
+  if (exch && (!ws || overlap(ws, ws_bytes, out, tile_bytes))) return !ws ? CF_EWORKSPACE : CF_EINVAL;
   ka.out = out;
   ka.rows = (long)A->rows;
   ka.cols = (long)A->cols;
@@ -705,13 +713,15 @@ cf_status cf_auto_launch(cf_auto* A, const void* const* args, int nargs, float* 
     int64_t rg = 0;
     size_t need = 0;
     cf_status st = global_rows_per_round(A, dev, vec, &rg);
-    if (st == CF_OK) st = global_ws_bytes(A, dev, &need);
+    if (st == CF_OK && exch) st = global_ws_bytes(A, dev, &need);
     if (st != CF_OK) return st;
-    if (ws_bytes < need) return CF_EWORKSPACE;
-    char* base = static_cast<char*>(ws);
-    ka.err = reinterpret_cast<unsigned*>(base);
-    ka.joins = reinterpret_cast<unsigned long long*>(base + 256);
-    ka.slots = reinterpret_cast<unsigned long long*>(base + kSlotsOff);
+    if (exch) {
+      if (ws_bytes < need) return CF_EWORKSPACE;
+      char* base = static_cast<char*>(ws);
+      ka.err = reinterpret_cast<unsigned*>(base);
+      ka.joins = reinterpret_cast<unsigned long long*>(base + 256);
+      ka.slots = reinterpret_cast<unsigned long long*>(base + kSlotsOff);
+    }
     ka.S = A->members;
     ka.RG = (int)rg;
     grid = (unsigned)(rg * A->members);

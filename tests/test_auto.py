@@ -101,3 +101,16 @@ def test_global_source_exchanges_tagged_partials():
         first_take = src.index("cf_take(pp + q", start)
         await_ = src.index("cf_await(a.joins + rs, jold", start)
         assert clear < arrive < loop < await_ < first_take
+
+
+def test_global_mapping_without_reductions_has_no_launch_join():
+    """An element-wise graph on rows wider than a workgroup is cut into member slices like any
+    Global graph, but with no reduction nothing crosses workgroups: the kernel arrives on no join
+    word (an arrival never awaited would leave a shared word off by the member count)."""
+    b = graphs.B()
+    x = b.ph("input", 0)
+    t = b.add("mul", b.add("silu", x), b.ph("rowvec", 1))
+    a = auto((b.nodes, t), 3, 40000)
+    assert a.describe()["mapping"]["workgroups_per_row"] == 5
+    src = a.source()
+    assert "cf_arrive(a.joins" not in src and "cf_await(a.joins" not in src and "cf_put(pp" not in src

@@ -160,6 +160,34 @@ def test_auto_global_layouts_and_library_ops_share_a_workspace():
             assert ws.error_word() == 0
 
 
+def test_auto_wide_rows_without_reductions_need_no_workspace():
+    """Element-wise work on rows of 40000 values: five member slices per row, no exchange, so no
+    workspace; a Global kernel with reductions still runs exactly before and after it on one."""
+    rows, cols = 300, 40000
+    x = gen.normal(97, 0, (rows, cols))
+    v = gen.normal(97, 1, (cols,))
+    b = graphs.B()
+    xi = b.ph("input", 0)
+    t = b.add("mul", b.add("silu", xi), b.ph("rowvec", 1))
+    e = cf.Auto(b.nodes, t, rows, cols)
+    assert e.describe()["mapping"]["workgroups_per_row"] == 5
+    assert e.workspace_bytes() == 0
+    out = torch.full((rows, cols), float("nan"), device="cuda")
+    assert e.launch([d32(x), d32(v)], out) is None
+    assert rownorm_err(host(out), oracle.graph.evaluate(b.nodes, t, [x, v])) <= TOL_F32
+    nodes, tl = graphs.layernorm(cols)
+    ln = cf.Auto(nodes, tl, rows, cols)
+    ws = cf.Workspace(ln.workspace_bytes())
+    y = torch.empty((rows, cols), device="cuda")
+    ln.launch([d32(x)], y, ws=ws)
+    first = host(y)
+    assert rownorm_err(first, oracle.graph.evaluate(nodes, tl, [x])) <= TOL_F32
+    e.launch([d32(x), d32(v)], out)
+    ln.launch([d32(x)], y, ws=ws)
+    assert np.array_equal(host(y), first)
+    assert ws.error_word() == 0
+
+
 @pytest.mark.parametrize("name", ["layernorm_750000x32", "silu_ln_scaled_750000x32", "softmax_512x65536"])
 def test_auto_bench_workloads_at_full_size(name):
     """The generated kernels the bench times, at the sizes it times them."""
