@@ -150,7 +150,8 @@ int cf_auto_describe(const cf_auto* a, char* buf, size_t n);
 int cf_auto_source(const cf_auto* a, char* buf, size_t n);
 
 /* Workspace bytes the generated kernel needs on the current device: 0 unless
- * rows span workgroups.  Then, in cf.h's fixed workspace layout: the header
+ * rows span workgroups and the graph has a row reduction (members that
+ * exchange nothing need none).  Then, in cf.h's fixed workspace layout: the header
  * and join-word region, followed by one 8-byte tagged partial slot per
  * member, row reduction and row of two rounds of co-resident rows.  Every
  * launch clears its slots and joins each row's members once before it reads
