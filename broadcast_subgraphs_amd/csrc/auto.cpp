@@ -224,7 +224,7 @@ std::string apply(int op, const std::string& a, const std::string& b) {
     case CF_G_SUB: return "(" + a + " - " + b + ")";
     case CF_G_MUL: return "(" + a + " * " + b + ")";
     case CF_G_DIV: return "(" + a + " * __builtin_amdgcn_rcpf(" + b + "))";
-    case CF_G_POW: return "__builtin_amdgcn_exp2f(" + b + " * __builtin_amdgcn_logf(" + a + "))";
+    case CF_G_POW: return "cf_pow(" + a + ", " + b + ")";
     case CF_G_EXP: return "__builtin_amdgcn_exp2f(1.44269504088896341f * " + a + ")";
     case CF_G_SQUARE: return "(" + a + " * " + a + ")";
     case CF_G_RSQRT: return "__builtin_amdgcn_rsqf(" + a + ")";
@@ -308,14 +308,17 @@ std::string body(const cf_auto* A, bool vec) {
       }
       if (A->waves_per_row > 1) {
         // Regional: the row's waves combine through LDS (two alternating slots,
-        // one barrier per reduction), in wave order on every lane
+        // one barrier per reduction), in wave order on every lane.  A workgroup
+        // may hold several rows (128 lanes per row: two rows of two waves), so
+        // each row reads the entries of its own waves, from its first wave on
         snprintf(b, sizeof b,
                  "      if ((threadIdx.x & 63) == 0) red[slot][threadIdx.x >> 6] = %s;\n"
                  "      __syncthreads();\n"
-                 "      %s = red[slot][0];\n"
-                 "#pragma unroll\n      for (int w = 1; w < %d; ++w) %s = %s(%s, red[slot][w]);\n"
+                 "      %s = red[slot][(threadIdx.x >> 6) & ~%du];\n"
+                 "#pragma unroll\n      for (int w = 1; w < %d; ++w) %s = %s(%s, red[slot][((threadIdx.x >> 6) & ~%du) + w]);\n"
                  "      slot ^= 1;\n",
-                 ri.c_str(), ri.c_str(), A->waves_per_row, ri.c_str(), comb.c_str(), ri.c_str());
+                 ri.c_str(), ri.c_str(), A->waves_per_row - 1, A->waves_per_row, ri.c_str(), comb.c_str(),
+                 ri.c_str(), A->waves_per_row - 1);
         s += b;
       }
       if (A->global) {
@@ -420,6 +423,29 @@ std::string generate(const cf_auto* A) {
        "    __builtin_amdgcn_s_sleep(1);\n  }\n"
        "  __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);\n}\n"
        "__device__ __forceinline__ float cf_add(float x, float y) { return x + y; }\n"
+       "// a^b as the real power: an integral exponent is real for either sign of\n"
+       "// a (square and multiply up to |b| = 16, else 2^(b log2|a|) with the sign\n"
+       "// of an odd power) and a^0 = 1, 0^0 included; any other exponent is\n"
+       "// 2^(b log2 a), which is NaN for a negative base, as the real power is\n"
+       "__device__ __forceinline__ float cf_pow(float a, float b) {\n"
+       "  if (b == __builtin_rintf(b)) {\n"
+       "    const float n = __builtin_fabsf(b);\n"
+       "    float r;\n"
+       "    if (n <= 16.0f) {\n"
+       "      r = 1.0f;\n"
+       "      float q = a;\n"
+       "      for (int k = (int)n; k != 0; k >>= 1) {\n"
+       "        if (k & 1) r *= q;\n"
+       "        q *= q;\n"
+       "      }\n"
+       "    } else {\n"
+       "      r = __builtin_amdgcn_exp2f(n * __builtin_amdgcn_logf(__builtin_fabsf(a)));\n"
+       "      if (a < 0.0f && n * 0.5f != __builtin_truncf(n * 0.5f)) r = -r;\n"
+       "    }\n"
+       "    return b < 0.0f ? 1.0f / r : r;\n"
+       "  }\n"
+       "  return __builtin_amdgcn_exp2f(b * __builtin_amdgcn_logf(a));\n"
+       "}\n"
        "__device__ __forceinline__ f4 ntld4(const f4* p) { return __builtin_nontemporal_load(p); }\n";
   for (int vec = 1; vec >= 0; --vec) {
     if (A->global) {

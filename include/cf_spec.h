@@ -61,7 +61,9 @@ typedef enum cf_gop {
   CF_G_SUB = 8,
   CF_G_MUL = 9,
   CF_G_DIV = 10,
-  CF_G_POW = 11,      /* in0 ^ in1 (in1 a constant)                                      */
+  CF_G_POW = 11,      /* in0 ^ in1 (in1 a constant): the real power; an integral         */
+                      /* exponent takes either sign of in0, x^0 = 1, a negative in0     */
+                      /* with a non-integral exponent gives NaN                          */
   CF_G_EXP = 12,
   CF_G_SQUARE = 13,
   CF_G_RSQRT = 14,

@@ -388,6 +388,17 @@ def pin_gemm_act_closed_forms():
            what="square of ones")
 
 
+def pin_activation_values():
+    """GELU (tanh form) and SiLU at the points the golden file derives by hand in 50-digit decimal
+    arithmetic (a route that shares nothing with the oracle's float64 formula), reached through
+    the activation GEMM with an identity weight, so the values pass the epilogue unchanged."""
+    gd = _golden()
+    for key, act in (("gelu_tanh_values", "gelu_tanh"), ("silu_values", "silu")):
+        x = np.array([gd[key]["x"]])
+        y = oracle.gemm_act(x, np.eye(x.shape[1]), None, act)
+        _close(y, [gd[key]["y"]], 1e-15, 1e-15, what=f"{act} at golden points")
+
+
 def pin_gemm_act_rsqrt():
     """rsqrt epilogue: brute force on positive operands (every u > 0), and closed forms:
     a ones GEMM with K = 9 gives 1/3, with K = 4 exactly 0.5; a diagonal GEMM gives 1/sqrt of

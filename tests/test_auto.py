@@ -17,6 +17,7 @@ def auto(g, rows, cols):
 
 @pytest.mark.parametrize("cols,lanes,frags,wg,waves", [
     (32, 8, 1, 256, 1), (33, 8, 2, 256, 1), (5, 8, 1, 256, 1), (1024, 64, 4, 256, 1), (1000, 64, 4, 256, 1),
+    (1500, 128, 3, 256, 2), (2048, 128, 4, 256, 2),
     (4096, 256, 4, 256, 4), (30000, 1024, 8, 1024, 16), (32768, 1024, 8, 1024, 16)])
 def test_thread_mapping_follows_the_row_length(cols, lanes, frags, wg, waves):
     d = auto(graphs.layernorm(cols), 100, cols).describe()
@@ -28,6 +29,27 @@ def test_thread_mapping_follows_the_row_length(cols, lanes, frags, wg, waves):
     schemes = {e["scheme"] for e in d["edges"]}
     assert schemes == ({"local", "regional"} if waves > 1 else {"local"})
     assert d["kernels"] == 1 and d["code_bytes"] > 0
+
+
+def test_regional_reduction_reads_the_waves_of_its_own_row():
+    """Rows of 1025 to 2048 values take 128 lanes: two rows of two waves share a 256-lane
+    workgroup, so each row's LDS combine starts at its own first wave (wave index with the
+    low bit cleared), never at wave 0 for every row."""
+    d = auto(graphs.layernorm(2048), 33, 2048)
+    m = d.describe()["mapping"]
+    assert (m["rows_per_workgroup"], m["waves_per_row"]) == (2, 2)
+    src = d.source()
+    assert src.count("red[slot][(threadIdx.x >> 6) & ~1u]") == 2 * 2  # two reductions, both variants
+    assert "red[slot][0]" not in src
+
+
+def test_pow_is_the_real_power():
+    """pow in a generated kernel: integral exponents are real for negative bases (square and
+    multiply), x^0 = 1 for every x, other exponents go through 2^(b log2 a)."""
+    b = graphs.B()
+    t = b.add("pow", b.ph("input", 0), b.c(3.0))
+    src = auto((b.nodes, t), 8, 64).source()
+    assert "cf_pow(" in src and "__builtin_rintf(b)" in src
 
 
 def test_dominants_and_merge():

@@ -11,8 +11,8 @@ from tests.test_gpu_parity import TOL_F32, d32, dbf16, host, rownorm_err
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(1000, 32), (999, 36), (5, 3), (7, 100), (33, 1024), (3, 5000), (4, 30000), (2, 32768), (4099, 33),
-          (3, 32769), (2, 100000), (5, 70001), (600, 40000)]
+SHAPES = [(1000, 32), (999, 36), (5, 3), (7, 100), (33, 1024), (33, 2048), (5, 1500), (34, 1025), (3, 5000),
+          (4, 30000), (2, 32768), (4099, 33), (3, 32769), (2, 100000), (5, 70001), (600, 40000)]
 
 
 def _inputs(rows, cols, seed):
@@ -51,6 +51,47 @@ def test_auto_graphs(rows, cols):
             assert ws.error_word() == 0, "a cross-workgroup wait gave up"
         want = oracle.graph.evaluate(nodes, t, hargs)
         assert rownorm_err(got, want) <= TOL_F32, (name, a.describe()["mapping"])
+
+
+@pytest.mark.parametrize("p", [2.0, 3.0, 0.0, -1.0, 1.5])
+def test_auto_pow_on_signed_input(p):
+    """pow(x, p) + a row statistic on N(0,1) input (negative bases): integral exponents give the
+    real power for either sign, x^0 = 1, and the non-integral 1.5 gives NaN exactly where the
+    oracle's real power does (negative x)."""
+    rows, cols = 37, 515
+    x = gen.normal(95, 0, (rows, cols))
+    b = graphs.B()
+    xi = b.ph("input", 0)
+    pw = b.add("pow", xi, b.c(p))
+    t = b.add("add", pw, b.add("div", b.add("rowsum", b.add("square", xi)), b.c(cols)))
+    a = cf.Auto(b.nodes, t, rows, cols)
+    out = torch.full((rows, cols), 7.0, device="cuda")
+    a.launch([d32(x)], out)
+    got = host(out).astype(np.float64)
+    want = oracle.graph.evaluate(b.nodes, t, [x])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert ok.any()
+    assert rownorm_err(np.where(ok, got, 0.0), np.where(ok, want, 0.0)) <= TOL_F32
+
+
+@pytest.mark.parametrize("act,key", [("gelu_tanh", "gelu_tanh_values"), ("silu", "silu_values")])
+def test_auto_activation_at_golden_points(act, key):
+    """The generated kernel's GELU (tanh form) and SiLU in fp32 at the points the golden file
+    derives by hand: the erf form of GELU is 1.5e-4 away at x = 1, far outside fp32 rounding."""
+    import json
+    import os
+    gd = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")))[key]
+    xs = np.array(gd["x"], np.float32)
+    rows, cols = 3, 64
+    x = np.resize(xs, (rows, cols)).astype(np.float32)
+    want = np.resize(np.array(gd["y"]), (rows, cols))
+    b = graphs.B()
+    t = b.add(act, b.ph("input", 0))
+    out = torch.full((rows, cols), float("nan"), device="cuda")
+    cf.Auto(b.nodes, t, rows, cols).launch([d32(x)], out)
+    got = host(out).astype(np.float64)
+    assert np.max(np.abs(got - want) / np.abs(want)) <= 2e-6
 
 
 def test_auto_misaligned_takes_the_scalar_variant_and_repeats_bitwise():

@@ -3,6 +3,8 @@
 A mistake counts as caught when at least one pin raises (a wrong value, a
 non-finite value, or a shape error all count).
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -122,6 +124,10 @@ MUTANTS = {
     "rmsnorm_centers": (subgraphs, "rmsnorm_rows", _rms_centered),
     "gelu_erf_constant_dropped": (ops, "map_gelu_tanh", lambda x: 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * x))),
     "silu_sign": (ops, "map_silu", lambda x: x / (1.0 + np.exp(x))),
+    "gelu_erf_form": (ops, "map_gelu_tanh", lambda x: 0.5 * x * (1.0 + np.vectorize(math.erf)(x / np.sqrt(2.0)))),
+    "gelu_cubic_0_0447": (ops, "map_gelu_tanh",
+                          lambda x: 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.0447 * x ** 3)))),
+    "silu_sigmoid_2x": (ops, "map_silu", lambda x: x / (1.0 + np.exp(-2.0 * x))),
     "relu_is_abs": (ops, "map_relu", lambda x: np.abs(x)),
     "rsqrt_is_sqrt": (ops, "map_rsqrt", lambda x: np.sqrt(x)),
     "rsqrt_with_eps": (ops, "map_rsqrt", lambda x: 1.0 / np.sqrt(x + 1e-5)),
@@ -148,3 +154,22 @@ def test_mutant_is_caught(name, monkeypatch):
             except Exception as e:  # noqa: BLE001 - any failure is a catch
                 caught.append((pin.__name__, type(e).__name__))
     assert caught, f"mutant {name} survived every pin"
+
+
+@pytest.mark.parametrize("name", ["gelu_erf_form", "gelu_cubic_0_0447", "silu_sigmoid_2x",
+                                  "gelu_erf_constant_dropped", "silu_sign"])
+def test_activation_mutant_is_caught_by_an_independent_pin(name, monkeypatch):
+    """Each plausible activation mistake is caught by a pin other than the GEMM + activation brute
+    force (whose per-element activation restates the oracle's formula)."""
+    mod, attr, fn = MUTANTS[name]
+    monkeypatch.setattr(mod, attr, fn)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin in pins.ALL_PINS:
+            if pin.__name__ == "pin_gemm_act_brute_force":
+                continue
+            try:
+                pin()
+            except Exception:  # noqa: BLE001 - any failure is a catch
+                caught.append(pin.__name__)
+    assert caught, f"mutant {name} is caught only by the brute force"
