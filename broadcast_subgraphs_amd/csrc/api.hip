@@ -124,6 +124,7 @@ cf_status plan_rows(int op, int64_t rows, int64_t cols, bool vec_ok, RowPlan* pl
     const int64_t s_min = (nvec + 256 * 16 - 1) / (256 * 16);
     int64_t S = std::max<int64_t>(s_min, rows >= di->cus ? 1 : pow2ceil((di->cus + rows - 1) / rows));
     if (force_split > 1) S = std::max<int64_t>(force_split, s_min);
+    if (S > kMaxSplit) return CF_EUNSUPPORTED;
     const int64_t slice_vec = (nvec + S - 1) / S;
     p.split = (int)S;
     p.nv = pow2ceil((slice_vec + 255) / 256);
@@ -141,7 +142,8 @@ cf_status plan_rows(int op, int64_t rows, int64_t cols, bool vec_ok, RowPlan* pl
     int occ = 0;
     if (rows_split_occupancy(op, p, &occ) != hipSuccess || occ <= 0) return CF_EHIP;
     p.occupancy = occ;
-    const int64_t cap = (int64_t)occ * di->cus;
+    // CF_FORCE_CUS plans for a device with fewer CUs (a test hook for the refusal below)
+    const int64_t cap = (int64_t)occ * std::min<long>(di->cus, std::max<long>(1, env_int("CF_FORCE_CUS", di->cus)));
     const int64_t items = rows * p.split;
     int64_t G = std::min<int64_t>(items, cap / p.split * p.split);
     if (G < p.split) return CF_EOCCUPANCY;
@@ -152,9 +154,12 @@ cf_status plan_rows(int op, int64_t rows, int64_t cols, bool vec_ok, RowPlan* pl
   return CF_OK;
 }
 
+// Split plans: per group of S members, 2 parities x 2 fields x S tagged 8-byte
+// slots, i.e. 32 bytes per resident workgroup.
 size_t rows_ws_bytes(const RowPlan& p, int64_t rows) {
+  (void)rows;
   if (p.split <= 1) return 0;
-  return ws_layout(rows * p.split * 4).total;
+  return ws_layout((int64_t)p.grid * 8).total;
 }
 
 void record_rows_plan(const char* name, const RowPlan& p, int64_t rows, int64_t cols) {
@@ -193,11 +198,11 @@ cf_status run_rows(const char* name, int op, const float* x, float* y, float* y_
   a.gamma = gamma; a.beta = beta;
   a.rows = rows; a.cols = cols;
   if (need > 0) {
-    const WsLayout L = ws_layout(rows * p.split * 4);
+    const WsLayout L = ws_layout((int64_t)p.grid * 8);
     char* base = static_cast<char*>(ws);
     a.err = reinterpret_cast<uint32_t*>(base);
     a.joins = reinterpret_cast<uint64_t*>(base + L.joins_off);
-    a.partials = reinterpret_cast<float*>(base + L.partials_off);
+    a.slots = reinterpret_cast<uint64_t*>(base + L.partials_off);
   }
   a.S = p.split;
   a.slice = p.slice;

@@ -80,6 +80,53 @@ __device__ __forceinline__ float group_reduce(float v) {
   return v;
 }
 
+// ------------------------------------------------- online pair reductions
+//
+// Softmax statistics as one (max, sum) pair in the base-2 domain: the sum is
+// taken relative to the pair's own max, and two pairs merge by rescaling both
+// sums to the larger max (the online softmax identity; an empty pair is
+// (-inf, 0)).  LayerNorm statistics as (count, mean, M2), merged with Chan's
+// pairwise update.  Each merges a row's statistics in ONE reduction instead of
+// two chained ones (max then sum; mean then centred second moment), equal in
+// exact arithmetic.
+struct SmPair {
+  float m, l;
+};
+__device__ __forceinline__ SmPair sm_merge(SmPair a, SmPair b) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == -INFINITY) return {M, 0.0f};
+  return {M, a.l * __builtin_amdgcn_exp2f(a.m - M) + b.l * __builtin_amdgcn_exp2f(b.m - M)};
+}
+struct MomPair {
+  float n, mean, m2;
+};
+__device__ __forceinline__ MomPair mom_merge(MomPair a, MomPair b) {
+  const float n = a.n + b.n;
+  if (b.n == 0.0f) return a;
+  if (a.n == 0.0f) return b;
+  const float d = b.mean - a.mean, f = b.n / n;
+  return {n, fmaf(d, f, a.mean), a.m2 + b.m2 + d * d * (a.n * f)};
+}
+// Butterfly over all 64 lanes of the wave: every lane ends with the wave's
+// pair.  Both lanes of an exchange merge (lower lane's pair, upper lane's
+// pair), so they compute the same bits even where the merge is not symmetric.
+__device__ __forceinline__ SmPair wave_reduce(SmPair p) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const SmPair q = {__shfl_xor(p.m, o, kWave), __shfl_xor(p.l, o, kWave)};
+    p = (threadIdx.x & o) ? sm_merge(q, p) : sm_merge(p, q);
+  }
+  return p;
+}
+__device__ __forceinline__ MomPair wave_reduce(MomPair p) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const MomPair q = {__shfl_xor(p.n, o, kWave), __shfl_xor(p.mean, o, kWave), __shfl_xor(p.m2, o, kWave)};
+    p = (threadIdx.x & o) ? mom_merge(q, p) : mom_merge(p, q);
+  }
+  return p;
+}
+
 // ------------------------------------------------------ cross-workgroup join
 //
 // One 64-bit join word per group of cooperating workgroups:
@@ -148,6 +195,53 @@ __device__ __forceinline__ bool join_arrive_and_wait(uint64_t* j, uint32_t membe
   }
   __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return false;
+}
+
+// Split form of the join, for a launch join: arrive early (the last arriver
+// advances the generation at once), await later with the returned word, so the
+// wait overlaps whatever runs between the two.
+__device__ __forceinline__ uint64_t join_arrive(uint64_t* j, uint32_t members) {
+  const uint64_t old = __hip_atomic_fetch_add(j, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((uint32_t)old == members - 1)
+    __hip_atomic_fetch_add(j, (1ull << 32) - members, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return old;
+}
+__device__ __forceinline__ bool join_await(uint64_t* j, uint64_t old, uint32_t members, uint32_t* err) {
+  const uint32_t gen0 = (uint32_t)(old >> 32);
+  if ((uint32_t)old == members - 1) return true;
+  for (uint32_t it = 0; it < kSpinCap; ++it) {
+    const uint64_t w = __hip_atomic_load(j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(w >> 32) != gen0) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
+
+// ------------------------------------------------------------ tagged slots
+//
+// A 64-bit slot {tag:32 | value:32} written with ONE device-scope store: a
+// reader that sees the tag it waits for has the value that came with it, so
+// publishing a partial needs no separate arrival, fence or reload.  Tags are
+// the 1-based index of the row within the launch; a launch join after every
+// member has cleared its own slots makes sure no slot a reader polls still
+// holds an earlier launch's word (tag 0 never matches).
+__device__ __forceinline__ void slot_put(uint64_t* s, uint32_t tag, float v) {
+  __hip_atomic_store(s, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void slot_clear(uint64_t* s) {
+  __hip_atomic_store(s, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The slot's value once it carries `tag`; capped spin: on giving up the error
+// word is set and 0 returned, so the kernel still finishes.
+__device__ __forceinline__ float slot_take(uint64_t* s, uint32_t tag, uint32_t* err) {
+  for (uint32_t it = 0; it < kSpinCap; ++it) {
+    const uint64_t w = __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(w >> 32) == tag) return __uint_as_float((uint32_t)w);
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return 0.0f;
 }
 
 // Logical workgroup index that keeps consecutive logical ids on one XCD.

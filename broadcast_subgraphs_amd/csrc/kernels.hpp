@@ -26,10 +26,14 @@ struct RowArgs {
   int64_t cols;
   uint32_t* err;    // workspace error word
   uint64_t* joins;  // split plans: one join word per group of S workgroups
-  float* partials;  // split plans: rows * S * 4 floats
-  int S;            // workgroups per row (split plans)
+  uint64_t* slots;  // split plans: groups * 4 * S tagged slots ([parity][field][member])
+  int S;            // workgroups per row (split plans), at most kMaxSplit
   int64_t slice;    // columns per member (split plans)
 };
+
+// Most workgroups one row may be split over (the members' partials of a row
+// sit in LDS while they are merged).
+constexpr int kMaxSplit = 256;
 
 struct RowPlan {
   int block = 256;  // lanes per workgroup (256; 512 or 1024 for one wide row per workgroup)

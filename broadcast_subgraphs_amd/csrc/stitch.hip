@@ -50,6 +50,24 @@ __device__ __forceinline__ float row_reduce(float v, float* red, int& slot, int 
   }
 }
 
+// One pair reduction over the whole workgroup: lane butterfly, then the waves'
+// pairs through LDS, merged in wave order by every lane (the same bits on every
+// lane).  The caller's next use of `lds` is behind a later barrier.
+template <int WAVES, class P>
+__device__ __forceinline__ P block_reduce_pair(P p, P* lds, int wave) {
+  p = wave_reduce(p);
+  if constexpr (WAVES == 1) return p;
+  if ((threadIdx.x & (kWave - 1)) == 0) lds[wave] = p;
+  __syncthreads();
+  P r = lds[0];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) {
+    if constexpr (sizeof(P) == sizeof(SmPair)) r = sm_merge(r, lds[w]);
+    else r = mom_merge(r, lds[w]);
+  }
+  return r;
+}
+
 template <int W>
 __device__ __forceinline__ void load_frag(float (&d)[W], const float* p) {
   if constexpr (W == 4) {
@@ -101,6 +119,15 @@ __global__ __launch_bounds__(BLOCK) void k_rows(RowArgs a) {
   for (int64_t rb = blockIdx.x; rb < nblk; rb += gridDim.x) {
     float x[RPI][NV][W];
     bool rv[RPI];
+    // pow-softmax: the rows' v, issued ahead of the fragment loads so v^p is
+    // ready when they land
+    float vrow = 0.0f;
+    if constexpr (OP == kPowSoftmax) {
+      if (t < RPI * RPW) {
+        const int64_t row = (rb * RPI + t / RPW) * RPW + (t % RPW);
+        if (row < rows) vrow = a.v[row];
+      }
+    }
     // ---- fragment loads (all in flight before any reduction)
 #pragma unroll
     for (int r = 0; r < RPI; ++r) {
@@ -121,10 +148,7 @@ __global__ __launch_bounds__(BLOCK) void k_rows(RowArgs a) {
 
     if constexpr (OP == kPowSoftmax) {
       // Regional scheme: v_i^p once per row per workgroup, broadcast via LDS.
-      if (t < RPI * RPW) {
-        const int64_t row = (rb * RPI + t / RPW) * RPW + (t % RPW);
-        pv_lds[pvbuf][t] = row < rows ? powf(a.v[row], a.p) : 0.0f;
-      }
+      if (t < RPI * RPW) pv_lds[pvbuf][t] = powf(vrow, a.p);
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < RPI; ++r) {
@@ -268,33 +292,59 @@ __global__ __launch_bounds__(BLOCK) void k_rows(RowArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Rows split over S workgroups (task splitting).  Logical item i = (row, s)
-// with row = i / S, s = i % S covers columns [s*slice, min((s+1)*slice, cols)).
-// Workgroup g handles items g, g+G, ... ; G is a multiple of S, so the S
-// members of a row run in the same round, and the host guarantees the grid is
-// resident at once.  Members publish partials, join, then every member reads
-// all S partials and combines them in member order (deterministic).
+// Rows split over S workgroups (task splitting).  Workgroup g is member
+// s = g % S of group g / S for the whole launch; the group walks rows g / S,
+// g / S + G / S, ... (G, a multiple of S, is resident at once), member s
+// covering columns [s*slice, min((s+1)*slice, cols)) of each.
+//
+// Exchange ([AStitch] "Four stitching schemes", Global; [ComFuse] inter-CTA
+// level, peer-to-peer): per row, each member publishes its two partials
+// (softmax: max and sum in the base-2 domain; the norms: mean and M2 of its
+// slice, whose count follows from the slice bounds) as tagged slots, one
+// 64-bit store each; wave 0 takes every member's slots once they carry the
+// row's tag (the value arrives with the tag: no arrival counter, no reload),
+// and every lane merges them from LDS in member order (deterministic).  A
+// slot is reused two rows later (double-buffered by row parity): before a
+// member rewrites it, every member has published the next row, which it does
+// only after taking this row's slots.  Across launches: before its first load
+// each member clears its slots and arrives on the group's join word; it awaits
+// the others before its first take, so the join overlaps the first loads, and
+// no slot read in a launch holds a word from an earlier one (tags restart at
+// 1, and a cleared slot carries tag 0).
 // ---------------------------------------------------------------------------
 template <int OP, int NV, int W>
 __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
-  __shared__ float red[2 * kWaves];
+  constexpr int WAVES = kWaves;
+  __shared__ SmPair red2[WAVES];
+  __shared__ MomPair red3[WAVES];
   __shared__ float bc[4];
+  __shared__ float pm[2][kMaxSplit];
   const int t = threadIdx.x;
   const int wave_in_row = t / kWave;
-  int slot = 0;
   const int64_t rows = a.rows, cols = a.cols;
   const int S = a.S;
   const uint32_t G = gridDim.x;
-  const int64_t items = rows * S;
   const uint32_t g = xcd_local_id(blockIdx.x, G);
+  const int s = (int)(g % (uint32_t)S);
+  const int64_t grp = g / (uint32_t)S, groups = G / (uint32_t)S;
+  uint64_t* const slots = a.slots + grp * (4 * S);  // [parity][field][member]
+  uint64_t jold = 0;
+  if (t == 0 && grp < rows) {  // (the planner gives every group a row)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) slot_clear(slots + k * S + s);
+    wait_stores();
+    jold = join_arrive(a.joins + grp, (uint32_t)S);
+  }
+  const int64_t cbeg = (int64_t)s * a.slice;
+  const int64_t cend = min(cols, cbeg + a.slice);
+  uint32_t it_ = 0;
 
-  for (int64_t it = g; it < items; it += G) {
-    const int64_t row = it / S;
-    const int s = (int)(it % S);
-    const int64_t cbeg = (int64_t)s * a.slice;
-    const int64_t cend = min(cols, cbeg + a.slice);
+  for (int64_t row = grp; row < rows; row += groups, ++it_) {
     const float* xr = a.x + row * cols;
-
+    float vrow = 0.0f;
+    if constexpr (OP == kPowSoftmax) {
+      if (t == 0) vrow = a.v[row];  // issued ahead of the row's loads, so v^p is ready when they land
+    }
     float x[NV][W];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
@@ -307,15 +357,18 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
       }
     }
 
-    float part0, part1, part2 = 0.0f;  // published partials of this member
+    // ---- the member's statistics in ONE reduction (lane, wave, LDS): the
+    // online (max, sum) pair, or (count, mean, M2)
+    float part0, part1;  // this member's published partials
+    float lane_ref;      // softmax: the lane's max; norms: the lane's mean
     if constexpr (OP == kSoftmax || OP == kPowSoftmax) {
       float pv = 0.0f;
       if constexpr (OP == kPowSoftmax) {
-        if (t == 0) bc[0] = powf(a.v[row], a.p);  // once per row per workgroup
+        if (t == 0) bc[0] = powf(vrow, a.p);  // once per row per workgroup
         __syncthreads();
         pv = bc[0];
       }
-      float mm = -INFINITY;
+      float mloc = -INFINITY;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         const int64_t c0 = cbeg + (int64_t)(v * kBlock + t) * W;
@@ -328,33 +381,34 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
 #pragma unroll
         for (int e = 0; e < W; ++e) {
           x[v][e] *= kLog2e;
-          mm = fmaxf(mm, x[v][e]);
+          mloc = fmaxf(mloc, x[v][e]);
         }
       }
-      const float m = row_reduce<OpMax, kBlock>(mm, red, slot, 0, wave_in_row);
-      float sl = 0.0f;
+      const float ms = mloc == -INFINITY ? 0.0f : mloc;  // an all-masked lane keeps exp2(-inf) = 0
+      float lloc = 0.0f;
 #pragma unroll
       for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int e = 0; e < W; ++e) {
-          const float ev = __builtin_amdgcn_exp2f(x[v][e] - m);
+          const float ev = __builtin_amdgcn_exp2f(x[v][e] - ms);
           x[v][e] = ev;
-          sl += ev;
+          lloc += ev;
         }
-      const float l = row_reduce<OpSum, kBlock>(sl, red, slot, 0, wave_in_row);
-      part0 = m;
-      part1 = l;
+      const SmPair w = block_reduce_pair<WAVES>(SmPair{mloc, lloc}, red2, wave_in_row);
+      part0 = w.m;
+      part1 = w.l;
+      lane_ref = mloc;
     } else {
-      const float n_loc = cend > cbeg ? (float)(cend - cbeg) : 0.0f;
-      float mean_loc = 0.0f;  // RMSNorm: the mean is held at 0 throughout
-      if constexpr (OP != kRmsNorm) {
-        float sx = 0.0f;
+      float nl = 0.0f, sx = 0.0f;
 #pragma unroll
-        for (int v = 0; v < NV; ++v)
+      for (int v = 0; v < NV; ++v) {
+        const int64_t c0 = cbeg + (int64_t)(v * kBlock + t) * W;
+        if (c0 < cend) nl += (float)W;
 #pragma unroll
-          for (int e = 0; e < W; ++e) sx += x[v][e];
-        mean_loc = row_reduce<OpSum, kBlock>(sx, red, slot, 0, wave_in_row) / fmaxf(n_loc, 1.0f);
+        for (int e = 0; e < W; ++e) sx += x[v][e];
       }
+      // RMSNorm: the mean is held at 0 throughout
+      const float ml = (OP == kRmsNorm || nl == 0.0f) ? 0.0f : sx / nl;
       float sq = 0.0f;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
@@ -362,43 +416,43 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
         const bool ok = c0 < cend;
 #pragma unroll
         for (int e = 0; e < W; ++e) {
-          const float c = ok ? x[v][e] - mean_loc : 0.0f;
+          const float c = ok ? x[v][e] - ml : 0.0f;
           x[v][e] = c;
           sq = fmaf(c, c, sq);
         }
       }
-      const float m2 = row_reduce<OpSum, kBlock>(sq, red, slot, 0, wave_in_row);
-      part0 = n_loc;
-      part1 = mean_loc;
-      part2 = m2;
+      const MomPair w = block_reduce_pair<WAVES>(MomPair{nl, ml, sq}, red3, wave_in_row);
+      part0 = w.mean;
+      part1 = w.m2;
+      lane_ref = ml;
     }
 
-    // ---- global level: publish, join, read all members' partials
-    float4* P = reinterpret_cast<float4*>(a.partials) + (size_t)row * S;
-    if (t == 0) {
-      st_dev4(P + s, make_float4(part0, part1, part2, 0.0f));
-      wait_stores();
-      join_arrive_and_wait(a.joins + g / S, (uint32_t)S, a.err);  // members share g / S every round
+    // ---- global level: tagged slots, published and taken by wave 0.  The
+    // first row waits for the launch join (every member's slots cleared)
+    // before any lane takes a slot.
+    const uint32_t tag = it_ + 1u;
+    uint64_t* const sp = slots + (it_ & 1u) * (2 * S);
+    if (it_ == 0) {
+      if (t == 0) join_await(a.joins + grp, jold, (uint32_t)S, a.err);
+      __syncthreads();
+    }
+    if (t < kWave) {
+      if (t == 0) {
+        slot_put(sp + s, tag, part0);
+        slot_put(sp + S + s, tag, part1);
+      }
+      for (int q = t; q < S; q += kWave) {
+        pm[0][q] = slot_take(sp + q, tag, a.err);
+        pm[1][q] = slot_take(sp + S + q, tag, a.err);
+      }
     }
     __syncthreads();
-    // Partials are read with device-scope loads, 8 in flight per batch.
     if constexpr (OP == kSoftmax || OP == kPowSoftmax) {
       float M = -INFINITY, L = 0.0f;
-      for (int k0 = 0; k0 < S; k0 += 8) {  // 8 partials in flight per batch
-        float4 q[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) q[k] = k0 + k < S ? ld_dev4(P + k0 + k) : make_float4(-INFINITY, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) M = fmaxf(M, q[k].x);
-      }
-      for (int k0 = 0; k0 < S; k0 += 8) {
-        float4 q[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) q[k] = k0 + k < S ? ld_dev4(P + k0 + k) : make_float4(-INFINITY, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) L += q[k].x == -INFINITY ? 0.0f : q[k].y * __builtin_amdgcn_exp2f(q[k].x - M);
-      }
-      const float f = (part0 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(part0 - M)) / L;
+      for (int q = 0; q < S; ++q) M = fmaxf(M, pm[0][q]);
+      for (int q = 0; q < S; ++q) L += pm[0][q] == -INFINITY ? 0.0f : pm[1][q] * __builtin_amdgcn_exp2f(pm[0][q] - M);
+      // this lane's exponentials are relative to its own max
+      const float f = (lane_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lane_ref - M)) / L;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         const int64_t c0 = cbeg + (int64_t)(v * kBlock + t) * W;
@@ -409,25 +463,21 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
         }
       }
     } else {
-      // Chan's pairwise merge of (count, mean, M2), members in order.
+      // Chan's pairwise merge of (count, mean, M2), members in order; member
+      // q's count is the width of its slice
       float n = 0.0f, mean = 0.0f, M2 = 0.0f;
-      for (int k0 = 0; k0 < S; k0 += 8) {
-        float4 q[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) q[k] = k0 + k < S ? ld_dev4(P + k0 + k) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float nb = q[k].x;
-          if (nb == 0.0f) continue;
-          const float nn = n + nb;
-          const float d = q[k].y - mean;
-          mean += d * (nb / nn);
-          M2 += q[k].z + d * d * (n * nb / nn);
-          n = nn;
-        }
+      for (int q = 0; q < S; ++q) {
+        const int64_t qb = (int64_t)q * a.slice;
+        const float nb = qb < cols ? (float)(min(cols, qb + a.slice) - qb) : 0.0f;
+        if (nb == 0.0f) continue;
+        const float nn = n + nb;
+        const float d = pm[0][q] - mean;
+        mean += d * (nb / nn);
+        M2 += pm[1][q] + d * d * (n * nb / nn);
+        n = nn;
       }
       const float rs = rsqrtf(M2 / (float)cols + a.eps);
-      const float shift = part1 - mean;  // this member's values are x - mean_loc
+      const float shift = lane_ref - mean;  // this lane's values are x minus its own mean
       constexpr bool GAIN = OP == kLayerNormAffine || OP == kRmsNorm, BIAS = OP == kLayerNormAffine;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
@@ -452,7 +502,7 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
         }
       }
     }
-    __syncthreads();  // LDS slots and bc[] are reused by the next item
+    __syncthreads();  // LDS slots, bc[] and pm[] are reused by the next row
   }
 }
 

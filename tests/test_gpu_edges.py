@@ -1,0 +1,184 @@
+"""GPU parity on the stitched plans' hard cases: the 16-byte-fragment split kernel, softmax inputs
+whose exponentials overflow without the max shift, LayerNorm rows far from zero (cancellation in a
+one-pass variance), and the planner's occupancy refusal.
+
+[AStitch] "Adaptive thread mapping" (task splitting) and "Four stitching schemes" (Global);
+[ComFuse] Stage-Stream Execution Model (stage chaining: the max feeds the exponentials, the mean
+feeds the centred second moment).
+"""
+import json
+
+import numpy as np
+import pytest
+import torch
+
+import broadcast_subgraphs_amd as cf
+import gen
+import oracle
+from tests.test_gpu_parity import (TOL_BF16, TOL_F32, _gemm_ln_run, _gemm_sm_run, check_ws, d32, empty_f32, host,
+                                   rownorm_err)
+
+pytestmark = pytest.mark.gpu
+
+
+def _plan():
+    return json.loads(cf.last_plan())
+
+
+def _run_rows(op, x, extra, ws=None):
+    rows, cols = x.shape
+    y = empty_f32(rows, cols)
+    if op == "softmax":
+        ws = cf.cf_stitch_softmax(d32(x), y, ws=ws)
+        want = oracle.softmax_rows(x)
+    elif op == "layernorm":
+        ws = cf.cf_stitch_layernorm(d32(x), y, 1e-5, ws=ws)
+        want = oracle.layernorm_rows(x, 1e-5)
+    elif op == "rmsnorm":
+        ws = cf.cf_stitch_rmsnorm(d32(x), d32(extra["gamma"]), y, 1e-5, ws=ws)
+        want = oracle.rmsnorm_rows(x, extra["gamma"], 1e-5)
+    elif op == "layernorm_affine":
+        ws = cf.cf_stitch_layernorm_affine(d32(x), d32(extra["gamma"]), d32(extra["beta"]), y, 1e-5, ws=ws)
+        want = oracle.layernorm_affine_rows(x, extra["gamma"], extra["beta"], 1e-5)
+    else:
+        ypre = empty_f32(rows, cols)
+        ws = cf.cf_stitch_pow_bcast_add(d32(x), d32(extra["v"]), 1.5, y, ypre, ws=ws)
+        want, want_pre = oracle.pow_bcast_add_softmax(x, extra["v"], 1.5)
+        assert rownorm_err(host(ypre), want_pre) <= TOL_F32
+    plan = _plan()
+    check_ws(ws)
+    return host(y), want, plan
+
+
+def _extra(seed, rows, cols):
+    return {"gamma": (1.0 + 0.1 * gen.normal(seed, 5, (cols,)).astype(np.float64)).astype(np.float32),
+            "beta": gen.normal(seed, 6, (cols,), std=0.1), "v": gen.uniform(seed, 7, (rows,), 0.1, 2.0)}
+
+
+# 16-byte fragments (every row start 16-byte aligned) on the split plan: rows longer than one
+# 1024-lane workgroup holds, few rows longer than one 256-lane workgroup holds, and >= 256 rows
+# longer than 16384 values (two members per row)
+SPLIT16 = [("softmax", 2, 65536), ("layernorm", 3, 70000), ("rmsnorm", 3, 70000), ("layernorm_affine", 3, 70000),
+           ("pow", 8, 40000), ("softmax", 300, 20000), ("layernorm", 260, 16400), ("pow", 5, 32772)]
+
+
+@pytest.mark.parametrize("op,rows,cols", SPLIT16)
+def test_split_plan_16_byte_fragments(op, rows, cols):
+    x = gen.normal(201, 0, (rows, cols)) if op in ("softmax", "pow") else gen.uniform(201, 0, (rows, cols), -1, 1)
+    got, want, plan = _run_rows(op, x, _extra(201, rows, cols))
+    assert plan["kernel"] == "k_rows_split" and plan["frag_floats"] == 4, plan
+    assert rownorm_err(got, want) <= TOL_F32, plan
+
+
+@pytest.mark.parametrize("split", [2, 4, 8, 16])
+@pytest.mark.parametrize("op", ["pow", "softmax", "layernorm"])
+def test_split_plan_on_64x30000(monkeypatch, op, split):
+    """The short-wide workload on the split plan, S members per row (S x 64 workgroups)."""
+    monkeypatch.setenv("CF_FORCE_WIDE", "0")
+    monkeypatch.setenv("CF_FORCE_SPLIT", str(split))
+    rows, cols = 64, 30000
+    x = gen.pow_bcast_add_inputs(seed=3)["x"] if op != "layernorm" else gen.uniform(202, 0, (rows, cols), -1, 1)
+    ex = _extra(202, rows, cols)
+    if op == "pow":
+        ex["v"] = gen.pow_bcast_add_inputs(seed=3)["v"]
+    got, want, plan = _run_rows(op, x, ex)
+    assert (plan["kernel"], plan["split"], plan["frag_floats"], plan["grid"]) == ("k_rows_split", split, 4, 64 * split)
+    assert rownorm_err(got, want) <= TOL_F32, plan
+
+
+def test_split_plan_rows_in_rounds_repeat_bitwise(monkeypatch):
+    """More row groups than resident workgroups allow (CF_FORCE_CUS shrinks the resident grid):
+    each group walks several rows, its slots reused by row parity, and a second launch on the same
+    workspace (its slots holding the first launch's tags) gives the same bits."""
+    monkeypatch.setenv("CF_FORCE_CUS", "2")
+    rows, cols = 37, 40000
+    x = gen.normal(203, 0, (rows, cols))
+    ws = cf.Workspace(cf.cf_workspace_bytes(cf.CF_OP_STITCH_SOFTMAX, rows, cols, 0))
+    got, want, plan = _run_rows("softmax", x, {}, ws=ws)
+    assert plan["kernel"] == "k_rows_split" and plan["grid"] // plan["split"] < rows, plan
+    assert rownorm_err(got, want) <= TOL_F32
+    again, _, _ = _run_rows("softmax", x, {}, ws=ws)
+    assert np.array_equal(again, got)
+    lw = gen.uniform(204, 0, (rows, cols), -1, 1)
+    g2, w2, _ = _run_rows("layernorm", lw, {}, ws=ws)  # another op's slots on the same workspace
+    assert rownorm_err(g2, w2) <= TOL_F32
+    again, _, _ = _run_rows("softmax", x, {}, ws=ws)
+    assert np.array_equal(again, got)
+
+
+def test_occupancy_refusal_launches_nothing(monkeypatch):
+    """A split wider than the resident grid (S members on a device planned as one CU) is refused
+    with CF_EOCCUPANCY before any launch: the output keeps its sentinel and the error word stays 0."""
+    monkeypatch.setenv("CF_FORCE_CUS", "1")
+    monkeypatch.setenv("CF_FORCE_SPLIT", "256")
+    rows, cols = 2, 65536
+    x = gen.normal(205, 0, (rows, cols))
+    from broadcast_subgraphs_amd import _lib as L
+    assert cf.cf_workspace_bytes(cf.CF_OP_STITCH_SOFTMAX, rows, cols, 0) == 2 ** 64 - 1  # no plan to size
+    ws = cf.Workspace(1 << 20)
+    xd, y = d32(x), empty_f32(rows, cols)
+    status = L.lib().cf_stitch_softmax(L._ptr(xd), L._ptr(y), rows, cols, ws.ptr(), ws.nbytes, L._stream(None))
+    assert status == cf.CF_EOCCUPANCY
+    torch.cuda.synchronize()
+    assert torch.isnan(y).all()
+    assert ws.error_word() == 0
+
+
+# Every stitched plan: packed rows, 4-byte fragments (ragged), one row per 256-lane workgroup,
+# one wide row per 1024-lane workgroup, split rows (4-byte and 16-byte fragments)
+PLAN_SHAPES = [(4099, 32), (999, 36), (17, 1000), (4, 20000), (2, 65536), (3, 70001), (300, 20000)]
+
+
+def _overflow_rows(seed, rows, cols):
+    """N(0,1) x 80 with one +1000 entry in row 0: exp overflows fp32 without the max shift."""
+    x = (gen.normal(seed, 0, (rows, cols)).astype(np.float64) * 80.0).astype(np.float32)
+    x[0, cols // 3] = 1000.0
+    return x
+
+
+@pytest.mark.parametrize("rows,cols", PLAN_SHAPES)
+def test_softmax_overflow_scale(rows, cols):
+    x = _overflow_rows(206, rows, cols)
+    got, want, plan = _run_rows("softmax", x, {})
+    assert rownorm_err(got, want) <= TOL_F32, plan
+    assert got[0, cols // 3] == pytest.approx(1.0, abs=1e-6)
+
+
+@pytest.mark.parametrize("rows,cols", [(64, 30000), (130, 8), (7, 9), (5, 20001), (8, 40000)])
+def test_pow_softmax_overflow_scale(rows, cols):
+    x = _overflow_rows(207, rows, cols)
+    got, want, plan = _run_rows("pow", x, _extra(207, rows, cols))
+    assert rownorm_err(got, want) <= TOL_F32, plan
+
+
+@pytest.mark.parametrize("op", ["layernorm", "layernorm_affine", "rmsnorm"])
+@pytest.mark.parametrize("rows,cols", PLAN_SHAPES)
+def test_norms_large_offset(op, rows, cols):
+    """Rows of 100 + U(-1,1): a one-pass E[x^2] - E[x]^2 variance loses ~1e-3 of the variance
+    to cancellation in fp32 (a 5e-4 output error), the centred second moment does not."""
+    x = (100.0 + gen.uniform(208, 0, (rows, cols), -1, 1).astype(np.float64)).astype(np.float32)
+    got, want, plan = _run_rows(op, x, _extra(208, rows, cols))
+    assert rownorm_err(got, want) <= TOL_F32, plan
+
+
+def test_gemm_softmax_scores_above_exp_range():
+    """scale 4 on N(0,1) Q, K with D = 128: scores reach several hundred, far past fp32 exp's
+    range, so only a max-shifted exponent stays finite."""
+    M, N, D = 512, 2048, 128
+    d = gen.gemm_softmax_inputs(seed=209, M=M, N=N, D=D)
+    d["scale"] = 4.0
+    g = _gemm_sm_run(d, M, N, D)
+    o = oracle.gemm_softmax(d["q"], d["k"], d["scale"])
+    assert np.max(np.abs(np.asarray(d["q"], np.float64) @ np.asarray(d["k"], np.float64).T) * 4.0) > 150  # fp32 exp overflows past 88
+    assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 1024, 256), (4096, 4096, 1024)])
+def test_gemm_ln_large_bias_offset(M, N, K):
+    """bias + 2000: u is about 2000 +- 3, where E[u^2] - E[u]^2 in fp32 loses a third of the
+    variance; the per-tile (count, mean, M2) and their merge do not."""
+    d = gen.gemm_ln_inputs(seed=210, M=M, N=N, K=K)
+    d["bias"] = (d["bias"].astype(np.float64) + 2000.0).astype(np.float32)
+    g = _gemm_ln_run(d, M, N, K)
+    o = oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"], d["beta"], d["eps"])
+    assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()

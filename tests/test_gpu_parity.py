@@ -184,7 +184,7 @@ GEMM_LN_SHAPES = [(300, 264, 72), (512, 1024, 256), (256, 128, 64), (17, 8, 8), 
 
 
 def _gemm_ln_run(d, M, N, K, residual=True, unfused=False):
-    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    Y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")  # every element must be written
     ws = cf.cf_gemm_ln(dbf16(d["a_bits"]), dbf16(d["w_bits"]), d32(d["bias"]),
                        dbf16(d["r_bits"]) if residual else None, d32(d["gamma"]), d32(d["beta"]), Y,
                        eps=d["eps"], unfused=unfused)
@@ -231,7 +231,7 @@ GEMM_SM_SHAPES = [(300, 264, 72), (512, 1024, 128), (256, 128, 64), (17, 8, 8), 
 
 
 def _gemm_sm_run(d, M, N, D, unfused=False):
-    S = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    S = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")  # every element must be written
     ws = cf.cf_gemm_softmax(dbf16(d["q_bits"]), dbf16(d["k_bits"]), d["scale"], S, unfused=unfused)
     if not unfused:
         check_ws(ws)
