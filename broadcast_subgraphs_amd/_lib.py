@@ -55,6 +55,7 @@ _SIGS = {
     "cf_stitch_layernorm_affine": (_ST, [_P, _P, _P, _P, _I64, _I64, _F, _P, _SZ, _P]),
     "cf_stitch_rmsnorm": (_ST, [_P, _P, _P, _I64, _I64, _F, _P, _SZ, _P]),
     "cf_gemm_ln": (_ST, [_P, _P, _P, _P, _P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "cf_gemm_ln_noalloc": (_ST, [_P, _P, _P, _P, _P, _P, _F, _P, _I64, _I64, _I64, _P]),
     "cf_gemm_softmax": (_ST, [_P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_gemm_softmax_gemm": (_ST, [_P, _P, _P, _F, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_gemm_act": (_ST, [_P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _P, _SZ, _P]),
@@ -272,6 +273,22 @@ def cf_gemm_ln(A, W, bias, R, gamma, beta, Y, eps=1e-5, ws=None, stream=None, un
     _check(name, getattr(lib(), name)(_ptr(A), _ptr(W), _ptr(bias), _ptr(R), _ptr(gamma), _ptr(beta),
                                       float(eps), _ptr(Y), M, N, K, p, n, st))
     return w
+
+
+def cf_gemm_ln_noalloc(A, W, bias, R, gamma, beta, Y, eps=1e-5, stream=None):
+    """cf_gemm_ln with its workspace in the library's static scratch (nothing allocated)."""
+    torch = _torch()
+    for t, nm in ((A, "A"), (W, "W"), (Y, "Y")):
+        _need(t, torch.bfloat16, nm, 2)
+    if R is not None:
+        _need(R, torch.bfloat16, "R", 2)
+    for t, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta")):
+        _need(t, torch.float32, nm, 1)
+    M, K = A.shape
+    N = W.shape[1]
+    _check("cf_gemm_ln_noalloc", lib().cf_gemm_ln_noalloc(_ptr(A), _ptr(W), _ptr(bias), _ptr(R), _ptr(gamma),
+                                                          _ptr(beta), float(eps), _ptr(Y), M, N, K,
+                                                          _stream(stream)))
 
 
 def cf_gemm_softmax(Q, K, scale, S, ws=None, stream=None, unfused=False):

@@ -523,9 +523,9 @@ static cf_status run_gemm(const char* name, int epi, bool nn, GemmArgs a, void* 
   return launch_gemm(epi, p, a, stream) == hipSuccess ? CF_OK : CF_EHIP;
 }
 
-cf_status cf_gemm_ln(const cf_bf16* A, const cf_bf16* W, const float* bias, const cf_bf16* R, const float* gamma,
-                     const float* beta, float eps, cf_bf16* Y, int64_t M, int64_t N, int64_t K, void* ws,
-                     size_t ws_bytes, hipStream_t stream) {
+static cf_status check_gemm_ln_args(const cf_bf16* A, const cf_bf16* W, const float* bias, const cf_bf16* R,
+                                    const float* gamma, const float* beta, float eps, cf_bf16* Y, int64_t M,
+                                    int64_t N, int64_t K) {
   if (!A || !W || !bias || !gamma || !beta || !Y || !(eps >= 0.0f)) return CF_EINVAL;
   cf_status s = check_gemm_shape(M, N, K);
   if (s != CF_OK) return s;
@@ -536,10 +536,76 @@ cf_status cf_gemm_ln(const cf_bf16* A, const cf_bf16* W, const float* bias, cons
   if (overlap(Y, ybytes, A, (size_t)M * K * 2) || overlap(Y, ybytes, W, (size_t)K * N * 2) ||
       (R && overlap(Y, ybytes, R, ybytes)))
     return CF_EINVAL;
+  return CF_OK;
+}
+
+cf_status cf_gemm_ln(const cf_bf16* A, const cf_bf16* W, const float* bias, const cf_bf16* R, const float* gamma,
+                     const float* beta, float eps, cf_bf16* Y, int64_t M, int64_t N, int64_t K, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  cf_status s = check_gemm_ln_args(A, W, bias, R, gamma, beta, eps, Y, M, N, K);
+  if (s != CF_OK) return s;
   GemmArgs a{};
   a.A = A; a.B = W; a.bias = bias; a.R = R; a.gamma = gamma; a.beta = beta; a.eps = eps; a.Y = Y;
   a.M = M; a.N = N; a.K = K;
   return run_gemm("cf_gemm_ln", kEpiLN, true, a, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------ allocation-free GEMM + LN
+//
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): cf_gemm_ln's workspace
+// comes from this file-scope device array instead of the caller.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code the
+// array's name is only a host-side stand-in, never a device address: the
+// device address is looked up once per device, with that device current, and
+// only that address is handed to kernels.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchDev {
+  void* ptr = nullptr;
+  bool ok = false;
+};
+ScratchDev g_scratch[kMaxDev];
+std::once_flag g_scratch_once[kMaxDev];
+
+static cf_status scratch_on_current_device(void** out) {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDev) return CF_EHIP;
+  std::call_once(g_scratch_once[d], [d] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p != nullptr) {
+      g_scratch[d].ptr = p;
+      g_scratch[d].ok = true;
+    }
+  });
+  if (!g_scratch[d].ok) return CF_EHIP;
+  *out = g_scratch[d].ptr;
+  return CF_OK;
+}
+
+cf_status cf_gemm_ln_noalloc(const cf_bf16* A, const cf_bf16* W, const float* bias, const cf_bf16* R,
+                             const float* gamma, const float* beta, float eps, cf_bf16* Y, int64_t M, int64_t N,
+                             int64_t K, hipStream_t stream) {
+  cf_status s = check_gemm_ln_args(A, W, bias, R, gamma, beta, eps, Y, M, N, K);
+  if (s != CF_OK) return s;
+  GemmPlan p;
+  s = plan_gemm(kEpiLN, true, M, N, K, &p);
+  if (s != CF_OK) return s;
+  if (gemm_ws_bytes(p, M, N) > kScratchBytes) return CF_EWORKSPACE;  // the shape needs more than the scratch holds
+  void* ws = nullptr;
+  s = scratch_on_current_device(&ws);
+  if (s != CF_OK) return s;
+  // The error word and the join words this plan uses start at zero: cleared by
+  // a fill kernel on the caller's stream (no memset node if the stream is
+  // being captured), so a call after one whose wait gave up starts clean.
+  const int64_t tm = (M + p.bm - 1) / p.bm;
+  if (u_fill(static_cast<float*>(ws), (int64_t)(kHeader + tm * sizeof(uint64_t)) / 4, 0.0f, stream) != hipSuccess)
+    return CF_EHIP;
+  GemmArgs a{};
+  a.A = A; a.B = W; a.bias = bias; a.R = R; a.gamma = gamma; a.beta = beta; a.eps = eps; a.Y = Y;
+  a.M = M; a.N = N; a.K = K;
+  return run_gemm("cf_gemm_ln_noalloc", kEpiLN, true, a, ws, kScratchBytes, stream);
 }
 
 cf_status cf_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scale, cf_bf16* S, int64_t M, int64_t N,

@@ -166,6 +166,20 @@ cf_status cf_gemm_ln(const cf_bf16* A, const cf_bf16* W, const float* bias, cons
                      int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
                      hipStream_t stream);
 
+/* cf_gemm_ln without a workspace argument, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, kernels and results as cf_gemm_ln; the
+ * cross-tile partials and join words live in a 16 MiB static device array of
+ * the library (one per GPU, held until the process ends), and nothing is
+ * allocated or freed.  Shapes whose workspace (cf_workspace_bytes for
+ * CF_OP_GEMM_LN) exceeds 16 MiB return CF_EWORKSPACE before any launch.  Each
+ * call first clears the array's error and join words with a small kernel on
+ * `stream`.  Every call on one GPU shares the array: calls that overlap on one
+ * GPU (other streams, other host threads) race and must not be issued. */
+cf_status cf_gemm_ln_noalloc(const cf_bf16* A, const cf_bf16* W, const float* bias, const cf_bf16* R,
+                             const float* gamma, const float* beta, float eps, cf_bf16* Y,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 /* S = softmax(scale * Q.K^T) over each row of length N.
  * Q [M x D], K [N x D] (both D contiguous), S [M x N]; scale finite.
  * Cross-tile max and sum aggregation.  [ComFuse] B2BGEMM (eq. 3: S_tile =
