@@ -265,7 +265,9 @@ static B2bLayout b2b_layout(const GemmPlan& p, int64_t M) {
 }
 
 // the k_gemm_ln2 configuration without pipelining (8 waves, 256 x 256 tiles)
-static bool ln_one_at_a_time(int epi, const GemmPlan& p) { return epi == kEpiLN && p.algo == 1 && p.cfg == 0; }
+static bool ln_one_at_a_time(int epi, const GemmPlan& p) {
+  return epi == kEpiLN && p.algo == 1 && (p.cfg == 0 || p.cfg == 7);
+}
 
 cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan* pl) {
   DevInfo* di = nullptr;
@@ -287,7 +289,11 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   // Default tiles (measured on MI355X): 128x128 at two workgroups per CU for
   // the plain GEMM and the overlapped epilogues, 64x512 for the round-based
   // epilogues.
-  const int dflt = (epi == kEpiAct && p.algo == 1) ? 0 : ((plain || p.algo == 1) ? 3 : 4);
+  // GEMM + LN: the 256 x 256 one-tile-per-workgroup kernel (7) wherever a
+  // whole row block of its tiles fits the resident grid, else 128 x 128 (3)
+  const int dflt = (epi == kEpiAct && p.algo == 1) ? 0
+                   : (epi == kEpiLN && p.algo == 1) ? ((N + 255) / 256 <= di->cus ? 7 : 3)
+                                                    : ((plain || p.algo == 1) ? 3 : 4);
   p.cfg = (int)env_int(epi == kEpiSoftmax ? "CF_GEMM_SOFTMAX_CFG"
                        : epi == kEpiLN     ? "CF_GEMM_LN_CFG"
                        : epi == kEpiAct    ? "CF_GEMM_ACT_CFG"
@@ -347,9 +353,11 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   return CF_OK;
 }
 
+// Per-row partials of every column tile (4 floats each, rows rounded up to
+// whole row blocks), then 2 floats per row.
 size_t gemm_ws_bytes(const GemmPlan& p, int64_t M, int64_t N) {
-  const int64_t tn = (N + p.bn - 1) / p.bn;
-  return ws_layout(M * tn * 4 + M * 2).total;
+  const int64_t tn = (N + p.bn - 1) / p.bn, mp = (M + p.bm - 1) / p.bm * p.bm;
+  return ws_layout(mp * tn * 4 + M * 2).total;
 }
 
 void record_gemm_plan(const char* name, int epi, const GemmPlan& p, int64_t M, int64_t N, int64_t K) {
@@ -358,13 +366,16 @@ void record_gemm_plan(const char* name, int epi, const GemmPlan& p, int64_t M, i
   const char* kernel = epi == kEpiSoftmaxGemm
                            ? "k_gemm_b2b"
                            : (p.algo == 2 ? "k_gemm_sm3"
-                                          : (ov ? (epi == kEpiLN ? "k_gemm_ln2" : "k_gemm_sm2")
+                                          : (ov ? (epi == kEpiLN ? (p.cfg == 7 ? "k_gemm_ln3" : "k_gemm_ln2") : "k_gemm_sm2")
                                                 : (epi == kEpiAct && p.algo == 1 ? "k_gemm_act2" : "k_gemm")));
   const bool single = ln_one_at_a_time(epi, p);
   const char* sched = epi == kEpiSoftmaxGemm
                           ? "strips, back-to-back"
                           : (p.algo == 2 ? "strips"
-                                         : (ov ? (epi == kEpiLN ? (single ? "one-tile-at-a-time" : "pipelined") : "two-sweep")
+                                         : (ov ? (epi == kEpiLN ? (p.cfg == 7   ? "one-tile-per-launch-round"
+                                                                  : single      ? "one-tile-at-a-time"
+                                                                                : "pipelined")
+                                                                : "two-sweep")
                                                : (plain ? "independent-tiles" : "rounds")));
   char buf[512];
   snprintf(buf, sizeof buf,
@@ -507,12 +518,13 @@ static cf_status run_gemm(const char* name, int epi, bool nn, GemmArgs a, void* 
   const size_t need = gemm_ws_bytes(p, a.M, a.N);
   if (!ws || ws_bytes < need) return CF_EWORKSPACE;
   const int64_t tn = (a.N + p.bn - 1) / p.bn, tm = (a.M + p.bm - 1) / p.bm;
-  const WsLayout L = ws_layout(a.M * tn * 4 + a.M * 2);
+  const int64_t mp = tm * p.bm;  // rows rounded up to whole row blocks
+  const WsLayout L = ws_layout(mp * tn * 4 + a.M * 2);
   char* base = static_cast<char*>(ws);
   a.err = reinterpret_cast<uint32_t*>(base);
   a.joins = reinterpret_cast<uint64_t*>(base + L.joins_off);
   a.partials = reinterpret_cast<float*>(base + L.partials_off);
-  a.finals = a.partials + a.M * tn * 4;
+  a.finals = a.partials + mp * tn * 4;
   a.tiles_n = (int)tn;
   a.tiles_m = (int)tm;
   a.agg_leader = p.leader ? 1 : 0;

@@ -27,6 +27,8 @@
 // rows.  A persistent grid walks tiles in rounds of whole row groups sized to
 // what is resident at once ([AStitch] "What it costs"); each output element
 // has one owner ([sass2mlir] "Epilogue fusion").
+#include <utility>
+
 #include "dev.hpp"
 #include "kernels.hpp"
 
@@ -354,11 +356,16 @@ __device__ __forceinline__ void wait_vm_n(int n) {
 // of the tile at (nm0, nn0) are issued the same way as the tail frees slots,
 // so the next call's entry condition holds and their latency overlaps the
 // caller's epilogue.
-template <int BM, int BN, int BK, bool NN, int RB, int CB, int NWAVES, int NS>
+// `on_stage(st)` runs after stage st's barrier and ring refill, before its
+// MFMAs (an epilogue can issue its first loads behind the last stages).
+struct NoStageHook {
+  __device__ void operator()(int) const {}
+};
+template <int BM, int BN, int BK, bool NN, int RB, int CB, int NWAVES, int NS, class Hook = NoStageHook>
 __device__ __forceinline__ void main_loop_ns(const Ring<BM, BN, BK, NN, NWAVES>& rg, __amdgpu_buffer_rsrc_t rA,
                                              __amdgpu_buffer_rsrc_t rB, char* const (&sl)[NS], int m0, int n0,
                                              bool nxt, int nm0, int nn0, f32x16 (&acc)[RB][CB], int KT, int wm,
-                                             int wn) {
+                                             int wn, Hook on_stage = Hook{}) {
   using RG = Ring<BM, BN, BK, NN, NWAVES>;
   constexpr int LPS = RG::LA + RG::LB;  // loads per lane per stage
   static_assert(NS >= 2 && (NS - 2) * LPS <= 32, "ring depth");
@@ -374,6 +381,7 @@ __device__ __forceinline__ void main_loop_ns(const Ring<BM, BN, BK, NN, NWAVES>&
       const int sn = st + NS - 1;
       if (sn < KT) rg.load(rA, rB, sl[(i + NS - 1) % NS], m0, n0, sn * BK);
       else if (nxt && sn - KT < NS - 1) rg.load(rA, rB, sl[(i + NS - 1) % NS], nm0, nn0, (sn - KT) * BK);
+      on_stage(st);
       mma_stage<BM, BN, BK, NN, RB, CB, LPS>(sl[i], acc, wm, wn);
     }
   }
@@ -2186,6 +2194,281 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
   }
 }
 
+// GEMM + bias + residual + LayerNorm on large tiles: one workgroup of NWAVES
+// waves per CU (the activation kernel's MainLoop and ring) computes ONE tile
+// per launch; a launch covers a round of whole row blocks (every member of a
+// row block resident at once), and the host launches one per round, so no
+// register lives from one tile's epilogue into the next tile's MainLoop.  The
+// tile's bias, gamma and beta slices reach LDS with three direct wave loads
+// issued with the first stage.
+//
+// Epilogue, after the MainLoop:
+//  * u = acc + R + bias, one row block of the lane's accumulators at a time
+//    (two residual blocks in flight), and each block's lane statistics
+//    (count, mean, M2 over the lane's valid columns) as soon as it is in;
+//  * the lane pair and the column waves merged (tile statistics, one barrier);
+//  * exchange with the other tiles of the row block through tagged slots
+//    ([sass2mlir] "Counter-based mini-joins": one store publishes a value and
+//    its tag, readers poll by tag): each member's (mean, M2) per row as two
+//    64-bit {tag 1, value} slots, written once per launch.  Before its first
+//    loads each member clears its own slots; it arrives on the row block's
+//    join word after its MainLoop (the last member advances the generation),
+//    and no member reads a slot before the generation has moved, so every
+//    slot read holds 0 or this launch's value;
+//  * every member merges the row block's partials in member order (the same
+//    bits on every member), y = (u - mean) * rstd * gamma + beta, rounded to
+//    bf16 into the idle ring and written as whole row segments with
+//    non-temporal 16-byte stores.
+template <int BM, int BN, int BK, int WGM, int NWAVES>
+__global__ __launch_bounds__(NWAVES * 64, 1) void k_gemm_ln3(GemmArgs a) {
+  using RG = Ring<BM, BN, BK, true, NWAVES>;
+  constexpr int NS = 2;
+  constexpr int THREADS = NWAVES * 64;
+  constexpr int WGN = NWAVES / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int RB = WM / 32, CB = WN / 32;
+  constexpr int NP = THREADS / BM;  // threads per row in the partial merge
+  constexpr int C16 = BN * 2 / 16;  // 16-byte chunks per bf16 output row
+  constexpr int RC0 = RG::STAGE_BYTES / (BN * 2);
+  constexpr int RC = RC0 >= BM ? BM : (RC0 >= 128 ? 128 : (RC0 >= 64 ? 64 : 32));
+  constexpr int MAXT = 16;          // tiles per row block whose slots the NP threads of a row take per batch
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && WGM * WGN == NWAVES && RB >= 2, "wave tile");
+  static_assert(BM <= THREADS && THREADS % BM == 0 && NWAVES >= 3 && BN * 4 == 1024, "epilogue mapping");
+  static_assert(RC0 >= 32 && BM % RC == 0 && (RC * C16) % THREADS == 0 && C16 >= 16, "output staging");
+  static_assert((WGN * BM + THREADS) * 16 <= RG::STAGE_BYTES, "epilogue scratch in slot 0");
+  __shared__ __align__(16) char s0[RG::STAGE_BYTES];
+  __shared__ __align__(16) char s1[RG::STAGE_BYTES];
+  __shared__ __align__(16) float vec[3][BN];  // bias | gamma | beta of the tile's columns (zero past N)
+  __shared__ __align__(16) float2 stat[BM];   // (mean, rstd) per row
+  float4* const red = reinterpret_cast<float4*>(s0);  // after the MainLoop: WGN x BM tile partials
+  float4* const parts = red + WGN * BM;               // then NP x BM merged runs
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  const int hl = lane >> 5, l32 = lane & 31;
+  const int lrow = wm * WM + l32, lcol = wn * WN + 16 * hl;
+  const int M = (int)a.M, N = (int)a.N;
+  const int KT = (int)((a.K + BK - 1) / BK);
+  const int T = a.tiles_n;
+  const int tile = a.tile0 + (int)xcd_local_id(blockIdx.x, gridDim.x);
+  if (tile >= a.tiles_m * T) return;
+  const int rowblk = tile / T, tn = tile - rowblk * T;
+  const int m0 = rowblk * BM, n0 = tn * BN;
+  // tagged slots, member-major: {tag, mean} and {tag, M2} of row m0 + i of
+  // member k at ((rowblk * T + k) * BM + i) * 2, so a wave's puts and takes
+  // touch contiguous runs
+  uint64_t* const slots = reinterpret_cast<uint64_t*>(a.partials) + (size_t)rowblk * T * BM * 2;
+  f32x16 acc[RB][CB];
+  // residual: one row block of the lane's accumulators per fetch, RD in
+  // flight; rows past M lie past the buffer's range and read zero, a chunk
+  // past N reads the next row's values, which feed only columns past N,
+  // never counted or stored
+  constexpr int RD = RB >= 3 ? 3 : RB;
+  const __amdgpu_buffer_rsrc_t rR = rsrc(a.R, a.R ? (uint32_t)(a.M * a.N * 2) : 0u);  // no residual: reads zero
+  const uint32_t rbase = (uint32_t)((m0 + lrow) * N + n0 + lcol) * 2u;
+  u32x4 rr[RD][CB][2];
+  auto fetch = [&](auto rbc) {
+    constexpr int rb = decltype(rbc)::value;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        rr[rb % RD][cb][h] = bld16(rR, rbase + (uint32_t)(32 * rb * N + 32 * cb + 8 * h) * 2u);
+  };
+  {
+    const __amdgpu_buffer_rsrc_t rA = rsrc(a.A, (uint32_t)(a.M * a.K * 2));
+    const __amdgpu_buffer_rsrc_t rB = rsrc(a.B, (uint32_t)(a.N * a.K * 2));
+    const RG rg(a);
+    char* const all_slots[2] = {s0, s1};
+    zero_acc(acc);
+    prologue_ns<BM, BN, BK, true, NWAVES, NS>(rg, rA, rB, all_slots, m0, n0, KT);
+    if (w < 3) {
+      const __amdgpu_buffer_rsrc_t rv = rsrc(w == 0 ? a.bias : w == 1 ? a.gamma : a.beta, (uint32_t)(a.N * 4));
+      const int c = n0 + lane * 4;  // N % 8 == 0: a 16-byte chunk is wholly inside or past N
+      g2l16(rv, &vec[w][0], c < N ? (uint32_t)c * 4u : kOOB);  // lane i fills bytes [16i, 16i + 16)
+    }
+    // clear this member's slots (the MainLoop's first wait completes the
+    // stores, its barrier covers every thread's)
+    if (t < BM && m0 + t < M) {
+      slot_clear(slots + ((size_t)tn * BM + t) * 2);
+      slot_clear(slots + ((size_t)tn * BM + t) * 2 + 1);
+    }
+    // the first residual block goes out behind the last stage's MFMAs
+    main_loop_ns<BM, BN, BK, true, RB, CB, NWAVES, NS>(rg, rA, rB, all_slots, m0, n0, false, 0, 0, acc, KT, wm, wn,
+                                                        [&](int st) {
+                                                          if (st == KT - 1) fetch(IntC<0>{});
+                                                        });
+  }
+  // arrive on the row block's launch join (every member's slots are clear by now)
+  uint64_t* const jw = a.joins + rowblk;
+  uint64_t jold = 0;
+  if (t == 0) jold = join_arrive(jw, (uint32_t)T);
+
+  // ---- u = acc + R + bias and the lane statistics, one row block of the
+  // lane's accumulators at a time as its residual block lands
+  const bool full = n0 + BN <= N;  // uniform: every column of the tile is valid
+  int nvalid = 0;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) nvalid += (n0 + lcol + cb * 32 + 8 * h < N) ? 8 : 0;
+  float n_[RB], mu[RB], m2[RB];
+  {
+    auto block = [&](auto rbc) {
+      constexpr int rb = decltype(rbc)::value;
+      float sum = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int cl = lcol + cb * 32 + 8 * h;
+          const float4 b0 = *reinterpret_cast<const float4*>(&vec[0][cl]);
+          const float4 b1 = *reinterpret_cast<const float4*>(&vec[0][cl + 4]);
+          const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+          const bool ok = full || n0 + cl < N;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t wv = rr[rb % RD][cb][h][e >> 1];
+            const float u = acc[rb][cb][8 * h + e] + ((e & 1) ? bf16_hi(wv) : bf16_lo(wv)) + bv[e];
+            acc[rb][cb][8 * h + e] = u;
+            sum += ok ? u : 0.0f;
+          }
+        }
+      const float mean = nvalid > 0 ? sum / (float)nvalid : 0.0f;
+      float q2 = 0.0f;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const float d = (full || n0 + lcol + cb * 32 + (q & 8) < N) ? acc[rb][cb][q] - mean : 0.0f;
+          q2 = fmaf(d, d, q2);
+        }
+      n_[rb] = (float)nvalid;
+      mu[rb] = mean;
+      m2[rb] = q2;
+    };
+    [&]<int... Q>(std::integer_sequence<int, Q...>) { (fetch(IntC<Q + 1>{}), ...); }(
+        std::make_integer_sequence<int, RD - 1>{});
+    __syncthreads();  // every wave is done with the ring (slot 0 becomes the epilogue scratch); vec is in
+    [&]<int... Q>(std::integer_sequence<int, Q...>) {
+      (
+          [&] {
+            // block Q is in; the blocks after it (at most RD - 1) may still fly
+            constexpr int after = (RB - 1 - Q) < (RD - 1) ? (RB - 1 - Q) : (RD - 1);
+            wait_vm<after * CB * 2>();
+            block(IntC<Q>{});
+            if constexpr (Q + RD < RB) fetch(IntC<Q + RD>{});
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, RB>{});
+  }
+  tile_merge_ln<BM, WGN, RB>(n_, mu, m2, red, wm, wn);
+  if (wn == 0 && hl == 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = m0 + lrow + rb * 32;
+      if (row < M) {
+        slot_put(slots + ((size_t)tn * BM + row - m0) * 2, 1u, mu[rb]);
+        slot_put(slots + ((size_t)tn * BM + row - m0) * 2 + 1, 1u, m2[rb]);
+      }
+    }
+  }
+  if (t == 0) join_await(jw, jold, (uint32_t)T, a.err);  // every member's slots were cleared
+  __syncthreads();
+
+  // ---- the row block's statistics: NP threads per row take contiguous runs
+  // of members' slots (all in flight at once, re-polled until tagged), merge
+  // them in member order, then one thread per row merges the runs
+  {
+    const int rw = t % BM, q = t / BM;
+    const int per = (T + NP - 1) / NP;
+    const int kb = q * per, ke = min(T, kb + per);
+    float cn = 0.0f, cm = 0.0f, c2 = 0.0f;
+    if (m0 + rw < M) {
+      for (int k0 = kb; k0 < ke; k0 += MAXT / NP) {
+        const int kn = min(ke - k0, MAXT / NP);
+        float mv[MAXT / NP], qv[MAXT / NP];
+        uint64_t pending = kn >= 64 ? ~0ull : ((1ull << kn) - 1);
+        for (uint32_t it = 0; pending != 0 && it < kSpinCap; ++it) {
+#pragma unroll
+          for (int k = 0; k < MAXT / NP; ++k) {
+            if (pending >> k & 1) {
+              uint64_t* const sp = slots + ((size_t)(k0 + k) * BM + rw) * 2;
+              const uint64_t x0 = __hip_atomic_load(sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              const uint64_t x1 = __hip_atomic_load(sp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              if ((uint32_t)(x0 >> 32) == 1u && (uint32_t)(x1 >> 32) == 1u) {
+                mv[k] = __uint_as_float((uint32_t)x0);
+                qv[k] = __uint_as_float((uint32_t)x1);
+                pending &= ~(1ull << k);
+              }
+            }
+          }
+          if (pending != 0) __builtin_amdgcn_s_sleep(2);
+        }
+        if (pending != 0) __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int k = 0; k < MAXT / NP; ++k)
+          if (k < kn && !(pending >> k & 1)) merge_ln(cn, cm, c2, (float)min(BN, N - (k0 + k) * BN), mv[k], qv[k]);
+      }
+    }
+    parts[q * BM + rw] = make_float4(cn, cm, c2, 0.0f);
+    __syncthreads();
+    if (t < BM) {
+      float4 x = parts[t];
+      for (int k = 1; k < NP; ++k) merge_ln(x.x, x.y, x.z, parts[k * BM + t].x, parts[k * BM + t].y, parts[k * BM + t].z);
+      stat[t] = make_float2(x.y, rsqrtf(x.z / (float)N + a.eps));
+    }
+    __syncthreads();
+  }
+
+  // ---- y = (u - mean) * rstd * gamma + beta, bf16, staged through slot 1 in
+  // chunks of RC whole rows, written as non-temporal 16-byte row segments
+  float2 st[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) st[rb] = stat[lrow + rb * 32];
+  uint16_t* const stg = reinterpret_cast<uint16_t*>(s1);
+#pragma unroll 1
+  for (int qc = 0; qc < BM / RC; ++qc) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int cl = lcol + cb * 32 + 8 * h;
+        const float4 g0 = *reinterpret_cast<const float4*>(&vec[1][cl]);
+        const float4 g1 = *reinterpret_cast<const float4*>(&vec[1][cl + 4]);
+        const float4 b0 = *reinterpret_cast<const float4*>(&vec[2][cl]);
+        const float4 b1 = *reinterpret_cast<const float4*>(&vec[2][cl + 4]);
+        const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int rl = wm * WM + rb * 32;  // the wave's 32 rows of this block (uniform)
+          if (rl / RC != qc) continue;
+          const int rr = rl - qc * RC + l32;
+          float o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = fmaf((acc[rb][cb][8 * h + e] - st[rb].x) * st[rb].y, gg[e], bb[e]);
+          const u32x4 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                            pack_bf16x2(o[6], o[7])};
+          *reinterpret_cast<u32x4*>(stg + rr * BN + 8 * eswz(rr, cl / 8)) = pk;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < RC * C16 / THREADS; ++j) {
+      const int id = j * THREADS + t;
+      const int rr = id / C16, c = id % C16;
+      const int row = m0 + qc * RC + rr, col = n0 + 8 * c;
+      if (row < M && col < N)
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + rr * BN + 8 * eswz(rr, c)),
+                                    reinterpret_cast<u32x4*>(a.Y + (int64_t)row * N + col));
+    }
+    __syncthreads();
+  }
+}
+
 // GEMM + unary activation on large tiles, one workgroup of NWAVES waves per
 // CU walking tiles XCD-locally.  The tiles are independent (each output
 // element has one owner), so there is no join; while a tile's epilogue runs,
@@ -2339,6 +2622,7 @@ static const TileCfg kLnCfgs[] = {
     {128, 128, 64},  // 4: 2x2 waves of 64x64, 4-slot ring 128 KB, 1 WG/CU, pipelined
     {128, 128, 32},  // 5: 2x2 waves of 64x64, 4-slot ring 64 KB, 2 WG/CU, pipelined
     {128, 128, 32},  // 6: 2x2 waves of 64x64, 2-slot ring 32 KB, 2 WG/CU, pipelined
+    {256, 256, 64},  // 7: 8 waves of 128x64, 2-slot ring 128 KB, 1 WG/CU, one tile at a time, residual streamed in
 };
 
 static const TileCfg kActCfgs[] = {
@@ -2404,6 +2688,19 @@ static hipError_t launch_gemm_overlap(const GemmPlan& pl, const GemmArgs& a, hip
       case 4: return go(k_gemm_ln2<128, 128, 64, 2, 1, 4, true, 4>, 256);
       case 5: return go(k_gemm_ln2<128, 128, 32, 2, 2, 4, true, 4>, 256);
       case 6: return go(k_gemm_ln2<128, 128, 32, 2, 2, 4, true, 2>, 256);
+      case 7: {  // 8 waves of 128x64, one tile per workgroup: one launch per round
+        auto kfn = k_gemm_ln3<256, 256, 64, 2, 8>;
+        if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kfn, 512, 0);
+        const int tiles = a.tiles_m * a.tiles_n;
+        for (int t0 = 0; t0 < tiles; t0 += pl.grid) {
+          GemmArgs ar = a;
+          ar.tile0 = t0;
+          hipLaunchKernelGGL(kfn, dim3(std::min(pl.grid, tiles - t0)), dim3(512), 0, st, ar);
+          const hipError_t e = hipGetLastError();
+          if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+      }
     }
   } else {
     switch (pl.cfg) {

@@ -85,6 +85,7 @@ struct GemmArgs {
   int64_t Dv;
   float* opart;        // softmax-GEMM: per-strip partial outputs, M * strips * 128 floats
   int act;             // activation epilogue: ActId (bias nullable)
+  int tile0;           // one-tile-per-workgroup kernels launched per round: the round's first tile
 };
 
 struct GemmPlan {

@@ -202,6 +202,15 @@ def test_gemm_ln(M, N, K):
     assert err <= TOL_BF16, (err, cf.last_plan())
 
 
+def test_gemm_ln_default_plan_on_the_workload():
+    """The 4096 x 4096 x 1024 workload runs on the 256 x 256 kernel, one tile per workgroup
+    and a single launch (16 tiles per row block, all 256 tiles resident)."""
+    d = gen.gemm_ln_inputs(seed=4, M=512, N=4096, K=64)
+    _gemm_ln_run(d, 512, 4096, 64)
+    p = json.loads(cf.last_plan())
+    assert (p["kernel"], p["tile"][:2], p["row_group"]) == ("k_gemm_ln3", [256, 256], 16), p
+
+
 def test_gemm_ln_no_residual():
     M, N, K = 300, 264, 72
     d = gen.gemm_ln_inputs(seed=44, M=M, N=N, K=K, residual=False)
@@ -549,7 +558,7 @@ def test_gemm_softmax_every_schedule(monkeypatch, algo, M, N, D):
     assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
 
 
-@pytest.mark.parametrize("cfg", range(7))
+@pytest.mark.parametrize("cfg", range(8))
 @pytest.mark.parametrize("M,N,K", [(512, 1024, 256), (300, 264, 72)])
 def test_gemm_ln_every_tile_config(monkeypatch, cfg, M, N, K):
     """Every tile configuration of the overlapped GEMM+LN kernel (forced through
@@ -562,11 +571,12 @@ def test_gemm_ln_every_tile_config(monkeypatch, cfg, M, N, K):
     assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
 
 
-def test_gemm_ln_one_tile_at_a_time_rounds(monkeypatch):
+@pytest.mark.parametrize("cfg", [0, 7])
+def test_gemm_ln_one_tile_at_a_time_rounds(monkeypatch, cfg):
     """More 256 x 256 tiles than resident workgroups: whole row blocks per
-    round, the epilogue scratch in the ring reused by the next tile's
-    MainLoop; ragged last row block and column tile."""
-    monkeypatch.setenv("CF_GEMM_LN_CFG", "0")
+    round (one kernel round after another, or one launch per round), the
+    epilogue scratch in the ring; ragged last row block and column tile."""
+    monkeypatch.setenv("CF_GEMM_LN_CFG", str(cfg))
     M, N, K = 256 * 40 - 37, 2048 - 120, 64
     d = gen.gemm_ln_inputs(seed=10, M=M, N=N, K=K)
     g = _gemm_ln_run(d, M, N, K)
