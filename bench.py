@@ -268,6 +268,17 @@ EXTRA_NAMES = ["gemm_softmax_gemm_8192x8192x128x128", "rmsnorm_750000x32", "laye
                "auto_softmax_512x65536"]
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def shape_keys(w):
     """The timed workload's sizes for the JSON line's config: rows x cols, or the GEMM's M, N, K."""
     a, b, c = w.dims
@@ -430,10 +441,36 @@ def main():
                 cs.synchronize()
                 cf.cf_graph_destroy(h)
             t_graph = float(np.mean([a.elapsed_time(b) for a, b in evg])) * 1e3
+            # Host wall clock from issuing the chain to its completion (a
+            # synchronize on each side, the cache sweep outside): stream launches
+            # pay every kernel's host enqueue cost, one graph launch pays one,
+            # so their difference is the launch saving the graph buys.
+            def host_us(issue):
+                ts = []
+                for k in range(ks + 1):
+                    do_flush()
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    issue()
+                    torch.cuda.synchronize()
+                    if k >= 1:
+                        ts.append((time.perf_counter() - t0) * 1e6)
+                return float(np.median(ts))
+            with torch.cuda.stream(cs):
+                cf.cf_graph_begin()
+                w.unfused(w.uws)
+                h2 = cf.cf_graph_end()
+                cf.cf_graph_launch(h2)
+                cs.synchronize()
+                t_graph_host = host_us(lambda: cf.cf_graph_launch(h2))
+                t_stream_host = host_us(lambda: w.unfused(w.uws))
+                cf.cf_graph_destroy(h2)
             per[w.name]["unfused_stream_us"] = round(t_stream, 3)
             per[w.name]["unfused_graph_us"] = round(t_graph, 3)
+            per[w.name]["unfused_stream_host_us"] = round(t_stream_host, 3)
+            per[w.name]["unfused_graph_host_us"] = round(t_graph_host, 3)
             per[w.name]["speedup_vs_unfused_graph"] = round(t_graph / per[w.name]["us_mean"], 2)
-            per[w.name]["launch_savings_us"] = round(t_stream - t_graph, 3)
+            per[w.name]["launch_savings_us"] = round(t_stream_host - t_graph_host, 3)
             per[w.name]["roundtrip_savings_us"] = round(t_graph - per[w.name]["us_mean"], 3)
             del w.uws
             torch.cuda.empty_cache()
@@ -476,22 +513,42 @@ def main():
                      "launch_host_us": round(t_spec, 2), "direct_launch_host_us": round(t_direct, 2),
                      "bitwise_equal_to_direct": same}
 
-    # ---- CPU baseline: the oracle, on rank 0, on a bounded sample
+    # ---- CPU baseline: the oracle, on rank 0, on a bounded sample.  Rows are
+    # independent, so the oracle (unchanged) runs on row chunks of the input
+    # in a thread pool with one thread per core the process may use (numpy
+    # releases the interpreter lock inside each whole-array operator); the
+    # single-core rate (one thread, the whole input) is reported beside it.
     cpu = None
     if not args.no_cpu:
         import oracle
-        reps, t_cpu = 0, 0.0
-        t_start = time.perf_counter()
-        while True:
-            head.oracle_once(oracle)
-            reps += 1
-            t_cpu = time.perf_counter() - t_start
-            if t_cpu >= 12.0:
-                break
-        cpu = {"value": round(head.bytes * reps / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"{reps} full passes of the fp64 op-by-op oracle over the {head.name} input "
-                         f"({t_cpu:.1f} s; numpy elementwise ops, single-threaded)"}
+        from concurrent.futures import ThreadPoolExecutor
+        cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+        inp = head.inp
+        rows = inp["x"].shape[0]
+        bounds = np.linspace(0, rows, cores + 1).astype(int)
+
+        def chunk(i):
+            lo, hi = bounds[i], bounds[i + 1]
+            return oracle.layernorm_rows(inp["x"][lo:hi], 1e-5) if head.name == "layernorm_750000x32" \
+                else head.oracle_once(oracle)
+
+        def timed(fn, budget):
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                fn()
+                reps += 1
+                t = time.perf_counter() - t0
+                if t >= budget:
+                    return reps, t
+
+        reps1, t1 = timed(lambda: head.oracle_once(oracle), 4.0)
+        with ThreadPoolExecutor(max_workers=cores) as ex:
+            repsn, tn = timed(lambda: list(ex.map(chunk, range(cores))), 8.0)
+        cpu = {"value": round(head.bytes * repsn / tn / 1e9, 3), "unit": "GB/s", "cores": cores,
+               "kind": "oracle", "single_core_value": round(head.bytes * reps1 / t1 / 1e9, 3),
+               "cpu_model": _cpu_model(),
+               "sample": f"{repsn} full passes of the fp64 op-by-op oracle over the {head.name} input, rows "
+                         f"split over {cores} threads ({tn:.1f} s); single core: {reps1} passes ({t1:.1f} s)"}
 
     # ---- roofline of the headline kernel
     h = per[head.name]
@@ -537,6 +594,7 @@ def main():
         "per_config": per,
         "spec_ir": spec_info,
         "source_hash": cur_hash,
+        "planner_env": {k: v for k, v in sorted(os.environ.items()) if k.startswith("CF_")},
     }
     print(json.dumps(line))
 

@@ -56,6 +56,7 @@ _SIGS = {
     "cf_stitch_rmsnorm": (_ST, [_P, _P, _P, _I64, _I64, _F, _P, _SZ, _P]),
     "cf_gemm_ln": (_ST, [_P, _P, _P, _P, _P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_gemm_ln_noalloc": (_ST, [_P, _P, _P, _P, _P, _P, _F, _P, _I64, _I64, _I64, _P]),
+    "cf_workspace_error": (_ST, [_P, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32), _P]),
     "cf_gemm_softmax": (_ST, [_P, _P, _F, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_gemm_softmax_gemm": (_ST, [_P, _P, _P, _F, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
     "cf_gemm_act": (_ST, [_P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _P, _SZ, _P]),
@@ -187,6 +188,15 @@ class Workspace:
 
     def clear_error(self) -> None:
         self.buf[:4].zero_()
+
+
+def cf_workspace_error(ws, clear=False, stream=None) -> int:
+    """The workspace's error word through the C-ABI (waits for the stream); non-zero: a
+    cross-workgroup wait of a call that used it gave up and that call's output is wrong."""
+    out = ctypes.c_uint32(0)
+    _check("cf_workspace_error", lib().cf_workspace_error(ws.ptr(), 1 if clear else 0, ctypes.byref(out),
+                                                          _stream(stream)))
+    return int(out.value)
 
 
 _ws_cache: dict = {}
@@ -523,9 +533,11 @@ class Auto:
     def workspace_bytes(self) -> int:
         return int(lib().cf_auto_workspace_bytes(self._h))
 
-    def launch(self, args, out, ws=None, stream=None):
+    def launch(self, args, out, ws=None, stream=None, check=False):
         """args: fp32 tensors by slot (None where unused); out: fp32 [rows, cols].  A workspace is
-        allocated and cached when the kernel needs one and none is given; returns it."""
+        allocated and cached when the kernel needs one and none is given; returns it.  With
+        check=True the call waits for the stream and raises CFError(CF_EOCCUPANCY) if a
+        cross-workgroup wait gave up (its members were not all resident), clearing the word."""
         st = _stream(stream)
         nb = self.workspace_bytes()
         if nb == ctypes.c_size_t(-1).value:
@@ -536,4 +548,6 @@ class Auto:
         _check("cf_auto_launch", lib().cf_auto_launch(self._h, ptrs, len(args), _ptr(out),
                                                       None if ws is None else ws.ptr(),
                                                       0 if ws is None else ws.nbytes, st))
+        if check and ws is not None and cf_workspace_error(ws, clear=True, stream=st.value) != 0:
+            raise CFError("cf_auto_launch", CF_EOCCUPANCY)
         return ws

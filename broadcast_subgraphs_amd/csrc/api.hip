@@ -434,6 +434,20 @@ int cf_last_plan(char* buf, size_t n) {
   return (int)g_last_plan.size();
 }
 
+cf_status cf_workspace_error(const void* ws, int clear, uint32_t* out, hipStream_t stream) {
+  if (!ws || !out) return CF_EINVAL;
+  uint32_t w = 0;
+  if (hipMemcpyAsync(&w, ws, sizeof w, hipMemcpyDeviceToHost, stream) != hipSuccess) return CF_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return CF_EHIP;
+  if (clear) {
+    // a fill kernel, not a memset node: the word is one float's bytes
+    if (u_fill(static_cast<float*>(const_cast<void*>(ws)), 1, 0.0f, stream) != hipSuccess) return CF_EHIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return CF_EHIP;
+  }
+  *out = w;
+  return CF_OK;
+}
+
 size_t cf_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2) {
   if (d0 <= 0 || d1 <= 0) return (size_t)-1;
   switch (op) {

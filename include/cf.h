@@ -28,7 +28,17 @@
  *     clearing again.  Two calls that may run at the same time must not share
  *     a workspace.  Byte 0..3 of a workspace hold an error word: non-zero
  *     means a cross-workgroup wait gave up (see CF_EOCCUPANCY); the caller may
- *     read and clear it.
+ *     read and clear it (cf_workspace_error).
+ *   - Residency.  Plans whose workgroups wait on each other (rows split over
+ *     workgroups, the GEMM epilogues across tiles, the Global scheme of
+ *     generated kernels) size their grid to what the device keeps resident
+ *     when the call has it to itself, and assume that no other kernel holds
+ *     compute units while they run (a kernel on another stream, or another
+ *     process's).  If that does not hold, a member that waits for one that
+ *     was never scheduled gives up after its spin cap (about a second), sets
+ *     the error word, and the call's output is wrong: the call itself still
+ *     returns CF_OK, since it only enqueues.  Callers that cannot rule out
+ *     concurrent kernels check the word after the stream completes.
  *   - Errors are reported by the return value only.  Argument validation
  *     happens before any HIP call, so an invalid call enqueues nothing.
  *   - Results are bitwise reproducible run to run for a given shape and device:
@@ -58,6 +68,15 @@ typedef enum cf_status {
   CF_EOCCUPANCY = 5,    /* the workgroups that must wait on each other cannot all be resident */
   CF_EHIP = 6           /* a HIP runtime call failed (the launch, or a device query) */
 } cf_status;
+
+/* Read a workspace's error word (bytes 0..3) into *out: 0, or non-zero when a
+ * cross-workgroup wait of a call that used `ws` gave up (that call's output is
+ * wrong; see "Residency" above).  Enqueues the 4-byte read on `stream` and
+ * waits for the stream, so every earlier call on it has completed; with
+ * `clear` non-zero the word is then zeroed (by a kernel on `stream`, which the
+ * function also waits for).  This call synchronizes: it is not for use under
+ * graph capture.  CF_EINVAL for a NULL ws or out, CF_EHIP if a HIP call fails. */
+cf_status cf_workspace_error(const void* ws, int clear, uint32_t* out, hipStream_t stream);
 
 /* Operation ids for cf_workspace_bytes / cf_unfused_workspace_bytes. */
 enum {

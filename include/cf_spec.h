@@ -168,8 +168,12 @@ size_t cf_auto_workspace_bytes(cf_auto* a);
  * variant, anything else the 4-byte one.  ws/ws_bytes: the workspace (same
  * contract as cf.h's: zero-filled once, error word at byte 0), needed only
  * when cf_auto_workspace_bytes is non-zero; CF_EOCCUPANCY when not even one
- * row's workgroups can be resident.  Free the kernel (cf_auto_free) only
- * after the work it enqueued has completed. */
+ * row's workgroups can be resident.  The Global scheme's members wait on
+ * each other: they assume no other kernel holds compute units meanwhile (see
+ * "Residency" in cf.h); a wait that gives up sets the error word and leaves
+ * the output wrong, which cf_workspace_error reports after the stream
+ * completes.  Free the kernel (cf_auto_free) only after the work it enqueued
+ * has completed. */
 cf_status cf_auto_launch(cf_auto* a, const void* const* args, int nargs, float* out, void* ws, size_t ws_bytes,
                          hipStream_t stream);
 

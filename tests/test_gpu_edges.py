@@ -182,3 +182,49 @@ def test_gemm_ln_large_bias_offset(M, N, K):
     g = _gemm_ln_run(d, M, N, K)
     o = oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"], d["beta"], d["eps"])
     assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
+
+
+def _poison_first_join(ws):
+    """Set the first join word's arrival count to 0xFFFF, a state no launch leaves behind: no
+    arrival of that group sees itself as the last, so its members wait for a generation that never
+    comes, give up at the spin cap (the kernel still finishes) and set the error word."""
+    torch.cuda.synchronize()
+    ws.buf[256:264].view(torch.int64).fill_(0xFFFF)
+    torch.cuda.synchronize()
+
+
+def test_workspace_error_reports_a_wait_that_gave_up():
+    rows, cols = 2, 65536
+    x = gen.normal(211, 0, (rows, cols))
+    ws = cf.Workspace(cf.cf_workspace_bytes(cf.CF_OP_STITCH_SOFTMAX, rows, cols, 0))
+    y = empty_f32(rows, cols)
+    cf.cf_stitch_softmax(d32(x), y, ws=ws)
+    assert cf.cf_workspace_error(ws) == 0
+    assert _plan()["kernel"] == "k_rows_split"
+    _poison_first_join(ws)
+    cf.cf_stitch_softmax(d32(x), y, ws=ws)
+    assert cf.cf_workspace_error(ws, clear=True) != 0
+    assert cf.cf_workspace_error(ws) == 0  # cleared
+    ws.buf[256:264].view(torch.int64).fill_(0)
+    y2 = empty_f32(rows, cols)
+    cf.cf_stitch_softmax(d32(x), y2, ws=ws)
+    assert cf.cf_workspace_error(ws) == 0
+    assert rownorm_err(host(y2), oracle.softmax_rows(x)) <= TOL_F32
+
+
+def test_auto_checked_launch_raises_when_a_wait_gave_up():
+    from tests import graphs
+    rows, cols = 3, 40000
+    x = gen.normal(212, 0, (rows, cols))
+    nodes, t = graphs.softmax()
+    a = cf.Auto(nodes, t, rows, cols)
+    ws = cf.Workspace(a.workspace_bytes())
+    out = empty_f32(rows, cols)
+    a.launch([d32(x)], out, ws=ws, check=True)
+    _poison_first_join(ws)
+    with pytest.raises(cf.CFError) as e:
+        a.launch([d32(x)], out, ws=ws, check=True)
+    assert e.value.status == cf.CF_EOCCUPANCY
+    ws.buf[256:264].view(torch.int64).fill_(0)
+    a.launch([d32(x)], out, ws=ws, check=True)
+    assert rownorm_err(host(out), oracle.graph.evaluate(nodes, t, [x])) <= TOL_F32
