@@ -2251,8 +2251,13 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void k_gemm_ln3(GemmArgs a) {
   const int M = (int)a.M, N = (int)a.N;
   const int KT = (int)((a.K + BK - 1) / BK);
   const int T = a.tiles_n;
-  const int tile = a.tile0 + (int)xcd_local_id(blockIdx.x, gridDim.x);
-  if (tile >= a.tiles_m * T) return;
+  // the launch's tiles [tile0, tile0 + G): with a swizzle (sw_a row x sw_b
+  // column splits) each XCD takes a compact block of row blocks x column
+  // tiles, so its L2 holds that block's A rows and W columns
+  const int G = (int)gridDim.x;
+  const int tile = a.tile0 + round_tile((int)xcd_local_id(blockIdx.x, (uint32_t)G), 0, G, T, a.tiles_m * T - a.tile0,
+                                        a.sw_a, a.sw_b);
+  if (tile < a.tile0 || tile >= a.tiles_m * T) return;
   const int rowblk = tile / T, tn = tile - rowblk * T;
   const int m0 = rowblk * BM, n0 = tn * BN;
   // tagged slots, member-major: {tag, mean} and {tag, M2} of row m0 + i of
@@ -2695,7 +2700,9 @@ static hipError_t launch_gemm_overlap(const GemmPlan& pl, const GemmArgs& a, hip
         for (int t0 = 0; t0 < tiles; t0 += pl.grid) {
           GemmArgs ar = a;
           ar.tile0 = t0;
-          hipLaunchKernelGGL(kfn, dim3(std::min(pl.grid, tiles - t0)), dim3(512), 0, st, ar);
+          const int g = std::min(pl.grid, tiles - t0);
+          if (g != pl.grid) ar.sw_a = ar.sw_b = 0;  // the XCD split is sized for a full round
+          hipLaunchKernelGGL(kfn, dim3(g), dim3(512), 0, st, ar);
           const hipError_t e = hipGetLastError();
           if (e != hipSuccess) return e;
         }
