@@ -2204,7 +2204,8 @@ __global__ __launch_bounds__(NWAVES * 64, MINB) void k_gemm_ln2(GemmArgs a) {
 //
 // Epilogue, after the MainLoop:
 //  * u = acc + R + bias, one row block of the lane's accumulators at a time
-//    (two residual blocks in flight), and each block's lane statistics
+//    (up to three residual blocks in flight, the first issued behind the
+//    last stage's MFMAs), and each block's lane statistics
 //    (count, mean, M2 over the lane's valid columns) as soon as it is in;
 //  * the lane pair and the column waves merged (tile statistics, one barrier);
 //  * exchange with the other tiles of the row block through tagged slots
