@@ -284,7 +284,7 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   p.algo = epi == kEpiAct ? (int)env_int("CF_GEMM_ACT_ALGO", 1)
                           : (plain ? 0 : (int)env_int("CF_GEMM_ALGO", dalgo));
   if (epi == kEpiAct && (p.algo < 0 || p.algo > 1)) return CF_EUNSUPPORTED;
-  if (p.algo == 2 && (epi != kEpiSoftmax || K > 128)) return CF_EUNSUPPORTED;
+  if (p.algo >= 2 && (epi != kEpiSoftmax || K > 128 || p.algo > 2)) return CF_EUNSUPPORTED;
   if (p.algo == 2) return plan_gemm_strips(kEpiSoftmax, M, N, K, di, &p, pl);
   // Default tiles (measured on MI355X): 128x128 at two workgroups per CU for
   // the plain GEMM and the overlapped epilogues, 64x512 for the round-based

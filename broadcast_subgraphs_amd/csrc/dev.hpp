@@ -244,6 +244,29 @@ __device__ __forceinline__ float slot_take(uint64_t* s, uint32_t tag, uint32_t* 
   return 0.0f;
 }
 
+// Two slots taken together: both loads of each poll are in flight at once.
+__device__ __forceinline__ void slot_take2(uint64_t* s0, uint64_t* s1, uint32_t tag, uint32_t* err, float* v0,
+                                           float* v1) {
+  bool h0 = false, h1 = false;
+  for (uint32_t it = 0; it < kSpinCap; ++it) {
+    const uint64_t w0 = __hip_atomic_load(s0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t w1 = __hip_atomic_load(s1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!h0 && (uint32_t)(w0 >> 32) == tag) {
+      *v0 = __uint_as_float((uint32_t)w0);
+      h0 = true;
+    }
+    if (!h1 && (uint32_t)(w1 >> 32) == tag) {
+      *v1 = __uint_as_float((uint32_t)w1);
+      h1 = true;
+    }
+    if (h0 && h1) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!h0) *v0 = 0.0f;
+  if (!h1) *v1 = 0.0f;
+}
+
 // Logical workgroup index that keeps consecutive logical ids on one XCD.
 // MI355X hands workgroups to its 8 XCDs round-robin (physical id % 8), so
 // logical = (phys % 8) * (G / 8) + phys / 8 places logical ids [x*G/8, (x+1)*G/8)

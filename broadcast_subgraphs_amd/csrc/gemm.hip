@@ -2397,19 +2397,23 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void k_gemm_ln3(GemmArgs a) {
         float mv[MAXT / NP], qv[MAXT / NP];
         uint64_t pending = kn >= 64 ? ~0ull : ((1ull << kn) - 1);
         for (uint32_t it = 0; pending != 0 && it < kSpinCap; ++it) {
+          // every poll's loads in flight together (no load sits in a branch
+          // of its own, which would wait out each one); a member past the
+          // batch re-reads member k0 and is ignored
+          uint64_t x0[MAXT / NP], x1[MAXT / NP];
 #pragma unroll
           for (int k = 0; k < MAXT / NP; ++k) {
-            if (pending >> k & 1) {
-              uint64_t* const sp = slots + ((size_t)(k0 + k) * BM + rw) * 2;
-              const uint64_t x0 = __hip_atomic_load(sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              const uint64_t x1 = __hip_atomic_load(sp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              if ((uint32_t)(x0 >> 32) == 1u && (uint32_t)(x1 >> 32) == 1u) {
-                mv[k] = __uint_as_float((uint32_t)x0);
-                qv[k] = __uint_as_float((uint32_t)x1);
-                pending &= ~(1ull << k);
-              }
-            }
+            uint64_t* const sp = slots + ((size_t)(k < kn ? k0 + k : k0) * BM + rw) * 2;
+            x0[k] = __hip_atomic_load(sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            x1[k] = __hip_atomic_load(sp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
+#pragma unroll
+          for (int k = 0; k < MAXT / NP; ++k)
+            if ((pending >> k & 1) && (uint32_t)(x0[k] >> 32) == 1u && (uint32_t)(x1[k] >> 32) == 1u) {
+              mv[k] = __uint_as_float((uint32_t)x0[k]);
+              qv[k] = __uint_as_float((uint32_t)x1[k]);
+              pending &= ~(1ull << k);
+            }
           if (pending != 0) __builtin_amdgcn_s_sleep(2);
         }
         if (pending != 0) __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -441,10 +441,7 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
         slot_put(sp + s, tag, part0);
         slot_put(sp + S + s, tag, part1);
       }
-      for (int q = t; q < S; q += kWave) {
-        pm[0][q] = slot_take(sp + q, tag, a.err);
-        pm[1][q] = slot_take(sp + S + q, tag, a.err);
-      }
+      for (int q = t; q < S; q += kWave) slot_take2(sp + q, sp + S + q, tag, a.err, &pm[0][q], &pm[1][q]);
     }
     __syncthreads();
     if constexpr (OP == kSoftmax || OP == kPowSoftmax) {
