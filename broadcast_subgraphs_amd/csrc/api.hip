@@ -252,7 +252,7 @@ static cf_status plan_gemm_strips(int epi, int64_t M, int64_t N, int64_t K, DevI
 }
 
 // Workspace of the back-to-back GEMM past the header and join words: the
-// strips' partial outputs (strips x M x 128 floats), then their per-row
+// strips' partial outputs (strips x M x 128 bf16), then their per-row
 // (max, sum) pairs (strips x M float2).
 struct B2bLayout {
   size_t opart = 0, total = 0;
@@ -260,7 +260,7 @@ struct B2bLayout {
 static B2bLayout b2b_layout(const GemmPlan& p, int64_t M) {
   B2bLayout L;
   L.opart = kPartialsOff;
-  L.total = align_up(L.opart + (size_t)M * p.strips * (128 * 4 + 8), 256);
+  L.total = align_up(L.opart + (size_t)M * p.strips * (128 * 2 + 8), 256);
   return L;
 }
 
@@ -678,7 +678,7 @@ cf_status cf_gemm_softmax_gemm(const cf_bf16* Q, const cf_bf16* K, const cf_bf16
   if (s != CF_OK) return s;
   const B2bLayout L = b2b_layout(p, M);
   if (!ws || ws_bytes < L.total) return CF_EWORKSPACE;
-  if (M * p.strips * 128 * 4 >= (int64_t)1 << 32) return CF_EUNSUPPORTED;
+  if (M * p.strips * 128 * 2 >= (int64_t)1 << 31) return CF_EUNSUPPORTED;  // buffer offsets of the partials
   char* base = static_cast<char*>(ws);
   GemmArgs a{};
   a.A = Q; a.B = K; a.V = V; a.scale = scale; a.Y = O;

@@ -1556,9 +1556,9 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
   const __amdgpu_buffer_rsrc_t rB = rsrc(a.B, (uint32_t)(a.N * a.K * 2));
   const __amdgpu_buffer_rsrc_t rV = rsrc(a.V, (uint32_t)(a.N * a.Dv * 2));
   const __amdgpu_buffer_rsrc_t rO = rsrc(a.Y, (uint32_t)(a.M * a.Dv * 2));
-  // partial outputs, strip-major: [S][M][DV] fp32, then (max, sum) [S][M] float2
-  const __amdgpu_buffer_rsrc_t rOp = rsrc(a.opart, (uint32_t)(a.M * S * DV * 4));
-  float2* const Lp = reinterpret_cast<float2*>(a.opart + (size_t)a.M * S * DV);
+  // partial outputs, strip-major: [S][M][DV] bf16, then (max, sum) [S][M] float2
+  const __amdgpu_buffer_rsrc_t rOp = rsrc(a.opart, (uint32_t)(a.M * S * DV * 2));
+  float2* const Lp = reinterpret_cast<float2*>(reinterpret_cast<char*>(a.opart) + (size_t)a.M * S * DV * 2);
   const float sc = a.scale * kLog2e;
 
   // Direct loads: load q of a block puts key 32q + kl (kl = 4w + lane/16 <
@@ -1804,32 +1804,34 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
         }
       continue;
     }
-    // publish the strip's partial output through LDS (now idle): wave w's 32
-    // rows go to a 16 KB region of its own (Q rows for waves 0-3, ring slots
-    // for waves 4-7), 16-byte chunk k of row r at r*512 + 16*(k ^ r), then
-    // back out as whole rows, 1 KB per store instruction
+    // publish the strip's partial output, rounded to bf16, through LDS (now
+    // idle): wave w's 32 rows go to a region of its own (Q rows for waves
+    // 0-3, ring slots for waves 4-7), 16-byte chunk k (8 columns) of row r
+    // at r*256 + 16*(k ^ (r % 16)), then back out as whole rows, 1 KB per
+    // store instruction
     __syncthreads();  // every wave is done with the ring and the Q rows
     // (the region is picked at run time from separate LDS objects, so the
     // pointer is cast back to the LDS address space: the stores and loads
     // below are then LDS instructions with 32-bit addresses, not flat ones)
     lds_char_t* const stage = (lds_char_t*)(w < 4 ? sq + w * 16384 : ring(w - 4));
-    static_assert(NS >= 4 && SLOT == 16384 && BM * BK * 2 == 4 * 16384, "one 16 KB staging region per wave");
+    static_assert(NS >= 4 && SLOT == 16384 && BM * BK * 2 == 4 * 16384, "one staging region per wave");
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const int k4 = nb * 8 + 4 * hl + c4;  // 16-byte chunk index of columns 4*k4 .. +3
-        const f32x4 v = {oacc[nb][4 * c4], oacc[nb][4 * c4 + 1], oacc[nb][4 * c4 + 2], oacc[nb][4 * c4 + 3]};
-        *reinterpret_cast<lds_f32x4_t*>(stage + l32 * 512 + 16 * (k4 ^ l32)) = v;
+      for (int h = 0; h < 2; ++h) {
+        const int k8 = nb * 4 + 2 * hl + h;  // 16-byte chunk index of columns 8*k8 .. +7
+        const u32x4 v = {cvt_bf16x2(oacc[nb][8 * h], oacc[nb][8 * h + 1]), cvt_bf16x2(oacc[nb][8 * h + 2], oacc[nb][8 * h + 3]),
+                         cvt_bf16x2(oacc[nb][8 * h + 4], oacc[nb][8 * h + 5]), cvt_bf16x2(oacc[nb][8 * h + 6], oacc[nb][8 * h + 7])};
+        *reinterpret_cast<lds_u32x4_t*>(stage + l32 * 256 + 16 * (k8 ^ (l32 & 15))) = v;
       }
     if (hl == 0 && row < M) st_dev2(Lp + (size_t)su * M + row, make_float2(m, lsum));
     __syncthreads();
 #pragma unroll 4
-    for (int it = 0; it < 16; ++it) {
-      const int idx = it * 64 + lane, r = idx >> 5, k4 = idx & 31;
+    for (int it = 0; it < 8; ++it) {
+      const int idx = it * 64 + lane, r = idx >> 4, k8 = idx & 15;
       const int orow = m0 + w * 32 + r;
-      const u32x4 v = *reinterpret_cast<const lds_u32x4_t*>(stage + r * 512 + 16 * (k4 ^ r));
-      bst16_dev(rOp, orow < M ? (uint32_t)((((size_t)su * M + orow) * DV + 4 * k4) * 4) : kOOB, v);
+      const u32x4 v = *reinterpret_cast<const lds_u32x4_t*>(stage + r * 256 + 16 * (k8 ^ (r & 15)));
+      bst16_dev(rOp, orow < M ? (uint32_t)((((size_t)su * M + orow) * DV + 8 * k8) * 2) : kOOB, v);
     }
     wait_stores();
     __syncthreads();
@@ -1855,13 +1857,11 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
       float o[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
       float mb = -INFINITY, ls = 0.0f;
       for (int sk = 0; sk < S; sk += 8) {
-        u32x4 v[8][2];
+        u32x4 v[8];
         float2 lv[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            v[k][h] = bld16_dev(rOp, sk + k < S ? (uint32_t)((((size_t)(sk + k) * M + orow) * DV + c8 + 4 * h) * 4) : kOOB);
+          v[k] = bld16_dev(rOp, sk + k < S ? (uint32_t)((((size_t)(sk + k) * M + orow) * DV + c8) * 2) : kOOB);
           lv[k] = sk + k < S ? ld_dev2(Lp + (size_t)(sk + k) * M + orow) : make_float2(-INFINITY, 0.0f);
         }
 #pragma unroll
@@ -1876,7 +1876,10 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
           }
           const float wgt = __builtin_amdgcn_exp2f(lv[k].x - mb);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = fmaf(wgt, __uint_as_float(v[k][e >> 2][e & 3]), o[e]);
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t x = v[k][e >> 1];  // bf16 pair: column e & ~1 low, e | 1 high
+            o[e] = fmaf(wgt, __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16)), o[e]);
+          }
           ls = fmaf(wgt, lv[k].y, ls);
         }
       }

@@ -83,7 +83,7 @@ struct GemmArgs {
   int sw_a, sw_b;      // LN: per-round tile blocks per XCD (sw_a row x sw_b column splits; 0 = linear)
   const uint16_t* V;   // softmax-GEMM: second operand [N x Dv] bf16 (Y is then O [M x Dv])
   int64_t Dv;
-  float* opart;        // softmax-GEMM: per-strip partial outputs, M * strips * 128 floats
+  float* opart;        // softmax-GEMM: per-strip partial outputs, M * strips * 128 bf16, then (max, sum) pairs
   int act;             // activation epilogue: ActId (bias nullable)
   int tile0;           // one-tile-per-workgroup kernels launched per round: the round's first tile
 };
