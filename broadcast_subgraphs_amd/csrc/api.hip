@@ -112,9 +112,14 @@ cf_status plan_rows(int op, int64_t rows, int64_t cols, bool vec_ok, RowPlan* pl
     p.lpr = 256;
     p.nv = pow2ceil((nvec + 255) / 256);
     p.rpi = 1;
-  } else if (force_split <= 1 && force_wide != 0 && nvec <= 1024 * 8 && (rows < di->cus || force_wide == 1)) {
+  } else if (force_split <= 1 && force_wide != 0 && nvec <= 1024 * (op == kLayerNormAffine && p.w == 4 ? 4 : 8) &&
+             (rows < di->cus || force_wide == 1)) {
     // few wide rows: one row per workgroup of 1024 lanes holds the whole row
-    // (<= 8 fragments per lane), so no cross-workgroup exchange is needed
+    // (<= 8 fragments per lane), so no cross-workgroup exchange is needed.
+    // Affine LayerNorm on 16-byte fragments takes at most 4: with its gain
+    // and bias fragments, 8 exceed the registers a 1024-lane workgroup's
+    // waves have (measured: spills cost it 15 us on 64 x 30000), and wider
+    // rows go to the split plan
     p.block = 1024;
     p.lpr = 1024;
     p.nv = (int)std::max<int64_t>(4, pow2ceil((nvec + 1023) / 1024));

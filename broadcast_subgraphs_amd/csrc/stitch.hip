@@ -532,13 +532,13 @@ static hipError_t launch_rows_w(const RowPlan& pl, const RowArgs& a, hipStream_t
   CF_ROWS(128, 1, 1) CF_ROWS(128, 2, 1) CF_ROWS(128, 4, 1)
   CF_ROWS(256, 1, 1) CF_ROWS(256, 2, 1) CF_ROWS(256, 4, 1) CF_ROWS(256, 8, 1) CF_ROWS(256, 16, 1)
 #undef CF_ROWS
-  // one wide row per workgroup of 512 or 1024 lanes
+  // one wide row per workgroup of 1024 lanes
 #define CF_WIDE(BLOCK, NV)                                                                  \
   if (pl.block == BLOCK && pl.lpr == BLOCK && pl.nv == NV && pl.rpi == 1) {                 \
     hipLaunchKernelGGL((k_rows<OP, BLOCK, NV, W, 1, BLOCK>), grid, dim3(BLOCK), 0, st, a);  \
     return hipGetLastError();                                                               \
   }
-  CF_WIDE(512, 8) CF_WIDE(512, 16) CF_WIDE(1024, 4) CF_WIDE(1024, 8)
+  CF_WIDE(1024, 4) CF_WIDE(1024, 8)
 #undef CF_WIDE
   return hipErrorInvalidConfiguration;
 }

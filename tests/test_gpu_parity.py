@@ -128,6 +128,23 @@ def test_layernorm_affine(rows, cols):
     assert err <= TOL_F32, (err, cf.last_plan())
 
 
+def test_layernorm_affine_wide_rows_plan():
+    """A few rows of 30000: LayerNorm and RMSNorm hold each row in one 1024-lane
+    workgroup (8 fragments per lane); affine LayerNorm, whose gain and bias
+    fragments would not fit beside 8, splits the rows across workgroups."""
+    rows, cols = 64, 30000
+    d = gen.layernorm_affine_inputs(seed=18, rows=rows, cols=cols)
+    y = empty_f32(rows, cols)
+    cf.cf_stitch_layernorm(d32(d["x"]), y, d["eps"])
+    p = json.loads(cf.last_plan())
+    assert p["kernel"] == "k_rows" and p["lanes_per_row"] == 1024 and p["frags_per_lane"] == 8, p
+    cf.cf_stitch_layernorm_affine(d32(d["x"]), d32(d["gamma"]), d32(d["beta"]), y, d["eps"])
+    p = json.loads(cf.last_plan())
+    assert p["kernel"] == "k_rows_split", p
+    o = oracle.layernorm_affine_rows(d["x"], d["gamma"], d["beta"], d["eps"])
+    assert rownorm_err(host(y), o) <= TOL_F32, p
+
+
 @pytest.mark.parametrize("gain", [True, False])
 @pytest.mark.parametrize("rows,cols", NORM_SHAPES)
 def test_rmsnorm(rows, cols, gain):
