@@ -1233,12 +1233,63 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 // exchange, and they accumulate online across the strip.
 //   Sweep 1: strip statistics (max, sum of 2^(s - max)) per row, published
 //   once; the last strip of a row block to arrive merges the block's strips
-//   in order and publishes (max, 1/sum) per row.
+//   in order and publishes max + log2(sum) per row.
 //   Sweep 2: after the row block's statistics are in (usually long before),
-//   the strip is computed again, normalised and stored as bf16.
+//   the strip is computed again, normalised (2^(s - max - log2 sum): the
+//   division rides in the exponent) and stored as bf16.
 // The strip is recomputed rather than held across the wait: with a short
 // reduction dimension the second pass costs less than the exchange it hides.
 constexpr int kSmBM = 128, kSmBN = 128, kSmBK = 128;
+
+// One tile's contribution to this lane's running row statistics (m, l) in
+// the base-2 domain, from the raw products acc (scaled by sc).  Chunk q =
+// (cb, h) holds the 8 columns c0 + cb*32 + 8h + [0, 8), valid or not as a
+// whole; RAGGED tiles mask the chunks past N, full tiles skip the tests.
+// The extreme raw value (max for sc >= 0, min otherwise: scaling is monotone)
+// comes from three-input NaN-propagating max / min trees over independent
+// chunks, which take no canonicalising moves; a NaN product makes the row's
+// sum NaN either way.
+template <int CB, bool RAGGED>
+__device__ __forceinline__ void sm_tile_stats(const f32x16 (&acc)[CB], int c0, int N, float sc, float& m, float& l) {
+  bool ok[2 * CB];
+#pragma unroll
+  for (int q = 0; q < 2 * CB; ++q) ok[q] = !RAGGED || c0 + (q >> 1) * 32 + 8 * (q & 1) < N;
+  auto mx = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
+  auto mn = [](float x, float y) { return __builtin_elementwise_minimum(x, y); };
+  float cm[2 * CB];
+  const bool up = sc >= 0.0f;
+#pragma unroll
+  for (int q = 0; q < 2 * CB; ++q) {
+    float e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = acc[q >> 1][8 * (q & 1) + k];
+    const float x = up ? mx(mx(mx(e[0], e[1]), e[2]), mx(mx(mx(e[3], e[4]), e[5]), mx(e[6], e[7])))
+                       : mn(mn(mn(e[0], e[1]), e[2]), mn(mn(mn(e[3], e[4]), e[5]), mn(e[6], e[7])));
+    cm[q] = ok[q] ? x : (up ? -INFINITY : INFINITY);
+  }
+#pragma unroll
+  for (int st = 1; st < 2 * CB; st *= 2)
+#pragma unroll
+    for (int q = 0; q + st < 2 * CB; q += 2 * st) cm[q] = up ? mx(cm[q], cm[q + st]) : mn(cm[q], cm[q + st]);
+  const float ex = cm[0];
+  if (ex == INFINITY || ex == -INFINITY) return;
+  const float mnew = fmaxf(m, ex * sc);
+  float cs[2 * CB];
+#pragma unroll
+  for (int q = 0; q < 2 * CB; ++q) {
+    float e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = __builtin_amdgcn_exp2f(fmaf(acc[q >> 1][8 * (q & 1) + k], sc, -mnew));
+    const float x = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    cs[q] = ok[q] ? x : 0.0f;
+  }
+#pragma unroll
+  for (int st = 1; st < 2 * CB; st *= 2)
+#pragma unroll
+    for (int q = 0; q + st < 2 * CB; q += 2 * st) cs[q] += cs[q + st];
+  l = l * __builtin_amdgcn_exp2f(m - mnew) + cs[0];
+  m = mnew;
+}
 
 template <int KS, int MINB>
 __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
@@ -1377,64 +1428,10 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
     for (int j = strip_first(u); j < strip_end(u); ++j) {
       f32x16 acc[CB];
       step(1, u, j, qf, acc, false);
-      // 8-column chunks of this lane's row: chunk q = (cb, h) holds columns
-      // j*BN + cb*32 + 16*hl + 8*h + [0, 8); it is valid or not as a whole
+      // chunk (cb, h) of this lane's row holds columns j*BN + cb*32 + 16*hl + 8*h + [0, 8)
       const int c0 = j * BN + 16 * hl;
-      bool ok[2 * CB];
-#pragma unroll
-      for (int q = 0; q < 2 * CB; ++q) ok[q] = c0 + (q >> 1) * 32 + 8 * (q & 1) < N;
-      // the row max of the scaled values from the raw ones (scaling is
-      // monotone): a tree over independent chunks, no long dependency chain
-      float ex;
-      if (sc >= 0.0f) {
-        float cm[2 * CB];
-#pragma unroll
-        for (int q = 0; q < 2 * CB; ++q) {
-          float v[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) v[k] = acc[q >> 1][8 * (q & 1) + k];
-          const float x = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-          cm[q] = ok[q] ? x : -INFINITY;
-        }
-#pragma unroll
-        for (int st2 = 1; st2 < 2 * CB; st2 *= 2)
-#pragma unroll
-          for (int q = 0; q + st2 < 2 * CB; q += 2 * st2) cm[q] = fmaxf(cm[q], cm[q + st2]);
-        ex = cm[0];
-      } else {
-        float cm[2 * CB];
-#pragma unroll
-        for (int q = 0; q < 2 * CB; ++q) {
-          float v[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) v[k] = acc[q >> 1][8 * (q & 1) + k];
-          const float x = fminf(fminf(fminf(v[0], v[1]), fminf(v[2], v[3])), fminf(fminf(v[4], v[5]), fminf(v[6], v[7])));
-          cm[q] = ok[q] ? x : INFINITY;
-        }
-#pragma unroll
-        for (int st2 = 1; st2 < 2 * CB; st2 *= 2)
-#pragma unroll
-          for (int q = 0; q + st2 < 2 * CB; q += 2 * st2) cm[q] = fminf(cm[q], cm[q + st2]);
-        ex = cm[0];
-      }
-      if (ex != INFINITY && ex != -INFINITY) {
-        const float mn = fmaxf(m, ex * sc);
-        float cs[2 * CB];
-#pragma unroll
-        for (int q = 0; q < 2 * CB; ++q) {
-          float e[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) e[k] = __builtin_amdgcn_exp2f(fmaf(acc[q >> 1][8 * (q & 1) + k], sc, -mn));
-          const float x = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-          cs[q] = ok[q] ? x : 0.0f;
-        }
-#pragma unroll
-        for (int st2 = 1; st2 < 2 * CB; st2 *= 2)
-#pragma unroll
-          for (int q = 0; q + st2 < 2 * CB; q += 2 * st2) cs[q] += cs[q + st2];
-        l = l * __builtin_amdgcn_exp2f(m - mn) + cs[0];
-        m = mn;
-      }
+      if (j * BN + BN <= N) sm_tile_stats<CB, false>(acc, c0, N, sc, m, l);
+      else sm_tile_stats<CB, true>(acc, c0, N, sc, m, l);
     }
     merge_sm(m, l, __shfl_xor(m, 32, kWave), __shfl_xor(l, 32, kWave));
     const int row = m0 + w * 32 + l32;
@@ -1460,7 +1457,8 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) merge_sm(mm, ll, v[k].x, v[k].y);
         }
-        st_dev2(F + m0 + t, make_float2(mm, 1.0f / ll));
+        // the row's offset max + log2(sum): sweep 2 normalises inside the exponent
+        st_dev2(F + m0 + t, make_float2(mm + __builtin_amdgcn_logf(ll), 0.0f));
       }
       wait_stores();
       __syncthreads();
@@ -1477,7 +1475,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
     if (t == 0) wait_generation(a.joins + rowblk, gens[i], a.err);
     __syncthreads();
     const int row = m0 + w * 32 + l32;
-    const float2 fs = row < M ? ld_dev2(F + row) : make_float2(0.0f, 0.0f);
+    const float off = row < M ? ld_dev2(F + row).x : 0.0f;
     for (int j = strip_first(u); j < strip_end(u); ++j) {
       f32x16 acc[CB];
       step(2, u, j, qf, acc, j > strip_first(u));
@@ -1488,7 +1486,7 @@ __global__ __launch_bounds__(kThreads, MINB) void k_gemm_sm3(GemmArgs a) {
           const int col = j * BN + cb * 32 + 16 * hl + 8 * h;
           float o[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * h + e], sc, -fs.x)) * fs.y;
+          for (int e = 0; e < 8; ++e) o[e] = __builtin_amdgcn_exp2f(fmaf(acc[cb][8 * h + e], sc, -off));
           const u32x4 pk = {cvt_bf16x2(o[0], o[1]), cvt_bf16x2(o[2], o[3]), cvt_bf16x2(o[4], o[5]),
                             cvt_bf16x2(o[6], o[7])};
           bst16(rY, (row < M && col < N) ? (uint32_t)(row * N + col) * 2u : kOOB, pk);
