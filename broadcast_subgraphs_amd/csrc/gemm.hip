@@ -513,6 +513,11 @@ template <int V>
 struct IntC {
   static constexpr int value = V;
 };
+// f(IntC<Q>{}) for Q = 0, 1, ..., in order
+template <class F, int... Q>
+__device__ __forceinline__ void for_each_c(F&& f, std::integer_sequence<int, Q...>) {
+  (f(IntC<Q>{}), ...);
+}
 
 // Unary activations of the activation epilogue, in fp32.  Both sigmoid-gated
 // forms use 1 / (1 + 2^t): the tanh-form GELU 0.5 u (1 + tanh z), with
@@ -2355,20 +2360,18 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void k_gemm_ln3(GemmArgs a) {
       mu[rb] = mean;
       m2[rb] = q2;
     };
-    [&]<int... Q>(std::integer_sequence<int, Q...>) { (fetch(IntC<Q + 1>{}), ...); }(
-        std::make_integer_sequence<int, RD - 1>{});
+    for_each_c([&](auto qc) { fetch(IntC<decltype(qc)::value + 1>{}); }, std::make_integer_sequence<int, RD - 1>{});
     __syncthreads();  // every wave is done with the ring (slot 0 becomes the epilogue scratch); vec is in
-    [&]<int... Q>(std::integer_sequence<int, Q...>) {
-      (
-          [&] {
-            // block Q is in; the blocks after it (at most RD - 1) may still fly
-            constexpr int after = (RB - 1 - Q) < (RD - 1) ? (RB - 1 - Q) : (RD - 1);
-            wait_vm<after * CB * 2>();
-            block(IntC<Q>{});
-            if constexpr (Q + RD < RB) fetch(IntC<Q + RD>{});
-          }(),
-          ...);
-    }(std::make_integer_sequence<int, RB>{});
+    for_each_c(
+        [&](auto qc) {
+          constexpr int Q = decltype(qc)::value;
+          // block Q is in; the blocks after it (at most RD - 1) may still fly
+          constexpr int after = (RB - 1 - Q) < (RD - 1) ? (RB - 1 - Q) : (RD - 1);
+          wait_vm<after * CB * 2>();
+          block(IntC<Q>{});
+          if constexpr (Q + RD < RB) fetch(IntC<Q + RD>{});
+        },
+        std::make_integer_sequence<int, RB>{});
   }
   tile_merge_ln<BM, WGN, RB>(n_, mu, m2, red, wm, wn);
   if (wn == 0 && hl == 0) {
@@ -2524,7 +2527,6 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void k_gemm_act2(GemmArgs a) {
   if (g >= tiles) return;
   const __amdgpu_buffer_rsrc_t rA = rsrc(a.A, (uint32_t)(a.M * a.K * 2));
   const __amdgpu_buffer_rsrc_t rB = rsrc(a.B, (uint32_t)(a.N * a.K * 2));
-  const __amdgpu_buffer_rsrc_t rY = rsrc(a.Y, (uint32_t)(a.M * a.N * 2));
   const __amdgpu_buffer_rsrc_t rBias = rsrc(a.bias, a.bias ? (uint32_t)(a.N * 4) : 0u);  // no bias: reads zero
   const RG rg(a);
   char* const all_slots[4] = {s0, s1, s2, s3};

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kB) void u_k_rowreduce_wave(const float* x, float* 
   if (lane == 0) out[row] = v;
 }
 
-__global__ __launch_bounds__(kB) void u_k_rowreduce_block(const float* x, float* out, int64_t rows, int64_t cols, int is_max) {
+__global__ __launch_bounds__(kB) void u_k_rowreduce_block(const float* x, float* out, int64_t, int64_t cols, int is_max) {
   __shared__ float s[kB / 64];
   const int64_t row = blockIdx.x;
   const float* xr = x + row * cols;
