@@ -68,7 +68,8 @@ def test_auto_pow_on_signed_input(p):
     out = torch.full((rows, cols), 7.0, device="cuda")
     a.launch([d32(x)], out)
     got = host(out).astype(np.float64)
-    want = oracle.graph.evaluate(b.nodes, t, [x])
+    with np.errstate(invalid="ignore"):  # the real power of a negative base to 1.5 is NaN, as intended
+        want = oracle.graph.evaluate(b.nodes, t, [x])
     assert np.array_equal(np.isnan(got), np.isnan(want))
     ok = ~np.isnan(want)
     assert ok.any()
