@@ -1669,19 +1669,22 @@ __global__ __launch_bounds__(kB2bThreads, 1) void k_gemm_b2b(GemmArgs a) {
     float tx = sc >= 0.0f ? -INFINITY : INFINITY;  // max (or min) of the raw scores
     const bool whole = (j + 1) * BN <= N;           // every key of the tile is valid (uniform)
     if (sc >= 0.0f && whole) {
-      // a tree over 8-value chunks: no long dependency chain
+      // a tree of three-input NaN-propagating maxima over 8-value chunks: no
+      // long dependency chain and no canonicalising moves (a NaN score makes
+      // the row NaN either way)
+      auto mx = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
       float cm[2 * CB];
 #pragma unroll
       for (int q = 0; q < 2 * CB; ++q) {
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = acc[q >> 1][8 * (q & 1) + e];
-        cm[q] = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+        cm[q] = mx(mx(mx(v[0], v[1]), v[2]), mx(mx(mx(v[3], v[4]), v[5]), mx(v[6], v[7])));
       }
 #pragma unroll
       for (int d = 1; d < 2 * CB; d *= 2)
 #pragma unroll
-        for (int q = 0; q + d < 2 * CB; q += 2 * d) cm[q] = fmaxf(cm[q], cm[q + d]);
+        for (int q = 0; q + d < 2 * CB; q += 2 * d) cm[q] = mx(cm[q], cm[q + d]);
       tx = cm[0];
     } else if (sc >= 0.0f) {
 #pragma unroll
