@@ -15,8 +15,8 @@ import torch
 import broadcast_subgraphs_amd as cf
 import gen
 import oracle
-from tests.test_gpu_parity import (TOL_BF16, TOL_F32, _gemm_ln_run, _gemm_sm_run, check_ws, d32, empty_f32, host,
-                                   rownorm_err)
+from tests.test_gpu_parity import (TOL_BF16, TOL_F32, _gemm_ln_run, _gemm_sm_run, check_ws, d32, dbf16, empty_f32,
+                                   host, rownorm_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -228,3 +228,45 @@ def test_auto_checked_launch_raises_when_a_wait_gave_up():
     ws.buf[256:264].view(torch.int64).fill_(0)
     a.launch([d32(x)], out, ws=ws, check=True)
     assert rownorm_err(host(out), oracle.graph.evaluate(nodes, t, [x])) <= TOL_F32
+
+
+def test_gemm_softmax_nan_score_poisons_only_its_row():
+    """A NaN in one Q row makes that row's scores NaN: its whole output row is NaN (every element
+    written, from a finite sentinel), and every other row still matches the oracle."""
+    M, N, D = 300, 1000, 64
+    d = gen.gemm_softmax_inputs(seed=210, M=M, N=N, D=D)
+    r = 137
+    d["q_bits"] = d["q_bits"].copy()
+    d["q_bits"][r, 5] = 0x7FC0  # bf16 quiet NaN
+    q = np.array(d["q"], np.float32)
+    q[r, 5] = np.nan
+    S = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = cf.cf_gemm_softmax(dbf16(d["q_bits"]), dbf16(d["k_bits"]), d["scale"], S)
+    check_ws(ws)
+    g = host(S)
+    assert np.isnan(g[r]).all()
+    keep = np.arange(M) != r
+    assert not np.isnan(g[keep]).any()
+    o = oracle.gemm_softmax(q[keep], d["k"], d["scale"])
+    assert rownorm_err(g[keep], o) <= TOL_BF16, cf.last_plan()
+
+
+def test_gemm_softmax_gemm_nan_score_poisons_only_its_row():
+    """The back-to-back GEMM with a NaN in one Q row: that row of O is NaN (written over a finite
+    sentinel), the rest match the oracle."""
+    M, N, D, Dv = 512, 1024, 128, 128
+    d = gen.gemm_softmax_gemm_inputs(seed=211, M=M, N=N, D=D, Dv=Dv)
+    r = 300
+    d["q_bits"] = d["q_bits"].copy()
+    d["q_bits"][r, 17] = 0x7FC0
+    q = np.array(d["q"], np.float32)
+    q[r, 17] = np.nan
+    O = torch.full((M, Dv), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = cf.cf_gemm_softmax_gemm(dbf16(d["q_bits"]), dbf16(d["k_bits"]), dbf16(d["v_bits"]), d["scale"], O)
+    check_ws(ws)
+    g = host(O)
+    assert np.isnan(g[r]).all()
+    keep = np.arange(M) != r
+    assert not np.isnan(g[keep]).any()
+    o = oracle.gemm_softmax_gemm(q[keep], d["k"], d["v"], d["scale"])
+    assert rownorm_err(g[keep], o) <= TOL_BF16, cf.last_plan()
