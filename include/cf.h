@@ -201,7 +201,8 @@ cf_status cf_gemm_ln_noalloc(const cf_bf16* A, const cf_bf16* W, const float* bi
 
 /* S = softmax(scale * Q.K^T) over each row of length N.
  * Q [M x D], K [N x D] (both D contiguous), S [M x N]; scale finite.
- * Cross-tile max and sum aggregation.  [ComFuse] B2BGEMM (eq. 3: S_tile =
+ * Cross-tile max and sum aggregation.  A NaN score makes its whole output
+ * row NaN; other rows are unaffected.  [ComFuse] B2BGEMM (eq. 3: S_tile =
  * F(P_tile) formed in the first MatMul's epilogue) and the inter-CTA level. */
 cf_status cf_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scale, cf_bf16* S,
                           int64_t M, int64_t N, int64_t D, void* ws, size_t ws_bytes,
@@ -212,7 +213,8 @@ cf_status cf_gemm_softmax(const cf_bf16* Q, const cf_bf16* K, float scale, cf_bf
  * V [N x Dv] (Dv contiguous), O [M x Dv]; scale finite; D <= 128,
  * 8 <= Dv <= 128 with Dv % 8 == 0.  The S tile feeds the second MatMul from
  * registers; partial outputs over the contraction dimension N are summed in
- * a fixed order before the commit, so results are deterministic.
+ * a fixed order before the commit, so results are deterministic.  A NaN
+ * score makes its whole output row NaN; other rows are unaffected.
  * [ComFuse] B2BGEMM (eq. 3: S_tile = F(P_tile); eq. 4: partial products
  * S_tile.W2_tile over the contraction dimension; eq. 5: their sum at the
  * commit; one circular buffer shared by the W1 and W2 tiles), with F the
