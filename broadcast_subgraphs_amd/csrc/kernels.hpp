@@ -77,7 +77,7 @@ struct GemmArgs {
   uint32_t* err;
   uint64_t* joins;     // one join word per group of tiles_n workgroups
   float* partials;     // M * tiles_n * 4 floats
-  float* finals;       // M * 2 floats (leader aggregation)
+  float* finals;       // M * 2 floats: the leader's per-row results (strip softmax: max + log2(sum), unused)
   int agg_leader;      // 0: every member reads all partials; 1: last arriver combines
   int strips;          // strip softmax: strips per row block
   int sw_a, sw_b;      // LN: per-round tile blocks per XCD (sw_a row x sw_b column splits; 0 = linear)
