@@ -1,6 +1,7 @@
 """C-ABI checks that need no GPU: the library loads, exports every declared
 symbol, and rejects invalid arguments before making any HIP call."""
 import ctypes
+import os
 
 import pytest
 
@@ -130,3 +131,17 @@ def test_spec_and_auto_validation_before_any_hip_call(L):
     finally:
         L.cf_auto_free(h)
     assert L.cf_spec_launch(None, None, 0, P(A16), None, 0, None) == cf.CF_EINVAL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU: --gpus above 1 exits with status 2 and a JSON error line,
+    before touching torch or the device."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=root, timeout=120)
+    assert p.returncode == 2
+    msg = json.loads(p.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
