@@ -270,3 +270,17 @@ def test_gemm_softmax_gemm_nan_score_poisons_only_its_row():
     assert not np.isnan(g[keep]).any()
     o = oracle.gemm_softmax_gemm(q[keep], d["k"], d["v"], d["scale"])
     assert rownorm_err(g[keep], o) <= TOL_BF16, cf.last_plan()
+
+
+def test_gemm_softmax_zero_scale_is_uniform():
+    """scale = 0: every score is 0 whatever Q and K hold, so each output is 1/N (here N = 1000,
+    ragged against the 128-column tiles); the row max and the folded-in log-sum must not turn
+    0 * (raw score) into anything else."""
+    M, N, D = 260, 1000, 96
+    d = gen.gemm_softmax_inputs(seed=212, M=M, N=N, D=D)
+    d["scale"] = 0.0
+    g = _gemm_sm_run(d, M, N, D)
+    o = oracle.gemm_softmax(d["q"], d["k"], 0.0)
+    assert np.allclose(o, 1.0 / N)
+    assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
+    assert np.max(np.abs(g.astype(np.float64) * N - 1.0)) <= 2.0 ** -8
