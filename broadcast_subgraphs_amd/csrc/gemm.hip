@@ -2274,6 +2274,7 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void k_gemm_ln3(GemmArgs a) {
   // member k at ((rowblk * T + k) * BM + i) * 2, so a wave's puts and takes
   // touch contiguous runs
   uint64_t* const slots = reinterpret_cast<uint64_t*>(a.partials) + (size_t)rowblk * T * BM * 2;
+  const __amdgpu_buffer_rsrc_t rS = rsrc(slots, (uint32_t)(T * BM * 16));
   f32x16 acc[RB][CB];
   // residual: one row block of the lane's accumulators per fetch, RD in
   // flight; rows past M lie past the buffer's range and read zero, a chunk
@@ -2407,18 +2408,17 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void k_gemm_ln3(GemmArgs a) {
           // every poll's loads in flight together (no load sits in a branch
           // of its own, which would wait out each one); a member past the
           // batch re-reads member k0 and is ignored
-          uint64_t x0[MAXT / NP], x1[MAXT / NP];
-#pragma unroll
-          for (int k = 0; k < MAXT / NP; ++k) {
-            uint64_t* const sp = slots + ((size_t)(k < kn ? k0 + k : k0) * BM + rw) * 2;
-            x0[k] = __hip_atomic_load(sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            x1[k] = __hip_atomic_load(sp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
+          // a member's two slots of a row are one 16-byte pair: one device-scope
+          // load reads both (each 8-byte half is one store's word)
+          u32x4 xv[MAXT / NP];
 #pragma unroll
           for (int k = 0; k < MAXT / NP; ++k)
-            if ((pending >> k & 1) && (uint32_t)(x0[k] >> 32) == 1u && (uint32_t)(x1[k] >> 32) == 1u) {
-              mv[k] = __uint_as_float((uint32_t)x0[k]);
-              qv[k] = __uint_as_float((uint32_t)x1[k]);
+            xv[k] = bld16_dev(rS, (uint32_t)(((k < kn ? k0 + k : k0) * BM + rw) * 16));
+#pragma unroll
+          for (int k = 0; k < MAXT / NP; ++k)
+            if ((pending >> k & 1) && xv[k][1] == 1u && xv[k][3] == 1u) {
+              mv[k] = __uint_as_float(xv[k][0]);
+              qv[k] = __uint_as_float(xv[k][2]);
               pending &= ~(1ull << k);
             }
           if (pending != 0) __builtin_amdgcn_s_sleep(2);
