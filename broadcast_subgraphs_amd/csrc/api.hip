@@ -295,9 +295,15 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   // the plain GEMM and the overlapped epilogues, 64x512 for the round-based
   // epilogues.
   // GEMM + LN: the 256 x 256 one-tile-per-workgroup kernel (7) wherever a
-  // whole row block of its tiles fits the resident grid, else 128 x 128 (3)
+  // whole row block of its tiles fits the resident grid and its tiles fill at
+  // least half the CUs, else 128 x 128 at two workgroups per CU (3).  Measured
+  // on MI355X (K = 1024 unless noted): 64 large tiles, 1024 x 4096 39.9 us
+  // against 29.8 us and 2048 x 2048 x 2048 61.1 against 37.5 us; 128 tiles,
+  // 2048 x 4096 42.8 against 47.5 us (4096 x 2048: 41.8 against 38.5 us);
+  // 256 tiles, 4096 x 4096 49.7 against 63.4 us
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const int dflt = (epi == kEpiAct && p.algo == 1) ? 0
-                   : (epi == kEpiLN && p.algo == 1) ? ((N + 255) / 256 <= di->cus ? 7 : 3)
+                   : (epi == kEpiLN && p.algo == 1) ? ((N + 255) / 256 <= di->cus && 2 * big_tiles >= di->cus ? 7 : 3)
                                                     : ((plain || p.algo == 1) ? 3 : 4);
   p.cfg = (int)env_int(epi == kEpiSoftmax ? "CF_GEMM_SOFTMAX_CFG"
                        : epi == kEpiLN     ? "CF_GEMM_LN_CFG"

@@ -222,10 +222,11 @@ def test_gemm_ln(M, N, K):
 def test_gemm_ln_default_plan_on_the_workload():
     """The 4096 x 4096 x 1024 workload runs on the 256 x 256 kernel, one tile per workgroup
     and a single launch (16 tiles per row block, all 256 tiles resident)."""
-    d = gen.gemm_ln_inputs(seed=4, M=512, N=4096, K=64)
-    _gemm_ln_run(d, 512, 4096, 64)
+    d = gen.gemm_ln_inputs(seed=4, M=4096, N=4096, K=64)  # the workload's output shape, a short K
+    _gemm_ln_run(d, 4096, 4096, 64)
     p = json.loads(cf.last_plan())
     assert (p["kernel"], p["tile"][:2], p["row_group"]) == ("k_gemm_ln3", [256, 256], 16), p
+    assert p["rounds"] == 1, p
 
 
 def test_gemm_ln_no_residual():
@@ -780,3 +781,15 @@ def test_single_row_and_minimal_gemms(monkeypatch):
             b = gen.gemm_softmax_gemm_inputs(seed=74, M=M, N=N, D=K, Dv=8)
             assert rownorm_err(_b2b_run(b, M, N, K, 8), oracle.gemm_softmax_gemm(b["q"], b["k"], b["v"], b["scale"])) \
                 <= TOL_BF16
+
+
+@pytest.mark.parametrize("M,N,K", [(1024, 4096, 1024), (2048, 2048, 2048)])
+def test_gemm_ln_small_grid_takes_the_128_tiles(M, N, K):
+    """Fewer 256 x 256 tiles than half the CUs: the planner takes 128 x 128 tiles at two
+    workgroups per CU (the large tiles would leave most CUs idle); parity against the oracle."""
+    d = gen.gemm_ln_inputs(seed=13, M=M, N=N, K=K)
+    g = _gemm_ln_run(d, M, N, K)
+    p = json.loads(cf.last_plan())
+    assert p["kernel"] == "k_gemm_ln2" and p["tile"][:2] == [128, 128], p
+    o = oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"], d["beta"], d["eps"])
+    assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
