@@ -284,9 +284,14 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   const int dalgo = (epi == kEpiSoftmax && K <= 128) ? 2 : 1;
   const bool plain = epi == kEpiStoreF32 || epi == kEpiAct;  // tiles independent of each other
   // activation epilogue: 0 = the round-based kernel (128 x 128 tiles, two
-  // workgroups per CU), 1 = large tiles at one 8-wave workgroup per CU (the
-  // default: measured 3-7% faster on 4096 x 4096 x 1024)
-  p.algo = epi == kEpiAct ? (int)env_int("CF_GEMM_ACT_ALGO", 1)
+  // workgroups per CU), 1 = large tiles at one 8-wave workgroup per CU, the
+  // default where its 256 x 256 tiles fill at least three quarters of the CUs.
+  // Measured on MI355X (GELU, K = 1024 unless noted, large against 128 x 128
+  // tiles): 4096 x 4096 40.7 / 44.5 us, 8192 x 8192 156.8 / 204.4 us, 4096 x
+  // 4096 x 4096 122.1 / 151.5 us; 3072 x 4096 38.8 / 38.5 us; 2048 x 4096 36.3
+  // / 24.0 us, 1024 x 4096 33.8 / 18.7 us, 2048 x 2048 x 2048 55.0 / 28.3 us
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  p.algo = epi == kEpiAct ? (int)env_int("CF_GEMM_ACT_ALGO", 4 * big_tiles >= 3 * (int64_t)di->cus ? 1 : 0)
                           : (plain ? 0 : (int)env_int("CF_GEMM_ALGO", dalgo));
   if (epi == kEpiAct && (p.algo < 0 || p.algo > 1)) return CF_EUNSUPPORTED;
   if (p.algo >= 2 && (epi != kEpiSoftmax || K > 128 || p.algo > 2)) return CF_EUNSUPPORTED;
@@ -301,7 +306,6 @@ cf_status plan_gemm(int epi, bool nn, int64_t M, int64_t N, int64_t K, GemmPlan*
   // against 29.8 us and 2048 x 2048 x 2048 61.1 against 37.5 us; 128 tiles,
   // 2048 x 4096 42.8 against 47.5 us (4096 x 2048: 41.8 against 38.5 us);
   // 256 tiles, 4096 x 4096 49.7 against 63.4 us
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const int dflt = (epi == kEpiAct && p.algo == 1) ? 0
                    : (epi == kEpiLN && p.algo == 1) ? ((N + 255) / 256 <= di->cus && 2 * big_tiles >= di->cus ? 7 : 3)
                                                     : ((plain || p.algo == 1) ? 3 : 4);

@@ -793,3 +793,15 @@ def test_gemm_ln_small_grid_takes_the_128_tiles(M, N, K):
     assert p["kernel"] == "k_gemm_ln2" and p["tile"][:2] == [128, 128], p
     o = oracle.gemm_ln(d["a"], d["w"], d["bias"], d["r"], d["gamma"], d["beta"], d["eps"])
     assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
+
+
+def test_gemm_act_small_grid_takes_the_128_tiles():
+    """Fewer 256 x 256 tiles than three quarters of the CUs: the planner takes the 128 x 128
+    kernel at two workgroups per CU; parity against the oracle."""
+    M, N, K = 1024, 4096, 1024
+    d = _act_inputs("gelu_tanh", 59, M, N, K)
+    g = _gemm_act_run(d, M, N, "gelu_tanh")
+    plan = json.loads(cf.last_plan())
+    assert plan["kernel"] == "k_gemm" and plan["tile"][:2] == [128, 128], plan
+    o = oracle.gemm_act(d["a"], d["w"], d["bias"], "gelu_tanh")
+    assert act_err(g, o) <= 1.0, act_err(g, o)
