@@ -240,6 +240,12 @@ static cf_status plan_gemm_strips(int epi, int64_t M, int64_t N, int64_t K, DevI
   // one join word per row block (the back-to-back GEMM's is its second block of words)
   if ((epi == kEpiSoftmaxGemm ? 2 : 1) * tm > kMaxJoins) return CF_EUNSUPPORTED;
   int64_t S = std::max<int64_t>(1, std::min<int64_t>(tn, cap / tm));
+  // the softmax strips hold at least four tiles each: a strip's Q load,
+  // publication and join cost about as much as a few tiles.  Measured on
+  // MI355X (D = 128, strips: us): 4096 x 4096 16: 31.7, 8: 25.5;
+  // 2048 x 8192 32: 40.7, 16: 26.4; 8192 x 2048 8: 27.1-28.2, 4: 24.9;
+  // 8192 x 8192 8: 62.3-66.8, 4: 70.1, 16: 67.0
+  if (epi == kEpiSoftmax) S = std::max<int64_t>(1, std::min<int64_t>(S, tn / 4));
   const int64_t C = (tn + S - 1) / S;
   S = (tn + C - 1) / C;
   const int64_t units = tm * S;

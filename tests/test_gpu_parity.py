@@ -805,3 +805,16 @@ def test_gemm_act_small_grid_takes_the_128_tiles():
     assert plan["kernel"] == "k_gemm" and plan["tile"][:2] == [128, 128], plan
     o = oracle.gemm_act(d["a"], d["w"], d["bias"], "gelu_tanh")
     assert act_err(g, o) <= 1.0, act_err(g, o)
+
+
+@pytest.mark.parametrize("M,N,D", [(4096, 4096, 128), (8192, 2048, 128)])
+def test_gemm_softmax_strips_hold_four_tiles(M, N, D):
+    """The strip planner keeps at least four 128-column tiles per strip (fewer, longer strips
+    where the rows would allow more); parity against the oracle on sampled rows."""
+    d = gen.gemm_softmax_inputs(seed=14, M=M, N=N, D=D)
+    g = _gemm_sm_run(d, M, N, D)
+    p = json.loads(cf.last_plan())
+    assert p["kernel"] == "k_gemm_sm3" and p["row_group"] == N // 128 // 4, p
+    rows = np.arange(0, M, 37)
+    o = oracle.gemm_softmax(np.asarray(d["q"])[rows], d["k"], d["scale"])
+    assert rownorm_err(g[rows], o) <= TOL_BF16, cf.last_plan()
