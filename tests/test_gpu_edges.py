@@ -56,14 +56,15 @@ def _extra(seed, rows, cols):
 
 
 # 16-byte fragments (every row start 16-byte aligned) on the split plan: rows longer than one
-# 1024-lane workgroup holds, few rows longer than one 256-lane workgroup holds, and >= 256 rows
-# longer than 16384 values (two members per row)
+# 1024-lane workgroup holds, and (the wide plan switched off) few or >= 256 rows longer than
+# one 256-lane workgroup holds (two members per row)
 SPLIT16 = [("softmax", 2, 65536), ("layernorm", 3, 70000), ("rmsnorm", 3, 70000), ("layernorm_affine", 3, 70000),
            ("pow", 8, 40000), ("softmax", 300, 20000), ("layernorm", 260, 16400), ("pow", 5, 32772)]
 
 
 @pytest.mark.parametrize("op,rows,cols", SPLIT16)
-def test_split_plan_16_byte_fragments(op, rows, cols):
+def test_split_plan_16_byte_fragments(monkeypatch, op, rows, cols):
+    monkeypatch.setenv("CF_FORCE_WIDE", "0")
     x = gen.normal(201, 0, (rows, cols)) if op in ("softmax", "pow") else gen.uniform(201, 0, (rows, cols), -1, 1)
     got, want, plan = _run_rows(op, x, _extra(201, rows, cols))
     assert plan["kernel"] == "k_rows_split" and plan["frag_floats"] == 4, plan
@@ -284,3 +285,16 @@ def test_gemm_softmax_zero_scale_is_uniform():
     assert np.allclose(o, 1.0 / N)
     assert rownorm_err(g, o) <= TOL_BF16, cf.last_plan()
     assert np.max(np.abs(g.astype(np.float64) * N - 1.0)) <= 2.0 ** -8
+
+
+@pytest.mark.parametrize("op,rows,cols", [("softmax", 300, 20000), ("layernorm", 512, 32768), ("rmsnorm", 260, 16400),
+                                          ("pow", 400, 30000), ("softmax", 2000, 5001)])
+def test_wide_rows_at_any_row_count(op, rows, cols):
+    """Rows that one 1024-lane workgroup holds (at most 8 fragments per lane) take the one-wide-row
+    plan whatever the row count (no exchange; the grid walks the rows); a 5001-column row takes
+    the 4-byte-fragment form of it."""
+    x = gen.normal(212, 0, (rows, cols)) if op in ("softmax", "pow") else gen.uniform(212, 0, (rows, cols), -1, 1)
+    got, want, plan = _run_rows(op, x, _extra(212, rows, cols))
+    assert plan["kernel"] == "k_rows" and plan["lanes_per_row"] == 1024 and plan["split"] == 1, plan
+    assert plan["frag_floats"] == (1 if cols % 4 else 4), plan
+    assert rownorm_err(got, want) <= TOL_F32, plan
