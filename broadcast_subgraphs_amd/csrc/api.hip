@@ -127,17 +127,27 @@ cf_status plan_rows(int op, int64_t rows, int64_t cols, bool vec_ok, RowPlan* pl
     p.nv = (int)std::max<int64_t>(4, pow2ceil((nvec + 1023) / 1024));
     p.rpi = 1;
   } else {
-    // task splitting: S members per row, each holding <= 16 fragments per lane
-    const int64_t s_min = (nvec + 256 * 16 - 1) / (256 * 16);
+    // task splitting: S members per row, each a 256-lane workgroup holding
+    // <= 16 fragments per lane, or a 1024-lane one holding <= 8.  The softmax
+    // family on 16-byte fragments takes 1024-lane members for many rows wider
+    // than one of them holds (measured on MI355X, 256- against 1024-lane
+    // members: 256 x 65536 34.1 / 29.2 us, 128 x 131072 34.9 / 30.2 us,
+    // 2048 x 128256 420.0 / 373.9 us; the norms gain nothing, and few rows or
+    // 4-byte fragments lose)
+    const bool wide_members = !is_norm(op) && p.w == 4 && 2 * rows >= di->cus && nvec > 1024 * 8;
+    const int blk = op != kLayerNormAffine && env_int("CF_SPLIT_BLOCK", wide_members ? 1024 : 256) == 1024 ? 1024 : 256;
+    const int64_t per_member = blk == 1024 ? 1024 * 8 : 256 * 16;
+    const int64_t s_min = (nvec + per_member - 1) / per_member;
     int64_t S = std::max<int64_t>(s_min, rows >= di->cus ? 1 : pow2ceil((di->cus + rows - 1) / rows));
     if (force_split > 1) S = std::max<int64_t>(force_split, s_min);
     if (S > kMaxSplit) return CF_EUNSUPPORTED;
     const int64_t slice_vec = (nvec + S - 1) / S;
     p.split = (int)S;
-    p.nv = pow2ceil((slice_vec + 255) / 256);
-    if (p.nv > 16) return CF_EUNSUPPORTED;
+    p.block = blk;
+    p.nv = blk == 1024 ? (int)std::max<int64_t>(4, pow2ceil((slice_vec + 1023) / 1024)) : pow2ceil((slice_vec + 255) / 256);
+    if (p.nv > (blk == 1024 ? 8 : 16)) return CF_EUNSUPPORTED;
     p.slice = slice_vec * p.w;
-    p.lpr = 256;
+    p.lpr = blk;
     p.rpi = 1;
   }
   const int rows_per_blk = (p.block / p.lpr) * p.rpi;

@@ -312,9 +312,9 @@ __global__ __launch_bounds__(BLOCK) void k_rows(RowArgs a) {
 // no slot read in a launch holds a word from an earlier one (tags restart at
 // 1, and a cleared slot carries tag 0).
 // ---------------------------------------------------------------------------
-template <int OP, int NV, int W>
-__global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
-  constexpr int WAVES = kWaves;
+template <int OP, int NV, int W, int BLOCK = kBlock>
+__global__ __launch_bounds__(BLOCK) void k_rows_split(RowArgs a) {
+  constexpr int WAVES = BLOCK / kWave;
   __shared__ SmPair red2[WAVES];
   __shared__ MomPair red3[WAVES];
   __shared__ float bc[4];
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
     float x[NV][W];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const int64_t c0 = cbeg + (int64_t)(v * kBlock + t) * W;
+      const int64_t c0 = cbeg + (int64_t)(v * BLOCK + t) * W;
       if (c0 < cend) {
         load_frag<W>(x[v], xr + c0);
       } else {
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
       float mloc = -INFINITY;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const int64_t c0 = cbeg + (int64_t)(v * kBlock + t) * W;
+        const int64_t c0 = cbeg + (int64_t)(v * BLOCK + t) * W;
         const bool ok = c0 < cend;
         if constexpr (OP == kPowSoftmax) {
 #pragma unroll
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
       float nl = 0.0f, sx = 0.0f;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const int64_t c0 = cbeg + (int64_t)(v * kBlock + t) * W;
+        const int64_t c0 = cbeg + (int64_t)(v * BLOCK + t) * W;
         if (c0 < cend) nl += (float)W;
 #pragma unroll
         for (int e = 0; e < W; ++e) sx += x[v][e];
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
       float sq = 0.0f;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const int64_t c0 = cbeg + (int64_t)(v * kBlock + t) * W;
+        const int64_t c0 = cbeg + (int64_t)(v * BLOCK + t) * W;
         const bool ok = c0 < cend;
 #pragma unroll
         for (int e = 0; e < W; ++e) {
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
       const float f = (lane_ref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lane_ref - M)) / L;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const int64_t c0 = cbeg + (int64_t)(v * kBlock + t) * W;
+        const int64_t c0 = cbeg + (int64_t)(v * BLOCK + t) * W;
         if (c0 < cend) {
 #pragma unroll
           for (int e = 0; e < W; ++e) x[v][e] *= f;
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(kBlock) void k_rows_split(RowArgs a) {
       constexpr bool GAIN = OP == kLayerNormAffine || OP == kRmsNorm, BIAS = OP == kLayerNormAffine;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const int64_t c0 = cbeg + (int64_t)(v * kBlock + t) * W;
+        const int64_t c0 = cbeg + (int64_t)(v * BLOCK + t) * W;
         if (c0 < cend) {
           float gv[W], bv[W];
           if (GAIN && a.gamma != nullptr) {
@@ -509,13 +509,16 @@ template <int OP, int W>
 static hipError_t launch_rows_w(const RowPlan& pl, const RowArgs& a, hipStream_t st) {
   dim3 grid(pl.grid), block(kBlock);
   // Split plans first: they share (lpr, nv, rpi) with in-workgroup plans.
+  // Members are 256-lane workgroups (up to 16 fragments per lane) or, for
+  // many very wide rows, 1024-lane ones (up to 8).
   if (pl.split > 1) {
-#define CF_SPLIT(NV)                                                                        \
-  if (pl.nv == NV) {                                                                        \
-    hipLaunchKernelGGL((k_rows_split<OP, NV, W>), grid, block, 0, st, a);                   \
+#define CF_SPLIT(BLK, NV)                                                                   \
+  if (pl.block == BLK && pl.nv == NV) {                                                     \
+    hipLaunchKernelGGL((k_rows_split<OP, NV, W, BLK>), grid, dim3(BLK), 0, st, a);          \
     return hipGetLastError();                                                               \
   }
-    CF_SPLIT(1) CF_SPLIT(2) CF_SPLIT(4) CF_SPLIT(8) CF_SPLIT(16)
+    CF_SPLIT(kBlock, 1) CF_SPLIT(kBlock, 2) CF_SPLIT(kBlock, 4) CF_SPLIT(kBlock, 8) CF_SPLIT(kBlock, 16)
+    if constexpr (OP != kLayerNormAffine) { CF_SPLIT(1024, 4) CF_SPLIT(1024, 8) }
 #undef CF_SPLIT
     return hipErrorInvalidConfiguration;
   }
@@ -562,12 +565,20 @@ hipError_t launch_rows(int op, const RowPlan& pl, const RowArgs& a, hipStream_t 
 // Occupancy (resident workgroups per CU) of the split kernel for a plan.
 hipError_t rows_split_occupancy(int op, const RowPlan& pl, int* per_cu) {
 #define CF_OCC(OPV, NV, WV)                                                                 \
-  if (op == OPV && pl.nv == NV && pl.w == WV)                                               \
+  if (op == OPV && pl.nv == NV && pl.w == WV && pl.block == kBlock)                         \
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, k_rows_split<OPV, NV, WV>, kBlock, 0);
+#define CF_OCC_WIDE(OPV, NV, WV)                                                            \
+  if (op == OPV && pl.nv == NV && pl.w == WV && pl.block == 1024)                           \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, k_rows_split<OPV, NV, WV, 1024>, 1024, 0);
 #define CF_OCC_NV(OPV, WV) CF_OCC(OPV, 1, WV) CF_OCC(OPV, 2, WV) CF_OCC(OPV, 4, WV) CF_OCC(OPV, 8, WV) CF_OCC(OPV, 16, WV)
   CF_OCC_NV(kSoftmax, 4) CF_OCC_NV(kLayerNorm, 4) CF_OCC_NV(kPowSoftmax, 4)
   CF_OCC_NV(kSoftmax, 1) CF_OCC_NV(kLayerNorm, 1) CF_OCC_NV(kPowSoftmax, 1)
   CF_OCC_NV(kLayerNormAffine, 4) CF_OCC_NV(kRmsNorm, 4) CF_OCC_NV(kLayerNormAffine, 1) CF_OCC_NV(kRmsNorm, 1)
+#define CF_OCC_W(OPV, WV) CF_OCC_WIDE(OPV, 4, WV) CF_OCC_WIDE(OPV, 8, WV)
+  CF_OCC_W(kSoftmax, 4) CF_OCC_W(kLayerNorm, 4) CF_OCC_W(kPowSoftmax, 4) CF_OCC_W(kRmsNorm, 4)
+  CF_OCC_W(kSoftmax, 1) CF_OCC_W(kLayerNorm, 1) CF_OCC_W(kPowSoftmax, 1) CF_OCC_W(kRmsNorm, 1)
+#undef CF_OCC_W
+#undef CF_OCC_WIDE
 #undef CF_OCC_NV
 #undef CF_OCC
   return hipErrorInvalidConfiguration;

@@ -298,3 +298,26 @@ def test_wide_rows_at_any_row_count(op, rows, cols):
     assert plan["kernel"] == "k_rows" and plan["lanes_per_row"] == 1024 and plan["split"] == 1, plan
     assert plan["frag_floats"] == (1 if cols % 4 else 4), plan
     assert rownorm_err(got, want) <= TOL_F32, plan
+
+
+# Split rows with 1024-lane members (at most 8 fragments per lane): the default for the softmax
+# family on many rows wider than 32768 values; forced for the norms and 4-byte fragments
+SPLIT1024 = [("softmax", 256, 65536, None), ("pow", 128, 40000, None), ("softmax", 300, 70001, "1024"),
+             ("layernorm", 130, 65536, "1024"), ("rmsnorm", 129, 40000, "1024"), ("pow", 3, 70000, "1024")]
+
+
+@pytest.mark.parametrize("op,rows,cols,force", SPLIT1024)
+def test_split_plan_1024_lane_members(monkeypatch, op, rows, cols, force):
+    if force:
+        monkeypatch.setenv("CF_SPLIT_BLOCK", force)
+    x = gen.normal(213, 0, (rows, cols)) if op in ("softmax", "pow") else gen.uniform(213, 0, (rows, cols), -1, 1)
+    ws = cf.Workspace(cf.cf_workspace_bytes({"softmax": cf.CF_OP_STITCH_SOFTMAX, "pow": cf.CF_OP_STITCH_POW_BCAST_ADD,
+                                             "layernorm": cf.CF_OP_STITCH_LAYERNORM,
+                                             "rmsnorm": cf.CF_OP_STITCH_RMSNORM}[op], rows, cols, 0))
+    got, want, plan = _run_rows(op, x, _extra(213, rows, cols), ws=ws)
+    assert plan["kernel"] == "k_rows_split" and plan["block"] == 1024 and plan["split"] > 1, plan
+    assert plan["frag_floats"] == (1 if cols % 4 else 4), plan
+    assert rownorm_err(got, want) <= TOL_F32, plan
+    assert ws.error_word() == 0
+    again, _, _ = _run_rows(op, x, _extra(213, rows, cols), ws=ws)
+    assert np.array_equal(again, got)  # members merge in a fixed order: the same bits on a reused workspace
